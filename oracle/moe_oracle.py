@@ -1,0 +1,346 @@
+"""Plain float64 oracle of the top-k routed MoE FFN layer forward.
+
+TEST INFRASTRUCTURE: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use this module.  It shares no code
+with the HIP library.
+
+What the layer computes, and where it is stated:
+
+* Router logits and top-k routing.  "Sharding d'experts" (Kvasir wiki),
+  section "Deux rôles", backbone x worker pseudo-code: the backbone computes
+  ``top_k(softmax(cur @ router), 8)`` once and its choice is authoritative.
+  moe_stream.py, ``MoEFFN.forward``: ``gate`` is a bias-free linear layer, an
+  optional per-expert bias is added to the logits before the softmax, the
+  softmax runs over all experts, ``topk`` picks the k largest, and the k
+  weights are divided by their sum.
+* Grouping of (token, slot) pairs by expert.  ExpertMesh README, feature list:
+  "activation grouping" that keeps each token's identity and top-k slot.
+  MoEEvolve "Architecture": capacity-factor dispatch with static shapes, so
+  pairs beyond an expert's capacity are dropped.
+* Expert FFN.  kieve-moe "Features": top-k GeGLU experts; MoEEvolve
+  "Architecture": SwiGLU experts and one shared expert that is always active;
+  ExpertMesh runtime list: "INT4 SwiGLU".  The gated form is
+  ``down(act(gate x) * (up x))`` with no biases.
+* Combine.  "Sharding d'experts", "Deux rôles": ``x + combine(p, partials) +
+  shared(cur)``; ExpertMesh data-flow figure: "weighted top-k reduction";
+  moe_stream.py ``MoEFFN.forward``: ``out[mask] += w[mask] * expert_out``.
+* INT4 weights.  ExpertMesh README: group-scaled signed INT4 weights with FP16
+  group scales, laid out ``[expert, output, packed_input]``, plus a bit-exact
+  NumPy quantiser and dequantiser.
+
+Readings taken where the pages are silent (each is listed in the design notes
+of the repository):
+
+* selection is done on the logits (softmax is strictly increasing, so the
+  chosen set is the same as on the probabilities) and ties go to the lower
+  expert id; slot j holds the j-th largest logit;
+* the gate renormalisation has no epsilon;
+* capacity keeps, per expert, the first ``capacity`` pairs in ascending
+  flattened pair index p = t*k + j; dropped pairs contribute nothing and the
+  surviving gates are not renormalised;
+* GeGLU's GELU is the exact erf form; SiLU(g) = g / (1 + exp(-g));
+* the shared expert is added with weight 1 on every token;
+* INT4: per (output row, 128-input group) the scale is
+  ``fp16(fp32(max|w|) / 7)`` (both roundings to nearest-even), the code is
+  ``clip(rint(w / fp32(scale)), -8, 7)`` with the division in float32 and
+  ties to even, an all-zero group (or a scale that rounds to zero) gets code
+  0; byte i of a packed row holds input 2i in its low nibble and 2i+1 in its
+  high nibble, two's complement; the weight is ``float(scale) * code``.
+
+Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
+against closed forms, library routines, brute force and invariants.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+INT4_GROUP = 128
+
+
+# --------------------------------------------------------------------------
+# Routing
+# --------------------------------------------------------------------------
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """``L[t, e] = sum_i x[t, i] * Wr[e, i] + b[e]`` in float64.
+
+    "Sharding d'experts", "Deux rôles": ``cur @ router``; moe_stream.py
+    ``MoEFFN.forward``: bias-free ``gate`` linear layer plus the optional
+    per-expert bias added before the softmax.
+    """
+    L = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if bias is not None:
+        L = L + np.asarray(bias, np.float64)[None, :]
+    return L
+
+
+def select_topk(L, k: int) -> np.ndarray:
+    """The k largest logits of each row, largest first, ties to the lower id.
+
+    moe_stream.py ``MoEFFN.forward`` (``torch.topk`` of the softmax, which is
+    sorted); the tie rule is this build's reading.  Done as k rounds of
+    "take the first position of the row maximum, then strike it out".
+    """
+    L = np.asarray(L, np.float64)
+    T, E = L.shape
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    work = L.copy()
+    ids = np.empty((T, k), np.int64)
+    rows = np.arange(T)
+    for j in range(k):
+        e = np.argmax(work, axis=1)  # first occurrence of the maximum
+        ids[:, j] = e
+        work[rows, e] = -np.inf
+    return ids
+
+
+def gates(L, ids, renorm: bool) -> np.ndarray:
+    """Gate of each selected slot.
+
+    ``pi = softmax(L)`` over all experts (max-subtracted); the gate is
+    ``pi[t, ids[t, j]]``, divided by the sum over the k selected when
+    ``renorm`` (moe_stream.py ``MoEFFN.forward``), or used as is (the ``p`` of
+    the "Deux rôles" pseudo-code).
+    """
+    L = np.asarray(L, np.float64)
+    m = L.max(axis=1, keepdims=True)
+    ex = np.exp(L - m)
+    pi = ex / ex.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(pi, np.asarray(ids), axis=1)
+    if renorm:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
+def route(k: int, renorm: bool, x=None, w_router=None, bias=None, logits=None):
+    """Router step: returns (L, ids, w).  ``logits`` replaces the GEMM when given
+    (a share that receives its routing from upstream, as in the ExpertMesh
+    data-flow figure where the router sits before the dispatcher).  A bias is
+    added to given logits too."""
+    if logits is not None:
+        L = np.asarray(logits, np.float64)
+        if bias is not None:
+            L = L + np.asarray(bias, np.float64)[None, :]
+    else:
+        L = router_logits(x, w_router, bias)
+    ids = select_topk(L, k)
+    return L, ids, gates(L, ids, renorm)
+
+
+# --------------------------------------------------------------------------
+# Grouping of (token, slot) pairs by expert
+# --------------------------------------------------------------------------
+def permute(ids, expert_map=None, E_loc: Optional[int] = None, capacity: int = 0):
+    """Group the flattened pairs p = t*k + j by (local) expert.
+
+    Returns ``offsets [E_loc+1]``, ``sorted_pair [n_kept]`` (the pair index of
+    each grouped row) and ``pair_pos [T*k]`` (row of each pair, -1 when the pair
+    is dropped or its expert is not local).  Inside an expert, rows follow
+    ascending p; with ``capacity > 0`` only the first ``capacity`` of them are
+    kept (ExpertMesh feature list: grouping that keeps token and slot identity;
+    MoEEvolve "Architecture": capacity-factor dispatch).
+    """
+    ids = np.asarray(ids)
+    flat = ids.reshape(-1).astype(np.int64)
+    if expert_map is not None:
+        emap = np.asarray(expert_map, np.int64)
+        loc = emap[flat]
+        if E_loc is None:
+            E_loc = int(emap.max()) + 1
+    else:
+        loc = flat
+        if E_loc is None:
+            raise ValueError("E_loc is required without an expert map")
+    if capacity < 0:
+        raise ValueError("capacity must be >= 0")
+    P = flat.size
+    pair_pos = np.full(P, -1, np.int64)
+    offsets = np.zeros(E_loc + 1, np.int64)
+    groups = []
+    for e in range(E_loc):
+        members = np.nonzero(loc == e)[0]  # ascending p
+        if capacity > 0:
+            members = members[:capacity]
+        groups.append(members)
+        offsets[e + 1] = offsets[e] + members.size
+    sorted_pair = np.concatenate(groups) if groups else np.zeros(0, np.int64)
+    for e in range(E_loc):
+        pair_pos[groups[e]] = offsets[e] + np.arange(groups[e].size)
+    return offsets, sorted_pair.astype(np.int64), pair_pos
+
+
+# --------------------------------------------------------------------------
+# Expert FFN
+# --------------------------------------------------------------------------
+def silu(g):
+    """SiLU(g) = g / (1 + exp(-g)) (the SwiGLU gate of MoEEvolve's experts)."""
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def gelu_erf(g):
+    """Exact GELU, g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)) (kieve-moe's GeGLU;
+    moe_stream.py's experts use the default, exact form of ``nn.GELU``)."""
+    g = np.asarray(g, np.float64)
+    return 0.5 * g * (1.0 + _erf(g / np.sqrt(2.0)))
+
+
+_ACTS = {"swiglu": silu, "geglu": gelu_erf}
+
+
+def gated_ffn(a, wg, wu, wd, act: str) -> np.ndarray:
+    """``y = Wd (act(Wg a) * (Wu a))`` for each row a; weights ``[out, in]``.
+
+    Three matrices per expert (the kieve-moe "Parametric sizing" flagship,
+    15 layers x 32 experts of H=768, I=4096, is 4.5B parameters only with three
+    matrices per expert)."""
+    a = np.asarray(a, np.float64)
+    g = a @ np.asarray(wg, np.float64).T
+    u = a @ np.asarray(wu, np.float64).T
+    z = _ACTS[act](g) * u
+    return z @ np.asarray(wd, np.float64).T
+
+
+# --------------------------------------------------------------------------
+# Signed INT4 with fp16 group scales
+# --------------------------------------------------------------------------
+def pack_int4(q) -> np.ndarray:
+    """int codes [N, K] in [-8, 7] -> bytes [N, K/2]; input 2i in the low nibble."""
+    q = np.asarray(q)
+    if q.shape[-1] % 2:
+        raise ValueError("K must be even")
+    if q.min(initial=0) < -8 or q.max(initial=0) > 7:
+        raise ValueError("codes out of the signed 4-bit range")
+    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed) -> np.ndarray:
+    """bytes [N, K/2] -> int8 codes [N, K] (two's complement nibbles)."""
+    b = np.asarray(packed, np.uint8)
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def quantize_int4(w):
+    """float32 weights [..., N, K] -> (packed uint8 [..., N, K/2], scales float16 [..., N, K/128]).
+
+    Per output row and 128-input group: ``s = fp16(fp32(max|w|) / 7)``,
+    ``q = clip(rint(w / fp32(s)), -8, 7)`` (float32 division, ties to even);
+    a zero scale gives code 0."""
+    w32 = np.asarray(w, np.float32)
+    K = w32.shape[-1]
+    if K % INT4_GROUP:
+        raise ValueError("K must be a multiple of 128")
+    grp = w32.reshape(w32.shape[:-1] + (K // INT4_GROUP, INT4_GROUP))
+    amax = np.abs(grp).max(axis=-1)                     # exact in float32
+    s16 = (amax / np.float32(7.0)).astype(np.float16)   # float32 divide, then RNE to fp16
+    sf = s16.astype(np.float32)[..., None]
+    safe = np.where(sf > 0, sf, np.float32(1.0))
+    q = np.where(sf > 0, np.rint(grp / safe), np.float32(0.0))  # float32 divide, rint = ties-to-even
+    q = np.clip(q, -8, 7).astype(np.int8).reshape(w32.shape)
+    return pack_int4(q), s16
+
+
+def dequantize_int4(packed, scales) -> np.ndarray:
+    """(packed [..., N, K/2], fp16 scales [..., N, K/128]) -> float64 ``scale * code``."""
+    q = unpack_int4(packed).astype(np.float64)
+    s = np.asarray(scales, np.float16).astype(np.float64)
+    K = q.shape[-1]
+    return (q.reshape(q.shape[:-1] + (K // INT4_GROUP, INT4_GROUP)) * s[..., None]).reshape(q.shape)
+
+
+# --------------------------------------------------------------------------
+# Output rounding
+# --------------------------------------------------------------------------
+def round_to_dtype(v, dt: str) -> np.ndarray:
+    """Round float64 values once, to nearest-even, to ``dt`` ("f32" | "bf16"),
+    returned as float64."""
+    v = np.asarray(v, np.float64)
+    if dt == "f64":
+        return v.copy()
+    if dt == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if dt == "bf16":
+        _, e = np.frexp(v)
+        e = np.maximum(e, -125)           # below bf16's normal range the spacing stays 2**-133
+        return np.ldexp(np.rint(np.ldexp(v, 8 - e)), e - 8)
+    raise ValueError(dt)
+
+
+# --------------------------------------------------------------------------
+# The layer
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class LayerWeights:
+    """Local expert weights in float64, or INT4 packed codes and fp16 scales."""
+    wg: Optional[np.ndarray] = None       # [E_loc, h, d]
+    wu: Optional[np.ndarray] = None
+    wd: Optional[np.ndarray] = None       # [E_loc, d, h]
+    qg: Optional[tuple] = None            # (packed [E_loc, h, d/2], scales [E_loc, h, d/128])
+    qu: Optional[tuple] = None
+    qd: Optional[tuple] = None            # (packed [E_loc, d, h/2], scales [E_loc, d, h/128])
+
+    @property
+    def E_loc(self) -> int:
+        return (self.wg if self.wg is not None else self.qg[0]).shape[0]
+
+    def expert(self, e: int):
+        if self.wg is not None:
+            return self.wg[e], self.wu[e], self.wd[e]
+        return (dequantize_int4(self.qg[0][e], self.qg[1][e]),
+                dequantize_int4(self.qu[0][e], self.qu[1][e]),
+                dequantize_int4(self.qd[0][e], self.qd[1][e]))
+
+
+def moe_layer(x, weights: LayerWeights, k: int, renorm: bool, act: str, *,
+              w_router=None, logits=None, bias=None, expert_map=None, capacity: int = 0,
+              shared: Optional[Sequence] = None, tokens=None, ids=None):
+    """Forward pass of the layer (float64, not rounded).
+
+    ``out[t] = sum_{j: pair kept} w[t, j] * y[t*k + j] + shared(x[t])``, the
+    sum taken in ascending slot order, ``y`` being the pair's expert FFN of
+    ``x[t]`` (the combine of the "Deux rôles" pseudo-code).  ``tokens``
+    restricts the output to those rows (routing and capacity still look at all
+    tokens).  ``ids`` overrides the selection (gates are then taken from the
+    oracle's own logits at those ids).
+    Returns a dict with ``out`` and the routing intermediates.
+    """
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    L, ids_o, w = route(k, renorm, x=x, w_router=w_router, bias=bias, logits=logits)
+    if ids is not None:
+        ids_o = np.asarray(ids, np.int64)
+        w = gates(L, ids_o, renorm)
+    E_loc = weights.E_loc
+    offsets, sorted_pair, pair_pos = permute(ids_o, expert_map, E_loc, capacity)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    want = np.zeros(T, bool)
+    want[toks] = True
+    Y = np.zeros((T, k, d), np.float64)
+    for e in range(E_loc):
+        rows = sorted_pair[offsets[e]:offsets[e + 1]]
+        rows = rows[want[rows // k]]
+        if rows.size == 0:
+            continue
+        wg, wu, wd = weights.expert(e)
+        Y[rows // k, rows % k] = gated_ffn(x[rows // k], wg, wu, wd, act)
+    kept = (pair_pos >= 0).reshape(T, k)
+    out = np.zeros((toks.size, d), np.float64)
+    for j in range(k):
+        out += np.where(kept[toks, j], w[toks, j], 0.0)[:, None] * Y[toks, j]
+    if shared is not None:
+        out += gated_ffn(x[toks], shared[0], shared[1], shared[2], act)
+    return {"out": out, "L": L, "ids": ids_o, "w": w, "offsets": offsets,
+            "sorted_pair": sorted_pair, "pair_pos": pair_pos, "tokens": toks}

@@ -1,0 +1,62 @@
+"""Readers for the hand-worked fixtures under tests/golden/."""
+import math
+import os
+from fractions import Fraction
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln and not ln.startswith("#"):
+                yield ln
+
+
+def _logit(tok):
+    neg = tok.startswith("-")
+    t = tok[1:] if neg else tok
+    v = math.log(float(t[3:-1])) if t.startswith("ln(") else float(t)
+    return -v if neg else v
+
+
+def route_cases():
+    cases, cur = [], {}
+    for ln in _lines("route_worked_example.txt"):
+        key, _, val = ln.partition(":")
+        toks = val.split()
+        if key == "logits":
+            cur = {"logits": [_logit(t) for t in toks]}
+            cases.append(cur)
+        elif key == "k":
+            cur["k"] = int(toks[0])
+        elif key == "ids":
+            cur["ids"] = [int(t) for t in toks]
+        else:
+            cur[key] = [float(Fraction(t)) for t in toks]
+    return cases
+
+
+def int4_case():
+    out = {}
+    for ln in _lines("int4_worked_example.txt"):
+        key, _, val = ln.partition(":")
+        toks = val.split()
+        if key.endswith("_w"):
+            out[key] = [float(t) for t in toks]
+        elif key.endswith("_scale_bits"):
+            out[key] = int(toks[0], 16)
+        elif key.endswith("_codes"):
+            out[key] = [int(t) for t in toks]
+        elif key.endswith("_bytes"):
+            out[key] = [int(t, 16) for t in toks]
+    return out
+
+
+def activation_points():
+    pts = []
+    for ln in _lines("activations.txt"):
+        name, g, v = ln.split()
+        pts.append((name, float(g), float(v)))
+    return pts

@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks one oracle function against a hand-worked fixture, a closed
+form, a library routine, brute force on tiny inputs, or an invariant of the
+method, chosen so that a dropped term, a wrong sign or index, or a transposed
+operand fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as orc
+from golden_io import activation_points, int4_case, route_cases
+
+RNG = np.random.default_rng(1234)
+
+
+def _rand_layer(T, d, E, k, h, *, E_loc=None, dtype=np.float64, shared_h=0, seed=0):
+    rng = np.random.default_rng(seed)
+    E_loc = E if E_loc is None else E_loc
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / np.sqrt(d)
+    W = orc.LayerWeights(wg=rng.standard_normal((E_loc, h, d)) / np.sqrt(d),
+                         wu=rng.standard_normal((E_loc, h, d)) / np.sqrt(d),
+                         wd=rng.standard_normal((E_loc, d, h)) / np.sqrt(h))
+    shared = None
+    if shared_h:
+        shared = (rng.standard_normal((shared_h, d)) / np.sqrt(d),
+                  rng.standard_normal((shared_h, d)) / np.sqrt(d),
+                  rng.standard_normal((d, shared_h)) / np.sqrt(shared_h))
+    return x, wr, W, shared
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("case", route_cases())
+def test_route_worked_examples(case):
+    L = np.array([case["logits"]])
+    ids = orc.select_topk(L, case["k"])
+    assert ids[0].tolist() == case["ids"]
+    np.testing.assert_allclose(orc.gates(L, ids, True)[0], case["w_renorm"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(orc.gates(L, ids, False)[0], case["w_raw"], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 2), (192, 4), (128, 8), (896, 16), (5, 5)])
+def test_selection_equals_stable_sort(E, k):
+    # integer-valued logits from a small range: many exact ties
+    L = RNG.integers(-3, 4, size=(300, E)).astype(np.float64)
+    ref = np.argsort(-L, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(orc.select_topk(L, k), ref)
+    L2 = RNG.standard_normal((200, E))
+    np.testing.assert_array_equal(orc.select_topk(L2, k),
+                                  np.argsort(-L2, axis=1, kind="stable")[:, :k])
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 4, 5, 6])
+def test_selection_brute_force_over_subsets(E):
+    for k in range(1, E + 1):
+        for _ in range(40):
+            row = RNG.integers(0, 3, size=E).astype(np.float64)
+
+            def beats(a, b):
+                return row[a] > row[b] or (row[a] == row[b] and a < b)
+            winners = [S for S in itertools.combinations(range(E), k)
+                       if all(beats(s, o) for s in S for o in range(E) if o not in S)]
+            assert len(winners) == 1
+            S = sorted(winners[0], key=lambda e: (-row[e], e))
+            assert orc.select_topk(row[None, :], k)[0].tolist() == S
+
+
+def test_gates_closed_forms_and_invariants():
+    for E, k in [(8, 2), (192, 4), (128, 8), (896, 16)]:
+        L = RNG.standard_normal((100, E)) * 3
+        ids = orc.select_topk(L, k)
+        sel = np.take_along_axis(L, ids, axis=1)
+        w_r = orc.gates(L, ids, True)
+        w_n = orc.gates(L, ids, False)
+        # renormalised gates = softmax over the selected logits only (library softmax)
+        np.testing.assert_allclose(w_r, scipy.special.softmax(sel, axis=1), rtol=1e-14, atol=1e-16)
+        # raw gates = the selected entries of the full softmax (library softmax)
+        np.testing.assert_allclose(w_n, np.take_along_axis(scipy.special.softmax(L, axis=1), ids, 1),
+                                   rtol=1e-14, atol=1e-18)
+        np.testing.assert_allclose(w_r.sum(1), 1.0, rtol=0, atol=1e-14)
+        assert np.all(np.diff(w_r, axis=1) <= 0) and np.all(np.diff(w_n, axis=1) <= 0)
+        assert np.all(w_n.sum(1) <= 1 + 1e-14)
+    # k = E: raw gates are the whole softmax and sum to one
+    L = RNG.standard_normal((50, 7))
+    assert np.allclose(orc.gates(L, orc.select_topk(L, 7), False).sum(1), 1.0, atol=1e-14)
+
+
+def test_bias_shifts_logits_before_selection():
+    x = RNG.standard_normal((20, 16))
+    wr = RNG.standard_normal((6, 16))
+    b = np.array([0, 0, 100.0, 0, 0, 0])
+    L, ids, w = orc.route(2, True, x=x, w_router=wr, bias=b)
+    assert np.all(ids[:, 0] == 2)  # a huge bias wins every token
+    np.testing.assert_allclose(L, x @ wr.T + b, rtol=1e-14, atol=1e-12)
+
+
+def test_zero_input_special_case():
+    T, d, E, k, h = 16, 32, 8, 3, 16
+    _, wr, W, shared = _rand_layer(T, d, E, k, h, shared_h=8)
+    x = np.zeros((T, d))
+    for renorm, g in [(True, 1 / k), (False, 1 / E)]:
+        r = orc.moe_layer(x, W, k, renorm, "swiglu", w_router=wr, shared=shared)
+        assert np.all(r["ids"] == np.arange(k))
+        np.testing.assert_allclose(r["w"], g, rtol=1e-15)
+        assert np.all(r["out"] == 0.0)
+
+
+# ---------------------------------------------------------------- permutation
+@pytest.mark.parametrize("T,k,E,owners", [(64, 2, 8, 1), (333, 4, 192, 1), (512, 16, 896, 32),
+                                          (100, 8, 128, 4)])
+def test_permutation_equals_stable_sort(T, k, E, owners):
+    L = RNG.standard_normal((T, E))
+    ids = orc.select_topk(L, k)
+    emap = np.full(E, -1)
+    mine = np.arange(0, E, owners)
+    emap[mine] = np.arange(mine.size)
+    E_loc = mine.size
+    offsets, sp, pos = orc.permute(ids, emap if owners > 1 else None, E_loc)
+    loc = emap[ids.reshape(-1)]
+    order = np.argsort(np.where(loc < 0, E_loc, loc), kind="stable")  # library stable sort
+    n_kept = int((loc >= 0).sum())
+    np.testing.assert_array_equal(sp, order[:n_kept])
+    np.testing.assert_array_equal(np.diff(offsets), np.bincount(loc[loc >= 0], minlength=E_loc))
+    assert offsets[-1] == n_kept
+    np.testing.assert_array_equal(pos[sp], np.arange(n_kept))
+    assert np.all(pos[loc < 0] == -1)
+
+
+def test_permutation_capacity_invariants():
+    T, k, E, cap = 500, 4, 16, 97
+    ids = orc.select_topk(RNG.standard_normal((T, E)) + np.linspace(2, 0, E), k)
+    offsets, sp, pos = orc.permute(ids, None, E, cap)
+    cnt = np.bincount(ids.reshape(-1), minlength=E)
+    np.testing.assert_array_equal(np.diff(offsets), np.minimum(cnt, cap))
+    assert np.all(np.diff(offsets) >= 0)
+    for e in range(E):
+        rows = sp[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(rows) > 0)                    # ascending p inside an expert
+        assert np.all(ids.reshape(-1)[rows] == e)
+    np.testing.assert_array_equal(pos[sp], np.arange(sp.size))
+    assert (pos >= 0).sum() == sp.size
+
+
+def test_capacity_brute_force_sequential_dispatch():
+    # exhaustive over tiny cases: a sequential per-expert counter that admits
+    # a pair while its expert has room (static-capacity dispatch in token order)
+    E, k = 3, 2
+    choices = list(itertools.permutations(range(E), k))
+    for T in (1, 2, 3):
+        for combo in itertools.product(choices, repeat=T):
+            ids = np.array(combo)
+            for cap in (0, 1, 2, 3):
+                counter = [0] * E
+                expect = []
+                for p, e in enumerate(ids.reshape(-1)):
+                    if cap == 0 or counter[e] < cap:
+                        counter[e] += 1
+                        expect.append(True)
+                    else:
+                        expect.append(False)
+                _, _, pos = orc.permute(ids, None, E, cap)
+                assert (pos >= 0).tolist() == expect
+
+
+# ---------------------------------------------------------------- expert FFN
+@pytest.mark.parametrize("name,g,v", activation_points())
+def test_activation_textbook_points(name, g, v):
+    f = orc.silu if name == "silu" else orc.gelu_erf
+    assert abs(float(f(g)) - v) <= 2e-16 * max(1.0, abs(v))
+
+
+def test_activations_equal_torch_float64():
+    g = np.linspace(-30, 30, 10001)
+    tg = torch.from_numpy(g)
+    np.testing.assert_allclose(orc.silu(g), torch.nn.functional.silu(tg).numpy(), rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(orc.gelu_erf(g), torch.nn.functional.gelu(tg).numpy(), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+def test_single_expert_is_a_dense_gated_mlp(act):
+    # E = 1, k = 1: every token goes to the one expert with gate 1
+    T, d, h = 40, 24, 48
+    x, wr, W, _ = _rand_layer(T, d, 1, 1, h)
+    r = orc.moe_layer(x, W, 1, True, act, w_router=wr)
+    tx = torch.from_numpy(x)
+    a = torch.nn.functional.silu if act == "swiglu" else torch.nn.functional.gelu
+    ref = torch.nn.functional.linear(
+        a(torch.nn.functional.linear(tx, torch.from_numpy(W.wg[0])))
+        * torch.nn.functional.linear(tx, torch.from_numpy(W.wu[0])), torch.from_numpy(W.wd[0]))
+    np.testing.assert_allclose(r["out"], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_k_equals_E_is_the_full_softmax_mixture():
+    T, d, E, h = 30, 16, 5, 12
+    x, wr, W, _ = _rand_layer(T, d, E, E, h)
+    r = orc.moe_layer(x, W, E, True, "swiglu", w_router=wr)
+    pi = scipy.special.softmax(x @ wr.T, axis=1)
+    ys = np.stack([orc.gated_ffn(x, W.wg[e], W.wu[e], W.wd[e], "swiglu") for e in range(E)], 1)
+    np.testing.assert_allclose(r["out"], (pi[:, :, None] * ys).sum(1), rtol=1e-11, atol=1e-12)
+
+
+def _dense_masked(x, wr, W, k, renorm, act, bias=None, shared=None, keep=None):
+    """All experts on all tokens, times a [T, E] gate matrix that is zero off the top-k."""
+    L = x @ wr.T + (0 if bias is None else bias)
+    E = L.shape[1]
+    ids = np.argsort(-L, axis=1, kind="stable")[:, :k]
+    pi = scipy.special.softmax(L, axis=1)
+    G = np.zeros_like(L)
+    np.put_along_axis(G, ids, np.take_along_axis(pi, ids, 1), 1)
+    if renorm:
+        G = G / G.sum(1, keepdims=True)
+    if keep is not None:
+        G = G * keep
+    out = np.zeros_like(x)
+    for e in range(E):
+        out += G[:, e:e + 1] * orc.gated_ffn(x, W.wg[e], W.wu[e], W.wd[e], act)
+    if shared is not None:
+        out += orc.gated_ffn(x, *shared, act)
+    return out
+
+
+@pytest.mark.parametrize("renorm,act", [(True, "swiglu"), (False, "swiglu"), (True, "geglu")])
+def test_sparse_equals_dense_masked(renorm, act):
+    T, d, E, k, h = 256, 64, 8, 2, 128
+    x, wr, W, shared = _rand_layer(T, d, E, k, h, shared_h=32)
+    bias = -1.1 * np.log1p(np.arange(E))
+    r = orc.moe_layer(x, W, k, renorm, act, w_router=wr, bias=bias, shared=shared)
+    ref = _dense_masked(x, wr, W, k, renorm, act, bias=bias, shared=shared)
+    assert np.abs(r["out"] - ref).max() <= 1e-12 * np.sqrt((ref ** 2).mean())
+
+
+def test_sparse_equals_dense_masked_with_capacity():
+    T, d, E, k, h, cap = 120, 16, 6, 2, 8, 30
+    x, wr, W, _ = _rand_layer(T, d, E, k, h)
+    r = orc.moe_layer(x, W, k, True, "swiglu", w_router=wr, capacity=cap)
+    # keep mask from a sequential per-expert counter in token order
+    ids = np.argsort(-(x @ wr.T), axis=1, kind="stable")[:, :k]
+    keep = np.zeros((T, E))
+    cnt = np.zeros(E, int)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            if cnt[e] < cap:
+                keep[t, e] = 1
+                cnt[e] += 1
+    ref = _dense_masked(x, wr, W, k, True, "swiglu", keep=keep)
+    assert np.abs(r["out"] - ref).max() <= 1e-12 * np.sqrt((ref ** 2).mean())
+
+
+def test_sum_over_owner_shares_equals_full_layer():
+    T, d, E, k, h, owners = 64, 32, 64, 8, 16, 32
+    x, wr, W, _ = _rand_layer(T, d, E, k, h)
+    full = orc.moe_layer(x, W, k, True, "swiglu", w_router=wr)["out"]
+    acc = np.zeros_like(full)
+    for o in range(owners):
+        mine = np.arange(o, E, owners)
+        emap = np.full(E, -1)
+        emap[mine] = np.arange(mine.size)
+        Wo = orc.LayerWeights(wg=W.wg[mine], wu=W.wu[mine], wd=W.wd[mine])
+        acc += orc.moe_layer(x, Wo, k, True, "swiglu", w_router=wr, expert_map=emap)["out"]
+    assert np.abs(acc - full).max() <= 1e-12 * np.sqrt((full ** 2).mean())
+
+
+def test_token_subset_matches_full_rows():
+    T, d, E, k, h = 90, 16, 6, 2, 8
+    x, wr, W, shared = _rand_layer(T, d, E, k, h, shared_h=8)
+    full = orc.moe_layer(x, W, k, True, "swiglu", w_router=wr, capacity=25, shared=shared)["out"]
+    sub = [0, 7, 33, 89]
+    part = orc.moe_layer(x, W, k, True, "swiglu", w_router=wr, capacity=25, shared=shared,
+                         tokens=sub)["out"]
+    np.testing.assert_allclose(part, full[sub], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_force_layer(x, wr, W, k, renorm, act, capacity, shared):
+    """Pure-Python loops, following moe_stream.py's per-expert mask / gather /
+    scatter-add formulation of MoEFFN.forward."""
+    T, d = len(x), len(x[0])
+    E = len(wr)
+
+    def dot(a, b):
+        return sum(ai * bi for ai, bi in zip(a, b))
+
+    def actf(g):
+        return g / (1 + math.exp(-g)) if act == "swiglu" else 0.5 * g * (1 + math.erf(g / math.sqrt(2)))
+
+    def ffn(a, wg, wu, wd):
+        z = [actf(dot(wg[n], a)) * dot(wu[n], a) for n in range(len(wg))]
+        return [dot(wd[i], z) for i in range(len(wd))]
+
+    top_idx, top_w = [], []
+    for t in range(T):
+        L = [dot(x[t], wr[e]) for e in range(E)]
+        m = max(L)
+        ex = [math.exp(v - m) for v in L]
+        s = sum(ex)
+        p = [v / s for v in ex]
+        chosen = []
+        for _ in range(k):
+            best = None
+            for e in range(E):
+                if e in chosen:
+                    continue
+                if best is None or L[e] > L[best]:
+                    best = e
+            chosen.append(best)
+        w = [p[e] for e in chosen]
+        if renorm:
+            sw = sum(w)
+            w = [v / sw for v in w]
+        top_idx.append(chosen)
+        top_w.append(w)
+    kept = [[True] * k for _ in range(T)]
+    if capacity:
+        cnt = [0] * E
+        for t in range(T):
+            for j in range(k):
+                e = top_idx[t][j]
+                kept[t][j] = cnt[e] < capacity
+                cnt[e] += kept[t][j]
+    out = [[0.0] * d for _ in range(T)]
+    for i in range(E):
+        for t in range(T):
+            w = sum(top_w[t][j] for j in range(k) if top_idx[t][j] == i and kept[t][j])
+            if any(top_idx[t][j] == i and kept[t][j] for j in range(k)):
+                y = ffn(x[t], W.wg[i].tolist(), W.wu[i].tolist(), W.wd[i].tolist())
+                for c in range(d):
+                    out[t][c] += w * y[c]
+    if shared is not None:
+        for t in range(T):
+            y = ffn(x[t], *(m.tolist() for m in shared))
+            for c in range(d):
+                out[t][c] += y[c]
+    return np.array(out)
+
+
+@pytest.mark.parametrize("renorm,act,cap,sh", [(True, "swiglu", 0, 0), (False, "geglu", 0, 4),
+                                               (True, "swiglu", 3, 4)])
+def test_vectorised_oracle_equals_pure_python_loops(renorm, act, cap, sh):
+    T, d, E, k, h = 12, 6, 5, 2, 4
+    x, wr, W, shared = _rand_layer(T, d, E, k, h, shared_h=sh, seed=7)
+    r = orc.moe_layer(x, W, k, renorm, act, w_router=wr, capacity=cap, shared=shared)
+    ref = _brute_force_layer(x.tolist(), wr.tolist(), W, k, renorm, act, cap, shared)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- INT4
+def test_int4_worked_example():
+    c = int4_case()
+    w = np.zeros((1, 384), np.float32)
+    for g in range(3):
+        vals = c[f"group{g}_w"]
+        w[0, 128 * g:128 * g + len(vals)] = vals
+    packed, scales = orc.quantize_int4(w)
+    codes = orc.unpack_int4(packed)[0]
+    for g in range(3):
+        assert int(scales[0, g].view(np.uint16)) == c[f"group{g}_scale_bits"]
+        n = len(c[f"group{g}_codes"])
+        assert codes[128 * g:128 * g + n].tolist() == c[f"group{g}_codes"]
+        assert np.all(codes[128 * g + n:128 * (g + 1)] == 0)
+        nb = len(c[f"group{g}_bytes"])
+        assert packed[0, 64 * g:64 * g + nb].tolist() == c[f"group{g}_bytes"]
+        assert np.all(packed[0, 64 * g + nb:64 * (g + 1)] == 0)
+    deq = orc.dequantize_int4(packed, scales)
+    assert deq[0, 0] == 0.875 and deq[0, 1] == 0.25 and deq[0, 5] == -0.875
+    assert deq[0, 256] == 7 * 0.142822265625
+
+
+def test_int4_pack_unpack_all_bytes():
+    b = np.arange(256, dtype=np.uint8)[None, :]
+    q = orc.unpack_int4(b)
+    assert q.min() == -8 and q.max() == 7
+    np.testing.assert_array_equal(orc.pack_int4(q), b)
+    # byte 0x8f: low nibble 0xf = -1, high nibble 0x8 = -8
+    assert orc.unpack_int4(np.array([[0x8F]], np.uint8)).tolist() == [[-1, -8]]
+
+
+def test_int4_quantise_dequantise_round_trip_is_bit_exact():
+    w = (np.random.default_rng(5).standard_normal((256, 7168)) / np.sqrt(7168)).astype(np.float32)
+    p1, s1 = orc.quantize_int4(w)
+    deq = orc.dequantize_int4(p1, s1)
+    # dequantised weights are exact in float32 (11-bit significand times |q| <= 8)
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
+    p2, s2 = orc.quantize_int4(deq.astype(np.float32))
+    assert np.array_equal(p1, p2) and np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
+    q = orc.unpack_int4(p1).reshape(256, 56, 128)
+    assert np.all(np.abs(q).max(-1) == 7) and q.min() > -8
+    # the scale is the float32 max|w|/7 rounded once to fp16: within half an fp16 ulp
+    amax = np.abs(w.reshape(256, 56, 128)).max(-1).astype(np.float64)
+    s = s1.astype(np.float64)
+    ulp = np.spacing(s.astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(s - amax / 7) <= 0.5 * ulp + 1e-12 * s)
+
+
+def test_int4_zero_and_tiny_groups():
+    w = np.zeros((2, 256), np.float32)
+    w[1, :128] = 1e-9      # max/7 underflows fp16 to zero: codes must be 0
+    p, s = orc.quantize_int4(w)
+    assert np.all(p == 0) and np.all(s == 0)
+
+
+# ---------------------------------------------------------------- rounding
+def test_round_bf16_matches_torch_on_float32_values():
+    v = RNG.standard_normal(100000).astype(np.float32) * np.float32(10.0) ** RNG.integers(-30, 30, 100000)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_to_dtype(v.astype(np.float64), "bf16"), ref)
+
+
+def test_round_bf16_ties_and_single_rounding():
+    r = orc.round_to_dtype(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, -(1 + 2 ** -8)]), "bf16")
+    # ties go to even; a float64 value just above a tie rounds up (no detour via float32)
+    assert r.tolist() == [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0]
