@@ -1,0 +1,263 @@
+/*
+ * moe_lds.h - C ABI of the top-k routed Mixture-of-Experts FFN layer forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (forward only) runs in five steps, each a call below:
+ *   moe_route       router logits GEMM, softmax and top-k selection
+ *   moe_permute     grouping of (token, slot) pairs by expert
+ *   moe_expert_ffn  grouped gated expert GEMMs (SwiGLU / GeGLU; bf16, fp32 or
+ *                   signed INT4 with fp16 group scales)
+ *   moe_combine     weighted top-k combine plus the optional shared expert
+ *   moe_layer_fwd   all of the above, fused where it pays, on one stream
+ *
+ * Sources of the operation (web pages; section named where the page has one):
+ *   "Sharding d'experts" (Kvasir wiki), section "Deux roles": the backbone x
+ *     worker cut  ids,p = top_k(softmax(cur @ router), k); the worker's
+ *     "3 mat-muls"; x + combine(p, partials) + shared(cur).
+ *   moe_stream.py (MoE-Stream), MoEFFN.forward: bias-free router, optional
+ *     per-expert logit bias before the softmax, softmax over all experts, topk,
+ *     division of the k gates by their sum, per-expert gather / scatter-add.
+ *   MoEEvolve, "Architecture": SwiGLU experts, one always-active shared
+ *     expert, capacity-factor static-shape dispatch.
+ *   kieve-moe, "Features": top-k GeGLU experts.
+ *   ExpertMesh README: group-scaled signed INT4 weights with FP16 group
+ *     scales in the [expert, output, packed_input] layout, a stable C ABI,
+ *     activation grouping that keeps token and top-k slot identity, and a
+ *     weighted top-k reduction.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers unless stated otherwise; the
+ *     caller owns every buffer (inputs, outputs, workspace).  The library never
+ *     allocates or frees memory, keeps no pointer after returning and has no
+ *     mutable global state; calls on different streams may run concurrently.
+ *   - Arrays are dense and row-major; weight matrices are [out, in].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; no call synchronises the device or reads device memory
+ *     on the host.
+ *   - Every call returns MOE_OK (0) or a negative error code.  Arguments are
+ *     validated before anything is enqueued, so an error never leaves a
+ *     partial launch behind; MOE_EHIP reports a failed launch (text via
+ *     moe_last_error()).
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ *   - bf16 values are passed as their 16-bit patterns (uint16 storage);
+ *     fp16 scales likewise.
+ *
+ * Limits (MOE_EUNSUPPORTED beyond them): 1 <= k <= min(E, 32), E <= 1024,
+ * E_loc <= E, d and h multiples of 64 (of 128 for INT4 weights), T*k < 2^31.
+ */
+#ifndef MOE_LDS_H
+#define MOE_LDS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ---------------------------------------------------- */
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* null required pointer, negative size, k > E, ... */
+  MOE_EUNSUPPORTED = -2,  /* dtype/activation mix or shape outside the limits */
+  MOE_EWORKSPACE = -3,    /* ws_bytes below the matching *_workspace_bytes()  */
+  MOE_EHIP = -4           /* a HIP launch failed                              */
+};
+
+/* ---- element types -------------------------------------------------- */
+enum moe_dtype {
+  MOE_F32 = 0,     /* IEEE float32                                            */
+  MOE_BF16 = 1,    /* bfloat16                                                */
+  MOE_I4G128 = 2   /* weights only: signed INT4 codes, two per byte (input 2i
+                      in the low nibble, 2i+1 in the high nibble, two's
+                      complement), packed [.., N, K/2] uint8, plus fp16 scales
+                      [.., N, K/128]; weight = scale[n, k/128] * code[n, k]    */
+};
+
+/* ---- gate activations ----------------------------------------------- */
+enum moe_act {
+  MOE_SWIGLU = 0,  /* z = SiLU(g) * u, SiLU(g) = g / (1 + exp(-g))            */
+  MOE_GEGLU = 1    /* z = GELU(g) * u, exact erf GELU                         */
+};
+
+/*
+ * moe_route - router logits, softmax and top-k ("Deux roles" pseudo-code;
+ * moe_stream.py MoEFFN.forward).
+ *
+ *   L[t,e] = sum_i x[t,i] * w_router[e,i] + expert_bias[e]      (fp32 accumulate)
+ *            or logits_in[t,e] + expert_bias[e] when logits_in != NULL
+ *   topk_ids[t,j]  = the j-th largest L[t,.] (ties: lower expert id first)
+ *   topk_w[t,j]    = softmax(L[t,.])[id] over all E experts; with renorm != 0
+ *                    divided by the sum over the k selected (no epsilon)
+ *
+ *   T, d, E, k     tokens, model width, experts, top-k (T = 0 is a no-op)
+ *   act_dtype      MOE_F32 or MOE_BF16: dtype of x and w_router
+ *   x              [T, d]; w_router [E, d]; both ignored (may be NULL) when
+ *                  logits_in != NULL
+ *   logits_in      [T, E] fp32 or NULL
+ *   expert_bias    [E] fp32 or NULL (added before selection and softmax)
+ *   topk_ids       out [T, k] int32;  topk_w  out [T, k] fp32
+ *   logits_out     out [T, E] fp32 or NULL: the L used for selection
+ */
+int moe_route(int T, int d, int E, int k, int act_dtype,
+              const void* x, const void* w_router, const float* logits_in,
+              const float* expert_bias, int renorm,
+              int32_t* topk_ids, float* topk_w, float* logits_out, void* stream);
+
+/*
+ * moe_permute - group the pairs p = t*k + j by local expert (ExpertMesh:
+ * grouping that keeps token and top-k slot identity; MoEEvolve: capacity
+ * dispatch).
+ *
+ *   local(p)        = expert_map ? expert_map[topk_ids[p]] : topk_ids[p]
+ *                     (-1 = not local; expert_map == NULL requires E_loc == E;
+ *                     ids outside [0, E) and map entries outside [0, E_loc)
+ *                     also count as not local)
+ *   kept            the first `capacity` pairs of each expert in ascending p
+ *                   (capacity 0 = all), local pairs only
+ *   expert_offsets  out [E_loc+1]: exclusive prefix sum of kept counts
+ *   sorted_pair     out [T*k]: sorted_pair[r] = p of the pair in grouped row r,
+ *                   rows in ascending p inside each expert; entries at rows >=
+ *                   expert_offsets[E_loc] are unspecified
+ *   pair_pos        out [T*k]: the row of pair p, or -1 if dropped / not local
+ *   x, d, act_dtype optional row gather: x_perm[r, :] = x[sorted_pair[r] / k, :]
+ *                   into x_perm [T*k, d]; pass x_perm = NULL to skip (then x
+ *                   and d are ignored)
+ *   ws, ws_bytes    device workspace of at least moe_permute_workspace_bytes()
+ * Output is deterministic (no dependence on atomic ordering).
+ */
+size_t moe_permute_workspace_bytes(int T, int k, int E_loc);
+int moe_permute(int T, int k, int E, const int32_t* topk_ids,
+                const int32_t* expert_map, int E_loc, int capacity,
+                int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                const void* x, int d, int act_dtype, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn - grouped gated expert FFN ("Deux roles": the worker's
+ * "3 mat-muls"; ExpertMesh: INT4 SwiGLU routed experts).  For each local
+ * expert e and each row r in [expert_offsets[e], expert_offsets[e+1]):
+ *
+ *   g = W_gate[e] a,  u = W_up[e] a,  z = act(g) * u,  y_perm[r] = W_down[e] z
+ *   with a = x_perm[r].  Accumulation in fp32; z is rounded to act_dtype.
+ *
+ *   E_loc, d, h     local experts, model width, expert hidden width
+ *   rows_max        rows of x_perm / y_perm (>= expert_offsets[E_loc]); the
+ *                   offsets are read on the device only
+ *   act_dtype       MOE_F32 (requires w_dtype MOE_F32) or MOE_BF16 (w_dtype
+ *                   MOE_BF16 or MOE_I4G128)
+ *   x_perm          [rows_max, d] act_dtype;   y_perm out [rows_max, d] act_dtype
+ *   expert_offsets  [E_loc+1] int32, non-decreasing, offsets[0] = 0;
+ *                   NULL = one group of rows_max rows (E_loc must be 1)
+ *   w_gate, w_up    [E_loc, h, d]  (MOE_I4G128: uint8 [E_loc, h, d/2])
+ *   w_down          [E_loc, d, h]  (MOE_I4G128: uint8 [E_loc, d, h/2])
+ *   s_gate, s_up    MOE_I4G128 only: fp16 [E_loc, h, d/128]; s_down [E_loc, d, h/128];
+ *                   NULL otherwise
+ *   ws, ws_bytes    at least moe_expert_ffn_workspace_bytes()
+ * Rows of y_perm outside the groups are left untouched.
+ */
+size_t moe_expert_ffn_workspace_bytes(int E_loc, int rows_max, int d, int h, int act_dtype);
+int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype, int w_dtype,
+                   const void* x_perm, const int32_t* expert_offsets,
+                   const void* w_gate, const void* w_up, const void* w_down,
+                   const void* s_gate, const void* s_up, const void* s_down,
+                   void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine - weighted top-k combine ("Deux roles": combine(p, partials) +
+ * shared(cur); ExpertMesh: weighted top-k reduction).
+ *
+ *   out[t] = sum_{j ascending, pair_pos[t*k+j] >= 0} topk_w[t,j] * y_perm[pair_pos[t*k+j]]
+ *            + shared_y[t]                         (fp32 sum, one final rounding)
+ *
+ *   y_perm     [rows, d] act_dtype;  pair_pos [T*k] int32;  topk_w [T*k] fp32
+ *   shared_y   [T, d] act_dtype or NULL;  out  out [T, d] act_dtype
+ * Tokens with no kept pair and no shared expert get zeros.
+ */
+int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm,
+                const int32_t* pair_pos, const float* topk_w, const void* shared_y,
+                void* out, void* stream);
+
+/*
+ * moe_layer_fwd - the whole layer forward on one stream.
+ */
+struct moe_layer_desc {
+  int T, d, E, k, h;          /* tokens, model width, global experts, top-k, hidden */
+  int act;                    /* enum moe_act (routed and shared experts)           */
+  int act_dtype;              /* MOE_F32 or MOE_BF16: x, out, w_router, shared weights */
+  int w_dtype;                /* routed expert weights: MOE_F32, MOE_BF16, MOE_I4G128 */
+  int renorm;                 /* 1: gates divided by their top-k sum                 */
+  int capacity;               /* per-expert pair limit, 0 = unlimited                */
+  int E_loc;                  /* resident experts (== E without expert_map)          */
+  const int32_t* expert_map;  /* [E] global -> local id or -1, or NULL (identity)    */
+  const void* w_router;       /* [E, d]; NULL when routing comes as logits_in        */
+  const float* expert_bias;   /* [E] or NULL                                         */
+  const void* w_gate;         /* routed expert weights and scales, as moe_expert_ffn */
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+  int h_shared;               /* 0 = no shared expert                                */
+  const void* ws_gate;        /* shared expert [h_shared, d], act_dtype              */
+  const void* ws_up;          /* [h_shared, d]                                       */
+  const void* ws_down;        /* [d, h_shared]                                       */
+};
+
+/* Optional device outputs of the intermediate results, and optional timing
+ * events (any field may be NULL). */
+enum {
+  MOE_EV_START = 0,           /* before the router                         */
+  MOE_EV_ROUTED = 1,          /* after routing (logits, softmax, top-k)     */
+  MOE_EV_GROUPED = 2,         /* after the grouping of pairs by expert      */
+  MOE_EV_GATE_UP = 3,         /* after the routed gate/up GEMM              */
+  MOE_EV_DOWN = 4,            /* after the routed down GEMM                 */
+  MOE_EV_SHARED = 5,          /* after the shared expert (if any)           */
+  MOE_EV_END = 6,             /* after the combine                          */
+  MOE_NUM_EVENTS = 7
+};
+struct moe_layer_trace {
+  float* logits;              /* [T, E] fp32 logits used for selection (router GEMM path) */
+  int32_t* topk_ids;          /* [T, k]   */
+  float* topk_w;              /* [T, k]   */
+  int32_t* expert_offsets;    /* [E_loc+1] */
+  int32_t* pair_pos;          /* [T*k]    */
+  void* events[MOE_NUM_EVENTS]; /* hipEvent_t handles owned by the caller, each
+                                   recorded on `stream` at its step boundary */
+};
+
+/*
+ *   x          [T, d] act_dtype (always read: the experts run on it)
+ *   logits_in  [T, E] fp32 routing logits (a share that receives its routing
+ *              from upstream), or NULL to run the router GEMM on w_router
+ *   out        out [T, d] act_dtype
+ *   trace      NULL or a struct of optional outputs
+ *   ws         at least moe_layer_workspace_bytes(desc)
+ */
+size_t moe_layer_workspace_bytes(const struct moe_layer_desc* L);
+int moe_layer_fwd(const struct moe_layer_desc* L, const void* x, const float* logits_in,
+                  void* out, const struct moe_layer_trace* trace,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_quantize_int4 - weight preparation for MOE_I4G128 (ExpertMesh: bit-exact
+ * quantiser of group-scaled signed INT4 weights with FP16 scales).  For each of
+ * `rows` rows of K inputs and each 128-input group:
+ *   scale = fp16_rne(fp32(max |w|) / 7);  code = clip(rint_even(w / fp32(scale)), -8, 7)
+ *   (code 0 when the scale is 0)
+ *   w       [rows, K] fp32;  packed out [rows, K/2] uint8;  scales out [rows, K/128] fp16
+ * K must be a multiple of 128.
+ */
+int moe_quantize_int4(int rows, int K, const float* w, uint8_t* packed, uint16_t* scales,
+                      void* stream);
+
+/* Static text of an error code; and the text of the last HIP error seen by
+ * this thread (empty if none). */
+const char* moe_strerror(int code);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LDS_H */

@@ -336,11 +336,28 @@ def moe_layer(x, weights: LayerWeights, k: int, renorm: bool, act: str, *,
             continue
         wg, wu, wd = weights.expert(e)
         Y[rows // k, rows % k] = gated_ffn(x[rows // k], wg, wu, wd, act)
-    kept = (pair_pos >= 0).reshape(T, k)
-    out = np.zeros((toks.size, d), np.float64)
-    for j in range(k):
-        out += np.where(kept[toks, j], w[toks, j], 0.0)[:, None] * Y[toks, j]
+    shared_y = None
     if shared is not None:
-        out += gated_ffn(x[toks], shared[0], shared[1], shared[2], act)
+        shared_y = gated_ffn(x[toks], shared[0], shared[1], shared[2], act)
+    out = combine(Y[toks], pair_pos.reshape(T, k)[toks], w[toks], shared_y)
     return {"out": out, "L": L, "ids": ids_o, "w": w, "offsets": offsets,
             "sorted_pair": sorted_pair, "pair_pos": pair_pos, "tokens": toks}
+
+
+def combine(y_slots, pair_pos, w, shared_y=None) -> np.ndarray:
+    """Weighted top-k combine of one token row at a time.
+
+    ``y_slots [T, k, d]`` holds each slot's expert output, ``pair_pos [T, k]``
+    marks kept slots (>= 0), ``w [T, k]`` the gates:
+    ``out[t] = sum_{j ascending, kept} w[t, j] y[t, j] (+ shared_y[t])`` ("Deux
+    rôles": ``combine(p, partials) + shared(cur)``; ExpertMesh: weighted top-k
+    reduction; moe_stream.py: ``out[mask] += w[mask] * expert_out``)."""
+    y_slots = np.asarray(y_slots, np.float64)
+    T, k, d = y_slots.shape
+    kept = np.asarray(pair_pos) >= 0
+    out = np.zeros((T, d), np.float64)
+    for j in range(k):
+        out += np.where(kept[:, j], np.asarray(w, np.float64)[:, j], 0.0)[:, None] * y_slots[:, j]
+    if shared_y is not None:
+        out += np.asarray(shared_y, np.float64)
+    return out

@@ -1,0 +1,355 @@
+// C ABI of the MoE layer forward (declared in include/moe_lds.h): argument
+// checks, workspace carving and the launch sequence on the caller's stream.
+#include "../../include/moe_lds.h"
+
+#include <string.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e) {
+  g_last_error = hipGetErrorString(e);
+  return MOE_EHIP;
+}
+
+#define MOE_HIP(call)                          \
+  do {                                         \
+    const hipError_t e_ = (call);              \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline size_t elt_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// A bump allocator over the caller's workspace.
+struct Carver {
+  unsigned char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<unsigned char*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+bool act_ok(int a) { return a == MOE_SWIGLU || a == MOE_GEGLU; }
+bool act_dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// Weight/activation mixes the kernels implement.
+bool mix_ok(int act_dtype, int w_dtype) {
+  if (act_dtype == MOE_F32) return w_dtype == MOE_F32;
+  if (act_dtype == MOE_BF16) return w_dtype == MOE_BF16 || w_dtype == MOE_I4G128;
+  return false;
+}
+
+int wtype_of(int w_dtype) { return w_dtype == MOE_F32 ? W_F32 : (w_dtype == MOE_BF16 ? W_BF16 : W_I4); }
+
+int check_width(int v, int w_dtype) {
+  if (v <= 0) return MOE_EINVAL;
+  if (v % 64) return MOE_EUNSUPPORTED;
+  if (w_dtype == MOE_I4G128 && v % 128) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_route_dims(int T, int E, int k) {
+  if (T < 0 || E <= 0 || k <= 0) return MOE_EINVAL;
+  if (k > E) return MOE_EINVAL;
+  if (E > kMaxE || k > kMaxK) return MOE_EUNSUPPORTED;
+  if ((long long)T * k >= (1LL << 31) || (long long)T * E >= (1LL << 40)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Gate/up then down over grouped rows; `offsets` NULL means one group.
+int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A,
+            const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile, int BM,
+            const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
+            const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
+            void* mid_event = nullptr) {
+  const int wt = wtype_of(w_dtype);
+  FfnGemmArgs g{};
+  g.A = A;
+  g.row_index = row_index;
+  g.row_div = row_div > 0 ? row_div : 1;
+  g.W0 = wg;
+  g.W1 = wu;
+  g.S0 = static_cast<const uint16_t*>(sg);
+  g.S1 = static_cast<const uint16_t*>(su);
+  g.out = z;
+  g.offsets = offsets;
+  g.mtile_start = mtile;
+  g.E_loc = E_loc;
+  g.rows_max = rows_max;
+  g.K = d;
+  g.N = h;
+  g.act = act == MOE_GEGLU ? 1 : 0;
+  g.out_f32 = plan.split_z ? 1 : 0;
+  MOE_HIP(launch_ffn_gemm(g, true, wt, false, BM, plan.NF_up, s));
+  if (mid_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(mid_event), s));
+  FfnGemmArgs dn = g;
+  dn.A = z;
+  dn.row_index = nullptr;
+  dn.row_div = 1;
+  dn.W0 = wd;
+  dn.W1 = nullptr;
+  dn.S0 = static_cast<const uint16_t*>(sd);
+  dn.S1 = nullptr;
+  dn.out = y;
+  dn.out_f32 = y_f32 ? 1 : 0;
+  dn.K = h;
+  dn.N = d;
+  MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BM, plan.NF_down, s));
+  return MOE_OK;
+}
+
+// Rows a grouped GEMM may see: at most T*k pairs, and at most capacity per expert.
+int layer_rows_max(const moe_layer_desc* L) {
+  long long r = (long long)L->T * L->k;
+  if (L->capacity > 0) {
+    const long long c = (long long)L->capacity * L->E_loc;
+    if (c < r) r = c;
+  }
+  return (int)r;
+}
+
+int check_layer(const moe_layer_desc* L) {
+  if (!L) return MOE_EINVAL;
+  int rc = check_route_dims(L->T, L->E, L->k);
+  if (rc) return rc;
+  if (!act_ok(L->act) || !act_dtype_ok(L->act_dtype)) return MOE_EUNSUPPORTED;
+  if (L->w_dtype < MOE_F32 || L->w_dtype > MOE_I4G128) return MOE_EUNSUPPORTED;
+  if (!mix_ok(L->act_dtype, L->w_dtype)) return MOE_EUNSUPPORTED;
+  if ((rc = check_width(L->d, L->w_dtype)) || (rc = check_width(L->h, L->w_dtype))) return rc;
+  if (L->E_loc <= 0 || L->E_loc > L->E || L->capacity < 0 || L->h_shared < 0) return MOE_EINVAL;
+  if (!L->expert_map && L->E_loc != L->E) return MOE_EINVAL;
+  if (!L->w_gate || !L->w_up || !L->w_down) return MOE_EINVAL;
+  if (L->w_dtype == MOE_I4G128 && (!L->s_gate || !L->s_up || !L->s_down)) return MOE_EINVAL;
+  if (L->h_shared > 0) {
+    if (L->h_shared % 64) return MOE_EUNSUPPORTED;
+    if (!L->ws_gate || !L->ws_up || !L->ws_down) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+struct LayerBufs {
+  int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts;
+  float* tw;
+  void *z, *y, *zs, *ys;
+};
+
+size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
+  Carver c(ws);
+  const size_t P = (size_t)L->T * L->k;
+  const size_t rows = (size_t)layer_rows_max(L);
+  const size_t eb = elt_bytes(L->act_dtype);
+  b->ids = c.take<int32_t>(P * 4);
+  b->tw = c.take<float>(P * 4);
+  b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
+  b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
+  b->sorted_pair = c.take<int32_t>(P * 4);
+  b->pair_pos = c.take<int32_t>(P * 4);
+  b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
+  b->z = c.take<void>(rows * L->h * 4);  // fp32 when the down projection splits z
+  b->y = c.take<void>(rows * L->d * 4);  // expert outputs stay fp32 until the combine
+  b->zs = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->h_shared * eb : 0);
+  b->ys = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->d * 4 : 0);
+  return c.used;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported dtype, activation or shape";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_route(int T, int d, int E, int k, int act_dtype, const void* x, const void* w_router,
+              const float* logits_in, const float* expert_bias, int renorm, int32_t* topk_ids,
+              float* topk_w, float* logits_out, void* stream) {
+  int rc = check_route_dims(T, E, k);
+  if (rc) return rc;
+  if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
+  if (!logits_in) {
+    if ((rc = check_width(d, act_dtype))) return rc;
+    if (!x || !w_router) return MOE_EINVAL;
+  }
+  if (T > 0 && (!topk_ids || !topk_w)) return MOE_EINVAL;
+  MOE_HIP(launch_route(T, d, E, k, act_dtype == MOE_BF16, x, w_router, logits_in, expert_bias, renorm,
+                       topk_ids, topk_w, logits_out, as_stream(stream)));
+  return MOE_OK;
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E_loc) {
+  if (T < 0 || k <= 0 || E_loc <= 0) return 0;
+  return align_up(permute_ws_bytes(T * k, E_loc));
+}
+
+int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* expert_map, int E_loc,
+                int capacity, int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                const void* x, int d, int act_dtype, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_route_dims(T, E, k);
+  if (rc) return rc;
+  if (E_loc <= 0 || E_loc > E || capacity < 0) return MOE_EINVAL;
+  if (!expert_map && E_loc != E) return MOE_EINVAL;
+  if (!expert_offsets) return MOE_EINVAL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_EINVAL;
+  if (x_perm) {
+    if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
+    if ((rc = check_width(d, act_dtype))) return rc;
+    if (!x) return MOE_EINVAL;
+  }
+  if (ws_bytes < moe_permute_workspace_bytes(T, k, E_loc)) return MOE_EWORKSPACE;
+  if (T > 0 && !ws) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+  MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr,
+                         sorted_pair, pair_pos, static_cast<int32_t*>(ws), s));
+  if (x_perm && T > 0)
+    MOE_HIP(launch_gather_rows(T * k, d, act_dtype == MOE_BF16, x, sorted_pair, k, expert_offsets + E_loc,
+                               x_perm, s));
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int E_loc, int rows_max, int d, int h, int act_dtype) {
+  (void)d;
+  if (E_loc <= 0 || rows_max < 0 || h <= 0 || !act_dtype_ok(act_dtype)) return 0;
+  return align_up((size_t)rows_max * h * 4) + align_up((size_t)(E_loc + 1) * 4);
+}
+
+int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype, int w_dtype,
+                   const void* x_perm, const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
+                   void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (E_loc <= 0 || rows_max < 0) return MOE_EINVAL;
+  if (E_loc > kMaxE) return MOE_EUNSUPPORTED;
+  if (!act_ok(act) || !act_dtype_ok(act_dtype) || !mix_ok(act_dtype, w_dtype)) return MOE_EUNSUPPORTED;
+  int rc;
+  if ((rc = check_width(d, w_dtype)) || (rc = check_width(h, w_dtype))) return rc;
+  if (!expert_offsets && E_loc != 1) return MOE_EINVAL;
+  if (!w_gate || !w_up || !w_down) return MOE_EINVAL;
+  if (w_dtype == MOE_I4G128 && (!s_gate || !s_up || !s_down)) return MOE_EINVAL;
+  if (rows_max > 0 && (!x_perm || !y_perm)) return MOE_EINVAL;
+  if (ws_bytes < moe_expert_ffn_workspace_bytes(E_loc, rows_max, d, h, act_dtype)) return MOE_EWORKSPACE;
+  if (rows_max == 0) return MOE_OK;
+  if (!ws) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+  Carver c(ws);
+  void* z = c.take<void>((size_t)rows_max * h * 4);
+  int32_t* mtile = c.take<int32_t>((size_t)(E_loc + 1) * 4);
+  const int wt = wtype_of(w_dtype);
+  const FfnPlan plan = plan_ffn(E_loc, rows_max, d, h, wt);
+  if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, s));
+  return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, nullptr, 1, expert_offsets,
+                 expert_offsets ? mtile : nullptr, plan.BM, plan, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                 z, y_perm, false, s);
+}
+
+int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const int32_t* pair_pos,
+                const float* topk_w, const void* shared_y, void* out, void* stream) {
+  if (T < 0 || k <= 0 || k > kMaxK) return k > kMaxK ? MOE_EUNSUPPORTED : MOE_EINVAL;
+  if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
+  int rc;
+  if ((rc = check_width(d, act_dtype))) return rc;
+  if (T > 0 && (!y_perm || !pair_pos || !topk_w || !out)) return MOE_EINVAL;
+  MOE_HIP(launch_combine(T, k, d, act_dtype == MOE_BF16, act_dtype == MOE_F32, y_perm, pair_pos, topk_w,
+                         shared_y, out, as_stream(stream)));
+  return MOE_OK;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* L) {
+  if (check_layer(L) != MOE_OK) return 0;
+  LayerBufs b;
+  return carve_layer(L, nullptr, &b);
+}
+
+int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in, void* out,
+                  const moe_layer_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!logits_in && !L->w_router) return MOE_EINVAL;
+  if (L->T > 0 && (!x || !out)) return MOE_EINVAL;
+  const size_t need = moe_layer_workspace_bytes(L);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (L->T == 0) return MOE_OK;
+  if (!ws) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+  LayerBufs b;
+  carve_layer(L, ws, &b);
+  moe_layer_trace tr{};
+  if (trace) tr = *trace;
+  int32_t* ids = tr.topk_ids ? tr.topk_ids : b.ids;
+  float* tw = tr.topk_w ? tr.topk_w : b.tw;
+  int32_t* offsets = tr.expert_offsets ? tr.expert_offsets : b.offsets;
+  int32_t* pair_pos = tr.pair_pos ? tr.pair_pos : b.pair_pos;
+  const bool bf16 = L->act_dtype == MOE_BF16;
+  const int T = L->T, k = L->k;
+  auto mark = [&](int i) -> hipError_t {
+    return tr.events[i] ? hipEventRecord(static_cast<hipEvent_t>(tr.events[i]), s) : hipSuccess;
+  };
+  const int rows = layer_rows_max(L);
+  const int wt = wtype_of(L->w_dtype);
+
+  MOE_HIP(mark(MOE_EV_START));
+  // 1-2: router
+  MOE_HIP(launch_route(T, L->d, L->E, k, bf16, x, L->w_router, logits_in, L->expert_bias, L->renorm, ids, tw,
+                       tr.logits, s));
+  MOE_HIP(mark(MOE_EV_ROUTED));
+  // 3: grouping (the m-tile prefix of the grouped GEMMs comes out of the same scan)
+  const FfnPlan plan = plan_ffn(L->E_loc, rows, L->d, L->h, wt);
+  MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
+                         b.sorted_pair, pair_pos, b.counts, s));
+  MOE_HIP(mark(MOE_EV_GROUPED));
+  // 4: routed experts, activations gathered straight from x by pair index
+  rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, b.sorted_pair, k, offsets, b.mtile, plan.BM,
+               plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, true, s,
+               tr.events[MOE_EV_GATE_UP]);
+  if (rc) return rc;
+  MOE_HIP(mark(MOE_EV_DOWN));
+  // 5: shared expert on every token, then the weighted combine
+  const void* shared_y = nullptr;
+  if (L->h_shared > 0) {
+    const int swt = L->act_dtype;  // shared weights are in the activation dtype
+    const FfnPlan sp = plan_ffn(1, T, L->d, L->h_shared, wtype_of(swt));
+    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, nullptr, 1, nullptr, nullptr, sp.BM, sp, L->ws_gate,
+                 L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, s);
+    if (rc) return rc;
+    shared_y = b.ys;
+  }
+  MOE_HIP(mark(MOE_EV_SHARED));
+  MOE_HIP(launch_combine(T, k, L->d, bf16, true, b.y, pair_pos, tw, shared_y, out, s));
+  MOE_HIP(mark(MOE_EV_END));
+  return MOE_OK;
+}
+
+int moe_quantize_int4(int rows, int K, const float* w, uint8_t* packed, uint16_t* scales, void* stream) {
+  if (rows < 0 || K <= 0) return MOE_EINVAL;
+  if (K % kI4Group) return MOE_EUNSUPPORTED;
+  if (rows > 0 && (!w || !packed || !scales)) return MOE_EINVAL;
+  MOE_HIP(launch_quantize_int4(rows, K, w, packed, scales, as_stream(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

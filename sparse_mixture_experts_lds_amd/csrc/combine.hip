@@ -1,0 +1,98 @@
+// Weighted top-k combine.
+//
+// Operation ("Sharding d'experts", "Deux roles": x + combine(p, partials) +
+// shared(cur); ExpertMesh data-flow figure: weighted top-k reduction;
+// moe_stream.py MoEFFN.forward: out[mask] += w[mask] * expert_out):
+//   out[t] = sum_{j ascending, pair_pos[t*k+j] >= 0} w[t,j] * y[pair_pos[t*k+j]] + shared_y[t]
+// in fp32, rounded once to the output type.
+//
+// A gather, not a scatter: each thread owns 8 consecutive values of one
+// output row and reads the k expert rows of that token, so no atomics are
+// needed and the result does not depend on scheduling.  Consecutive threads
+// cover consecutive pieces of a row: every load and store is coalesced.
+// Inside the layer the expert rows and the shared expert's output arrive in
+// fp32 (one rounding, at the end); the standalone entry point takes them in
+// the output dtype.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// 8 consecutive values of a row: bf16 (one 16-byte vector) or fp32 (two).
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, size_t idx8, float* v) {
+  if constexpr (F32) {
+    const u32x4* p = static_cast<const u32x4*>(base) + 2 * idx8;
+    const u32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  } else {
+    const u32x4 a = static_cast<const u32x4*>(base)[idx8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(a[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+    }
+  }
+}
+
+template <bool OUT_BF16, bool Y_F32>
+__global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_row, const void* __restrict__ y,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ tw,
+                                                      const void* __restrict__ shared_y, void* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t t = i / v8_per_row;
+  if (t >= (size_t)T) return;
+  const int c = (int)(i - t * v8_per_row);
+  float acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int pos = pair_pos[t * k + j];
+    if (pos < 0) continue;
+    const float w = tw[t * k + j];
+    float yv[8];
+    load8<Y_F32 || !OUT_BF16>(y, (size_t)pos * v8_per_row + c, yv);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = fmaf(w, yv[v], acc[v]);
+  }
+  if (shared_y) {
+    float sv[8];
+    load8<Y_F32 || !OUT_BF16>(shared_y, t * v8_per_row + c, sv);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] += sv[v];
+  }
+  if constexpr (OUT_BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = pack_bf16x2(acc[2 * v], acc[2 * v + 1]);
+    static_cast<u32x4*>(out)[t * v8_per_row + c] = o;
+  } else {
+    u32x4* o = static_cast<u32x4*>(out) + 2 * (t * v8_per_row + c);
+    o[0] = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+    o[1] = u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int T, int k, int d, bool out_bf16, bool y_f32, const void* y, const int32_t* pair_pos,
+                          const float* tw, const void* shared_y, void* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int v8 = d / 8;
+  const size_t n = (size_t)T * v8;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (out_bf16 && y_f32)
+    combine_kernel<true, true><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  else if (out_bf16)
+    combine_kernel<true, false><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  else
+    combine_kernel<false, true><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

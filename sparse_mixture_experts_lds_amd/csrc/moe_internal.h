@@ -1,0 +1,113 @@
+// Internal declarations of the gfx950 MoE kernels: device helpers, kernel
+// argument blocks and the host-side launchers used by the C ABI (abi.hip).
+// Nothing here is exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum WType { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kI4Group = 128;
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even float -> bf16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, wave_shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += wave_shfl_xor(v, m);
+  return v;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already checked.
+
+// Router: logits GEMM (or given logits) + bias, softmax, top-k.
+hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
+                        const float* logits_in, const float* bias, int renorm, int32_t* ids,
+                        float* tw, float* logits_out, hipStream_t s);
+
+// Grouping of pairs by local expert.
+struct PermuteWs {
+  int32_t* counts;       // [nblk * E_loc] per-block counts, then per-block bases
+  int nblk;
+};
+size_t permute_ws_bytes(int P, int E_loc);
+int permute_block_pairs();
+hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t* expert_map, int E_loc,
+                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* counts, hipStream_t s);
+hipError_t launch_gather_rows(int rows_max, int d, bool bf16, const void* x, const int32_t* sorted_pair,
+                              int k, const int32_t* offsets_end, void* x_perm, hipStream_t s);
+hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_t* mtile_start,
+                               hipStream_t s);
+
+// Grouped GEMMs.
+struct FfnGemmArgs {
+  const void* A;             // activations [rows, K] (bf16 or f32)
+  const int32_t* row_index;  // NULL: A row = grouped row; else A row = row_index[r] / row_div
+  int row_div;
+  const void* W0;            // [E_loc, N, K] (I4: bytes [E_loc, N, K/2])
+  const void* W1;            // second matrix (up projection) for gate/up, else NULL
+  const uint16_t* S0;        // I4 scales [E_loc, N, K/128]
+  const uint16_t* S1;
+  void* out;                 // [rows, N]
+  const int32_t* offsets;    // [E_loc+1] or NULL (single group of rows_max rows)
+  const int32_t* mtile_start;// [E_loc+1] m-tile prefix, or NULL with offsets == NULL
+  int E_loc, rows_max, K, N;
+  int act;                   // 0 SiLU, 1 GELU (gate/up only)
+  int out_f32;               // 1: store the output as fp32 whatever the operand type
+};
+struct FfnPlan {
+  int BM;                    // rows per tile (16 * MF)
+  int NF_up, NF_down;        // 16-col fragments per wave
+  bool split_z;              // z kept in fp32, down projection on its hi/lo bf16 parts
+};
+FfnPlan plan_ffn(int E_loc, int rows_max, int d, int h, int w_type);
+int ffn_max_mtiles(int E_loc, int rows_max, int BM);
+// split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
+hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,
+                           int NF, hipStream_t s);
+
+// Weighted combine.
+// y and shared_y are fp32 when y_f32, else in the output dtype.
+hipError_t launch_combine(int T, int k, int d, bool out_bf16, bool y_f32, const void* y, const int32_t* pair_pos,
+                          const float* tw, const void* shared_y, void* out, hipStream_t s);
+
+// INT4 quantiser.
+hipError_t launch_quantize_int4(int rows, int K, const float* w, uint8_t* packed, uint16_t* scales,
+                                hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,231 @@
+// Grouping of (token, slot) pairs by local expert: LDS histogram, prefix sums
+// and a stable scatter that keeps each pair's identity p = t*k + j.
+//
+// Operation (ExpertMesh README: activation grouping that preserves token and
+// top-k slot identity; MoEEvolve "Architecture": capacity-factor dispatch with
+// overflow dropped): pairs of each local expert are laid out in ascending p;
+// with a capacity C only the first C of them are kept.
+//
+// Three launches, none of which depends on the order of atomic operations:
+//   1. count:   one wave per block of kBlockPairs pairs builds the block's
+//               per-expert histogram in LDS and writes it out;
+//   2. scan:    one workgroup turns the histograms into per-block bases (an
+//               exclusive scan over blocks, per expert), clamps each expert's
+//               total to the capacity, scans over experts into the offsets and
+//               also writes the m-tile prefix of the grouped GEMMs;
+//   3. scatter: one wave per block walks its pairs 64 at a time in p order;
+//               each lane finds the lanes with the same expert by 11 ballots
+//               over the key bits (a wave multisplit) and takes its rank from
+//               a popcount, added to the block's running per-expert count.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBlockPairs = 1024;
+constexpr int kScanThreads = 1024;
+
+// Local expert of pair p, or -1 (not resident, or an id outside [0, E)).
+__device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids, const int32_t* __restrict__ emap,
+                                            int E, int E_loc, int p) {
+  const int g = ids[p];
+  if (g < 0 || g >= E) return -1;
+  const int e = emap ? emap[g] : g;
+  return (e >= 0 && e < E_loc) ? e : -1;
+}
+
+__global__ __launch_bounds__(64) void count_kernel(int P, const int32_t* __restrict__ ids,
+                                                   const int32_t* __restrict__ emap, int E, int E_loc,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int32_t hist[kMaxE];
+  for (int e = threadIdx.x; e < E_loc; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kBlockPairs;
+  const int p1 = min(P, p0 + kBlockPairs);
+  for (int p = p0 + threadIdx.x; p < p1; p += 64) {
+    const int e = local_expert(ids, emap, E, E_loc, p);
+    if (e >= 0) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  int32_t* out = counts + (size_t)blockIdx.x * E_loc;
+  for (int e = threadIdx.x; e < E_loc; e += 64) out[e] = hist[e];
+}
+
+// Block-wide exclusive scan of one value per thread (kScanThreads threads).
+__device__ int block_exclusive_scan(int v, int* total, int* sh /* [kScanThreads/64] */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kScanThreads / 64 ? sh[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(wi, o, 64);
+      if (lane >= o) wi += n;
+    }
+    if (lane < kScanThreads / 64) sh[lane] = wi - w;
+    if (lane == kScanThreads / 64 - 1) sh[kScanThreads / 64] = wi;
+  }
+  __syncthreads();
+  const int r = sh[wave] + incl - v;
+  *total = sh[kScanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int nblk, int E_loc, int capacity, int BM,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ mtile_start) {
+  __shared__ int sh[kScanThreads / 64 + 1];
+  const int e = threadIdx.x;
+  int kept = 0;
+  if (e < E_loc) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int32_t* c = counts + (size_t)b * E_loc + e;
+      const int v = *c;
+      *c = run;  // exclusive base of block b for expert e
+      run += v;
+    }
+    kept = capacity > 0 ? min(run, capacity) : run;
+  }
+  int total;
+  const int off = block_exclusive_scan(kept, &total, sh);
+  if (e < E_loc) offsets[e] = off;
+  if (e == 0) offsets[E_loc] = total;
+  if (mtile_start != nullptr) {
+    const int mt = (kept + BM - 1) / BM;
+    int mtotal;
+    const int moff = block_exclusive_scan(mt, &mtotal, sh);
+    if (e < E_loc) mtile_start[e] = moff;
+    if (e == 0) mtile_start[E_loc] = mtotal;
+  }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(int P, const int32_t* __restrict__ ids,
+                                                     const int32_t* __restrict__ emap, int E, int E_loc,
+                                                     int capacity, const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_pair,
+                                                     int32_t* __restrict__ pair_pos) {
+  __shared__ int32_t run[kMaxE];
+  __shared__ int32_t off[kMaxE];
+  const int lane = threadIdx.x;
+  const int32_t* base = counts + (size_t)blockIdx.x * E_loc;
+  for (int e = lane; e < E_loc; e += 64) {
+    run[e] = base[e];
+    off[e] = offsets[e];
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int p0 = blockIdx.x * kBlockPairs;
+  const int p1 = min(P, p0 + kBlockPairs);
+  for (int c = p0; c < p1; c += 64) {
+    const int p = c + lane;
+    const int e = p < p1 ? local_expert(ids, emap, E, E_loc, p) : -1;
+    const int key = e + 1;  // 0 = not local / inactive lane
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    int r = 0;
+    if (e >= 0) r = run[e] + rank;
+    __syncthreads();  // every lane has read run[] before the leaders update it
+    if (e >= 0 && rank == 0) run[e] += __popcll(peers);
+    __syncthreads();
+    if (p < p1) {
+      const bool kept = e >= 0 && (capacity == 0 || r < capacity);
+      const int pos = kept ? off[e] + r : -1;
+      pair_pos[p] = pos;
+      if (kept) sorted_pair[pos] = p;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void mtile_kernel(int E_loc, int BM, const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ mtile_start) {
+  __shared__ int sh[kScanThreads / 64 + 1];
+  const int e = threadIdx.x;
+  const int n = e < E_loc ? offsets[e + 1] - offsets[e] : 0;
+  int total;
+  const int moff = block_exclusive_scan((n + BM - 1) / BM, &total, sh);
+  if (e < E_loc) mtile_start[e] = moff;
+  if (e == 0) mtile_start[E_loc] = total;
+}
+
+template <typename V>
+__global__ __launch_bounds__(256) void gather_kernel(int rows_max, int vec_per_row, const V* __restrict__ x,
+                                                     const int32_t* __restrict__ sorted_pair, int k,
+                                                     const int32_t* __restrict__ offsets_end,
+                                                     V* __restrict__ x_perm) {
+  const int n_rows = *offsets_end;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t r = i / vec_per_row;
+  if (r >= (size_t)n_rows || r >= (size_t)rows_max) return;
+  const int c = (int)(i - r * vec_per_row);
+  const int t = sorted_pair[r] / k;
+  x_perm[r * vec_per_row + c] = x[(size_t)t * vec_per_row + c];
+}
+
+__global__ void zero_offsets_kernel(int E_loc, int32_t* offsets, int32_t* mtile_start) {
+  for (int e = threadIdx.x; e <= E_loc; e += blockDim.x) {
+    offsets[e] = 0;
+    if (mtile_start) mtile_start[e] = 0;
+  }
+}
+
+}  // namespace
+
+int permute_block_pairs() { return kBlockPairs; }
+
+size_t permute_ws_bytes(int P, int E_loc) {
+  const size_t nblk = ((size_t)P + kBlockPairs - 1) / kBlockPairs;
+  return (nblk > 0 ? nblk : 1) * (size_t)E_loc * sizeof(int32_t);
+}
+
+hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t* expert_map, int E_loc,
+                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* counts, hipStream_t s) {
+  const int P = T * k;
+  if (P == 0) {
+    zero_offsets_kernel<<<1, 256, 0, s>>>(E_loc, offsets, mtile_start);
+    return hipGetLastError();
+  }
+  const int nblk = (P + kBlockPairs - 1) / kBlockPairs;
+  count_kernel<<<nblk, 64, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
+  scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E_loc, capacity, BM, counts, offsets, mtile_start);
+  scatter_kernel<<<nblk, 64, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets, sorted_pair,
+                                     pair_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_t* mtile_start,
+                               hipStream_t s) {
+  mtile_kernel<<<1, 1024, 0, s>>>(E_loc, BM, offsets, mtile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int rows_max, int d, bool bf16, const void* x, const int32_t* sorted_pair,
+                              int k, const int32_t* offsets_end, void* x_perm, hipStream_t s) {
+  if (rows_max == 0) return hipSuccess;
+  const int vec = bf16 ? d / 8 : d / 4;  // 16-byte vectors per row
+  const size_t n = (size_t)rows_max * vec;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  gather_kernel<u32x4><<<grid, 256, 0, s>>>(rows_max, vec, static_cast<const u32x4*>(x), sorted_pair, k,
+                                            offsets_end, static_cast<u32x4*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

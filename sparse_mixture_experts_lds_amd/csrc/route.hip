@@ -1,0 +1,188 @@
+// Router step: logits GEMM on MFMA, softmax and wave-level top-k selection.
+//
+// Operation ("Sharding d'experts", "Deux roles": ids,p = top_k(softmax(cur @
+// router), k); moe_stream.py MoEFFN.forward: bias-free router, per-expert bias
+// added before the softmax, softmax over all experts, topk, gates divided by
+// their sum):
+//   L[t,e]   = sum_i x[t,i] w[e,i] + b[e]           (fp32 accumulate)
+//   ids[t,j] = j-th largest L[t,.], ties to the lower expert id
+//   w[t,j]   = exp(L_j - m) / (renorm ? sum_sel exp(L - m) : sum_all exp(L - m))
+//
+// One workgroup (4 waves) handles 16 tokens.  The logits tile [16, E] is built
+// in LDS (MFMA 16x16x32 bf16 or 16x16x4 f32, each wave a strided set of
+// 16-expert column fragments), then each wave selects for 4 tokens: every lane
+// holds E/64 logits in registers and k rounds of a (value, lower-id) wave
+// arg-max pick the experts.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokTile = 16;
+
+template <int NF, bool BF16>
+__global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, const void* __restrict__ xv,
+                                                    const void* __restrict__ wv,
+                                                    const float* __restrict__ logits_in,
+                                                    const float* __restrict__ bias, int renorm,
+                                                    int32_t* __restrict__ ids, float* __restrict__ tw,
+                                                    float* __restrict__ logits_out) {
+  constexpr int ES = NF * 64;  // logits row stride in LDS (E padded)
+  __shared__ float Ls[kTokTile * ES];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kTokTile;
+
+  if (logits_in != nullptr) {
+    for (int i = threadIdx.x; i < kTokTile * E; i += 256) {
+      const int r = i / E, e = i - r * E;
+      const int t = t0 + r;
+      float v = 0.f;
+      if (t < T) v = logits_in[(size_t)t * E + e];
+      if (bias) v += bias[e];
+      Ls[r * ES + e] = v;
+    }
+  } else {
+    const int row = lane & 15;  // A row (token) / B column (expert) inside a fragment
+    const int q = lane >> 4;    // K slice held by this lane group
+    const int t = t0 + row;
+    const bool tok_ok = t < T;
+    f32x4 acc[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF16) {
+      const uint16_t* x = static_cast<const uint16_t*>(xv);
+      const uint16_t* w = static_cast<const uint16_t*>(wv);
+      const uint16_t* xrow = x + (size_t)(tok_ok ? t : 0) * d;
+      for (int k0 = 0; k0 < d; k0 += 32) {
+        u32x4 av = tok_ok ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * q) : u32x4{0, 0, 0, 0};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const int e = 16 * (wave + 4 * i) + row;
+          u32x4 bv = u32x4{0, 0, 0, 0};
+          if (e < E) bv = *reinterpret_cast<const u32x4*>(w + (size_t)e * d + k0 + 8 * q);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+        }
+      }
+    } else {
+      const float* x = static_cast<const float*>(xv);
+      const float* w = static_cast<const float*>(wv);
+      const float* xrow = x + (size_t)(tok_ok ? t : 0) * d;
+      for (int k0 = 0; k0 < d; k0 += 4) {
+        const float a = tok_ok ? xrow[k0 + q] : 0.f;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const int e = 16 * (wave + 4 * i) + row;
+          const float b = (e < E) ? w[(size_t)e * d + k0 + q] : 0.f;
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[i], 0, 0, 0);
+        }
+      }
+    }
+    // D[i][j]: lane holds column j = lane & 15 and rows 4q + r.
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int e = 16 * (wave + 4 * i) + row;
+      if (e < E) {
+        const float bv = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ls[(4 * q + r) * ES + e] = acc[i][r] + bv;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (logits_out != nullptr) {
+    for (int i = threadIdx.x; i < kTokTile * E; i += 256) {
+      const int r = i / E, e = i - r * E;
+      const int t = t0 + r;
+      if (t < T) logits_out[(size_t)t * E + e] = Ls[r * ES + e];
+    }
+  }
+
+  // Selection: wave w handles tokens w, w+4, w+8, w+12 of the tile.
+  for (int r = wave; r < kTokTile; r += 4) {
+    const int t = t0 + r;
+    if (t >= T) break;
+    float v[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? Ls[r * ES + e] : -INFINITY;
+    }
+    float m = v[0];
+#pragma unroll
+    for (int i = 1; i < NF; ++i) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+      if (lane + 64 * i < E) se += expf(v[i] - m);
+    const float sum_all = wave_sum(se);
+
+    uint32_t taken = 0;
+    float my_v = -INFINITY;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const int e = lane + 64 * i;
+        // strict '>' keeps the lower id among this lane's equal values
+        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
+          bv = v[i];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int msk = 32; msk >= 1; msk >>= 1) {
+        const float ov = wave_shfl_xor(bv, msk);
+        const int oe = wave_shfl_xor(be, msk);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      if (lane == j) {
+        my_v = bv;
+        my_e = be;
+      }
+    }
+    const float ex = lane < k ? expf(my_v - m) : 0.f;
+    const float denom = renorm ? wave_sum(ex) : sum_all;
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_e;
+      tw[(size_t)t * k + lane] = ex / denom;
+    }
+  }
+}
+
+template <int NF>
+hipError_t launch_nf(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
+                     const float* logits_in, const float* bias, int renorm, int32_t* ids, float* tw,
+                     float* logits_out, hipStream_t s) {
+  const dim3 grid((T + kTokTile - 1) / kTokTile);
+  if (bf16)
+    route_kernel<NF, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, logits_in, bias, renorm, ids, tw, logits_out);
+  else
+    route_kernel<NF, false><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, logits_in, bias, renorm, ids, tw, logits_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
+                        const float* logits_in, const float* bias, int renorm, int32_t* ids,
+                        float* tw, float* logits_out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nf = (E + 63) / 64;
+  if (nf <= 1) return launch_nf<1>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+  if (nf <= 2) return launch_nf<2>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+  if (nf <= 4) return launch_nf<4>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+  if (nf <= 8) return launch_nf<8>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+  return launch_nf<16>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+}
+
+}  // namespace moe

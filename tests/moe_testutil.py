@@ -1,0 +1,139 @@
+"""Shared helpers of the GPU parity tests: device copies of the seeded inputs,
+oracle-side weights, and the comparison protocol."""
+import numpy as np
+import torch
+
+import oracle as orc
+from moe_synth import make_inputs
+from moe_synth.generate import as_f64
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "i4g128": 2e-2}
+
+
+def relerr(got, ref) -> float:
+    """max |got - ref| / RMS(ref)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if rms == 0:
+        return float(np.abs(got - ref).max(initial=0.0))
+    return float(np.abs(got - ref).max(initial=0.0) / rms)
+
+
+_MANT = {"bf16": 8, "f32": 24}
+
+
+def out_err(got, ref, out_dt: str) -> float:
+    """Error of a result delivered in ``out_dt`` against the exact (float64)
+    value, relative to RMS(ref), net of the one final rounding to ``out_dt``
+    that the definition of the output includes:
+    max_i (|got_i - ref_i| - ulp_i / 2) / RMS(ref), ulp taken at the larger of
+    |got_i|, |ref_i| (0 when the result is at most half an ulp off)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    _, e = np.frexp(np.maximum(np.abs(got), np.abs(ref)))
+    half_ulp = np.ldexp(1.0, e - _MANT[out_dt] - 1)
+    ex = np.maximum(np.abs(got - ref) - half_ulp, 0.0).max(initial=0.0)
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(ex / rms) if rms > 0 else float(ex)
+
+
+def quantize_inputs(inp):
+    """INT4 codes and scales of the expert weights, from the oracle's quantiser."""
+    return {n: orc.quantize_int4(getattr(inp, n).numpy()) for n in ("wg", "wu", "wd")}
+
+
+def oracle_weights(inp, q=None):
+    if inp.cfg.w_dtype == "i4g128":
+        q = q or quantize_inputs(inp)
+        return orc.LayerWeights(qg=q["wg"], qu=q["wu"], qd=q["wd"])
+    return orc.LayerWeights(wg=as_f64(inp.wg), wu=as_f64(inp.wu), wd=as_f64(inp.wd))
+
+
+def device_weights(inp, q=None, dev="cuda"):
+    import sparse_mixture_experts_lds_amd as moe
+    cfg = inp.cfg
+
+    def d(t):
+        return None if t is None else t.to(dev).contiguous()
+    if cfg.w_dtype == "i4g128":
+        q = q or quantize_inputs(inp)
+        wg, sg = (torch.from_numpy(q["wg"][0]).to(dev), torch.from_numpy(q["wg"][1]).to(dev))
+        wu, su = (torch.from_numpy(q["wu"][0]).to(dev), torch.from_numpy(q["wu"][1]).to(dev))
+        wd, sd = (torch.from_numpy(q["wd"][0]).to(dev), torch.from_numpy(q["wd"][1]).to(dev))
+    else:
+        wg, wu, wd = d(inp.wg), d(inp.wu), d(inp.wd)
+        sg = su = sd = None
+    emap = torch.from_numpy(inp.expert_map).to(dev) if inp.expert_map is not None else None
+    return moe.LayerWeights(E=cfg.E, k=cfg.k, act=cfg.act, renorm=cfg.renorm, wg=wg, wu=wu, wd=wd,
+                            sg=sg, su=su, sd=sd, w_router=d(inp.w_router), bias=d(inp.bias),
+                            expert_map=emap, capacity=inp.capacity, wsg=d(inp.wsg), wsu=d(inp.wsu),
+                            wsd=d(inp.wsd))
+
+
+def sample_tokens(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed + 17)
+    s = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+def shared_f64(inp):
+    if inp.wsg is None:
+        return None
+    return (as_f64(inp.wsg), as_f64(inp.wsu), as_f64(inp.wsd))
+
+
+def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
+    """Run the GPU layer and check it against the oracle with the comparison
+    protocol: selection bit-exact on the GPU's own fp32 logits, grouping
+    bit-exact on the GPU's ids, outputs within the dtype tolerance of the
+    oracle (run with the GPU's ids only where a near-tie legitimately flipped)."""
+    import sparse_mixture_experts_lds_amd as moe
+    cfg = inp.cfg
+    dev = "cuda"
+    wdev = wdev or device_weights(inp, q, dev)
+    x = inp.x.to(dev)
+    logits_dev = inp.logits.to(dev) if inp.logits is not None else None
+    out, tr = moe.layer_fwd(x, wdev, logits=logits_dev, trace=True)
+    torch.cuda.synchronize()
+    ids_g = tr["topk_ids"].cpu().numpy().astype(np.int64)
+    tw_g = tr["topk_w"].cpu().numpy().astype(np.float64)
+    if "logits" in tr:
+        Lg = tr["logits"].cpu().numpy().astype(np.float64)
+    else:
+        Lg = as_f64(inp.logits) + (as_f64(inp.bias)[None, :] if inp.bias is not None else 0.0)
+    # (a) selection and gates on the GPU's own logits
+    ids_a = orc.select_topk(Lg, cfg.k)
+    np.testing.assert_array_equal(ids_g, ids_a)
+    w_a = orc.gates(Lg, ids_a, cfg.renorm)
+    assert np.abs(w_a - tw_g).max() <= 1e-6
+    # (c) grouping of the GPU's ids, bit-exact
+    offs, sp, pos = orc.permute(ids_g, inp.expert_map, cfg.E_loc, inp.capacity)
+    np.testing.assert_array_equal(tr["expert_offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(tr["pair_pos"].cpu().numpy(), pos)
+    # (b) end to end against the independent oracle
+    Wo = oracle_weights(inp, q)
+    x64 = as_f64(inp.x)
+    kw = dict(w_router=as_f64(inp.w_router), logits=as_f64(inp.logits), bias=as_f64(inp.bias),
+              expert_map=inp.expert_map, capacity=inp.capacity, shared=shared_f64(inp),
+              tokens=tokens)
+    r = orc.moe_layer(x64, Wo, cfg.k, cfg.renorm, cfg.act, **kw)
+    flipped = 0
+    if not np.array_equal(r["ids"], ids_g):
+        L = r["L"]
+        srt = -np.sort(-L, axis=1)
+        margin = srt[:, cfg.k - 1] - srt[:, cfg.k] if cfg.k < L.shape[1] else np.full(L.shape[0], np.inf)
+        bad = np.nonzero((r["ids"] != ids_g).any(1))[0]
+        tau = 1e-4 * np.sqrt(np.mean(L ** 2))
+        assert np.all(margin[bad] < tau), "top-k mismatch outside near-ties"
+        flipped = bad.size
+        r = orc.moe_layer(x64, Wo, cfg.k, cfg.renorm, cfg.act, ids=ids_g, **kw)
+    got = out.float().cpu().numpy()[r["tokens"]]
+    err = out_err(got, r["out"], cfg.dtype)
+    if report is not None:
+        report.update(err=err, flipped=flipped, tokens=len(r["tokens"]))
+    assert err <= TOL[cfg.w_dtype if cfg.w_dtype != "bf16" else "bf16"], \
+        "relative error %.3g above tolerance (flipped %d)" % (err, flipped)
+    return out, tr, err

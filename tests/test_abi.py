@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every function the header declares, and
+rejects bad arguments before touching the GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_lds_amd as moe
+from sparse_mixture_experts_lds_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe_lds.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.load()
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_texts():
+    lib = moe.load()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.moe_strerror(code)
+    assert lib.moe_last_error() == b""
+
+
+def test_argument_errors_before_launch():
+    lib = moe.load()
+    P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    # k > E, k = 0, E beyond the limit, d not a multiple of 64
+    assert lib.moe_route(4, 64, 8, 9, 0, P, P, None, None, 1, P, P, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_route(4, 64, 8, 0, 0, P, P, None, None, 1, P, P, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_route(4, 64, 2048, 2, 0, P, P, None, None, 1, P, P, None, None) == _lib.MOE_EUNSUPPORTED
+    assert lib.moe_route(4, 65, 8, 2, 0, P, P, None, None, 1, P, P, None, None) == _lib.MOE_EUNSUPPORTED
+    assert lib.moe_route(4, 64, 8, 2, 0, None, P, None, None, 1, P, P, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_route(4, 64, 8, 2, 7, P, P, None, None, 1, P, P, None, None) == _lib.MOE_EUNSUPPORTED
+    # permute: workspace too small, E_loc without a map, negative capacity
+    need = lib.moe_permute_workspace_bytes(100, 2, 8)
+    assert need > 0
+    assert lib.moe_permute(100, 2, 8, P, None, 8, 0, P, P, P, None, 0, 1, None, P, need - 1, None) == _lib.MOE_EWORKSPACE
+    assert lib.moe_permute(100, 2, 8, P, None, 4, 0, P, P, P, None, 0, 1, None, P, need, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute(100, 2, 8, P, None, 8, -1, P, P, P, None, 0, 1, None, P, need, None) == _lib.MOE_EINVAL
+    # expert FFN: fp32 activations with bf16 weights; INT4 with d % 128 != 0; missing scales
+    nb = lib.moe_expert_ffn_workspace_bytes(4, 64, 256, 128, 1)
+    assert lib.moe_expert_ffn(4, 64, 256, 128, 0, 0, 1, P, P, P, P, P, None, None, None, P, P, nb, None) == _lib.MOE_EUNSUPPORTED
+    assert lib.moe_expert_ffn(4, 64, 192, 128, 0, 1, 2, P, P, P, P, P, P, P, P, P, P, nb, None) == _lib.MOE_EUNSUPPORTED
+    assert lib.moe_expert_ffn(4, 64, 256, 128, 0, 1, 2, P, P, P, P, P, None, P, P, P, P, nb, None) == _lib.MOE_EINVAL
+    assert lib.moe_expert_ffn(4, 64, 256, 128, 0, 1, 1, P, P, P, P, P, None, None, None, P, P, nb - 1, None) == _lib.MOE_EWORKSPACE
+    assert lib.moe_expert_ffn(4, 64, 256, 128, 5, 1, 1, P, P, P, P, P, None, None, None, P, P, nb, None) == _lib.MOE_EUNSUPPORTED
+    # combine: k too large
+    assert lib.moe_combine(4, 64, 128, 1, P, P, P, None, P, None) == _lib.MOE_EUNSUPPORTED
+    # quantiser: K not a multiple of 128
+    assert lib.moe_quantize_int4(4, 200, P, P, P, None) == _lib.MOE_EUNSUPPORTED
+
+
+def _desc(**over):
+    L = _lib.LayerDesc()
+    base = dict(T=64, d=128, E=8, k=2, h=128, act=0, act_dtype=1, w_dtype=1, renorm=1, capacity=0,
+                E_loc=8, h_shared=0)
+    base.update(over)
+    for k, v in base.items():
+        setattr(L, k, v)
+    L.w_router = L.w_gate = L.w_up = L.w_down = 16
+    return L
+
+
+def test_layer_workspace_and_validation():
+    lib = moe.load()
+    L = _desc()
+    nb = lib.moe_layer_workspace_bytes(ctypes.byref(L))
+    assert nb > 64 * 2 * 128 * 2  # at least the expert outputs
+    # a bigger T needs more workspace
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(_desc(T=640))) > nb
+    # shared expert adds its buffers
+    Ls = _desc(h_shared=128)
+    Ls.ws_gate = Ls.ws_up = Ls.ws_down = 16
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(Ls)) > nb
+    P = ctypes.c_void_p(16)
+    assert lib.moe_layer_fwd(ctypes.byref(L), P, None, P, None, P, nb - 1, None) == _lib.MOE_EWORKSPACE
+    bad = _desc(E_loc=4)  # E_loc != E without an expert map
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.moe_layer_fwd(ctypes.byref(bad), P, None, P, None, P, 1 << 30, None) == _lib.MOE_EINVAL
+    i4 = _desc(w_dtype=2)  # INT4 without scales
+    assert lib.moe_layer_fwd(ctypes.byref(i4), P, None, P, None, P, 1 << 30, None) == _lib.MOE_EINVAL
+    f32i4 = _desc(act_dtype=0, w_dtype=2)
+    assert lib.moe_layer_fwd(ctypes.byref(f32i4), P, None, P, None, P, 1 << 30, None) == _lib.MOE_EUNSUPPORTED
+    # no router weights and no logits
+    nr = _desc()
+    nr.w_router = None
+    assert lib.moe_layer_fwd(ctypes.byref(nr), P, None, P, None, P, 1 << 30, None) == _lib.MOE_EINVAL
+
+
+@pytest.mark.parametrize("T", [0])
+def test_empty_batch_layer_is_a_no_op(T):
+    lib = moe.load()
+    L = _desc(T=T)
+    nb = lib.moe_layer_workspace_bytes(ctypes.byref(L))
+    assert lib.moe_layer_fwd(ctypes.byref(L), None, None, None, None, None, nb, None) == _lib.MOE_OK

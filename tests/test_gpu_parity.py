@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Integer work (top-k ids, grouping, INT4 codes) must match bit for bit; float
+outputs must be within tol * RMS(ref) of the exact float64 result, tol 1e-5
+for fp32 and 2e-2 for bf16 / INT4, on top of the half ulp of the one final
+rounding to the output dtype (see moe_testutil.out_err).  Top-k selection is compared on the GPU's own fp32 logits
+(both sides decide in the same precision); end-to-end outputs are compared
+with the independent oracle, and only tokens whose oracle top-k margin is a
+near-tie may legitimately select differently.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from moe_synth import CONFIGS, make_inputs, scaled
+from moe_synth.generate import as_f64
+from moe_testutil import (TOL, check_layer, device_weights, oracle_weights, out_err, quantize_inputs,
+                          relerr, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _moe():
+    import sparse_mixture_experts_lds_amd as moe
+    moe.load()  # fail loudly if the library is missing
+    return moe
+
+
+# ------------------------------------------------------------------ scaled workloads
+SCALED = {
+    "tiny_fp32": CONFIGS["tiny_fp32"],
+    "granular_small": scaled("granular_bf16", T=512, d=256, E=48, h=128, h_shared=256),
+    "wide_geglu_small": scaled("wide_geglu_bf16", T=1024, d=256, E=8, h=512),
+    "decode_small": scaled("decode_bf16", T=136, d=512, E=32, h=256, h_shared=256),
+    "int4_small": scaled("int4_share", T=72, d=512, E=64, h=256, owners=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SCALED))
+def test_layer_scaled_workloads(name):
+    _moe()
+    inp = make_inputs(SCALED[name])
+    rep = {}
+    check_layer(inp, report=rep)
+    print(name, rep)
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("T", [1, 17, 100])
+def test_ragged_and_single_token_batches(T):
+    _moe()
+    check_layer(make_inputs(scaled("granular_bf16", T=T, d=128, E=16, h=64, h_shared=64)))
+
+
+def test_heavy_capacity_drops():
+    _moe()
+    cfg = scaled("granular_bf16", T=400, d=128, E=16, h=64, h_shared=0, capacity_factor=0.5)
+    inp = make_inputs(cfg)
+    out, tr, _ = check_layer(inp)
+    pos = tr["pair_pos"].cpu().numpy()
+    assert (pos < 0).sum() >= 0.4 * pos.size  # half the pairs cannot fit
+
+
+def test_all_tokens_to_one_expert():
+    moe = _moe()
+    cfg = scaled("wide_geglu_bf16", T=700, d=128, E=8, h=128, zipf_bias=None)
+    inp = make_inputs(cfg)
+    inp.bias = torch.tensor([0.0] * 7 + [1000.0], dtype=torch.float32)  # expert 7 wins slot 0 everywhere
+    out, tr, _ = check_layer(inp)
+    offs = tr["expert_offsets"].cpu().numpy()
+    assert offs[8] - offs[7] == 700
+
+
+def test_zero_input_gives_zero_output_and_first_k_ids():
+    moe = _moe()
+    cfg = scaled("decode_bf16", T=64, d=256, E=16, h=128, h_shared=128)
+    inp = make_inputs(cfg)
+    inp.x = torch.zeros_like(inp.x)
+    out, tr, _ = check_layer(inp)
+    assert torch.all(out == 0)
+    ids = tr["topk_ids"].cpu().numpy()
+    assert np.all(ids == np.arange(cfg.k))
+    np.testing.assert_allclose(tr["topk_w"].cpu().numpy(), 1.0 / cfg.E, rtol=1e-6)
+
+
+def test_k_equals_E():
+    _moe()
+    check_layer(make_inputs(scaled("tiny_fp32", T=48, E=4, k=4)))
+
+
+def test_int4_share_with_no_local_hits():
+    moe = _moe()
+    cfg = scaled("int4_share", T=32, d=256, E=64, h=128, owners=8, k=2)
+    inp = make_inputs(cfg)
+    # all routing mass on experts 1 and 2 (owned by owners 1 and 2, not by owner 0)
+    L = torch.full((cfg.T, cfg.E), -50.0)
+    L[:, 1] = 5.0
+    L[:, 2] = 4.0
+    inp.logits = L
+    out, tr, _ = check_layer(inp)
+    assert torch.all(out == 0)
+    assert int(tr["expert_offsets"][-1]) == 0
+
+
+def test_layer_is_deterministic():
+    moe = _moe()
+    inp = make_inputs(SCALED["granular_small"])
+    w = device_weights(inp)
+    x = inp.x.to(DEV)
+    a = moe.layer_fwd(x, w)
+    b = moe.layer_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ entry points one by one
+@pytest.mark.parametrize("E,k,dt", [(8, 2, torch.float32), (192, 4, torch.bfloat16), (896, 16, torch.bfloat16),
+                                    (33, 5, torch.bfloat16), (1024, 32, torch.bfloat16)])
+def test_route_entry_point(E, k, dt):
+    moe = _moe()
+    rng = np.random.default_rng(E + k)
+    T, d = 131, 128
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dt)
+    w = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(dt)
+    b = torch.from_numpy(rng.standard_normal(E).astype(np.float32))
+    for renorm in (True, False):
+        ids, tw, L = moe.route(x.to(DEV), w.to(DEV), k, renorm, bias=b.to(DEV), want_logits=True)
+        Lg = L.cpu().numpy().astype(np.float64)
+        Lo = orc.router_logits(as_f64(x), as_f64(w), as_f64(b))
+        assert relerr(Lg, Lo) <= (1e-5 if dt == torch.float32 else 1e-4)
+        ids_o = orc.select_topk(Lg, k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+        assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
+
+
+def test_route_ties_from_given_logits():
+    moe = _moe()
+    rng = np.random.default_rng(3)
+    L = rng.integers(-2, 3, size=(200, 96)).astype(np.float32)  # many exact ties
+    ids, tw, _ = moe.route(None, None, 8, True, logits=torch.from_numpy(L).to(DEV))
+    ref = np.argsort(-L.astype(np.float64), axis=1, kind="stable")[:, :8]
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,k,E,owners,cap", [(1000, 2, 8, 1, 0), (8192, 4, 192, 1, 214), (512, 16, 896, 32, 0),
+                                              (3000, 8, 128, 4, 40), (5, 3, 7, 1, 1), (4500, 2, 1024, 1, 0)])
+def test_permute_entry_point_bit_exact(T, k, E, owners, cap):
+    moe = _moe()
+    rng = np.random.default_rng(T + E)
+    Lz = rng.standard_normal((T, E)) + np.linspace(1.5, 0, E)
+    ids = orc.select_topk(Lz, k).astype(np.int32)
+    emap = None
+    E_loc = E
+    if owners > 1:
+        emap = np.full(E, -1, np.int32)
+        mine = np.arange(0, E, owners)
+        emap[mine] = np.arange(mine.size)
+        E_loc = mine.size
+    d = 64
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    offs, sp, pos, xp = moe.permute(torch.from_numpy(ids).to(DEV), E, E_loc,
+                                    torch.from_numpy(emap).to(DEV) if emap is not None else None, cap,
+                                    x=x.to(DEV))
+    o_offs, o_sp, o_pos = orc.permute(ids, emap, E_loc, cap)
+    np.testing.assert_array_equal(offs.cpu().numpy(), o_offs)
+    n = int(o_offs[-1])
+    np.testing.assert_array_equal(sp.cpu().numpy()[:n], o_sp)
+    np.testing.assert_array_equal(pos.cpu().numpy(), o_pos)
+    assert torch.equal(xp[:n].cpu(), x[torch.from_numpy(o_sp // k)])
+
+
+@pytest.mark.parametrize("wdt,act", [("bf16", "swiglu"), ("bf16", "geglu"), ("f32", "swiglu"),
+                                     ("i4g128", "swiglu"), ("i4g128", "geglu")])
+@pytest.mark.parametrize("counts", [[0, 5, 130, 1, 0, 64, 17], [300], [16, 16, 16, 16]])
+def test_expert_ffn_entry_point(wdt, act, counts):
+    moe = _moe()
+    rng = np.random.default_rng(len(counts) * 7 + len(wdt))
+    E_loc = len(counts)
+    d, h = 256, 384
+    rows = int(sum(counts))
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    adt = torch.float32 if wdt == "f32" else torch.bfloat16
+    a = torch.from_numpy(rng.standard_normal((rows, d)).astype(np.float32)).to(adt)
+    wg = (rng.standard_normal((E_loc, h, d)) / np.sqrt(d)).astype(np.float32)
+    wu = (rng.standard_normal((E_loc, h, d)) / np.sqrt(d)).astype(np.float32)
+    wd = (rng.standard_normal((E_loc, d, h)) / np.sqrt(h)).astype(np.float32)
+    if wdt == "i4g128":
+        qs = [orc.quantize_int4(w) for w in (wg, wu, wd)]
+        y = moe.expert_ffn(a.to(DEV), torch.from_numpy(offs).to(DEV),
+                           *[torch.from_numpy(q[0]).to(DEV) for q in qs], act=act,
+                           sg=torch.from_numpy(qs[0][1]).to(DEV), su=torch.from_numpy(qs[1][1]).to(DEV),
+                           sd=torch.from_numpy(qs[2][1]).to(DEV))
+        W = [orc.dequantize_int4(*q) for q in qs]
+    else:
+        wt = [torch.from_numpy(w).to(adt) for w in (wg, wu, wd)]
+        y = moe.expert_ffn(a.to(DEV), torch.from_numpy(offs).to(DEV), *[w.to(DEV) for w in wt], act=act)
+        W = [as_f64(w) for w in wt]
+    yg = y.float().cpu().numpy()
+    ref = np.zeros((rows, d))
+    a64 = as_f64(a)
+    for e in range(E_loc):
+        sl = slice(offs[e], offs[e + 1])
+        if offs[e + 1] > offs[e]:
+            ref[sl] = orc.gated_ffn(a64[sl], W[0][e], W[1][e], W[2][e], act)
+    assert out_err(yg, ref, "f32" if wdt == "f32" else "bf16") <= TOL[wdt]
+
+
+def test_expert_ffn_single_group_without_offsets():
+    moe = _moe()
+    rng = np.random.default_rng(11)
+    T, d, h = 77, 128, 256
+    a = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    ws = [torch.from_numpy((rng.standard_normal(s) / np.sqrt(s[-1])).astype(np.float32)).to(torch.bfloat16)
+          for s in [(1, h, d), (1, h, d), (1, d, h)]]
+    y = moe.expert_ffn(a.to(DEV), None, *[w.to(DEV) for w in ws], act="swiglu")
+    ref = orc.gated_ffn(as_f64(a), as_f64(ws[0][0]), as_f64(ws[1][0]), as_f64(ws[2][0]), "swiglu")
+    assert out_err(y.float().cpu().numpy(), ref, "bf16") <= 2e-2
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_combine_entry_point(dt):
+    moe = _moe()
+    rng = np.random.default_rng(5)
+    T, k, d = 300, 4, 256
+    rows = 900
+    y = torch.from_numpy(rng.standard_normal((rows, d)).astype(np.float32)).to(dt)
+    pos = rng.integers(-1, rows, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    sh = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dt)
+    for shared in (None, sh):
+        out = moe.combine(y.to(DEV), torch.from_numpy(pos).to(DEV).reshape(-1), torch.from_numpy(w).to(DEV),
+                          None if shared is None else shared.to(DEV))
+        y64 = as_f64(y)
+        slots = np.where((pos >= 0)[..., None], y64[np.maximum(pos, 0)], 0.0)
+        ref = orc.combine(slots, pos, w.astype(np.float64), None if shared is None else as_f64(shared))
+        tol = 1e-6 if dt == torch.float32 else 2e-2
+        assert out_err(out.float().cpu().numpy(), ref, "f32" if dt == torch.float32 else "bf16") <= tol
+
+
+def test_quantize_entry_point_bit_exact():
+    moe = _moe()
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((300, 1024)) / 32).astype(np.float32)
+    w[0, :128] = 0.0                  # zero group
+    w[1, :128] = 1e-9                 # scale rounds to zero
+    w[2, :128] = 0.0
+    w[2, :6] = [0.875, 0.3125, 0.4375, -0.0625, -0.1875, -0.875]  # exact halves
+    p, s = moe.quantize_int4(torch.from_numpy(w).to(DEV))
+    po, so = orc.quantize_int4(w)
+    np.testing.assert_array_equal(p.cpu().numpy(), po)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint16), so.view(np.uint16))
+
+
+# ------------------------------------------------------------------ full-size workloads
+@pytest.mark.parametrize("name", ["tiny_fp32", "granular_bf16", "wide_geglu_bf16", "decode_bf16",
+                                  "int4_share"])
+def test_layer_full_size(name):
+    _moe()
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg)
+    rep = {}
+    check_layer(inp, tokens=sample_tokens(cfg.T, 48), report=rep)
+    print(name, rep)
