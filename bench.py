@@ -42,6 +42,9 @@ def parse_args(argv=None):
     p.add_argument("--warm-cache", action="store_true", help="do not flush the Infinity Cache between steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes (5 times), to scale hardware "
+                        "byte counters against a kernel of known traffic")
     return p.parse_args(argv)
 
 
@@ -154,6 +157,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 3
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
     cfg = CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)

@@ -28,6 +28,7 @@ class LayerDesc(ctypes.Structure):
         ("s_gate", _vp), ("s_up", _vp), ("s_down", _vp),
         ("h_shared", _c_int),
         ("ws_gate", _vp), ("ws_up", _vp), ("ws_down", _vp),
+        ("tile_m", _c_int), ("tile_n_up", _c_int), ("tile_n_down", _c_int),
     ]
 
 

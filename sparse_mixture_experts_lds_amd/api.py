@@ -162,6 +162,7 @@ class LayerWeights:
     wsg: Optional[torch.Tensor] = None
     wsu: Optional[torch.Tensor] = None
     wsd: Optional[torch.Tensor] = None
+    tiles: tuple = (0, 0, 0)   # (tile_m, tile_n_up, tile_n_down) hints, 0 = automatic
 
     def desc(self, T: int, d: int, act_dtype: int) -> LayerDesc:
         E_loc, h = self.wg.shape[0], self.wg.shape[1]
@@ -179,6 +180,7 @@ class LayerWeights:
             p = _p(t)
             setattr(L, name, p.value if p is not None else None)
         L.h_shared = self.wsg.shape[0] if self.wsg is not None else 0
+        L.tile_m, L.tile_n_up, L.tile_n_down = (int(v) for v in self.tiles)
         return L
 
 

@@ -22,13 +22,22 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
          "-I", os.path.join(ROOT, "include")]
 
 
+# Per-file flags.  The fp32/bf16 GEMMs (and the router) carry MFMA accumulators
+# across their k-loops; the "VGPR form" keeps those in VGPRs instead of
+# shuffling them through AGPRs around every MFMA.
+FILE_FLAGS = {
+    "ffn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

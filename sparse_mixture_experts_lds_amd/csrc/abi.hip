@@ -1,6 +1,6 @@
 // C ABI of the MoE layer forward (declared in include/moe_lds.h): argument
 // checks, workspace carving and the launch sequence on the caller's stream.
-#include "../../include/moe_lds.h"
+#include "moe_lds.h"
 
 #include <string.h>
 
@@ -73,7 +73,8 @@ int check_route_dims(int T, int E, int k) {
 
 // Gate/up then down over grouped rows; `offsets` NULL means one group.
 int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A,
-            const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile, int BM,
+            const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
+            const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
             const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
             void* mid_event = nullptr) {
@@ -89,6 +90,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   g.out = z;
   g.offsets = offsets;
   g.mtile_start = mtile;
+  g.tile_tab = tile_tab;
   g.E_loc = E_loc;
   g.rows_max = rows_max;
   g.K = d;
@@ -139,10 +141,30 @@ int check_layer(const moe_layer_desc* L) {
     if (L->h_shared % 64) return MOE_EUNSUPPORTED;
     if (!L->ws_gate || !L->ws_up || !L->ws_down) return MOE_EINVAL;
   }
+  if (L->tile_m) {
+    const int m = L->tile_m;
+    const int mmax = L->w_dtype == MOE_I4G128 ? 64 : (L->w_dtype == MOE_F32 ? 32 : 128);
+    if ((m != 16 && m != 32 && m != 64 && m != 128) || m > mmax) return MOE_EUNSUPPORTED;
+  }
+  if (L->tile_n_up && (L->tile_n_up != 64 && L->tile_n_up != 128)) return MOE_EUNSUPPORTED;
+  if (L->tile_n_down && (L->tile_n_down != 64 && L->tile_n_down != 128)) return MOE_EUNSUPPORTED;
+  if (L->tile_n_up == 128 && L->h % 128) return MOE_EUNSUPPORTED;
+  if (L->tile_n_down == 128 && L->d % 128) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
+// The automatic plan, overridden by the descriptor's tile hints.
+FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
+  (void)rows;
+  FfnPlan p = plan_ffn((double)L->T * L->k / L->E, L->d, L->h, wtype_of(L->w_dtype));
+  if (L->tile_m) p.BM = L->tile_m;
+  if (L->tile_n_up) p.NF_up = L->tile_n_up / 64;
+  if (L->tile_n_down) p.NF_down = L->tile_n_down / 64;
+  return p;
+}
+
 struct LayerBufs {
+  int4* tiles;
   int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts;
   float* tw;
   void *z, *y, *zs, *ys;
@@ -157,6 +179,7 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->tw = c.take<float>(P * 4);
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
+  b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, 16) * sizeof(int4));
   b->sorted_pair = c.take<int32_t>(P * 4);
   b->pair_pos = c.take<int32_t>(P * 4);
   b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
@@ -224,7 +247,7 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* exp
   if (ws_bytes < moe_permute_workspace_bytes(T, k, E_loc)) return MOE_EWORKSPACE;
   if (T > 0 && !ws) return MOE_EINVAL;
   hipStream_t s = as_stream(stream);
-  MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr,
+  MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr, nullptr,
                          sorted_pair, pair_pos, static_cast<int32_t*>(ws), s));
   if (x_perm && T > 0)
     MOE_HIP(launch_gather_rows(T * k, d, act_dtype == MOE_BF16, x, sorted_pair, k, expert_offsets + E_loc,
@@ -235,7 +258,8 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* exp
 size_t moe_expert_ffn_workspace_bytes(int E_loc, int rows_max, int d, int h, int act_dtype) {
   (void)d;
   if (E_loc <= 0 || rows_max < 0 || h <= 0 || !act_dtype_ok(act_dtype)) return 0;
-  return align_up((size_t)rows_max * h * 4) + align_up((size_t)(E_loc + 1) * 4);
+  return align_up((size_t)rows_max * h * 4) + align_up((size_t)(E_loc + 1) * 4) +
+         align_up((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
 }
 
 int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype, int w_dtype,
@@ -258,12 +282,13 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   Carver c(ws);
   void* z = c.take<void>((size_t)rows_max * h * 4);
   int32_t* mtile = c.take<int32_t>((size_t)(E_loc + 1) * 4);
+  int4* tab = c.take<int4>((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
   const int wt = wtype_of(w_dtype);
-  const FfnPlan plan = plan_ffn(E_loc, rows_max, d, h, wt);
-  if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, s));
+  const FfnPlan plan = plan_ffn((double)rows_max / E_loc, d, h, wt);
+  if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, tab, s));
   return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, nullptr, 1, expert_offsets,
-                 expert_offsets ? mtile : nullptr, plan.BM, plan, w_gate, w_up, w_down, s_gate, s_up, s_down,
-                 z, y_perm, false, s);
+                 expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
+                 w_down, s_gate, s_up, s_down, z, y_perm, false, s);
 }
 
 int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const int32_t* pair_pos,
@@ -309,7 +334,6 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     return tr.events[i] ? hipEventRecord(static_cast<hipEvent_t>(tr.events[i]), s) : hipSuccess;
   };
   const int rows = layer_rows_max(L);
-  const int wt = wtype_of(L->w_dtype);
 
   MOE_HIP(mark(MOE_EV_START));
   // 1-2: router
@@ -317,12 +341,13 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
                        tr.logits, s));
   MOE_HIP(mark(MOE_EV_ROUTED));
   // 3: grouping (the m-tile prefix of the grouped GEMMs comes out of the same scan)
-  const FfnPlan plan = plan_ffn(L->E_loc, rows, L->d, L->h, wt);
+  const FfnPlan plan = layer_plan(L, rows);
   MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
-                         b.sorted_pair, pair_pos, b.counts, s));
+                         b.tiles, b.sorted_pair, pair_pos, b.counts, s));
   MOE_HIP(mark(MOE_EV_GROUPED));
   // 4: routed experts, activations gathered straight from x by pair index
-  rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, b.sorted_pair, k, offsets, b.mtile, plan.BM,
+  rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, b.sorted_pair, k, offsets, b.mtile, b.tiles,
+               plan.BM,
                plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, true, s,
                tr.events[MOE_EV_GATE_UP]);
   if (rc) return rc;
@@ -331,8 +356,8 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const void* shared_y = nullptr;
   if (L->h_shared > 0) {
     const int swt = L->act_dtype;  // shared weights are in the activation dtype
-    const FfnPlan sp = plan_ffn(1, T, L->d, L->h_shared, wtype_of(swt));
-    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, nullptr, 1, nullptr, nullptr, sp.BM, sp, L->ws_gate,
+    const FfnPlan sp = plan_ffn((double)T, L->d, L->h_shared, wtype_of(swt));
+    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp, L->ws_gate,
                  L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, s);
     if (rc) return rc;
     shared_y = b.ys;

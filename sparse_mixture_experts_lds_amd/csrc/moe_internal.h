@@ -66,13 +66,15 @@ struct PermuteWs {
 };
 size_t permute_ws_bytes(int P, int E_loc);
 int permute_block_pairs();
+// mtile_start/tile_tab (may be NULL): the m-tile prefix and per-m-tile table of
+// the grouped GEMMs for tiles of BM rows.
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t* expert_map, int E_loc,
-                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start,
+                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start, int4* tile_tab,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* counts, hipStream_t s);
 hipError_t launch_gather_rows(int rows_max, int d, bool bf16, const void* x, const int32_t* sorted_pair,
                               int k, const int32_t* offsets_end, void* x_perm, hipStream_t s);
 hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_t* mtile_start,
-                               hipStream_t s);
+                               int4* tile_tab, hipStream_t s);
 
 // Grouped GEMMs.
 struct FfnGemmArgs {
@@ -86,6 +88,7 @@ struct FfnGemmArgs {
   void* out;                 // [rows, N]
   const int32_t* offsets;    // [E_loc+1] or NULL (single group of rows_max rows)
   const int32_t* mtile_start;// [E_loc+1] m-tile prefix, or NULL with offsets == NULL
+  const int4* tile_tab;      // per m-tile {expert, first row, rows, 0}, or NULL with offsets == NULL
   int E_loc, rows_max, K, N;
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
@@ -95,7 +98,8 @@ struct FfnPlan {
   int NF_up, NF_down;        // 16-col fragments per wave
   bool split_z;              // z kept in fp32, down projection on its hi/lo bf16 parts
 };
-FfnPlan plan_ffn(int E_loc, int rows_max, int d, int h, int w_type);
+// avg_rows: expected rows per local expert.
+FfnPlan plan_ffn(double avg_rows, int d, int h, int w_type);
 int ffn_max_mtiles(int E_loc, int rows_max, int BM);
 // split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
 hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,

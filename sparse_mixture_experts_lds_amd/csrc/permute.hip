@@ -34,21 +34,26 @@ __device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids, con
   return (e >= 0 && e < E_loc) ? e : -1;
 }
 
-__global__ __launch_bounds__(64) void count_kernel(int P, const int32_t* __restrict__ ids,
-                                                   const int32_t* __restrict__ emap, int E, int E_loc,
-                                                   int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void count_kernel(int P, const int32_t* __restrict__ ids,
+                                                    const int32_t* __restrict__ emap, int E, int E_loc,
+                                                    int32_t* __restrict__ counts) {
   __shared__ int32_t hist[kMaxE];
-  for (int e = threadIdx.x; e < E_loc; e += 64) hist[e] = 0;
+  for (int e = threadIdx.x; e < E_loc; e += 256) hist[e] = 0;
   __syncthreads();
   const int p0 = blockIdx.x * kBlockPairs;
-  const int p1 = min(P, p0 + kBlockPairs);
-  for (int p = p0 + threadIdx.x; p < p1; p += 64) {
-    const int e = local_expert(ids, emap, E, E_loc, p);
-    if (e >= 0) atomicAdd(&hist[e], 1);
+  constexpr int PER = kBlockPairs / 256;
+  int ev[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = p0 + threadIdx.x + 256 * i;
+    ev[i] = p < P ? local_expert(ids, emap, E, E_loc, p) : -1;
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (ev[i] >= 0) atomicAdd(&hist[ev[i]], 1);
   __syncthreads();
   int32_t* out = counts + (size_t)blockIdx.x * E_loc;
-  for (int e = threadIdx.x; e < E_loc; e += 64) out[e] = hist[e];
+  for (int e = threadIdx.x; e < E_loc; e += 256) out[e] = hist[e];
 }
 
 // Block-wide exclusive scan of one value per thread (kScanThreads threads).
@@ -80,20 +85,31 @@ __device__ int block_exclusive_scan(int v, int* total, int* sh /* [kScanThreads/
   return r;
 }
 
+// Per-m-tile table of the grouped GEMMs: {expert, first row, rows, 0}.
+__device__ void write_tiles(int e, int off, int n, int BM, int mstart, int4* __restrict__ tab) {
+  for (int mb = 0, r = 0; r < n; ++mb, r += BM) tab[mstart + mb] = int4{e, off + r, min(BM, n - r), 0};
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int nblk, int E_loc, int capacity, int BM,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ mtile_start) {
+                                                            int32_t* __restrict__ mtile_start,
+                                                            int4* __restrict__ tile_tab) {
   __shared__ int sh[kScanThreads / 64 + 1];
   const int e = threadIdx.x;
   int kept = 0;
   if (e < E_loc) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int32_t* c = counts + (size_t)b * E_loc + e;
-      const int v = *c;
-      *c = run;  // exclusive base of block b for expert e
-      run += v;
+    constexpr int U = 16;  // blocks read per batch, all loads in flight together
+    for (int b0 = 0; b0 < nblk; b0 += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = b0 + u < nblk ? counts[(size_t)(b0 + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u < nblk) counts[(size_t)(b0 + u) * E_loc + e] = run;  // exclusive base of the block
+        run += v[u];
+      }
     }
     kept = capacity > 0 ? min(run, capacity) : run;
   }
@@ -107,6 +123,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int nblk, int E_loc,
     const int moff = block_exclusive_scan(mt, &mtotal, sh);
     if (e < E_loc) mtile_start[e] = moff;
     if (e == 0) mtile_start[E_loc] = mtotal;
+    if (tile_tab != nullptr && e < E_loc) write_tiles(e, off, kept, BM, moff, tile_tab);
   }
 }
 
@@ -128,9 +145,19 @@ __global__ __launch_bounds__(64) void scatter_kernel(int P, const int32_t* __res
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int p0 = blockIdx.x * kBlockPairs;
   const int p1 = min(P, p0 + kBlockPairs);
-  for (int c = p0; c < p1; c += 64) {
+  constexpr int NCHK = kBlockPairs / 64;
+  int ev[NCHK];  // the block's local expert ids, loaded up front
+#pragma unroll
+  for (int i = 0; i < NCHK; ++i) {
+    const int p = p0 + 64 * i + lane;
+    ev[i] = p < p1 ? local_expert(ids, emap, E, E_loc, p) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < NCHK; ++i) {
+    const int c = p0 + 64 * i;
+    if (c >= p1) break;
     const int p = c + lane;
-    const int e = p < p1 ? local_expert(ids, emap, E, E_loc, p) : -1;
+    const int e = ev[i];
     const int key = e + 1;  // 0 = not local / inactive lane
     uint64_t peers = ~0ull;
 #pragma unroll
@@ -155,7 +182,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(int P, const int32_t* __res
 }
 
 __global__ __launch_bounds__(1024) void mtile_kernel(int E_loc, int BM, const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ mtile_start) {
+                                                     int32_t* __restrict__ mtile_start, int4* __restrict__ tile_tab) {
   __shared__ int sh[kScanThreads / 64 + 1];
   const int e = threadIdx.x;
   const int n = e < E_loc ? offsets[e + 1] - offsets[e] : 0;
@@ -163,6 +190,7 @@ __global__ __launch_bounds__(1024) void mtile_kernel(int E_loc, int BM, const in
   const int moff = block_exclusive_scan((n + BM - 1) / BM, &total, sh);
   if (e < E_loc) mtile_start[e] = moff;
   if (e == 0) mtile_start[E_loc] = total;
+  if (e < E_loc) write_tiles(e, offsets[e], n, BM, moff, tile_tab);
 }
 
 template <typename V>
@@ -196,7 +224,7 @@ size_t permute_ws_bytes(int P, int E_loc) {
 }
 
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t* expert_map, int E_loc,
-                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start,
+                          int capacity, int BM, int32_t* offsets, int32_t* mtile_start, int4* tile_tab,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* counts, hipStream_t s) {
   const int P = T * k;
   if (P == 0) {
@@ -204,16 +232,16 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t
     return hipGetLastError();
   }
   const int nblk = (P + kBlockPairs - 1) / kBlockPairs;
-  count_kernel<<<nblk, 64, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
-  scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E_loc, capacity, BM, counts, offsets, mtile_start);
+  count_kernel<<<nblk, 256, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
+  scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E_loc, capacity, BM, counts, offsets, mtile_start, tile_tab);
   scatter_kernel<<<nblk, 64, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets, sorted_pair,
                                      pair_pos);
   return hipGetLastError();
 }
 
 hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_t* mtile_start,
-                               hipStream_t s) {
-  mtile_kernel<<<1, 1024, 0, s>>>(E_loc, BM, offsets, mtile_start);
+                               int4* tile_tab, hipStream_t s) {
+  mtile_kernel<<<1, 1024, 0, s>>>(E_loc, BM, offsets, mtile_start, tile_tab);
   return hipGetLastError();
 }
 

@@ -50,32 +50,73 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
     f32x4 acc[NF];
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The k-loop runs in chunks of KC MFMA steps: every load of a chunk is
+    // issued before its first MFMA, so each wave keeps KC*(NF+1) loads in flight.
     if constexpr (BF16) {
+      constexpr int KC = 8;
       const uint16_t* x = static_cast<const uint16_t*>(xv);
       const uint16_t* w = static_cast<const uint16_t*>(wv);
-      const uint16_t* xrow = x + (size_t)(tok_ok ? t : 0) * d;
-      for (int k0 = 0; k0 < d; k0 += 32) {
-        u32x4 av = tok_ok ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * q) : u32x4{0, 0, 0, 0};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+      const uint16_t* xrow = x + (size_t)(tok_ok ? t : 0) * d + 8 * q;
+      const uint16_t* wrow[NF];
+      bool e_ok[NF];
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const int e = 16 * (wave + 4 * i) + row;
-          u32x4 bv = u32x4{0, 0, 0, 0};
-          if (e < E) bv = *reinterpret_cast<const u32x4*>(w + (size_t)e * d + k0 + 8 * q);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+      for (int i = 0; i < NF; ++i) {
+        const int e = 16 * (wave + 4 * i) + row;
+        e_ok[i] = e < E;
+        wrow[i] = w + (size_t)(e_ok[i] ? e : 0) * d + 8 * q;
+      }
+      for (int k0 = 0; k0 < d; k0 += 32 * KC) {
+        const int nk = min(KC, (d - k0) / 32);
+        u32x4 av[KC], bv[KC][NF];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const int kk = k0 + 32 * min(c, nk - 1);  // in-bounds re-read past the end; not used
+          av[c] = *reinterpret_cast<const u32x4*>(xrow + kk);
+#pragma unroll
+          for (int i = 0; i < NF; ++i) bv[c][i] = *reinterpret_cast<const u32x4*>(wrow[i] + kk);
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          if (c < nk) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok ? av[c] : u32x4{0, 0, 0, 0});
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
+              acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a, __builtin_bit_cast(bf16x8, e_ok[i] ? bv[c][i] : u32x4{0, 0, 0, 0}), acc[i], 0, 0, 0);
+          }
         }
       }
     } else {
+      constexpr int KC = 16;
       const float* x = static_cast<const float*>(xv);
       const float* w = static_cast<const float*>(wv);
-      const float* xrow = x + (size_t)(tok_ok ? t : 0) * d;
-      for (int k0 = 0; k0 < d; k0 += 4) {
-        const float a = tok_ok ? xrow[k0 + q] : 0.f;
+      const float* xrow = x + (size_t)(tok_ok ? t : 0) * d + q;
+      const float* wrow[NF];
+      bool e_ok[NF];
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-          const int e = 16 * (wave + 4 * i) + row;
-          const float b = (e < E) ? w[(size_t)e * d + k0 + q] : 0.f;
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[i], 0, 0, 0);
+      for (int i = 0; i < NF; ++i) {
+        const int e = 16 * (wave + 4 * i) + row;
+        e_ok[i] = e < E;
+        wrow[i] = w + (size_t)(e_ok[i] ? e : 0) * d + q;
+      }
+      for (int k0 = 0; k0 < d; k0 += 4 * KC) {
+        const int nk = min(KC, (d - k0) / 4);
+        float av[KC], bv[KC][NF];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const int kk = k0 + 4 * min(c, nk - 1);
+          av[c] = xrow[kk];
+#pragma unroll
+          for (int i = 0; i < NF; ++i) bv[c][i] = wrow[i][kk];
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          if (c < nk) {
+            const float a = tok_ok ? av[c] : 0.f;
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
+              acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, e_ok[i] ? bv[c][i] : 0.f, acc[i], 0, 0, 0);
+          }
         }
       }
     }
