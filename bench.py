@@ -77,6 +77,42 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
             "P": P, "touched": touched}
 
 
+GEMM_SOURCES = ("ffn_kernel.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
+FETCH_SCALE = 2.00   # FETCH_SIZE of a plain 256 MiB copy reads half the bytes moved
+WRITE_SCALE = 1.00   # WRITE_SIZE of the same copy reads the bytes moved
+
+
+def gemm_source_hash():
+    """sha256 over the sources of the grouped GEMM kernel, to tell whether a
+    stored counter profile was taken on the kernel as it is now."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_lds_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` ("gate_up" or "down") from the committed
+    rocprofv3 counter summary, scaled by the copy calibration; None when there
+    is no summary or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "ffn_gemm_%s_%s_pmc.txt" % (kernel, workload))
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "#", "-")):
+                    key, val = line.split(":", 1)
+                    kv[key.strip()] = val.strip()
+        if kv.get("gemm_source_sha256") != gemm_source_hash():
+            return None
+        return round(float(kv["fetch_kib_per_launch"]) * 1024 * FETCH_SCALE
+                     + float(kv["write_kib_per_launch"]) * 1024 * WRITE_SCALE)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def roofline_entry(work, ms, peak_tflops):
     """Bound, achieved rate and fraction of peak for `work` done in `ms`."""
     s = ms * 1e-3
@@ -237,7 +273,7 @@ def main(argv=None):
     dom = max(("gate_up", "down"), key=lambda n: seg_ms[n])
     roof = roofline_entry(work[dom], seg_ms[dom], peak)
     roof.update({"kernel": "ffn_gemm_kernel (routed %s)" % dom.replace("_", "/"),
-                 "avg_ms": seg_ms[dom], "traffic": None,
+                 "avg_ms": seg_ms[dom], "traffic": measured_traffic(cfg.name, dom),
                  "algorithmic": {"bytes": work[dom]["bytes"], "flops": work[dom]["flops"]}})
     layer_roof = roofline_entry(work["layer"], ms, peak)
 

@@ -11,9 +11,11 @@
  *   moe_layer_fwd   all of the above, fused where it pays, on one stream
  *
  * Sources of the operation (web pages; section named where the page has one):
- *   "Sharding d'experts" (Kvasir wiki), section "Deux roles": the backbone x
- *     worker cut  ids,p = top_k(softmax(cur @ router), k); the worker's
- *     "3 mat-muls"; x + combine(p, partials) + shared(cur).
+ *   "Sharding d'experts" (Kvasir wiki), section "Deux roles": the backbone /
+ *     worker cut of an MoE layer; the backbone routes once (softmax of the
+ *     router logits, top k), a worker runs the three matrix products of each
+ *     selected expert, and the backbone adds the gate-weighted partial outputs
+ *     and the shared expert's output.
  *   moe_stream.py (MoE-Stream), MoEFFN.forward: bias-free router, optional
  *     per-expert logit bias before the softmax, softmax over all experts, topk,
  *     division of the k gates by their sum, per-expert gather / scatter-add.
@@ -22,8 +24,8 @@
  *   kieve-moe, "Features": top-k GeGLU experts.
  *   ExpertMesh README: group-scaled signed INT4 weights with FP16 group
  *     scales in the [expert, output, packed_input] layout, a stable C ABI,
- *     activation grouping that keeps token and top-k slot identity, and a
- *     weighted top-k reduction.
+ *     per-expert grouping of activations that keeps each token and top-k
+ *     slot, and a reduction of the expert outputs with the top-k weights.
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers unless stated otherwise; the
@@ -134,8 +136,8 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids,
                 void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_expert_ffn - grouped gated expert FFN ("Deux roles": the worker's
- * "3 mat-muls"; ExpertMesh: INT4 SwiGLU routed experts).  For each local
+ * moe_expert_ffn - grouped gated expert FFN ("Deux roles": the three matrix
+ * products a worker runs per expert; ExpertMesh: SwiGLU experts on INT4 weights).  For each local
  * expert e and each row r in [expert_offsets[e], expert_offsets[e+1]):
  *
  *   g = W_gate[e] a,  u = W_up[e] a,  z = act(g) * u,  y_perm[r] = W_down[e] z
@@ -164,8 +166,9 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
                    void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_combine - weighted top-k combine ("Deux roles": combine(p, partials) +
- * shared(cur); ExpertMesh: weighted top-k reduction).
+ * moe_combine - weighted top-k combine ("Deux roles": gate-weighted sum of the
+ * partial outputs plus the shared expert; ExpertMesh data-flow figure: the
+ * expert outputs reduced with the top-k weights).
  *
  *   out[t] = sum_{j ascending, pair_pos[t*k+j] >= 0} topk_w[t,j] * y_perm[pair_pos[t*k+j]]
  *            + shared_y[t]                         (fp32 sum, one final rounding)

@@ -7,23 +7,26 @@ with the HIP library.
 What the layer computes, and where it is stated:
 
 * Router logits and top-k routing.  "Sharding d'experts" (Kvasir wiki),
-  section "Deux rôles", backbone x worker pseudo-code: the backbone computes
-  ``top_k(softmax(cur @ router), 8)`` once and its choice is authoritative.
-  moe_stream.py, ``MoEFFN.forward``: ``gate`` is a bias-free linear layer, an
-  optional per-expert bias is added to the logits before the softmax, the
-  softmax runs over all experts, ``topk`` picks the k largest, and the k
-  weights are divided by their sum.
+  section "Deux rôles", backbone/worker pseudo-code: the backbone multiplies
+  the normed activations by the router matrix, applies a softmax, keeps the 8
+  most probable experts, and that choice is final.  moe_stream.py,
+  ``MoEFFN.forward``: the router is a linear layer without bias, an optional
+  per-expert bias is added to the logits before the softmax, the softmax runs
+  over all experts, the k largest are kept and their weights are divided by
+  their sum.
 * Grouping of (token, slot) pairs by expert.  ExpertMesh README, feature list:
-  "activation grouping" that keeps each token's identity and top-k slot.
-  MoEEvolve "Architecture": capacity-factor dispatch with static shapes, so
-  pairs beyond an expert's capacity are dropped.
+  the activations are grouped per expert while each token's identity and
+  top-k slot are kept.  MoEEvolve "Architecture": capacity-factor dispatch
+  with static shapes, so pairs beyond an expert's capacity are dropped.
 * Expert FFN.  kieve-moe "Features": top-k GeGLU experts; MoEEvolve
   "Architecture": SwiGLU experts and one shared expert that is always active;
-  ExpertMesh runtime list: "INT4 SwiGLU".  The gated form is
-  ``down(act(gate x) * (up x))`` with no biases.
-* Combine.  "Sharding d'experts", "Deux rôles": ``x + combine(p, partials) +
-  shared(cur)``; ExpertMesh data-flow figure: "weighted top-k reduction";
-  moe_stream.py ``MoEFFN.forward``: ``out[mask] += w[mask] * expert_out``.
+  ExpertMesh runtime list: SwiGLU experts with INT4 weights.  The gated form
+  is ``down(act(gate x) * (up x))`` with no biases.
+* Combine.  "Sharding d'experts", "Deux rôles": the backbone adds to the
+  residual the gate-weighted sum of the workers' partial outputs and the shared
+  expert's output; ExpertMesh data-flow figure: the expert outputs are reduced
+  with the top-k weights; moe_stream.py ``MoEFFN.forward``: each expert's
+  output is scaled by its gate and scattered back into the rows it came from.
 * INT4 weights.  ExpertMesh README: group-scaled signed INT4 weights with FP16
   group scales, laid out ``[expert, output, packed_input]``, plus a bit-exact
   NumPy quantiser and dequantiser.
@@ -67,7 +70,7 @@ INT4_GROUP = 128
 def router_logits(x, w_router, bias=None) -> np.ndarray:
     """``L[t, e] = sum_i x[t, i] * Wr[e, i] + b[e]`` in float64.
 
-    "Sharding d'experts", "Deux rôles": ``cur @ router``; moe_stream.py
+    "Sharding d'experts", "Deux rôles": activations times the router matrix; moe_stream.py
     ``MoEFFN.forward``: bias-free ``gate`` linear layer plus the optional
     per-expert bias added before the softmax.
     """
@@ -350,8 +353,9 @@ def combine(y_slots, pair_pos, w, shared_y=None) -> np.ndarray:
     ``y_slots [T, k, d]`` holds each slot's expert output, ``pair_pos [T, k]``
     marks kept slots (>= 0), ``w [T, k]`` the gates:
     ``out[t] = sum_{j ascending, kept} w[t, j] y[t, j] (+ shared_y[t])`` ("Deux
-    rôles": ``combine(p, partials) + shared(cur)``; ExpertMesh: weighted top-k
-    reduction; moe_stream.py: ``out[mask] += w[mask] * expert_out``)."""
+    rôles": gate-weighted partial outputs plus the shared expert; ExpertMesh:
+    expert outputs reduced with the top-k weights; moe_stream.py: each expert's
+    output scaled by its gate and added back into its token's row)."""
     y_slots = np.asarray(y_slots, np.float64)
     T, k, d = y_slots.shape
     kept = np.asarray(pair_pos) >= 0

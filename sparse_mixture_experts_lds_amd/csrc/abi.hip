@@ -72,7 +72,7 @@ int check_route_dims(int T, int E, int k) {
 }
 
 // Gate/up then down over grouped rows; `offsets` NULL means one group.
-int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A,
+int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A, int a_rows,
             const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
@@ -93,6 +93,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   g.tile_tab = tile_tab;
   g.E_loc = E_loc;
   g.rows_max = rows_max;
+  g.a_rows = a_rows;
   g.K = d;
   g.N = h;
   g.act = act == MOE_GEGLU ? 1 : 0;
@@ -109,9 +110,46 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   dn.S1 = nullptr;
   dn.out = y;
   dn.out_f32 = y_f32 ? 1 : 0;
+  dn.a_rows = rows_max;
   dn.K = h;
   dn.N = d;
   MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BM, plan.NF_down, s));
+  return MOE_OK;
+}
+
+// Second stream of the layer forward: the shared expert depends on x only, so it
+// runs beside routing, grouping and the routed experts and is joined back into
+// the caller's stream before the combine.  One stream and two events per
+// (host thread, device), created on first use, default priority, kept for the
+// life of the thread.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+thread_local SideStream g_side[kMaxDevices];
+
+int side_stream(hipStream_t caller, SideStream** out) {
+  int dev = 0;
+  if (caller) MOE_HIP(hipStreamGetDevice(caller, &dev));
+  else MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    int cur = 0;
+    MOE_HIP(hipGetDevice(&cur));
+    if (cur != dev) MOE_HIP(hipSetDevice(dev));
+    hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      ss = SideStream{};
+      return hip_fail(e);
+    }
+  }
+  *out = &ss;
   return MOE_OK;
 }
 
@@ -141,6 +179,9 @@ int check_layer(const moe_layer_desc* L) {
     if (L->h_shared % 64) return MOE_EUNSUPPORTED;
     if (!L->ws_gate || !L->ws_up || !L->ws_down) return MOE_EINVAL;
   }
+  // the grouped GEMMs address activation rows with 32-bit byte offsets
+  const size_t lim = 0xFFFFFFFFull;
+  if ((size_t)L->T * L->d * 4 > lim || (size_t)layer_rows_max(L) * L->h * 4 > lim) return MOE_EUNSUPPORTED;
   if (L->tile_m) {
     const int m = L->tile_m;
     const int mmax = L->w_dtype == MOE_I4G128 ? 64 : (L->w_dtype == MOE_F32 ? 32 : 128);
@@ -166,7 +207,7 @@ FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
 struct LayerBufs {
   int4* tiles;
   int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts;
-  float* tw;
+  float *tw, *logits;
   void *z, *y, *zs, *ys;
 };
 
@@ -177,6 +218,7 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   const size_t eb = elt_bytes(L->act_dtype);
   b->ids = c.take<int32_t>(P * 4);
   b->tw = c.take<float>(P * 4);
+  b->logits = c.take<float>(L->w_router ? (size_t)L->T * L->E * 4 : 0);  // router GEMM output
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
   b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, 16) * sizeof(int4));
@@ -275,6 +317,8 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   if (!w_gate || !w_up || !w_down) return MOE_EINVAL;
   if (w_dtype == MOE_I4G128 && (!s_gate || !s_up || !s_down)) return MOE_EINVAL;
   if (rows_max > 0 && (!x_perm || !y_perm)) return MOE_EINVAL;
+  // the grouped GEMMs address activation rows with 32-bit byte offsets
+  if ((size_t)rows_max * d * 4 > 0xFFFFFFFFull || (size_t)rows_max * h * 4 > 0xFFFFFFFFull) return MOE_EUNSUPPORTED;
   if (ws_bytes < moe_expert_ffn_workspace_bytes(E_loc, rows_max, d, h, act_dtype)) return MOE_EWORKSPACE;
   if (rows_max == 0) return MOE_OK;
   if (!ws) return MOE_EINVAL;
@@ -286,7 +330,7 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   const int wt = wtype_of(w_dtype);
   const FfnPlan plan = plan_ffn((double)rows_max / E_loc, d, h, wt);
   if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, tab, s));
-  return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, nullptr, 1, expert_offsets,
+  return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, rows_max, nullptr, 1, expert_offsets,
                  expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
                  w_down, s_gate, s_up, s_down, z, y_perm, false, s);
 }
@@ -336,32 +380,58 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const int rows = layer_rows_max(L);
 
   MOE_HIP(mark(MOE_EV_START));
-  // 1-2: router
-  MOE_HIP(launch_route(T, L->d, L->E, k, bf16, x, L->w_router, logits_in, L->expert_bias, L->renorm, ids, tw,
-                       tr.logits, s));
-  MOE_HIP(mark(MOE_EV_ROUTED));
-  // 3: grouping (the m-tile prefix of the grouped GEMMs comes out of the same scan)
-  const FfnPlan plan = layer_plan(L, rows);
-  MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
-                         b.tiles, b.sorted_pair, pair_pos, b.counts, s));
-  MOE_HIP(mark(MOE_EV_GROUPED));
-  // 4: routed experts, activations gathered straight from x by pair index
-  rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, b.sorted_pair, k, offsets, b.mtile, b.tiles,
-               plan.BM,
-               plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, true, s,
-               tr.events[MOE_EV_GATE_UP]);
-  if (rc) return rc;
-  MOE_HIP(mark(MOE_EV_DOWN));
-  // 5: shared expert on every token, then the weighted combine
+  // 5a: shared expert on every token, forked onto the side stream
   const void* shared_y = nullptr;
+  SideStream* side = nullptr;
   if (L->h_shared > 0) {
+    if ((rc = side_stream(s, &side))) return rc;
+    MOE_HIP(hipEventRecord(side->fork, s));
+    MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
     const int swt = L->act_dtype;  // shared weights are in the activation dtype
     const FfnPlan sp = plan_ffn((double)T, L->d, L->h_shared, wtype_of(swt));
-    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp, L->ws_gate,
-                 L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, s);
-    if (rc) return rc;
+    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
+                 L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s);
+    // the join is recorded even if a launch failed; on failure the caller's
+    // stream waits for whatever the side stream did take before returning
+    const hipError_t e = hipEventRecord(side->join, side->s);
+    if (rc || e != hipSuccess) {
+      if (e == hipSuccess) (void)hipStreamWaitEvent(s, side->join, 0);
+      return rc ? rc : hip_fail(e);
+    }
     shared_y = b.ys;
   }
+  // 1-4 on the caller's stream; the side stream is joined whatever their outcome
+  auto routed = [&]() -> int {
+    // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
+    const float* lsrc = logits_in;
+    if (!lsrc) {
+      float* lbuf = tr.logits ? tr.logits : b.logits;
+      MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, s));
+      lsrc = lbuf;
+    }
+    MOE_HIP(launch_select(T, L->E, k, lsrc, L->expert_bias, L->renorm, ids, tw, tr.logits, s));
+    MOE_HIP(mark(MOE_EV_ROUTED));
+    // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
+    const FfnPlan plan = layer_plan(L, rows);
+    MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
+                           b.tiles, b.sorted_pair, pair_pos, b.counts, s));
+    MOE_HIP(mark(MOE_EV_GROUPED));
+    // 4: routed experts, activations gathered straight from x by pair index
+    const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
+                          b.tiles, plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down,
+                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP]);
+    if (r) return r;
+    MOE_HIP(mark(MOE_EV_DOWN));
+    return MOE_OK;
+  };
+  rc = routed();
+  // 5b: join the shared expert, then the weighted combine
+  if (side) {
+    const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
+    if (rc) return rc;
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (rc) return rc;
   MOE_HIP(mark(MOE_EV_SHARED));
   MOE_HIP(launch_combine(T, k, L->d, bf16, true, b.y, pair_pos, tw, shared_y, out, s));
   MOE_HIP(mark(MOE_EV_END));

@@ -1,8 +1,9 @@
 // Weighted top-k combine.
 //
-// Operation ("Sharding d'experts", "Deux roles": x + combine(p, partials) +
-// shared(cur); ExpertMesh data-flow figure: weighted top-k reduction;
-// moe_stream.py MoEFFN.forward: out[mask] += w[mask] * expert_out):
+// Operation ("Sharding d'experts", "Deux roles": gate-weighted sum of the
+// partial outputs plus the shared expert; ExpertMesh data-flow figure: expert
+// outputs reduced with the top-k weights; moe_stream.py MoEFFN.forward: each
+// expert's output scaled by its gate and added back into its token's row):
 //   out[t] = sum_{j ascending, pair_pos[t*k+j] >= 0} w[t,j] * y[pair_pos[t*k+j]] + shared_y[t]
 // in fp32, rounded once to the output type.
 //

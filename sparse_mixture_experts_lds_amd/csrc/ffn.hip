@@ -43,6 +43,9 @@ FfnPlan plan_ffn(double avg_rows, int d, int h, int w_type) {
 
 hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM, int NF,
                            hipStream_t s) {
+  // activation rows are addressed with 32-bit byte offsets
+  const size_t gelt = (w_type == W_F32 || split) ? 4 : 2;
+  if (a.a_rows < 0 || (size_t)a.a_rows * (size_t)a.K * gelt > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (w_type == W_F32) return gateup ? launch_mf_nf<W_F32, true, false>(a, BM, NF, s) : launch_mf_nf<W_F32, false, false>(a, BM, NF, s);
   if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);
   if (gateup) return launch_mf_nf<W_BF16, true, false>(a, BM, NF, s);

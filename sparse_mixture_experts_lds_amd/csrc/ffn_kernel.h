@@ -1,7 +1,8 @@
 // Grouped expert GEMM kernel template on MFMA: the gate/up projection fused with the gated
 // activation, and the down projection.
 //
-// Operation ("Sharding d'experts", "Deux roles": the worker's "3 mat-muls";
+// Operation ("Sharding d'experts", "Deux roles": the three matrix products a
+// worker runs per expert;
 // MoEEvolve "Architecture": SwiGLU experts; kieve-moe "Features": GeGLU
 // experts; ExpertMesh README: group-scaled signed INT4 routed experts):
 //   gate/up:  z[r, n] = act(sum_k a[r,k] Wg[e,n,k]) * (sum_k a[r,k] Wu[e,n,k])
@@ -37,6 +38,8 @@
 // out of a word in the order 0,4,1,5,2,6,3,7; the activations are staged in
 // LDS in the same order.
 #pragma once
+
+#include <algorithm>
 
 #include "moe_internal.h"
 
@@ -117,6 +120,12 @@ __device__ __forceinline__ float sum_bf16x8(u32x4 d) {
   return s;
 }
 
+// Tiles one workgroup can hold decoded in LDS (row sources of NT_MAX tiles: 8 KB).
+template <int BM>
+struct TileCap {
+  static constexpr int NT_MAX = 2048 / BM;
+};
+
 template <int WT, int MF, int NF, bool GATEUP, bool SPLIT>
 __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
   using Tr = Traits<WT>;
@@ -138,90 +147,172 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
   constexpr int GV = CHE * GELT / 16;                  // 16-byte global loads per chunk
   constexpr int NCH = (BM * CPR + 255) / 256;          // chunks per thread
   constexpr int STEPS = Tr::QS / Tr::EPS;
-  constexpr int NS = kStages;                          // pipeline depth (prefetch distance NS-1)
+  // register stages (prefetch distance NS-1); the largest tiles keep one stage
+  // less so that two workgroups still fit on a CU
+  constexpr int NS = MF * NB_FR >= 16 ? 3 : kStages;
+  constexpr int NT_MAX = TileCap<BM>::NT_MAX;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_a[NS][NPL][BM * AS * LELT];
-  __shared__ __attribute__((aligned(16))) float lds_s[NS][I4 ? BM : 4];
+  // LDS: the activation double buffer, reused after each tile's k-loop as the
+  // output staging tile; the decoded tiles of this workgroup.
+  constexpr int ABUF = NPL * BM * AS * LELT;
+  constexpr int RING = 2 * ABUF;
+  constexpr int OS_MAX = BN * 4 + 16;  // output row stride in bytes for fp32 outputs (+16 B pad)
+  constexpr int LDS_BYTES = RING > BM * OS_MAX ? RING : BM * OS_MAX;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_s[2][I4 ? BM : 4];
+  __shared__ int4 lds_tile[NT_MAX];      // {expert, row0, rows, n-block}
+  __shared__ int lds_src[NT_MAX][BM];    // source activation row of every tile row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lrow = lane & 15;
   const int q = lane >> 4;
-
-  // ---------------- tile decode (device-side tile count, XCD-contiguous ranges)
   const int N = args.N, K = args.K;
   const int NBLK = N / BN;
+
+  // ---------------- work range of this workgroup
+  // Tiles are numbered R = 0..total-1 in grouped-M order; XCD x = blockIdx % 8
+  // owns the contiguous range [x*per, (x+1)*per) and its S workgroups stride
+  // through it, so the tiles that share a weight slice or activation rows run
+  // side by side on one XCD and hit its L2.
   int total_mt;
   if (args.offsets) total_mt = args.mtile_start[args.E_loc];
   else total_mt = (args.rows_max + BM - 1) / BM;
   const int total = total_mt * NBLK;
-  const int G = gridDim.x;  // multiple of 8
+  const int S = gridDim.x >> 3;  // grid is a multiple of 8
   const int per = (total + 7) / 8;
-  const int slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int R = (blockIdx.x & 7) * per + slot;
-  if (R >= total) return;
-  (void)G;
+  const int lo = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int hi = min(((int)(blockIdx.x & 7) + 1) * per, total);
+  const int ntiles = lo < hi ? min((hi - lo + S - 1) / S, NT_MAX) : 0;
+  if (ntiles == 0) return;
 
-  // Tile order: groups of kGroupM m-tiles, m-tile fastest inside a group, so a
-  // weight slice is re-read by the group's tiles side by side and the group's
-  // activation rows stay in L2 across its n-blocks.
-  int e = 0, row0, nrows, nb;
-  {
+  // ---------------- decode every tile of this workgroup into LDS (once)
+  if (tid < ntiles) {
+    const int R = lo + tid * S;
+    // groups of kGroupM m-tiles, m-tile fastest inside a group
     const int grp = R / (kGroupM * NBLK);
     const int t0 = grp * kGroupM;
     const int gm = min(kGroupM, total_mt - t0);
     const int rr = R - grp * kGroupM * NBLK;
-    nb = rr / gm;
+    const int nb = rr / gm;
     const int t = t0 + (rr - nb * gm);
+    int4 ti;
     if (args.tile_tab) {
-      const int4 ti = args.tile_tab[t];
-      e = ti.x;
-      row0 = ti.y;
-      nrows = ti.z;
+      ti = args.tile_tab[t];
     } else {
-      row0 = t * BM;
-      nrows = min(BM, args.rows_max - row0);
+      ti.x = 0;
+      ti.y = t * BM;
+      ti.z = min(BM, args.rows_max - t * BM);
     }
+    ti.w = nb;
+    lds_tile[tid] = ti;
   }
-  const int n0 = nb * BN;
+  __syncthreads();
+  for (int idx = tid; idx < ntiles * BM; idx += 256) {
+    const int i = idx / BM;
+    const int r = idx - i * BM;
+    const int4 ti = lds_tile[i];
+    const int gr = ti.y + min(r, max(ti.z - 1, 0));
+    lds_src[i][r] = args.row_index ? args.row_index[gr] / args.row_div : gr;
+  }
+  __syncthreads();
 
-  // ---------------- activation staging setup
+  // ---------------- per-tile operand addresses
   // Every lane issues the same loads every k-block (no branches around loads,
-  // so the compiler can count outstanding loads exactly): rows past the tile
-  // end re-read the last valid row and are zeroed, k-blocks past the end re-read
-  // the last block and are zeroed, and lanes without a chunk duplicate one.
+  // so the compiler can count outstanding loads exactly).  Rows past the tile
+  // end re-read the tile's last row: a row of the product depends only on the
+  // same row of the activations, and those rows are never stored.  k-blocks
+  // past the end (padding) re-read the last block and are zeroed.  Activation
+  // rows are 32-bit byte offsets (the activation matrix is below 4 GiB); the
+  // weight slice of a tile is a uniform base plus a fixed per-lane offset.
   constexpr int CH_TOT = BM * CPR;
-  const unsigned char* a_src[NCH];
   int a_dst[NCH];
-  bool a_ok[NCH];
+  int a_row[NCH];
+  uint32_t a_col[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + 256 * j;
     const int ce = c % CH_TOT;
-    const int r = ce / CPR;
-    const int cc = ce - r * CPR;
-    a_dst[j] = c < CH_TOT ? (r * AS + cc * CHE) * LELT : -1;
-    a_ok[j] = r < nrows;
-    const int gr = row0 + min(r, nrows - 1);
-    const int srow = args.row_index ? args.row_index[gr] / args.row_div : gr;
-    a_src[j] = static_cast<const unsigned char*>(args.A) + ((size_t)srow * K + cc * CHE) * GELT;
+    a_row[j] = ce / CPR;
+    const int cc = ce - a_row[j] * CPR;
+    a_col[j] = (uint32_t)(cc * CHE * GELT);
+    a_dst[j] = c < CH_TOT ? (a_row[j] * AS + cc * CHE) * LELT : -1;
   }
+  uint32_t b_lane[NB_FR];  // lane offset of fragment f inside a tile's weight slice (bytes)
+  uint32_t s_lane[NB_FR];  // INT4: lane offset into the scales (elements)
+#pragma unroll
+  for (int f = 0; f < NB_FR; ++f) {
+    const int fl = (GATEUP && f >= NF) ? f - NF : f;
+    const int nl = 16 * (NF * wave + fl) + lrow;
+    if constexpr (I4) {
+      b_lane[f] = (uint32_t)(nl * (K / 2) + q * 16);
+      s_lane[f] = (uint32_t)(nl * (K / kI4Group));
+    } else {
+      b_lane[f] = (uint32_t)((nl * K + q * Tr::QS) * Tr::AELT);
+      s_lane[f] = 0;
+    }
+  }
+  const unsigned char* const Abase = static_cast<const unsigned char*>(args.A);
+  struct Ptrs {
+    uint32_t a[NCH];
+    const unsigned char* w0;
+    const unsigned char* w1;
+    const uint16_t* s0;
+    const uint16_t* s1;
+  };
+  auto setup = [&](int i, Ptrs& P) {
+    const int4 ti = lds_tile[i];
+    const int e = __builtin_amdgcn_readfirstlane(ti.x);
+    const int n0 = __builtin_amdgcn_readfirstlane(ti.w) * BN;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) P.a[j] = (uint32_t)lds_src[i][a_row[j]] * (uint32_t)(K * GELT) + a_col[j];
+    const size_t row_first = (size_t)e * N + n0;  // first weight row of the tile
+    if constexpr (I4) {
+      P.w0 = static_cast<const unsigned char*>(args.W0) + row_first * (size_t)(K / 2);
+      P.w1 = GATEUP ? static_cast<const unsigned char*>(args.W1) + row_first * (size_t)(K / 2) : P.w0;
+      P.s0 = args.S0 + row_first * (size_t)(K / kI4Group);
+      P.s1 = GATEUP ? args.S1 + row_first * (size_t)(K / kI4Group) : P.s0;
+    } else {
+      P.w0 = static_cast<const unsigned char*>(args.W0) + row_first * (size_t)K * Tr::AELT;
+      P.w1 = GATEUP ? static_cast<const unsigned char*>(args.W1) + row_first * (size_t)K * Tr::AELT : P.w0;
+      P.s0 = P.s1 = nullptr;
+    }
+  };
+
   u32x4 a_reg[NS][NCH][GV];
-  auto load_a = [&](int st, int kb) {
+  u32x4 bbuf[NS][NB_FR][Tr::VPB];
+  float sbuf[NS][NB_FR];
+  auto load_a = [&](int st, const Ptrs& P, int kb) {
     const bool kin = kb < K;
-    const int kbe = kin ? kb : K - KB;
+    const unsigned char* base = Abase + (size_t)(kin ? kb : K - KB) * GELT;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
 #pragma unroll
       for (int v = 0; v < GV; ++v) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(a_src[j] + (size_t)kbe * GELT + 16 * v);
-        a_reg[st][j][v] = (kin && a_ok[j]) ? t : u32x4{0, 0, 0, 0};
+        const u32x4 t = *reinterpret_cast<const u32x4*>(base + P.a[j] + 16 * v);
+        a_reg[st][j][v] = kin ? t : u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto store_a = [&](int st, int buf) {
+  auto load_b = [&](int st, const Ptrs& P, int kb) {
+    const int kbe = min(kb, K - KB);  // past the end: re-read the last block (its activations are zero)
+#pragma unroll
+    for (int f = 0; f < NB_FR; ++f) {
+      const bool second = GATEUP && f >= NF;
+      if constexpr (I4) {
+        const unsigned char* w = (second ? P.w1 : P.w0) + kbe / 2;
+        bbuf[st][f][0] = *reinterpret_cast<const u32x4*>(w + b_lane[f]);
+        sbuf[st][f] = half_bits_to_f32(((second ? P.s1 : P.s0) + kbe / kI4Group)[s_lane[f]]);
+      } else {
+        const unsigned char* w = (second ? P.w1 : P.w0) + (size_t)kbe * Tr::AELT;
+#pragma unroll
+        for (int v = 0; v < Tr::VPB; ++v) bbuf[st][f][v] = *reinterpret_cast<const u32x4*>(w + b_lane[f] + 16 * v);
+      }
+    }
+  };
+  auto lds_a_at = [&](int lb, int pl) -> unsigned char* { return lds_raw + lb * ABUF + pl * (BM * AS * LELT); };
+  auto store_a = [&](int st, int lb) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       if (a_dst[j] < 0) continue;
@@ -244,58 +335,20 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
         sm += wave_shfl_xor(sm, 2);
         sm += wave_shfl_xor(sm, 4);
         sm += wave_shfl_xor(sm, 8);
-        if ((lane & 15) == 0) lds_s[buf][(tid + 256 * j) / CPR] = sm;
+        if ((lane & 15) == 0) lds_s[lb][(tid + 256 * j) / CPR] = sm;
         hi = perm_04152637(hi);
         if constexpr (SPLIT) lo = perm_04152637(lo);
       }
-      *reinterpret_cast<u32x4*>(&lds_a[buf][0][a_dst[j]]) = hi;
-      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(&lds_a[buf][NPL - 1][a_dst[j]]) = lo;
-    }
-  };
-
-  // ---------------- weight fragment pointers
-  const unsigned char* b_ptr[NB_FR];
-  const uint16_t* s_ptr[NB_FR];
-#pragma unroll
-  for (int f = 0; f < NB_FR; ++f) {
-    const bool second = GATEUP && f >= NF;
-    const int fl = second ? f - NF : f;
-    const int n = n0 + 16 * (NF * wave + fl) + lrow;
-    const void* W = second ? args.W1 : args.W0;
-    if constexpr (I4) {
-      b_ptr[f] = static_cast<const unsigned char*>(W) + ((size_t)e * N + n) * (size_t)(K / 2) + q * 16;
-      s_ptr[f] = (second ? args.S1 : args.S0) + ((size_t)e * N + n) * (size_t)(K / kI4Group);
-    } else {
-      b_ptr[f] = static_cast<const unsigned char*>(W) + (((size_t)e * N + n) * (size_t)K + q * Tr::QS) * Tr::AELT;
-      s_ptr[f] = nullptr;
-    }
-  }
-  u32x4 bbuf[NS][NB_FR][Tr::VPB];
-  float sbuf[NS][NB_FR];
-  auto load_b = [&](int buf, int kb) {
-    const int kbe = min(kb, K - KB);  // past the end: re-read the last block (its activations are zero)
-#pragma unroll
-    for (int f = 0; f < NB_FR; ++f) {
-      if constexpr (I4) {
-        bbuf[buf][f][0] = *reinterpret_cast<const u32x4*>(b_ptr[f] + (size_t)kbe / 2);
-        sbuf[buf][f] = half_bits_to_f32(s_ptr[f][kbe / kI4Group]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < Tr::VPB; ++v)
-          bbuf[buf][f][v] = *reinterpret_cast<const u32x4*>(b_ptr[f] + (size_t)kbe * Tr::AELT + 16 * v);
-      }
+      *reinterpret_cast<u32x4*>(lds_a_at(lb, 0) + a_dst[j]) = hi;
+      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(lds_a_at(lb, NPL - 1) + a_dst[j]) = lo;
     }
   };
 
   f32x4 acc[MF][NB_FR];
-#pragma unroll
-  for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-    for (int f = 0; f < NB_FR; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
-    const unsigned char* As = lds_a[buf][0];
-    const unsigned char* Al = lds_a[buf][NPL - 1];
+  auto compute = [&](int st, int lb) {
+    const unsigned char* As = lds_a_at(lb, 0);
+    const unsigned char* Al = lds_a_at(lb, NPL - 1);
     if constexpr (WT == W_F32) {
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
@@ -305,7 +358,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
           a[mi] = *reinterpret_cast<const float*>(As + ((16 * mi + lrow) * AS + Tr::QS * q + s) * LELT);
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
-          const u32x4 bv = bbuf[buf][f][s >> 2];
+          const u32x4 bv = bbuf[st][f][s >> 2];
           const float b = __uint_as_float(bv[s & 3]);
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi) acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mi], b, acc[mi][f], 0, 0, 0);
@@ -323,7 +376,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
         }
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, bbuf[buf][f][s]);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, bbuf[st][f][s]);
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi) {
             acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, acc[mi][f], 0, 0, 0);
@@ -348,7 +401,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
         }
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, i4_word_to_bf16x8(bbuf[buf][f][0][s]));
+          const bf16x8 b = __builtin_bit_cast(bf16x8, i4_word_to_bf16x8(bbuf[st][f][0][s]));
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi) {
             gacc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, gacc[mi][f], 0, 0, 0);
@@ -358,10 +411,10 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
       }
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi) {
-        const f32x4 rs = *reinterpret_cast<const f32x4*>(&lds_s[buf][16 * mi + 4 * q]);
+        const f32x4 rs = *reinterpret_cast<const f32x4*>(&lds_s[lb][16 * mi + 4 * q]);
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
-          const float sc = sbuf[buf][f];
+          const float sc = sbuf[st][f];
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mi][f][r] = fmaf(sc, fmaf(-136.0f, rs[r], gacc[mi][f][r]), acc[mi][f][r]);
         }
@@ -369,61 +422,139 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
     }
   };
 
-  // ---------------- main loop: NS-stage software pipeline, one LDS barrier per k-block.
-  // Loads for k-block j+NS-1 are issued before k-block j is computed (activations
-  // first, then weights), so the in-order vmcnt waits that guard each use leave
-  // the newer prefetches in flight.  The barrier orders LDS only: a plain
-  // __syncthreads would also drain every outstanding global load.
+  // ---------------- tile loop with a continuous NS-stage software pipeline.
+  // Loads for k-block j+NS-1 are issued before k-block j is computed, so the
+  // in-order vmcnt waits that guard each use leave the newer prefetches in
+  // flight; the barrier orders LDS only (a plain __syncthreads would also drain
+  // every outstanding global load).  During the last NS-1 k-blocks of a tile
+  // the prefetches already fetch the first k-blocks of the workgroup's next
+  // tile (of the same tile again after the last one; never computed), so the
+  // epilogue overlaps those loads.  k-block j of a tile sits in register stage
+  // j % NS; consecutive k-blocks of the whole sequence alternate between the
+  // two LDS buffers.
   const int NKB = K / KB;
   const int NIT = (NKB + NS - 1) / NS * NS;  // padded with all-zero activation blocks
+  const bool f32out = F32 || args.out_f32;
+  const int osz = f32out ? 4 : 2;
+  const int OS = BN * osz + 16;
+  const int cpr = BN * osz / 16;  // 16-byte chunks per output row
+
+  Ptrs cur, nxt;
+  setup(0, cur);
+  setup(min(1, ntiles - 1), nxt);
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) {
-    load_a(st, st * KB);
-    load_b(st, st * KB);
+    load_a(st, cur, st * KB);
+    load_b(st, cur, st * KB);
   }
-  store_a(0, 0);
-  lds_barrier();
-  for (int i = 0; i < NIT; i += NS) {
+  int par = 0;  // LDS buffer of the tile's k-block 0
+  for (int it = 0; it < ntiles; ++it) {
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int j = i + u;
-      const int pf = (u + NS - 1) % NS;
-      load_a(pf, (j + NS - 1) * KB);
-      load_b(pf, (j + NS - 1) * KB);
-      compute(u);
-      store_a((u + 1) % NS, (u + 1) % NS);
-      lds_barrier();
-    }
-  }
-
-  // ---------------- epilogue
-  const bool f32out = F32 || args.out_f32;
+    for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
-  for (int mi = 0; mi < MF; ++mi) {
+      for (int f = 0; f < NB_FR; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    store_a(0, par);
+    lds_barrier();
+    for (int i = 0; i < NIT - NS; i += NS) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int n = n0 + 16 * (NF * wave + f) + lrow;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mi + 4 * q + r;
-        if (row >= nrows) continue;
-        float v = acc[mi][f][r];
-        if constexpr (GATEUP) v = act_fn(v, args.act) * acc[mi][NF + f][r];
-        const size_t o = (size_t)(row0 + row) * N + n;
-        if (f32out) static_cast<float*>(args.out)[o] = v;
-        else static_cast<uint16_t*>(args.out)[o] = (uint16_t)f32_to_bf16_bits(v);
+      for (int u = 0; u < NS; ++u) {
+        const int pf = (u + NS - 1) % NS;
+        const int lb = (par + i + u) & 1;
+        load_a(pf, cur, (i + u + NS - 1) * KB);
+        load_b(pf, cur, (i + u + NS - 1) * KB);
+        compute(u, lb);
+        store_a((u + 1) % NS, lb ^ 1);
+        lds_barrier();
       }
     }
+    // last NS k-blocks: the first prefetch is this tile's last k-block, the
+    // others are k-blocks 0..NS-2 of the next tile
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int pf = (u + NS - 1) % NS;
+      const int lb = (par + NIT - NS + u) & 1;
+      if (u == 0) {
+        load_a(pf, cur, (NIT - 1) * KB);
+        load_b(pf, cur, (NIT - 1) * KB);
+      } else {
+        load_a(pf, nxt, (u - 1) * KB);
+        load_b(pf, nxt, (u - 1) * KB);
+      }
+      compute(u, lb);
+      if (u + 1 < NS) store_a(u + 1, lb ^ 1);
+      lds_barrier();
+    }
+    par = (par + NIT) & 1;
+
+    // epilogue: results -> LDS tile (output dtype) -> 16-byte row stores
+    {
+      const int4 ti = lds_tile[it];
+      const int row0 = ti.y, nrows = ti.z, n0 = ti.w * BN;
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int col = 16 * (NF * wave + f) + lrow;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mi + 4 * q + r;
+            float v = acc[mi][f][r];
+            if constexpr (GATEUP) v = act_fn(v, args.act) * acc[mi][NF + f][r];
+            unsigned char* dst = lds_raw + row * OS + col * osz;
+            if (f32out) *reinterpret_cast<float*>(dst) = v;
+            else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
+          }
+        }
+      }
+      lds_barrier();
+      unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * osz;
+      for (int c = tid; c < nrows * cpr; c += 256) {
+        const int row = c / cpr;
+        const int cc = c - row * cpr;
+        *reinterpret_cast<u32x4*>(obase + (size_t)row * N * osz + cc * 16) =
+            *reinterpret_cast<const u32x4*>(lds_raw + row * OS + cc * 16);
+      }
+      lds_barrier();
+    }
+    cur = nxt;
+    setup(min(it + 2, ntiles - 1), nxt);
   }
+}
+
+template <int WT, int MF, int NF, bool GU, bool SPLIT>
+int resident_groups(int& cus) {
+  static int cached_occ = -1, cached_cus = -1;
+  if (cached_occ < 0) {
+    int dev = 0, occ = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>, 256, 0) !=
+            hipSuccess) {
+      occ = 1;
+      n = 256;
+    }
+    cached_cus = n > 0 ? n : 256;
+    cached_occ = occ > 0 ? occ : 1;
+  }
+  cus = cached_cus;
+  return cached_occ;
 }
 
 template <int WT, int MF, int NF, bool GU, bool SPLIT>
 hipError_t launch_one(const FfnGemmArgs& a, hipStream_t s) {
   const int BM = 16 * MF, BN = 64 * NF;
   const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
-  long long g = (long long)mt * (a.N / BN);
-  g = (g + 7) / 8 * 8;
-  if (g == 0) return hipSuccess;
+  const long long total_ub = (long long)mt * (a.N / BN);
+  if (total_ub == 0) return hipSuccess;
+  // Persistent grid: every resident slot once, but no more than the tiles there
+  // can be, and enough workgroups that none holds more than NT_MAX tiles.
+  int cus = 256;
+  const int occ = resident_groups<WT, MF, NF, GU, SPLIT>(cus);
+  constexpr int NT_MAX = TileCap<16 * MF>::NT_MAX;
+  const long long per_ub = (total_ub + 7) / 8;
+  long long S = std::max<long long>((long long)occ * cus / 8, (per_ub + NT_MAX - 1) / NT_MAX);
+  S = std::min<long long>(S, per_ub);
+  const long long g = 8 * S;
   ffn_gemm_kernel<WT, MF, NF, GU, SPLIT><<<dim3((unsigned)g), 256, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -58,6 +58,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                         const float* logits_in, const float* bias, int renorm, int32_t* ids,
                         float* tw, float* logits_out, hipStream_t s);
+// Router logits without bias: L[t,e] = sum_i x[t,i] w[e,i], fp32 [T, E].
+hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits,
+                                hipStream_t s);
+// Softmax + top-k from logits rows src[T, E] plus bias; logits_out (may alias
+// src or be NULL) receives src + bias.
+hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
+                         float* tw, float* logits_out, hipStream_t s);
 
 // Grouping of pairs by local expert.
 struct PermuteWs {
@@ -90,6 +97,7 @@ struct FfnGemmArgs {
   const int32_t* mtile_start;// [E_loc+1] m-tile prefix, or NULL with offsets == NULL
   const int4* tile_tab;      // per m-tile {expert, first row, rows, 0}, or NULL with offsets == NULL
   int E_loc, rows_max, K, N;
+  int a_rows;                // rows of A as addressed (a_rows * K elements must stay below 4 GiB)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
 };

@@ -1,9 +1,9 @@
 // Grouping of (token, slot) pairs by local expert: LDS histogram, prefix sums
 // and a stable scatter that keeps each pair's identity p = t*k + j.
 //
-// Operation (ExpertMesh README: activation grouping that preserves token and
-// top-k slot identity; MoEEvolve "Architecture": capacity-factor dispatch with
-// overflow dropped): pairs of each local expert are laid out in ascending p;
+// Operation (ExpertMesh README, feature list: activations grouped per expert
+// with each token's identity and top-k slot kept; MoEEvolve "Architecture":
+// capacity-factor dispatch, overflow dropped): pairs of each local expert are laid out in ascending p;
 // with a capacity C only the first C of them are kept.
 //
 // Three launches, none of which depends on the order of atomic operations:

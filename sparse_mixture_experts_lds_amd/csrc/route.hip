@@ -1,18 +1,23 @@
 // Router step: logits GEMM on MFMA, softmax and wave-level top-k selection.
 //
-// Operation ("Sharding d'experts", "Deux roles": ids,p = top_k(softmax(cur @
-// router), k); moe_stream.py MoEFFN.forward: bias-free router, per-expert bias
-// added before the softmax, softmax over all experts, topk, gates divided by
-// their sum):
+// Operation ("Sharding d'experts", "Deux roles": the backbone routes once,
+// softmax of the router logits then the k most probable experts;
+// moe_stream.py MoEFFN.forward: bias-free router, per-expert bias added before
+// the softmax, softmax over all experts, top k, gates divided by their sum):
 //   L[t,e]   = sum_i x[t,i] w[e,i] + b[e]           (fp32 accumulate)
 //   ids[t,j] = j-th largest L[t,.], ties to the lower expert id
 //   w[t,j]   = exp(L_j - m) / (renorm ? sum_sel exp(L - m) : sum_all exp(L - m))
 //
-// One workgroup (4 waves) handles 16 tokens.  The logits tile [16, E] is built
-// in LDS (MFMA 16x16x32 bf16 or 16x16x4 f32, each wave a strided set of
-// 16-expert column fragments), then each wave selects for 4 tokens: every lane
-// holds E/64 logits in registers and k rounds of a (value, lower-id) wave
-// arg-max pick the experts.
+// Two kernels.  The logits kernel: one workgroup (4 waves) handles 16 tokens
+// and builds the logits tile [16, E] in LDS (MFMA 16x16x32 bf16 or 16x16x4 f32,
+// each wave a strided set of 16-expert column fragments); it either selects
+// for its tokens directly or only writes the logits.  The select kernel takes
+// logits from memory with one wave per token.  Selection: every lane holds
+// E/64 logits in registers and k rounds of a (value, lower-id) wave arg-max
+// pick the experts.  When the activations are bf16 and E is a multiple of 64
+// the logits of a whole layer come from the grouped GEMM kernel (one group,
+// fp32 output) instead, which reuses each router weight slice across 16-64
+// tokens per workgroup rather than 16.
 #include "moe_internal.h"
 
 namespace moe {
@@ -20,10 +25,64 @@ namespace {
 
 constexpr int kTokTile = 16;
 
-template <int NF, bool BF16>
+// Softmax and top-k of one token held by one wave: lane l holds experts l+64i in
+// v[i] (-inf past E).  Writes k ids (descending logit, ties to the lower id) and
+// their gates (renormalised over the selection, or over all E).
+template <int NF>
+__device__ __forceinline__ void select_token(const float (&v)[NF], int E, int k, int renorm, int lane,
+                                             int32_t* ids_row, float* tw_row) {
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < NF; ++i) m = fmaxf(m, v[i]);
+  m = wave_max(m);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
+    if (lane + 64 * i < E) se += expf(v[i] - m);
+  const float sum_all = wave_sum(se);
+
+  uint32_t taken = 0;
+  float my_v = -INFINITY;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int e = lane + 64 * i;
+      // strict '>' keeps the lower id among this lane's equal values
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+      const float ov = wave_shfl_xor(bv, msk);
+      const int oe = wave_shfl_xor(be, msk);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  const float ex = lane < k ? expf(my_v - m) : 0.f;
+  const float denom = renorm ? wave_sum(ex) : sum_all;
+  if (lane < k) {
+    ids_row[lane] = my_e;
+    tw_row[lane] = ex / denom;
+  }
+}
+
+// SELECT false: only the logits (without bias) are written, to logits_out.
+template <int NF, bool BF16, bool SELECT>
 __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, const void* __restrict__ xv,
                                                     const void* __restrict__ wv,
-                                                    const float* __restrict__ logits_in,
                                                     const float* __restrict__ bias, int renorm,
                                                     int32_t* __restrict__ ids, float* __restrict__ tw,
                                                     float* __restrict__ logits_out) {
@@ -33,16 +92,7 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kTokTile;
 
-  if (logits_in != nullptr) {
-    for (int i = threadIdx.x; i < kTokTile * E; i += 256) {
-      const int r = i / E, e = i - r * E;
-      const int t = t0 + r;
-      float v = 0.f;
-      if (t < T) v = logits_in[(size_t)t * E + e];
-      if (bias) v += bias[e];
-      Ls[r * ES + e] = v;
-    }
-  } else {
+  {
     const int row = lane & 15;  // A row (token) / B column (expert) inside a fragment
     const int q = lane >> 4;    // K slice held by this lane group
     const int t = t0 + row;
@@ -125,7 +175,7 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
     for (int i = 0; i < NF; ++i) {
       const int e = 16 * (wave + 4 * i) + row;
       if (e < E) {
-        const float bv = bias ? bias[e] : 0.f;
+        const float bv = (SELECT && bias) ? bias[e] : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ls[(4 * q + r) * ES + e] = acc[i][r] + bv;
       }
@@ -141,74 +191,82 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
     }
   }
 
-  // Selection: wave w handles tokens w, w+4, w+8, w+12 of the tile.
-  for (int r = wave; r < kTokTile; r += 4) {
-    const int t = t0 + r;
-    if (t >= T) break;
-    float v[NF];
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? Ls[r * ES + e] : -INFINITY;
-    }
-    float m = v[0];
-#pragma unroll
-    for (int i = 1; i < NF; ++i) m = fmaxf(m, v[i]);
-    m = wave_max(m);
-    float se = 0.f;
-#pragma unroll
-    for (int i = 0; i < NF; ++i)
-      if (lane + 64 * i < E) se += expf(v[i] - m);
-    const float sum_all = wave_sum(se);
-
-    uint32_t taken = 0;
-    float my_v = -INFINITY;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+  if constexpr (SELECT) {
+    // wave w handles tokens w, w+4, w+8, w+12 of the tile
+    for (int r = wave; r < kTokTile; r += 4) {
+      const int t = t0 + r;
+      if (t >= T) break;
+      float v[NF];
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
         const int e = lane + 64 * i;
-        // strict '>' keeps the lower id among this lane's equal values
-        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
-          bv = v[i];
-          be = e;
-        }
+        v[i] = e < E ? Ls[r * ES + e] : -INFINITY;
       }
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const float ov = wave_shfl_xor(bv, msk);
-        const int oe = wave_shfl_xor(be, msk);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == j) {
-        my_v = bv;
-        my_e = be;
-      }
-    }
-    const float ex = lane < k ? expf(my_v - m) : 0.f;
-    const float denom = renorm ? wave_sum(ex) : sum_all;
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = my_e;
-      tw[(size_t)t * k + lane] = ex / denom;
+      select_token<NF>(v, E, k, renorm, lane, ids + (size_t)t * k, tw + (size_t)t * k);
     }
   }
+}
+
+// One wave per token: logits row (+ bias) from memory, optionally written back
+// with the bias added (logits_out may alias src).
+template <int NF>
+__global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const float* src,
+                                                     const float* __restrict__ bias, int renorm,
+                                                     int32_t* __restrict__ ids, float* __restrict__ tw,
+                                                     float* logits_out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = src + (size_t)t * E;
+  float v[NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int e = lane + 64 * i;
+    const int ec = e < E ? e : E - 1;
+    const float b = bias ? bias[ec] : 0.f;
+    const float x = row[ec] + b;
+    v[i] = e < E ? x : -INFINITY;
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) logits_out[(size_t)t * E + e] = v[i];
+    }
+  }
+  select_token<NF>(v, E, k, renorm, lane, ids + (size_t)t * k, tw + (size_t)t * k);
 }
 
 template <int NF>
 hipError_t launch_nf(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                      const float* logits_in, const float* bias, int renorm, int32_t* ids, float* tw,
                      float* logits_out, hipStream_t s) {
+  if (logits_in != nullptr) {
+    select_kernel<NF><<<dim3((T + 3) / 4), 256, 0, s>>>(T, E, k, logits_in, bias, renorm, ids, tw, logits_out);
+    return hipGetLastError();
+  }
   const dim3 grid((T + kTokTile - 1) / kTokTile);
   if (bf16)
-    route_kernel<NF, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, logits_in, bias, renorm, ids, tw, logits_out);
+    route_kernel<NF, true, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out);
   else
-    route_kernel<NF, false><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, logits_in, bias, renorm, ids, tw, logits_out);
+    route_kernel<NF, false, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out);
+  return hipGetLastError();
+}
+
+template <int NF>
+hipError_t logits_nf(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits, hipStream_t s) {
+  const dim3 grid((T + kTokTile - 1) / kTokTile);
+  if (bf16)
+    route_kernel<NF, true, false><<<grid, 256, 0, s>>>(T, d, E, 1, x, wr, nullptr, 0, nullptr, nullptr, logits);
+  else
+    route_kernel<NF, false, false><<<grid, 256, 0, s>>>(T, d, E, 1, x, wr, nullptr, 0, nullptr, nullptr, logits);
+  return hipGetLastError();
+}
+
+template <int NF>
+hipError_t select_nf(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
+                     float* tw, float* logits_out, hipStream_t s) {
+  select_kernel<NF><<<dim3((T + 3) / 4), 256, 0, s>>>(T, E, k, src, bias, renorm, ids, tw, logits_out);
   return hipGetLastError();
 }
 
@@ -219,11 +277,60 @@ hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, co
                         float* tw, float* logits_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nf = (E + 63) / 64;
-  if (nf <= 1) return launch_nf<1>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
-  if (nf <= 2) return launch_nf<2>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
-  if (nf <= 4) return launch_nf<4>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
-  if (nf <= 8) return launch_nf<8>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
-  return launch_nf<16>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s);
+#define MOE_CALL(NFv) launch_nf<NFv>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s)
+  if (nf <= 1) return MOE_CALL(1);
+  if (nf <= 2) return MOE_CALL(2);
+  if (nf <= 4) return MOE_CALL(4);
+  if (nf <= 8) return MOE_CALL(8);
+  return MOE_CALL(16);
+#undef MOE_CALL
+}
+
+int router_logits_tile_m(int T, int E) {
+  const long long nb = E / 64;
+  for (int bm : {64, 32})
+    if ((long long)((T + bm - 1) / bm) * nb >= 512) return bm;
+  return 16;
+}
+
+hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits,
+                                hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (bf16 && E % 64 == 0) {
+    FfnGemmArgs g{};
+    g.A = x;
+    g.row_div = 1;
+    g.W0 = wr;
+    g.out = logits;
+    g.E_loc = 1;
+    g.rows_max = T;
+    g.a_rows = T;
+    g.K = d;
+    g.N = E;
+    g.out_f32 = 1;
+    return launch_ffn_gemm(g, false, W_BF16, false, router_logits_tile_m(T, E), 1, s);
+  }
+  const int nf = (E + 63) / 64;
+#define MOE_CALL(NFv) logits_nf<NFv>(T, d, E, bf16, x, wr, logits, s)
+  if (nf <= 1) return MOE_CALL(1);
+  if (nf <= 2) return MOE_CALL(2);
+  if (nf <= 4) return MOE_CALL(4);
+  if (nf <= 8) return MOE_CALL(8);
+  return MOE_CALL(16);
+#undef MOE_CALL
+}
+
+hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
+                         float* tw, float* logits_out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nf = (E + 63) / 64;
+#define MOE_CALL(NFv) select_nf<NFv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
+  if (nf <= 1) return MOE_CALL(1);
+  if (nf <= 2) return MOE_CALL(2);
+  if (nf <= 4) return MOE_CALL(4);
+  if (nf <= 8) return MOE_CALL(8);
+  return MOE_CALL(16);
+#undef MOE_CALL
 }
 
 }  // namespace moe
