@@ -184,8 +184,10 @@ int check_layer(const moe_layer_desc* L) {
   if ((size_t)L->T * L->d * 4 > lim || (size_t)layer_rows_max(L) * L->h * 4 > lim) return MOE_EUNSUPPORTED;
   if (L->tile_m) {
     const int m = L->tile_m;
-    const int mmax = L->w_dtype == MOE_I4G128 ? 64 : (L->w_dtype == MOE_F32 ? 32 : 128);
-    if ((m != 16 && m != 32 && m != 64 && m != 128) || m > mmax) return MOE_EUNSUPPORTED;
+    const int mmax = L->w_dtype == MOE_I4G128 ? 64 : (L->w_dtype == MOE_F32 ? 32 : 256);
+    if ((m != 16 && m != 32 && m != 64 && m != 128 && m != 256) || m > mmax) return MOE_EUNSUPPORTED;
+    // 256-row tiles are the wide bf16 kernel: 128-column gate/up and 256-column down tiles
+    if (m == 256 && (L->h % 128 || L->d % 256 || L->tile_n_up || L->tile_n_down)) return MOE_EUNSUPPORTED;
   }
   if (L->tile_n_up && (L->tile_n_up != 64 && L->tile_n_up != 128)) return MOE_EUNSUPPORTED;
   if (L->tile_n_down && (L->tile_n_down != 64 && L->tile_n_down != 128)) return MOE_EUNSUPPORTED;
@@ -197,10 +199,17 @@ int check_layer(const moe_layer_desc* L) {
 // The automatic plan, overridden by the descriptor's tile hints.
 FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
   (void)rows;
-  FfnPlan p = plan_ffn((double)L->T * L->k / L->E, L->d, L->h, wtype_of(L->w_dtype));
+  const int wt = wtype_of(L->w_dtype);
+  FfnPlan p = plan_ffn((double)L->T * L->k / L->E, L->E_loc, L->d, L->h, wt);
+  const bool hints = L->tile_m || L->tile_n_up || L->tile_n_down;
+  if (!hints) return p;
+  if (L->tile_m == 256) return FfnPlan{256, 0, 0, false};
+  // narrow tiles: the hinted sizes, the planner's choice for the rest
+  if (p.BM == 256) p = FfnPlan{128, 1, L->d % 128 == 0 ? 2 : 1, false};
   if (L->tile_m) p.BM = L->tile_m;
   if (L->tile_n_up) p.NF_up = L->tile_n_up / 64;
   if (L->tile_n_down) p.NF_down = L->tile_n_down / 64;
+  p.split_z = wt == W_I4;
   return p;
 }
 
@@ -328,7 +337,7 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   int32_t* mtile = c.take<int32_t>((size_t)(E_loc + 1) * 4);
   int4* tab = c.take<int4>((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
   const int wt = wtype_of(w_dtype);
-  const FfnPlan plan = plan_ffn((double)rows_max / E_loc, d, h, wt);
+  const FfnPlan plan = plan_ffn((double)rows_max / E_loc, E_loc, d, h, wt);
   if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, tab, s));
   return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, rows_max, nullptr, 1, expert_offsets,
                  expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
@@ -388,7 +397,7 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     MOE_HIP(hipEventRecord(side->fork, s));
     MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
     const int swt = L->act_dtype;  // shared weights are in the activation dtype
-    const FfnPlan sp = plan_ffn((double)T, L->d, L->h_shared, wtype_of(swt));
+    const FfnPlan sp = plan_ffn((double)T, 1, L->d, L->h_shared, wtype_of(swt));
     rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
                  L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s);
     // the join is recorded even if a launch failed; on failure the caller's

@@ -3,6 +3,7 @@
 // Built with the MFMA "VGPR form": accumulators carried across the k-loop stay
 // in ordinary VGPRs instead of being shuffled between register files.
 #include "ffn_kernel.h"
+#include "ffn_wide.h"
 
 namespace moe {
 
@@ -17,12 +18,24 @@ int ffn_max_mtiles(int E_loc, int rows_max, int BM) {
   return (int)(a < b ? a : b);
 }
 
-FfnPlan plan_ffn(double avg_rows, int d, int h, int w_type) {
+FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   // Tile shapes from measurements on MI355X: tiles as tall as the typical
   // expert (weights are then re-read from L2 at most a few times), 64-column
   // gate/up tiles once tiles are tall (halves the live accumulators), 128-column
   // down tiles whenever d allows.
   FfnPlan p;
+  // Wide tiles (256 rows x 256 weight rows, bf16): half the bytes per FLOP of
+  // the narrow tiles; worth it once experts average ~100 rows and there are
+  // enough tiles to give every CU one.
+  if (w_type == W_BF16 && avg_rows >= 96 && h % 128 == 0 && d % 256 == 0) {
+    const double mt = (double)groups * (double)(int)((avg_rows + 255) / 256);
+    if (mt * (h / 128) >= 256) {
+      p.BM = 256;
+      p.NF_up = p.NF_down = 0;
+      p.split_z = false;
+      return p;
+    }
+  }
   int BM;
   if (avg_rows <= 16) BM = 16;
   else if (avg_rows <= 24) BM = 32;
@@ -46,6 +59,10 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   // activation rows are addressed with 32-bit byte offsets
   const size_t gelt = (w_type == W_F32 || split) ? 4 : 2;
   if (a.a_rows < 0 || (size_t)a.a_rows * (size_t)a.K * gelt > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  if (BM == ffn_wide::BM) {
+    if (w_type != W_BF16 || split) return hipErrorInvalidValue;
+    return gateup ? ffn_wide::launch_wide<true>(a, s) : ffn_wide::launch_wide<false>(a, s);
+  }
   if (w_type == W_F32) return gateup ? launch_mf_nf<W_F32, true, false>(a, BM, NF, s) : launch_mf_nf<W_F32, false, false>(a, BM, NF, s);
   if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);
   if (gateup) return launch_mf_nf<W_BF16, true, false>(a, BM, NF, s);

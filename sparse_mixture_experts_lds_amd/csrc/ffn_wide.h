@@ -1,0 +1,315 @@
+// Wide-tile grouped expert GEMM for bf16 weights: tiles of 256 grouped rows by
+// 256 weight rows, eight waves, both operands loaded straight into LDS.
+//
+// Same operation as ffn_kernel.h ("Sharding d'experts", "Deux roles": the
+// three matrix products a worker runs per expert; MoEEvolve "Architecture":
+// SwiGLU experts; kieve-moe "Features": GeGLU experts):
+//   gate/up:  z[r, n] = act(sum_k a[r,k] Wg[e,n,k]) * (sum_k a[r,k] Wu[e,n,k])
+//   down:     y[r, n] = sum_k z[r,k] Wd[e,n,k]
+//
+// Why a second tile shape.  The narrow kernel's time follows the bytes its
+// workgroups pull through the CU caches: a 128x128 tile loads 32 KB per 64-deep
+// k-block for 2.1 MFLOP.  This tile loads 32 KB per 32-deep k-block for
+// 4.2 MFLOP, half the bytes per FLOP, and it is tall enough that an expert with
+// up to 256 rows reads each weight slice once.  It pays when experts get at
+// least ~100 rows.
+//
+// Layout.  Waves form a 4 x 2 grid: wave (wr, wc) owns rows 64*wr..64*wr+63
+// and 128 of the tile's 256 weight rows, as 4 x 8 MFMA 16x16x32 fragments (128
+// fp32 accumulators per lane).  For gate/up the tile's weight rows are 128 gate
+// rows then the 128 up rows of the same outputs, and wave wc takes gate and up
+// rows of output columns 64*wc..64*wc+63, so g and u of an output meet in one
+// lane.  For down the 256 weight rows are 256 output columns, 128 per wave
+// column.
+//
+// Pipeline.  Operands go global -> LDS with loads that write LDS directly
+// (global_load_lds_dwordx4, no staging registers), into four stages of 32 KB (A 256 x 64 B,
+// B 256 x 64 B); three k-blocks are in flight while one is computed.  Every
+// thread issues the same four loads per stage, so an explicit vmcnt wait plus
+// an LDS barrier marks a stage complete.  Inside a 64-byte row the four
+// 16-byte chunks are stored XOR-swizzled by (row / 2) % 4, so the eight lanes
+// served per LDS cycle (eight consecutive rows, one chunk each) hit eight
+// distinct groups of four banks.  Activation rows are gathered on load
+// (row_index); rows past the tile end re-read its last row.  A wave whose 64
+// rows all lie past the tile end skips its MFMAs.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace ffn_wide {
+
+constexpr int BM = 256;            // grouped rows per tile
+constexpr int KB = 32;             // inputs per k-block (one MFMA K step)
+constexpr int NS = 4;              // LDS stages
+constexpr int ROWB = KB * 2;       // bytes per operand row per k-block
+constexpr int OPB = BM * ROWB;     // one operand of one stage (16 KB)
+constexpr int STAGE = 2 * OPB;     // A then B
+constexpr int LPS = 4;             // loads per thread per stage
+constexpr int kGroupM = 4;         // m-tiles per group in the tile order
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their no-wait maxima)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 16, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+
+template <int ACT>  // 0 SiLU, 1 exact-erf GELU
+__device__ __forceinline__ float act_fn(float g) {
+  if constexpr (ACT == 0) return g / (1.0f + expf(-g));
+  else return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
+// uniform).  Written as asm so that the compiler, which cannot tell the four
+// stages apart, adds no waits of its own; the kernel waits explicitly
+// (wait_vm + lds_barrier) before it reads a stage.  The asm has no register
+// outputs, and the "memory" clobber keeps every LDS access on its side.
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+  // one wait state between the SALU write of M0 and the LDS-writing load
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+template <bool GATEUP, bool OUT_F32, int ACT>
+__global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
+  constexpr int BNO = GATEUP ? 128 : 256;  // output columns per tile
+  constexpr int MF = 4, NF = 8;
+  __shared__ __attribute__((aligned(16))) unsigned char stg[NS][STAGE];
+  __shared__ int lds_src[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lrow = lane & 15;
+  const int q = lane >> 4;
+  const int wr = wave & 3;
+  const int wc = wave >> 2;
+  const int N = args.N, K = args.K;
+  const int NBLK = N / BNO;
+
+  // ---------------- tile of this workgroup (XCD-contiguous ranges, grouped-M order)
+  int total_mt;
+  if (args.offsets) total_mt = args.mtile_start[args.E_loc];
+  else total_mt = (args.rows_max + BM - 1) / BM;
+  const int total = total_mt * NBLK;
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int R = (blockIdx.x & 7) * per + slot;
+  if (R >= total) return;
+  int e = 0, row0, nrows, nb;
+  {
+    const int grp = R / (kGroupM * NBLK);
+    const int t0 = grp * kGroupM;
+    const int gm = min(kGroupM, total_mt - t0);
+    const int rr = R - grp * kGroupM * NBLK;
+    nb = rr / gm;
+    const int t = t0 + (rr - nb * gm);
+    if (args.tile_tab) {
+      const int4 ti = args.tile_tab[t];
+      e = ti.x;
+      row0 = ti.y;
+      nrows = ti.z;
+    } else {
+      row0 = t * BM;
+      nrows = min(BM, args.rows_max - row0);
+    }
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  const int n0 = nb * BNO;
+
+  if (tid < BM) {
+    const int gr = row0 + min(tid, nrows - 1);
+    lds_src[tid] = args.row_index ? args.row_index[gr] / args.row_div : gr;
+  }
+  __syncthreads();
+
+  // ---------------- load addresses.  Load i (0, 1) of wave w fills 1 KB = 16
+  // rows of an operand: rows 16 (2w + i) + lane / 4, stored chunk lane % 4,
+  // holding logical chunk (lane % 4) ^ ((row / 2) % 4) of the row.  Rows
+  // past the tile end re-read the tile's last row (their results are never
+  // stored; a row of the product depends only on the same row of A).
+  const size_t wslice = (size_t)N * K * 2;  // one expert's matrix, bytes
+  const unsigned char* w0 = static_cast<const unsigned char*>(args.W0) + (size_t)e * wslice;
+  const unsigned char* w1 = GATEUP ? static_cast<const unsigned char*>(args.W1) + (size_t)e * wslice : w0;
+  const unsigned char* a_ptr[2];
+  const unsigned char* b_ptr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (2 * wave + i) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    a_ptr[i] = static_cast<const unsigned char*>(args.A) + ((size_t)lds_src[row] * K + chunk * 8) * 2;
+    // gate/up: tile rows 0..127 are gate rows, 128..255 the up rows of the same outputs
+    const unsigned char* w = (GATEUP && row >= 128) ? w1 : w0;
+    b_ptr[i] = w + ((size_t)(n0 + (GATEUP ? (row & 127) : row)) * K + chunk * 8) * 2;
+  }
+  auto issue = [&](int st, int kb) {  // kb: first input of the k-block
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(a_ptr[i] + kb * 2, stg[st] + (2 * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(b_ptr[i] + kb * 2, stg[st] + OPB + (2 * wave + i) * 1024);
+  };
+
+  // fragment reads: lane (lrow, q) needs logical chunk q of its row; rows of a
+  // fragment start at multiples of 16, so the stored chunk is q ^ ((lrow / 2) % 4)
+  const int rd = lrow * ROWB + ((q ^ ((lrow >> 1) & 3)) * 16);
+  const int a_rd = 64 * wr * ROWB + rd;
+  const int b_rd = (GATEUP ? 64 : 128) * wc * ROWB + rd;
+  const bool active = 64 * wr < nrows;  // wave-uniform
+
+  f32x4 acc[MF][NF];
+#pragma unroll
+  for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st) {
+    if (!active) return;
+    const unsigned char* A = stg[st];
+    const unsigned char* B = stg[st] + OPB;
+    bf16x8 a[MF];
+#pragma unroll
+    for (int mi = 0; mi < MF; ++mi)
+      a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + a_rd + 16 * mi * ROWB));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int fo = GATEUP ? (f >= 4 ? 128 : 0) + 16 * (f & 3) : 16 * f;  // B row offset of fragment f
+      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + b_rd + fo * ROWB));
+#pragma unroll
+      for (int mi = 0; mi < MF; ++mi) acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, acc[mi][f], 0, 0, 0);
+    }
+  };
+
+  // ---------------- k-loop.  At the top of k-block j the k-blocks j..j+NS-2 are
+  // in flight; waiting until at most NS-2 stages' loads remain, then a
+  // barrier, makes stage j complete for every wave and frees stage j-1, which
+  // then receives k-block j+NS-1.  K is a multiple of NS * KB.
+  const int NKB = K / KB;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st, st * KB);
+  for (int i = 0; i < NKB - NS; i += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      wait_vm<(NS - 2) * LPS>();
+      lds_barrier();
+      issue((u + NS - 1) % NS, (i + u + NS - 1) * KB);
+      compute(u);
+    }
+  }
+  // last NS k-blocks: one more load, then the pipeline drains
+  wait_vm<(NS - 2) * LPS>();
+  lds_barrier();
+  issue(NS - 1, (NKB - 1) * KB);
+  compute(0);
+  wait_vm<(NS - 2) * LPS>();
+  lds_barrier();
+  compute(1);
+  wait_vm<(NS - 3) * LPS>();
+  lds_barrier();
+  compute(2);
+  wait_vm<0>();
+  lds_barrier();
+  compute(3);
+  lds_barrier();
+
+  // ---------------- epilogue: four quarters of the output columns, staged
+  // through the (now free) stage memory
+  unsigned char* const lds = &stg[0][0];
+  unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * (OUT_F32 ? 4 : 2);
+  if constexpr (GATEUP) {
+    // g and u go to LDS as fp32; every thread then forms act(g)*u for 8
+    // columns at a time and stores them as 16 bytes of bf16, which keeps the
+    // activation's temporaries out of the accumulator-heavy code
+    constexpr int GS = 32 + 4;  // fp32 row stride of a staged quarter
+    float* G = reinterpret_cast<float*>(lds);
+    float* U = G + BM * GS;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      if (wc == (qq >> 1) && active) {
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+          for (int ff = 0; ff < 2; ++ff) {
+            const int f = 2 * (qq & 1) + ff;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int o = (64 * wr + 16 * mi + 4 * q + r) * GS + 16 * ff + lrow;
+              G[o] = acc[mi][f][r];
+              U[o] = acc[mi][f + 4][r];
+            }
+          }
+      }
+      lds_barrier();
+      for (int c = tid; c < nrows * 4; c += 512) {
+        const int row = c >> 2, cc = c & 3;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + row * GS + cc * 8);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + row * GS + cc * 8 + 4);
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8);
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8 + 4);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          o[i] = pack_bf16x2(act_fn<ACT>(g0[2 * i]) * u0[2 * i], act_fn<ACT>(g0[2 * i + 1]) * u0[2 * i + 1]);
+          o[i + 2] = pack_bf16x2(act_fn<ACT>(g1[2 * i]) * u1[2 * i], act_fn<ACT>(g1[2 * i + 1]) * u1[2 * i + 1]);
+        }
+        *reinterpret_cast<u32x4*>(obase + ((size_t)row * N + 32 * qq + cc * 8) * 2) = o;
+      }
+      lds_barrier();
+    }
+  } else {
+    constexpr int osz = OUT_F32 ? 4 : 2;
+    constexpr int QC = 64;              // output columns per quarter
+    constexpr int OS = QC * osz + 16;   // LDS row stride of a staged quarter
+    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row of a quarter
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      if (wc == (qq >> 1) && active) {
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+          for (int ff = 0; ff < 4; ++ff) {
+            const int f = 4 * (qq & 1) + ff;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              unsigned char* dst = lds + (64 * wr + 16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
+              if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = acc[mi][f][r];
+              else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(acc[mi][f][r]);
+            }
+          }
+      }
+      lds_barrier();
+      for (int c = tid; c < nrows * cpr; c += 512) {
+        const int row = c / cpr;
+        const int cc = c - row * cpr;
+        *reinterpret_cast<u32x4*>(obase + ((size_t)row * N + qq * QC) * osz + cc * 16) =
+            *reinterpret_cast<const u32x4*>(lds + row * OS + cc * 16);
+      }
+      lds_barrier();
+    }
+  }
+}
+
+template <bool GATEUP>
+hipError_t launch_wide(const FfnGemmArgs& a, hipStream_t s) {
+  // gate/up writes z in bf16 (the fp32 z of the INT4 path never comes here)
+  if (GATEUP && a.out_f32) return hipErrorInvalidValue;
+  const int BNO = GATEUP ? 128 : 256;
+  if (a.N % BNO || a.K % (KB * NS) || (size_t)a.N * a.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
+  long long g = (long long)mt * (a.N / BNO);
+  g = (g + 7) / 8 * 8;
+  if (g == 0) return hipSuccess;
+  if (!GATEUP && a.out_f32) wide_kernel<false, true, 0><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  else if (GATEUP && a.act == 1) wide_kernel<GATEUP, false, 1><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  else wide_kernel<GATEUP, false, 0><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ffn_wide
+}  // namespace moe

@@ -106,8 +106,8 @@ struct FfnPlan {
   int NF_up, NF_down;        // 16-col fragments per wave
   bool split_z;              // z kept in fp32, down projection on its hi/lo bf16 parts
 };
-// avg_rows: expected rows per local expert.
-FfnPlan plan_ffn(double avg_rows, int d, int h, int w_type);
+// avg_rows: expected rows per group (local expert); groups: number of groups.
+FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type);
 int ffn_max_mtiles(int E_loc, int rows_max, int BM);
 // split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
 hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,

@@ -13,10 +13,11 @@
 //               exclusive scan over blocks, per expert), clamps each expert's
 //               total to the capacity, scans over experts into the offsets and
 //               also writes the m-tile prefix of the grouped GEMMs;
-//   3. scatter: one wave per block walks its pairs 64 at a time in p order;
-//               each lane finds the lanes with the same expert by 11 ballots
-//               over the key bits (a wave multisplit) and takes its rank from
-//               a popcount, added to the block's running per-expert count.
+//   3. scatter: one workgroup per block, one wave per 64-pair chunk; each
+//               lane finds the lanes of its chunk with the same expert by 11
+//               ballots over the key bits (a wave multisplit) and takes its
+//               rank from a popcount; per-wave counts become per-wave bases
+//               in LDS, added to the block's base from the scan.
 #include "moe_internal.h"
 
 namespace moe {
@@ -127,57 +128,58 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int nblk, int E_loc,
   }
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(int P, const int32_t* __restrict__ ids,
-                                                     const int32_t* __restrict__ emap, int E, int E_loc,
-                                                     int capacity, const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted_pair,
-                                                     int32_t* __restrict__ pair_pos) {
-  __shared__ int32_t run[kMaxE];
-  __shared__ int32_t off[kMaxE];
-  const int lane = threadIdx.x;
-  const int32_t* base = counts + (size_t)blockIdx.x * E_loc;
-  for (int e = lane; e < E_loc; e += 64) {
-    run[e] = base[e];
+// One workgroup of kBlockPairs threads per block: wave w ranks chunk w (64
+// pairs) by a ballot multisplit, the per-wave counts are turned into per-wave
+// bases in LDS, and every lane then places its pair.
+__global__ __launch_bounds__(kBlockPairs) void scatter_kernel(int P, const int32_t* __restrict__ ids,
+                                                              const int32_t* __restrict__ emap, int E, int E_loc,
+                                                              int capacity, const int32_t* __restrict__ counts,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_pair,
+                                                              int32_t* __restrict__ pair_pos) {
+  constexpr int NW = kBlockPairs / 64;
+  __shared__ int32_t base[kMaxE];            // block's first rank per expert (exclusive over blocks)
+  __shared__ int32_t off[kMaxE];             // expert's first grouped row
+  __shared__ uint16_t wbase[NW][kMaxE];      // per-wave counts, then per-wave bases within the block
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int32_t* cb = counts + (size_t)blockIdx.x * E_loc;
+  for (int e = tid; e < E_loc; e += kBlockPairs) {
+    base[e] = cb[e];
     off[e] = offsets[e];
   }
-  __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int p0 = blockIdx.x * kBlockPairs;
-  const int p1 = min(P, p0 + kBlockPairs);
-  constexpr int NCHK = kBlockPairs / 64;
-  int ev[NCHK];  // the block's local expert ids, loaded up front
+  for (int i = tid; i < NW * E_loc; i += kBlockPairs) wbase[i / E_loc][i % E_loc] = 0;
+  const int p = blockIdx.x * kBlockPairs + tid;
+  const int e = p < P ? local_expert(ids, emap, E, E_loc, p) : -1;
+  const int key = e + 1;  // 0 = not local / past the end
+  uint64_t peers = ~0ull;
 #pragma unroll
-  for (int i = 0; i < NCHK; ++i) {
-    const int p = p0 + 64 * i + lane;
-    ev[i] = p < p1 ? local_expert(ids, emap, E, E_loc, p) : -1;
+  for (int b = 0; b < 11; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
   }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(peers & lt_mask);
+  __syncthreads();
+  if (e >= 0 && rank == 0) wbase[wave][e] = (uint16_t)__popcll(peers);
+  __syncthreads();
+  for (int x = tid; x < E_loc; x += kBlockPairs) {
+    int run = 0;
 #pragma unroll
-  for (int i = 0; i < NCHK; ++i) {
-    const int c = p0 + 64 * i;
-    if (c >= p1) break;
-    const int p = c + lane;
-    const int e = ev[i];
-    const int key = e + 1;  // 0 = not local / inactive lane
-    uint64_t peers = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
+    for (int w = 0; w < NW; ++w) {
+      const int c = wbase[w][x];
+      wbase[w][x] = (uint16_t)run;
+      run += c;
     }
-    const int rank = __popcll(peers & lt_mask);
-    int r = 0;
-    if (e >= 0) r = run[e] + rank;
-    __syncthreads();  // every lane has read run[] before the leaders update it
-    if (e >= 0 && rank == 0) run[e] += __popcll(peers);
-    __syncthreads();
-    if (p < p1) {
-      const bool kept = e >= 0 && (capacity == 0 || r < capacity);
-      const int pos = kept ? off[e] + r : -1;
-      pair_pos[p] = pos;
-      if (kept) sorted_pair[pos] = p;
-    }
+  }
+  __syncthreads();
+  if (p < P) {
+    const int r = e >= 0 ? base[e] + wbase[wave][e] + rank : 0;
+    const bool kept = e >= 0 && (capacity == 0 || r < capacity);
+    const int pos = kept ? off[e] + r : -1;
+    pair_pos[p] = pos;
+    if (kept) sorted_pair[pos] = p;
   }
 }
 
@@ -234,8 +236,8 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t
   const int nblk = (P + kBlockPairs - 1) / kBlockPairs;
   count_kernel<<<nblk, 256, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
   scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E_loc, capacity, BM, counts, offsets, mtile_start, tile_tab);
-  scatter_kernel<<<nblk, 64, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets, sorted_pair,
-                                     pair_pos);
+  scatter_kernel<<<nblk, kBlockPairs, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets,
+                                              sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

@@ -207,44 +207,133 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
   }
 }
 
-// One wave per token: logits row (+ bias) from memory, optionally written back
-// with the bias added (logits_out may alias src).
-template <int NF>
+// Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
+// Every lane of the group ends with the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dppf<kRowRor8>(x));
+  x = fmaxf(x, dppf<kRowRor4>(x));
+  x = fmaxf(x, dppf<kQuadSwap2>(x));
+  x = fmaxf(x, dppf<kQuadSwap1>(x));
+  if constexpr (G == 64) {
+    x = fmaxf(x, wave_shfl_xor(x, 16));
+    x = fmaxf(x, wave_shfl_xor(x, 32));
+  }
+  return x;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dppf<kRowRor8>(x);
+  x += dppf<kRowRor4>(x);
+  x += dppf<kQuadSwap2>(x);
+  x += dppf<kQuadSwap1>(x);
+  if constexpr (G == 64) {
+    x += wave_shfl_xor(x, 16);
+    x += wave_shfl_xor(x, 32);
+  }
+  return x;
+}
+__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& e) {  // larger value, then lower id
+  take_better(v, e, dppf<kRowRor8>(v), dpp<kRowRor8>(e));
+  take_better(v, e, dppf<kRowRor4>(v), dpp<kRowRor4>(e));
+  take_better(v, e, dppf<kQuadSwap2>(v), dpp<kQuadSwap2>(e));
+  take_better(v, e, dppf<kQuadSwap1>(v), dpp<kQuadSwap1>(e));
+  if constexpr (G == 64) {
+    take_better(v, e, wave_shfl_xor(v, 16), wave_shfl_xor(e, 16));
+    take_better(v, e, wave_shfl_xor(v, 32), wave_shfl_xor(e, 32));
+  }
+}
+
+// One group of G lanes per token: logits row (+ bias) from memory, optionally
+// written back with the bias added (logits_out may alias src).  Lane g of the
+// group holds experts g + G*i in v[i]; k rounds of a group arg-max pick the
+// experts, lane j of the group keeps the j-th pick.
+template <int G, int NV>
 __global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const float* src,
                                                      const float* __restrict__ bias, int renorm,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
                                                      float* logits_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int gl = threadIdx.x & (G - 1);
+  const int t = blockIdx.x * (256 / G) + threadIdx.x / G;
+  if (t >= T) return;  // whole groups leave together
   const float* row = src + (size_t)t * E;
-  float v[NF];
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    const int e = lane + 64 * i;
+  for (int i = 0; i < NV; ++i) {
+    const int e = gl + G * i;
     const int ec = e < E ? e : E - 1;
-    const float b = bias ? bias[ec] : 0.f;
-    const float x = row[ec] + b;
+    const float x = row[ec] + (bias ? bias[ec] : 0.f);
     v[i] = e < E ? x : -INFINITY;
   }
   if (logits_out) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      const int e = lane + 64 * i;
+    for (int i = 0; i < NV; ++i) {
+      const int e = gl + G * i;
       if (e < E) logits_out[(size_t)t * E + e] = v[i];
     }
   }
-  select_token<NF>(v, E, k, renorm, lane, ids + (size_t)t * k, tw + (size_t)t * k);
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) m = fmaxf(m, v[i]);
+  m = group_max<G>(m);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (gl + G * i < E) se += expf(v[i] - m);
+  const float sum_all = group_sum<G>(se);
+
+  uint32_t taken = 0;
+  float my_v = -INFINITY;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = gl + G * i;
+      // ascending e within the lane: strict '>' keeps the lower id among equal values
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    group_argmax<G>(bv, be);
+    if (be % G == gl) taken |= 1u << (be / G);
+    if (gl == j) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  const float ex = gl < k ? expf(my_v - m) : 0.f;
+  const float denom = renorm ? group_sum<G>(ex) : sum_all;
+  if (gl < k) {
+    ids[(size_t)t * k + gl] = my_e;
+    tw[(size_t)t * k + gl] = ex / denom;
+  }
 }
 
 template <int NF>
 hipError_t launch_nf(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                      const float* logits_in, const float* bias, int renorm, int32_t* ids, float* tw,
                      float* logits_out, hipStream_t s) {
-  if (logits_in != nullptr) {
-    select_kernel<NF><<<dim3((T + 3) / 4), 256, 0, s>>>(T, E, k, logits_in, bias, renorm, ids, tw, logits_out);
-    return hipGetLastError();
-  }
+  if (logits_in != nullptr) return launch_select(T, E, k, logits_in, bias, renorm, ids, tw, logits_out, s);
   const dim3 grid((T + kTokTile - 1) / kTokTile);
   if (bf16)
     route_kernel<NF, true, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out);
@@ -263,10 +352,11 @@ hipError_t logits_nf(int T, int d, int E, bool bf16, const void* x, const void* 
   return hipGetLastError();
 }
 
-template <int NF>
-hipError_t select_nf(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
+template <int G, int NV>
+hipError_t select_gn(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
                      float* tw, float* logits_out, hipStream_t s) {
-  select_kernel<NF><<<dim3((T + 3) / 4), 256, 0, s>>>(T, E, k, src, bias, renorm, ids, tw, logits_out);
+  constexpr int TPB = 256 / G;  // tokens per workgroup
+  select_kernel<G, NV><<<dim3((T + TPB - 1) / TPB), 256, 0, s>>>(T, E, k, src, bias, renorm, ids, tw, logits_out);
   return hipGetLastError();
 }
 
@@ -323,12 +413,23 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
 hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
                          float* tw, float* logits_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int nf = (E + 63) / 64;
-#define MOE_CALL(NFv) select_nf<NFv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
-  if (nf <= 1) return MOE_CALL(1);
-  if (nf <= 2) return MOE_CALL(2);
-  if (nf <= 4) return MOE_CALL(4);
-  if (nf <= 8) return MOE_CALL(8);
+  // 16 lanes per token while a lane holds at most 16 logits and the k picks fit
+  // in the group; the whole wave otherwise
+  if (E <= 256 && k <= 16) {
+    const int nv = (E + 15) / 16;
+#define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
+    if (nv <= 2) return MOE_CALL(2);
+    if (nv <= 4) return MOE_CALL(4);
+    if (nv <= 8) return MOE_CALL(8);
+    return MOE_CALL(16);
+#undef MOE_CALL
+  }
+  const int nv = (E + 63) / 64;
+#define MOE_CALL(NVv) select_gn<64, NVv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
+  if (nv <= 1) return MOE_CALL(1);
+  if (nv <= 2) return MOE_CALL(2);
+  if (nv <= 4) return MOE_CALL(4);
+  if (nv <= 8) return MOE_CALL(8);
   return MOE_CALL(16);
 #undef MOE_CALL
 }

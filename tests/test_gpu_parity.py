@@ -47,6 +47,27 @@ def test_layer_scaled_workloads(name):
     print(name, rep)
 
 
+# ------------------------------------------------------------------ wide (256-row) tiles
+WIDE = {
+    # skewed routing: experts from a few dozen rows (waves past the tile end
+    # idle) to several 256-row tiles; every output compared
+    "wide_swiglu_shared": scaled("granular_bf16", T=1200, d=512, E=8, k=2, h=256, h_shared=256,
+                                 capacity_factor=None, zipf_bias=1.0),
+    "wide_geglu": scaled("wide_geglu_bf16", T=900, d=256, E=6, h=384),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_layer_wide_tiles(name):
+    _moe()
+    inp = make_inputs(WIDE[name])
+    w = device_weights(inp)
+    w.tiles = (256, 0, 0)
+    rep = {}
+    check_layer(inp, wdev=w, report=rep)
+    print(name, rep)
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("T", [1, 17, 100])
 def test_ragged_and_single_token_batches(T):
