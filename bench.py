@@ -77,9 +77,7 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
             "P": P, "touched": touched}
 
 
-GEMM_SOURCES = ("ffn_kernel.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
-FETCH_SCALE = 2.00   # FETCH_SIZE of a plain 256 MiB copy reads half the bytes moved
-WRITE_SCALE = 1.00   # WRITE_SIZE of the same copy reads the bytes moved
+GEMM_SOURCES = ("ffn_kernel.h", "ffn_wide.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
 
 
 def gemm_source_hash():
@@ -95,8 +93,9 @@ def gemm_source_hash():
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` ("gate_up" or "down") from the committed
-    rocprofv3 counter summary, scaled by the copy calibration; None when there
-    is no summary or it was taken on other kernel sources."""
+    rocprofv3 counter summary: FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    same counter read for a plain copy of known size in the same session; None
+    when there is no summary or it was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "ffn_gemm_%s_%s_pmc.txt" % (kernel, workload))
     try:
         kv = {}
@@ -107,8 +106,8 @@ def measured_traffic(workload, kernel):
                     kv[key.strip()] = val.strip()
         if kv.get("gemm_source_sha256") != gemm_source_hash():
             return None
-        return round(float(kv["fetch_kib_per_launch"]) * 1024 * FETCH_SCALE
-                     + float(kv["write_kib_per_launch"]) * 1024 * WRITE_SCALE)
+        return round(float(kv["fetch_kib_per_launch"]) * 1024 * float(kv["fetch_scale"])
+                     + float(kv["write_kib_per_launch"]) * 1024 * float(kv["write_scale"]))
     except (OSError, KeyError, ValueError):
         return None
 

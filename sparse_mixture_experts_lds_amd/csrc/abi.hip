@@ -77,7 +77,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
             const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
-            void* mid_event = nullptr) {
+            void* mid_event = nullptr, int slot_div = 1) {
   const int wt = wtype_of(w_dtype);
   FfnGemmArgs g{};
   g.A = A;
@@ -97,6 +97,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   g.K = d;
   g.N = h;
   g.act = act == MOE_GEGLU ? 1 : 0;
+  g.slot_div = slot_div;
   g.out_f32 = plan.split_z ? 1 : 0;
   MOE_HIP(launch_ffn_gemm(g, true, wt, false, BM, plan.NF_up, s));
   if (mid_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(mid_event), s));
@@ -128,6 +129,11 @@ struct SideStream {
   hipEvent_t join = nullptr;
 };
 constexpr int kMaxDevices = 64;
+// The side stream's GEMMs take half of the resident workgroup slots, so that
+// routing and grouping on the caller's stream (the critical path) still find
+// free CUs; measured on MI355X with the granular workload (1/4 and 3/4 were
+// slower).
+constexpr int kSharedSlotDiv = 2;
 thread_local SideStream g_side[kMaxDevices];
 
 int side_stream(hipStream_t caller, SideStream** out) {
@@ -399,7 +405,8 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     const int swt = L->act_dtype;  // shared weights are in the activation dtype
     const FfnPlan sp = plan_ffn((double)T, 1, L->d, L->h_shared, wtype_of(swt));
     rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
-                 L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s);
+                 L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s, nullptr,
+                 kSharedSlotDiv);
     // the join is recorded even if a launch failed; on failure the caller's
     // stream waits for whatever the side stream did take before returning
     const hipError_t e = hipEventRecord(side->join, side->s);

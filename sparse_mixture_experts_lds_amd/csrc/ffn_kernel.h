@@ -552,7 +552,9 @@ hipError_t launch_one(const FfnGemmArgs& a, hipStream_t s) {
   const int occ = resident_groups<WT, MF, NF, GU, SPLIT>(cus);
   constexpr int NT_MAX = TileCap<16 * MF>::NT_MAX;
   const long long per_ub = (total_ub + 7) / 8;
-  long long S = std::max<long long>((long long)occ * cus / 8, (per_ub + NT_MAX - 1) / NT_MAX);
+  long long slots = (long long)occ * cus / 8;
+  if (a.slot_div > 1) slots = std::max<long long>(1, slots / a.slot_div);
+  long long S = std::max<long long>(slots, (per_ub + NT_MAX - 1) / NT_MAX);
   S = std::min<long long>(S, per_ub);
   const long long g = 8 * S;
   ffn_gemm_kernel<WT, MF, NF, GU, SPLIT><<<dim3((unsigned)g), 256, 0, s>>>(a);

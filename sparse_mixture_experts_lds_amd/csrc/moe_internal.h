@@ -98,6 +98,7 @@ struct FfnGemmArgs {
   const int4* tile_tab;      // per m-tile {expert, first row, rows, 0}, or NULL with offsets == NULL
   int E_loc, rows_max, K, N;
   int a_rows;                // rows of A as addressed (a_rows * K elements must stay below 4 GiB)
+  int slot_div;              // persistent grid = resident workgroup slots / slot_div (0, 1: all)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
 };
