@@ -271,7 +271,7 @@ def main(argv=None):
     peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
     dom = max(("gate_up", "down"), key=lambda n: seg_ms[n])
     roof = roofline_entry(work[dom], seg_ms[dom], peak)
-    roof.update({"kernel": "ffn_gemm_kernel (routed %s)" % dom.replace("_", "/"),
+    roof.update({"kernel": "grouped expert GEMM (routed %s)" % dom.replace("_", "/"),
                  "avg_ms": seg_ms[dom], "traffic": measured_traffic(cfg.name, dom),
                  "algorithmic": {"bytes": work[dom]["bytes"], "flops": work[dom]["flops"]}})
     layer_roof = roofline_entry(work["layer"], ms, peak)

@@ -23,8 +23,9 @@
 // column.
 //
 // Pipeline.  Operands go global -> LDS with loads that write LDS directly
-// (global_load_lds_dwordx4, no staging registers), into four stages of 32 KB (A 256 x 64 B,
-// B 256 x 64 B); three k-blocks are in flight while one is computed.  Every
+// (global_load_lds_dwordx4, no staging registers), into five stages of 32 KB (A 256 x 64 B,
+// B 256 x 64 B); the MFMA fragments are double-buffered in registers, so a
+// k-block's LDS reads overlap the previous k-block's MFMAs.  Every
 // thread issues the same four loads per stage, so an explicit vmcnt wait plus
 // an LDS barrier marks a stage complete.  Inside a 64-byte row the four
 // 16-byte chunks are stored XOR-swizzled by (row / 2) % 4, so the eight lanes
@@ -41,14 +42,20 @@ namespace ffn_wide {
 
 constexpr int BM = 256;            // grouped rows per tile
 constexpr int KB = 32;             // inputs per k-block (one MFMA K step)
-constexpr int NS = 4;              // LDS stages
+constexpr int NS = 5;              // LDS stages (5 x 32 KB = all 160 KB of LDS)
 constexpr int ROWB = KB * 2;       // bytes per operand row per k-block
 constexpr int OPB = BM * ROWB;     // one operand of one stage (16 KB)
 constexpr int STAGE = 2 * OPB;     // A then B
 constexpr int LPS = 4;             // loads per thread per stage
 constexpr int kGroupM = 4;         // m-tiles per group in the tile order
 
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier that orders LDS only: the compiler sees the lgkmcnt wait
+// (so it knows every LDS read has landed) and outstanding global loads stay in
+// flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+}
 
 // s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
 // lgkmcnt left at their no-wait maxima)
@@ -64,13 +71,13 @@ __device__ __forceinline__ float act_fn(float g) {
   else return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
 }
 
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
-// uniform).  Written as asm so that the compiler, which cannot tell the four
-// stages apart, adds no waits of its own; the kernel waits explicitly
-// (wait_vm + lds_barrier) before it reads a stage.  The asm has no register
-// outputs, and the "memory" clobber keeps every LDS access on its side.
-__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+// 16 bytes per lane from global memory into LDS at byte address lds_addr +
+// 16 * lane (lds_addr uniform).  Written as asm so that the compiler, which
+// cannot tell the stages apart, adds no waits of its own; the kernel waits
+// explicitly (wait_vm + lds_barrier) before it reads a stage.  The asm has no
+// register outputs, and the "memory" clobber keeps every LDS access on its side.
+__device__ __forceinline__ void dma16(const unsigned char* src, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
   // one wait state between the SALU write of M0 and the LDS-writing load
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
@@ -80,7 +87,6 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   constexpr int BNO = GATEUP ? 128 : 256;  // output columns per tile
   constexpr int MF = 4, NF = 8;
   __shared__ __attribute__((aligned(16))) unsigned char stg[NS][STAGE];
-  __shared__ int lds_src[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,6 +97,7 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   const int wc = wave >> 2;
   const int N = args.N, K = args.K;
   const int NBLK = N / BNO;
+  static_assert(NS >= 4, "the loop keeps two k-blocks out of the load window");
 
   // ---------------- tile of this workgroup (XCD-contiguous ranges, grouped-M order)
   int total_mt;
@@ -124,12 +131,6 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   nrows = __builtin_amdgcn_readfirstlane(nrows);
   const int n0 = nb * BNO;
 
-  if (tid < BM) {
-    const int gr = row0 + min(tid, nrows - 1);
-    lds_src[tid] = args.row_index ? args.row_index[gr] / args.row_div : gr;
-  }
-  __syncthreads();
-
   // ---------------- load addresses.  Load i (0, 1) of wave w fills 1 KB = 16
   // rows of an operand: rows 16 (2w + i) + lane / 4, stored chunk lane % 4,
   // holding logical chunk (lane % 4) ^ ((row / 2) % 4) of the row.  Rows
@@ -144,16 +145,27 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * (2 * wave + i) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 1) & 3);
-    a_ptr[i] = static_cast<const unsigned char*>(args.A) + ((size_t)lds_src[row] * K + chunk * 8) * 2;
+    const int gr = row0 + min(row, nrows - 1);
+    const int src = args.row_index ? args.row_index[gr] / args.row_div : gr;
+    a_ptr[i] = static_cast<const unsigned char*>(args.A) + ((size_t)src * K + chunk * 8) * 2;
     // gate/up: tile rows 0..127 are gate rows, 128..255 the up rows of the same outputs
     const unsigned char* w = (GATEUP && row >= 128) ? w1 : w0;
     b_ptr[i] = w + ((size_t)(n0 + (GATEUP ? (row & 127) : row)) * K + chunk * 8) * 2;
   }
-  auto issue = [&](int st, int kb) {  // kb: first input of the k-block
+  // k-block kb into stage st; past the last k-block every lane reads the same
+  // 16 bytes (one cached line) into the stage, which is never read again
+  const unsigned char* const dummy = static_cast<const unsigned char*>(args.A);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)&stg[0][0]);
+  // load l (0..3) of a stage: A rows (l = 0, 1), then B rows (l = 2, 3)
+  auto issue_one = [&](int l, int st, int kb, bool real) {
+    const uint32_t dst = lds_base + (uint32_t)(st * STAGE + (2 * wave) * 1024) + (l >= 2 ? OPB : 0) + (l & 1) * 1024;
+    const unsigned char* src = l < 2 ? a_ptr[l & 1] : b_ptr[l & 1];
+    dma16(real ? src + kb * 2 : dummy, dst);
+  };
+  auto issue = [&](int st, int kb, bool real) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(a_ptr[i] + kb * 2, stg[st] + (2 * wave + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(b_ptr[i] + kb * 2, stg[st] + OPB + (2 * wave + i) * 1024);
+    for (int l = 0; l < LPS; ++l) issue_one(l, st, kb, real);
   };
 
   // fragment reads: lane (lrow, q) needs logical chunk q of its row; rows of a
@@ -169,53 +181,73 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) {
-    if (!active) return;
-    const unsigned char* A = stg[st];
-    const unsigned char* B = stg[st] + OPB;
-    bf16x8 a[MF];
+  // MFMA fragments of one k-block, double-buffered in registers (two named
+  // sets): the fragments of k-block j+1 are read from LDS while k-block j's
+  // MFMAs run
+  bf16x8 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
+  auto read_frags = [&](bf16x8 (&fa)[MF], bf16x8 (&fb)[NF], int st) {
+    const unsigned char* A = &stg[0][0] + st * STAGE;
+    const unsigned char* B = A + OPB;
 #pragma unroll
     for (int mi = 0; mi < MF; ++mi)
-      a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + a_rd + 16 * mi * ROWB));
+      fa[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + a_rd + 16 * mi * ROWB));
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int fo = GATEUP ? (f >= 4 ? 128 : 0) + 16 * (f & 3) : 16 * f;  // B row offset of fragment f
-      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + b_rd + fo * ROWB));
+      fb[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + b_rd + fo * ROWB));
+    }
+  };
+  // The MFMAs of one k-block in four groups, with one of the stage's four loads
+  // issued after each group: a load issue that waits for the address unit
+  // (64 B/clk per CU) then overlaps the MFMAs already in the matrix pipe
+  // instead of holding up the whole k-block.
+  auto mfmas_issue = [&](const bf16x8 (&fa)[MF], const bf16x8 (&fb)[NF], int st, int kb, bool real) {
+    if (!active) {
+      issue(st, kb, real);
+      return;
+    }
 #pragma unroll
-      for (int mi = 0; mi < MF; ++mi) acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, acc[mi][f], 0, 0, 0);
+    for (int g = 0; g < LPS; ++g) {
+#pragma unroll
+      for (int f = 2 * g; f < 2 * g + 2; ++f)
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[f], acc[mi][f], 0, 0, 0);
+      issue_one(g, st, kb, real);
     }
   };
 
-  // ---------------- k-loop.  At the top of k-block j the k-blocks j..j+NS-2 are
-  // in flight; waiting until at most NS-2 stages' loads remain, then a
-  // barrier, makes stage j complete for every wave and frees stage j-1, which
-  // then receives k-block j+NS-1.  K is a multiple of NS * KB.
+  // ---------------- k-loop.  At the top of k-block j the fragments of j are in
+  // registers and the k-blocks j+1..j+NS-2 are in flight; waiting until at most
+  // NS-3 stages' loads remain, then a barrier, makes stage j+1 complete for
+  // every wave and frees stage j-1 (last read one iteration ago), which then
+  // receives k-block j+NS-1 (a dummy load past the end, so that every
+  // iteration issues the same loads and the wait count never changes).  The
+  // fragments of j+1 are read while j's MFMAs run (past the last k-block they
+  // read a stale stage and are never used).  K / KB is even.
   const int NKB = K / KB;
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st) issue(st, st * KB);
-  for (int i = 0; i < NKB - NS; i += NS) {
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      wait_vm<(NS - 2) * LPS>();
-      lds_barrier();
-      issue((u + NS - 1) % NS, (i + u + NS - 1) * KB);
-      compute(u);
-    }
+  for (int st = 0; st < NS - 1; ++st) issue(st, st * KB, st < NKB);
+  wait_vm<(NS - 2) * LPS>();
+  lds_barrier();
+  read_frags(fa0, fb0, 0);
+  int cst = 0;  // stage of k-block j
+  for (int j = 0; j < NKB; j += 2) {
+    wait_vm<(NS - 3) * LPS>();
+    lds_barrier();
+    const int st0 = cst == 0 ? NS - 1 : cst - 1;  // free stage (k-block j-1)
+    cst = cst + 1 == NS ? 0 : cst + 1;             // stage of k-block j+1
+    read_frags(fa1, fb1, cst);
+    mfmas_issue(fa0, fb0, st0, (j + NS - 1) * KB, j + NS - 1 < NKB);
+
+    wait_vm<(NS - 3) * LPS>();
+    lds_barrier();
+    const int st1 = cst == 0 ? NS - 1 : cst - 1;
+    cst = cst + 1 == NS ? 0 : cst + 1;  // stage of k-block j+2
+    read_frags(fa0, fb0, cst);
+    mfmas_issue(fa1, fb1, st1, (j + NS) * KB, j + NS < NKB);
   }
-  // last NS k-blocks: one more load, then the pipeline drains
-  wait_vm<(NS - 2) * LPS>();
-  lds_barrier();
-  issue(NS - 1, (NKB - 1) * KB);
-  compute(0);
-  wait_vm<(NS - 2) * LPS>();
-  lds_barrier();
-  compute(1);
-  wait_vm<(NS - 3) * LPS>();
-  lds_barrier();
-  compute(2);
-  wait_vm<0>();
-  lds_barrier();
-  compute(3);
+  wait_vm<0>();  // the dummy loads land before the stages become the epilogue's buffer
   lds_barrier();
 
   // ---------------- epilogue: four quarters of the output columns, staged
@@ -300,7 +332,7 @@ hipError_t launch_wide(const FfnGemmArgs& a, hipStream_t s) {
   // gate/up writes z in bf16 (the fp32 z of the INT4 path never comes here)
   if (GATEUP && a.out_f32) return hipErrorInvalidValue;
   const int BNO = GATEUP ? 128 : 256;
-  if (a.N % BNO || a.K % (KB * NS) || (size_t)a.N * a.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  if (a.N % BNO || a.K % (2 * KB) || (size_t)a.N * a.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
   const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
   long long g = (long long)mt * (a.N / BNO);
   g = (g + 7) / 8 * 8;
