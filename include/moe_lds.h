@@ -206,10 +206,12 @@ struct moe_layer_desc {
   const void* ws_up;          /* [h_shared, d]                                       */
   const void* ws_down;        /* [d, h_shared]                                       */
   /* Tile hints for the grouped GEMMs, 0 = automatic.  tile_m: rows per tile
-   * (16, 32, 64, 128; INT4 weights at most 64; fp32 at most 32); tile_n_up /
+   * (16, 32, 64, 128; INT4 weights at most 64; fp32 at most 32; 256 selects
+   * the wide bf16 kernel and needs h % 128 == 0 and d % 256 == 0); tile_n_up /
    * tile_n_down: output columns per workgroup of the gate/up and down GEMMs
-   * (64 or 128; 128 requires h resp. d to be a multiple of 128).  Other values
-   * give MOE_EUNSUPPORTED. */
+   * (64 or 128, 128 requiring h resp. d to be a multiple of 128; with
+   * tile_m 256: gate/up 64 or 128, down 128 or 256).  Other values give
+   * MOE_EUNSUPPORTED. */
   int tile_m, tile_n_up, tile_n_down;
 };
 

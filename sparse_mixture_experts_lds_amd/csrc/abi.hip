@@ -192,8 +192,14 @@ int check_layer(const moe_layer_desc* L) {
     const int m = L->tile_m;
     const int mmax = L->w_dtype == MOE_I4G128 ? 64 : (L->w_dtype == MOE_F32 ? 32 : 256);
     if ((m != 16 && m != 32 && m != 64 && m != 128 && m != 256) || m > mmax) return MOE_EUNSUPPORTED;
-    // 256-row tiles are the wide bf16 kernel: 128-column gate/up and 256-column down tiles
-    if (m == 256 && (L->h % 128 || L->d % 256 || L->tile_n_up || L->tile_n_down)) return MOE_EUNSUPPORTED;
+    // 256-row tiles are the wide bf16 kernel: 64- or 128-column gate/up and
+    // 128- or 256-column down tiles
+    if (m == 256) {
+      if (L->h % 128 || L->d % 256) return MOE_EUNSUPPORTED;
+      if (L->tile_n_up && L->tile_n_up != 64 && L->tile_n_up != 128) return MOE_EUNSUPPORTED;
+      if (L->tile_n_down && L->tile_n_down != 128 && L->tile_n_down != 256) return MOE_EUNSUPPORTED;
+      return MOE_OK;
+    }
   }
   if (L->tile_n_up && (L->tile_n_up != 64 && L->tile_n_up != 128)) return MOE_EUNSUPPORTED;
   if (L->tile_n_down && (L->tile_n_down != 64 && L->tile_n_down != 128)) return MOE_EUNSUPPORTED;
@@ -209,7 +215,14 @@ FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
   FfnPlan p = plan_ffn((double)L->T * L->k / L->E, L->E_loc, L->d, L->h, wt);
   const bool hints = L->tile_m || L->tile_n_up || L->tile_n_down;
   if (!hints) return p;
-  if (L->tile_m == 256) return FfnPlan{256, 0, 0, false};
+  if (L->tile_m == 256) {
+    // wide tiles: tile_n_up = output columns of gate/up (64 or 128 -> 128 or 256
+    // weight rows), tile_n_down = output columns of down (128 or 256)
+    FfnPlan w = p.BM == 256 ? p : FfnPlan{256, 4, 4, false};
+    if (L->tile_n_up) w.NF_up = 2 * L->tile_n_up / 64;
+    if (L->tile_n_down) w.NF_down = L->tile_n_down / 64;
+    return w;
+  }
   // narrow tiles: the hinted sizes, the planner's choice for the rest
   if (p.BM == 256) p = FfnPlan{128, 1, L->d % 128 == 0 ? 2 : 1, false};
   if (L->tile_m) p.BM = L->tile_m;

@@ -30,8 +30,11 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   if (w_type == W_BF16 && avg_rows >= 96 && h % 128 == 0 && d % 256 == 0) {
     const double mt = (double)groups * (double)(int)((avg_rows + 255) / 256);
     if (mt * (h / 128) >= 256) {
+      // 256 weight rows per tile (the 128-row variant, reachable through the
+      // tile hints, measured slower on every workload here: a k-block's fixed
+      // costs do not shrink with the tile)
       p.BM = 256;
-      p.NF_up = p.NF_down = 0;
+      p.NF_up = p.NF_down = 4;
       p.split_z = false;
       return p;
     }
@@ -61,7 +64,8 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   if (a.a_rows < 0 || (size_t)a.a_rows * (size_t)a.K * gelt > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (BM == ffn_wide::BM) {
     if (w_type != W_BF16 || split) return hipErrorInvalidValue;
-    return gateup ? ffn_wide::launch_wide<true>(a, s) : ffn_wide::launch_wide<false>(a, s);
+    // NF: weight rows per tile / 64 (4 -> 256, 2 -> 128)
+    return gateup ? ffn_wide::launch_wide<true>(a, 64 * NF, s) : ffn_wide::launch_wide<false>(a, 64 * NF, s);
   }
   if (w_type == W_F32) return gateup ? launch_mf_nf<W_F32, true, false>(a, BM, NF, s) : launch_mf_nf<W_F32, false, false>(a, BM, NF, s);
   if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);

@@ -14,19 +14,22 @@
 // up to 256 rows reads each weight slice once.  It pays when experts get at
 // least ~100 rows.
 //
-// Layout.  Waves form a 4 x 2 grid: wave (wr, wc) owns rows 64*wr..64*wr+63
-// and 128 of the tile's 256 weight rows, as 4 x 8 MFMA 16x16x32 fragments (128
-// fp32 accumulators per lane).  For gate/up the tile's weight rows are 128 gate
-// rows then the 128 up rows of the same outputs, and wave wc takes gate and up
-// rows of output columns 64*wc..64*wc+63, so g and u of an output meet in one
-// lane.  For down the 256 weight rows are 256 output columns, 128 per wave
-// column.
+// Layout.  A tile has BW = 256 (or 128) weight rows.  Waves form a 4 x 2
+// grid: wave (wr, wc) owns rows 64*wr..64*wr+63 and BW/2 of the weight rows,
+// as 4 x BW/32 MFMA 16x16x32 fragments (up to 128 fp32 accumulators per lane).
+// For gate/up the tile's weight rows are BW/2 gate rows then the BW/2 up rows
+// of the same outputs, and wave wc takes gate and up rows of the same output
+// columns, so g and u of an output meet in one lane.  For down the weight
+// rows are output columns, BW/2 per wave column.  The half-width tile exists
+// for workloads whose full-width tiles would leave the last round of
+// workgroups mostly empty.
 //
 // Pipeline.  Operands go global -> LDS with loads that write LDS directly
-// (global_load_lds_dwordx4, no staging registers), into five stages of 32 KB (A 256 x 64 B,
-// B 256 x 64 B); the MFMA fragments are double-buffered in registers, so a
-// k-block's LDS reads overlap the previous k-block's MFMAs.  Every
-// thread issues the same four loads per stage, so an explicit vmcnt wait plus
+// (global_load_lds_dwordx4, no staging registers), into as many stages as
+// LDS holds (A 256 x 64 B plus B BW x 64 B each: 5 stages for BW 256, 6 for
+// 128); the MFMA fragments are double-buffered in registers, so a k-block's
+// LDS reads overlap the previous k-block's MFMAs.  Every thread issues the
+// same loads per stage, so an explicit vmcnt wait plus
 // an LDS barrier marks a stage complete.  Inside a 64-byte row the four
 // 16-byte chunks are stored XOR-swizzled by (row / 2) % 4, so the eight lanes
 // served per LDS cycle (eight consecutive rows, one chunk each) hit eight
@@ -42,12 +45,20 @@ namespace ffn_wide {
 
 constexpr int BM = 256;            // grouped rows per tile
 constexpr int KB = 32;             // inputs per k-block (one MFMA K step)
-constexpr int NS = 5;              // LDS stages (5 x 32 KB = all 160 KB of LDS)
 constexpr int ROWB = KB * 2;       // bytes per operand row per k-block
-constexpr int OPB = BM * ROWB;     // one operand of one stage (16 KB)
-constexpr int STAGE = 2 * OPB;     // A then B
-constexpr int LPS = 4;             // loads per thread per stage
+constexpr int OPA = BM * ROWB;     // the A operand of one stage (16 KB)
 constexpr int kGroupM = 4;         // m-tiles per group in the tile order
+
+// Geometry for BW weight rows per tile (256 or 128).
+template <int BW>
+struct Geo {
+  static constexpr int OPB = BW * ROWB;                   // B operand of one stage
+  static constexpr int STAGE = OPA + OPB;                 // A then B
+  static constexpr int NS = (160 * 1024) / STAGE;         // LDS stages: 5 (BW 256) or 6 (BW 128)
+  static constexpr int LB = BW / 128;                     // B loads per thread per stage
+  static constexpr int LPS = 2 + LB;                      // loads per thread per stage
+  static constexpr int NF = BW / 32;                      // 16-row B fragments per wave
+};
 
 // Workgroup barrier that orders LDS only: the compiler sees the lgkmcnt wait
 // (so it knows every LDS read has landed) and outstanding global loads stay in
@@ -82,10 +93,13 @@ __device__ __forceinline__ void dma16(const unsigned char* src, uint32_t lds_add
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
 
-template <bool GATEUP, bool OUT_F32, int ACT>
+template <bool GATEUP, bool OUT_F32, int ACT, int BW>
 __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
-  constexpr int BNO = GATEUP ? 128 : 256;  // output columns per tile
-  constexpr int MF = 4, NF = 8;
+  using G = Geo<BW>;
+  constexpr int OPB = G::OPB, STAGE = G::STAGE, NS = G::NS, LPS = G::LPS, LB = G::LB;
+  constexpr int BNO = GATEUP ? BW / 2 : BW;  // output columns per tile
+  constexpr int MF = 4, NF = G::NF;
+  constexpr int HW = BW / 2;                 // weight rows per wave column
   __shared__ __attribute__((aligned(16))) unsigned char stg[NS][STAGE];
 
   const int tid = threadIdx.x;
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   const unsigned char* w0 = static_cast<const unsigned char*>(args.W0) + (size_t)e * wslice;
   const unsigned char* w1 = GATEUP ? static_cast<const unsigned char*>(args.W1) + (size_t)e * wslice : w0;
   const unsigned char* a_ptr[2];
-  const unsigned char* b_ptr[2];
+  const unsigned char* b_ptr[LB];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * (2 * wave + i) + (lane >> 2);
@@ -148,19 +162,25 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
     const int gr = row0 + min(row, nrows - 1);
     const int src = args.row_index ? args.row_index[gr] / args.row_div : gr;
     a_ptr[i] = static_cast<const unsigned char*>(args.A) + ((size_t)src * K + chunk * 8) * 2;
-    // gate/up: tile rows 0..127 are gate rows, 128..255 the up rows of the same outputs
-    const unsigned char* w = (GATEUP && row >= 128) ? w1 : w0;
-    b_ptr[i] = w + ((size_t)(n0 + (GATEUP ? (row & 127) : row)) * K + chunk * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int row = 16 * (LB * wave + i) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    // gate/up: tile rows 0..BW/2-1 are gate rows, BW/2..BW-1 the up rows of the same outputs
+    const unsigned char* w = (GATEUP && row >= BW / 2) ? w1 : w0;
+    b_ptr[i] = w + ((size_t)(n0 + (GATEUP ? row % (BW / 2) : row)) * K + chunk * 8) * 2;
   }
   // k-block kb into stage st; past the last k-block every lane reads the same
   // 16 bytes (one cached line) into the stage, which is never read again
   const unsigned char* const dummy = static_cast<const unsigned char*>(args.A);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)&stg[0][0]);
-  // load l (0..3) of a stage: A rows (l = 0, 1), then B rows (l = 2, 3)
+  // load l of a stage: A rows (l = 0, 1), then B rows (l = 2 .. 1 + LB)
   auto issue_one = [&](int l, int st, int kb, bool real) {
-    const uint32_t dst = lds_base + (uint32_t)(st * STAGE + (2 * wave) * 1024) + (l >= 2 ? OPB : 0) + (l & 1) * 1024;
-    const unsigned char* src = l < 2 ? a_ptr[l & 1] : b_ptr[l & 1];
+    const uint32_t dst = l < 2 ? lds_base + (uint32_t)(st * STAGE + (2 * wave + l) * 1024)
+                               : lds_base + (uint32_t)(st * STAGE + OPA + (LB * wave + l - 2) * 1024);
+    const unsigned char* src = l < 2 ? a_ptr[l] : b_ptr[l - 2];
     dma16(real ? src + kb * 2 : dummy, dst);
   };
   auto issue = [&](int st, int kb, bool real) {
@@ -172,7 +192,9 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   // fragment start at multiples of 16, so the stored chunk is q ^ ((lrow / 2) % 4)
   const int rd = lrow * ROWB + ((q ^ ((lrow >> 1) & 3)) * 16);
   const int a_rd = 64 * wr * ROWB + rd;
-  const int b_rd = (GATEUP ? 64 : 128) * wc * ROWB + rd;
+  // wave column wc: gate/up -> gate rows [BW/4 wc, BW/4 (wc+1)) and the same up
+  // rows at +BW/2; down -> rows [BW/2 wc, BW/2 (wc+1))
+  const int b_rd = (GATEUP ? HW / 2 : HW) * wc * ROWB + rd;
   const bool active = 64 * wr < nrows;  // wave-uniform
 
   f32x4 acc[MF][NF];
@@ -187,13 +209,14 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   bf16x8 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
   auto read_frags = [&](bf16x8 (&fa)[MF], bf16x8 (&fb)[NF], int st) {
     const unsigned char* A = &stg[0][0] + st * STAGE;
-    const unsigned char* B = A + OPB;
+    const unsigned char* B = A + OPA;
 #pragma unroll
     for (int mi = 0; mi < MF; ++mi)
       fa[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + a_rd + 16 * mi * ROWB));
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int fo = GATEUP ? (f >= 4 ? 128 : 0) + 16 * (f & 3) : 16 * f;  // B row offset of fragment f
+      // B row offset of fragment f: gate/up -> gate fragments then the up ones
+      const int fo = GATEUP ? (f >= NF / 2 ? BW / 2 : 0) + 16 * (f % (NF / 2)) : 16 * f;
       fb[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + b_rd + fo * ROWB));
     }
   };
@@ -209,7 +232,7 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
 #pragma unroll
     for (int g = 0; g < LPS; ++g) {
 #pragma unroll
-      for (int f = 2 * g; f < 2 * g + 2; ++f)
+      for (int f = g * NF / LPS; f < (g + 1) * NF / LPS; ++f)
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[f], acc[mi][f], 0, 0, 0);
@@ -250,38 +273,41 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   wait_vm<0>();  // the dummy loads land before the stages become the epilogue's buffer
   lds_barrier();
 
-  // ---------------- epilogue: four quarters of the output columns, staged
-  // through the (now free) stage memory
+  // ---------------- epilogue: the output columns in slices of 32 (gate/up) or
+  // 64 (down), staged through the (now free) stage memory; a wave column owns
+  // QPW consecutive slices
   unsigned char* const lds = &stg[0][0];
   unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * (OUT_F32 ? 4 : 2);
   if constexpr (GATEUP) {
     // g and u go to LDS as fp32; every thread then forms act(g)*u for 8
     // columns at a time and stores them as 16 bytes of bf16, which keeps the
     // activation's temporaries out of the accumulator-heavy code
-    constexpr int GS = 32 + 4;  // fp32 row stride of a staged quarter
-    float* G = reinterpret_cast<float*>(lds);
-    float* U = G + BM * GS;
+    constexpr int GS = 32 + 4;     // fp32 row stride of a staged slice
+    constexpr int NQ = BNO / 32;   // slices
+    constexpr int QPW = NQ / 2;    // slices per wave column
+    float* Gs = reinterpret_cast<float*>(lds);
+    float* U = Gs + BM * GS;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      if (wc == (qq >> 1) && active) {
+    for (int qq = 0; qq < NQ; ++qq) {
+      if (wc == qq / QPW && active) {
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
           for (int ff = 0; ff < 2; ++ff) {
-            const int f = 2 * (qq & 1) + ff;
+            const int f = 2 * (qq % QPW) + ff;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int o = (64 * wr + 16 * mi + 4 * q + r) * GS + 16 * ff + lrow;
-              G[o] = acc[mi][f][r];
-              U[o] = acc[mi][f + 4][r];
+              Gs[o] = acc[mi][f][r];
+              U[o] = acc[mi][f + NF / 2][r];
             }
           }
       }
       lds_barrier();
       for (int c = tid; c < nrows * 4; c += 512) {
         const int row = c >> 2, cc = c & 3;
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + row * GS + cc * 8);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + row * GS + cc * 8 + 4);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(Gs + row * GS + cc * 8);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(Gs + row * GS + cc * 8 + 4);
         const f32x4 u0 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8);
         const f32x4 u1 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8 + 4);
         u32x4 o;
@@ -296,17 +322,19 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
     }
   } else {
     constexpr int osz = OUT_F32 ? 4 : 2;
-    constexpr int QC = 64;              // output columns per quarter
-    constexpr int OS = QC * osz + 16;   // LDS row stride of a staged quarter
-    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row of a quarter
+    constexpr int QC = 64;              // output columns per slice
+    constexpr int OS = QC * osz + 16;   // LDS row stride of a staged slice
+    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row of a slice
+    constexpr int NQ = BNO / QC;        // slices
+    constexpr int QPW = NQ / 2;         // slices per wave column
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      if (wc == (qq >> 1) && active) {
+    for (int qq = 0; qq < NQ; ++qq) {
+      if (wc == qq / QPW && active) {
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
           for (int ff = 0; ff < 4; ++ff) {
-            const int f = 4 * (qq & 1) + ff;
+            const int f = 4 * (qq % QPW) + ff;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               unsigned char* dst = lds + (64 * wr + 16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
@@ -327,20 +355,28 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   }
 }
 
-template <bool GATEUP>
-hipError_t launch_wide(const FfnGemmArgs& a, hipStream_t s) {
-  // gate/up writes z in bf16 (the fp32 z of the INT4 path never comes here)
-  if (GATEUP && a.out_f32) return hipErrorInvalidValue;
-  const int BNO = GATEUP ? 128 : 256;
+template <bool GATEUP, int BW>
+hipError_t launch_bw(const FfnGemmArgs& a, hipStream_t s) {
+  constexpr int BNO = GATEUP ? BW / 2 : BW;
   if (a.N % BNO || a.K % (2 * KB) || (size_t)a.N * a.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
   const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
   long long g = (long long)mt * (a.N / BNO);
   g = (g + 7) / 8 * 8;
   if (g == 0) return hipSuccess;
-  if (!GATEUP && a.out_f32) wide_kernel<false, true, 0><<<dim3((unsigned)g), 512, 0, s>>>(a);
-  else if (GATEUP && a.act == 1) wide_kernel<GATEUP, false, 1><<<dim3((unsigned)g), 512, 0, s>>>(a);
-  else wide_kernel<GATEUP, false, 0><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  if (!GATEUP && a.out_f32) wide_kernel<false, true, 0, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  else if (GATEUP && a.act == 1) wide_kernel<GATEUP, false, 1, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  else wide_kernel<GATEUP, false, 0, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// bw: weight rows per tile (256 or 128)
+template <bool GATEUP>
+hipError_t launch_wide(const FfnGemmArgs& a, int bw, hipStream_t s) {
+  // gate/up writes z in bf16 (the fp32 z of the INT4 path never comes here)
+  if (GATEUP && a.out_f32) return hipErrorInvalidValue;
+  if (bw == 256) return launch_bw<GATEUP, 256>(a, s);
+  if (bw == 128) return launch_bw<GATEUP, 128>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ffn_wide

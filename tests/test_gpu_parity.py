@@ -57,15 +57,16 @@ WIDE = {
 }
 
 
+@pytest.mark.parametrize("tiles", [(256, 0, 0), (256, 64, 128)], ids=["full_width", "half_width"])
 @pytest.mark.parametrize("name", list(WIDE))
-def test_layer_wide_tiles(name):
+def test_layer_wide_tiles(name, tiles):
     _moe()
     inp = make_inputs(WIDE[name])
     w = device_weights(inp)
-    w.tiles = (256, 0, 0)
+    w.tiles = tiles
     rep = {}
     check_layer(inp, wdev=w, report=rep)
-    print(name, rep)
+    print(name, tiles, rep)
 
 
 # ------------------------------------------------------------------ edge cases
