@@ -22,6 +22,9 @@ What the layer computes, and where it is stated:
   "Architecture": SwiGLU experts and one shared expert that is always active;
   ExpertMesh runtime list: SwiGLU experts with INT4 weights.  The gated form
   is ``down(act(gate x) * (up x))`` with no biases.
+* Router by-products.  moe_stream.py ``MoEFFN.forward``: per-expert counts of
+  the tokens that chose each expert, the mean softmax probability per expert,
+  and the batch-local balance loss built from both.
 * Combine.  "Sharding d'experts", "Deux rôles": the backbone adds to the
   residual the gate-weighted sum of the workers' partial outputs and the shared
   expert's output; ExpertMesh data-flow figure: the expert outputs are reduced
@@ -84,7 +87,7 @@ def select_topk(L, k: int) -> np.ndarray:
     """The k largest logits of each row, largest first, ties to the lower id.
 
     moe_stream.py ``MoEFFN.forward`` (``torch.topk`` of the softmax, which is
-    sorted); the tie rule is this build's reading.  Done as k rounds of
+    sorted); the page leaves ties open, they go to the lower id here.  Done as k rounds of
     "take the first position of the row maximum, then strike it out".
     """
     L = np.asarray(L, np.float64)
@@ -132,6 +135,34 @@ def route(k: int, renorm: bool, x=None, w_router=None, bias=None, logits=None):
         L = router_logits(x, w_router, bias)
     ids = select_topk(L, k)
     return L, ids, gates(L, ids, renorm)
+
+
+def router_stats(L, ids):
+    """Router by-products of one batch: per-expert token counts, mean router
+    probabilities and the batch-local load-balancing loss.
+
+    moe_stream.py ``MoEFFN.forward``: over the S = T tokens of the batch,
+    ``count[e]`` is the number of tokens whose top-k choice contains e (a token
+    counts once per expert), ``f[e] = count[e] / T``, ``P[e]`` is the mean over
+    tokens of the softmax over all experts (bias included, i.e. of ``L``), and
+    the loss is ``E * sum_e f[e] P[e]``.  Ids outside ``[0, E)`` match no
+    expert.  T = 0 gives zero counts, zero P and a zero loss (the page divides
+    by S and says nothing of an empty batch).  Returns
+    ``(count int64 [E], P float64 [E], loss float)``.
+    """
+    L = np.asarray(L, np.float64)
+    T, E = L.shape
+    ids = np.asarray(ids)
+    ids = ids.reshape(T, ids.shape[-1] if ids.ndim > 1 else -1)
+    count = np.array([np.count_nonzero((ids == e).any(axis=1)) for e in range(E)], np.int64)
+    if T == 0:
+        return count, np.zeros(E), 0.0
+    m = L.max(axis=1, keepdims=True)
+    ex = np.exp(L - m)
+    pi = ex / ex.sum(axis=1, keepdims=True)
+    f = count / T
+    P = pi.sum(axis=0) / T
+    return count, P, float(E * np.sum(f * P))
 
 
 # --------------------------------------------------------------------------

@@ -111,6 +111,103 @@ def test_zero_input_special_case():
         assert np.all(r["out"] == 0.0)
 
 
+# ---------------------------------------------------------------- router by-products
+def test_router_stats_uniform_logits_give_loss_k():
+    """Equal logits: P = 1/E (to rounding), so the loss is the mean number of distinct
+    experts per token, k for distinct ids.  Dividing f by T*k, dropping the
+    factor E, or using the top-k gates for P all miss this."""
+    T, E, k = 37, 9, 3
+    L = np.full((T, E), 0.25)
+    ids = orc.select_topk(L, k)
+    cnt, P, loss = orc.router_stats(L, ids)
+    np.testing.assert_allclose(P, np.full(E, 1.0 / E), rtol=1e-14)
+    assert cnt.sum() == T * k
+    assert loss == pytest.approx(k, rel=1e-14)
+
+
+@pytest.mark.parametrize("E", [4, 8, 64])
+def test_router_stats_one_hot_extremes(E):
+    """k = 1 with a margin of 60 nats: all tokens on one expert gives loss E;
+    tokens spread evenly over the experts gives loss 1 (the two bounds of the
+    loss for one-hot routing); the closed-form P of a two-level row
+    ``e^a / (e^a + E - 1)`` is checked on the way."""
+    T, a = 4 * E, 60.0
+    L = np.zeros((T, E))
+    L[:, 2] = a
+    cnt, P, loss = orc.router_stats(L, orc.select_topk(L, 1))
+    assert cnt[2] == T and cnt.sum() == T
+    top = math.exp(a) / (math.exp(a) + E - 1)
+    assert P[2] == pytest.approx(top, rel=1e-15)
+    assert loss == pytest.approx(E * top, rel=1e-14)
+    L = np.zeros((T, E))
+    L[np.arange(T), np.arange(T) % E] = a
+    cnt, P, loss = orc.router_stats(L, orc.select_topk(L, 1))
+    np.testing.assert_array_equal(cnt, np.full(E, T // E))
+    assert loss == pytest.approx(top, rel=1e-14)
+
+
+def test_router_stats_brute_force_with_duplicate_and_foreign_ids():
+    """Per-token sets and math.fsum on a tiny batch; ids repeat inside a row
+    (the token counts once) and some lie outside [0, E) (they match nothing)."""
+    rng = np.random.default_rng(3)
+    T, E, k = 11, 5, 3
+    L = rng.standard_normal((T, E)) * 2
+    ids = rng.integers(-2, E + 2, size=(T, k))
+    ids[0] = [1, 1, 1]
+    cnt, P, loss = orc.router_stats(L, ids)
+    bc = [0] * E
+    cols = [[] for _ in range(E)]
+    for t in range(T):
+        for e in set(int(v) for v in ids[t]):
+            if 0 <= e < E:
+                bc[e] += 1
+        row = [math.exp(v) for v in L[t]]
+        z = math.fsum(row)
+        for e in range(E):
+            cols[e].append(row[e] / z)
+    Pb = [math.fsum(c) / T for c in cols]
+    lb = E * math.fsum(bc[e] / T * Pb[e] for e in range(E))
+    np.testing.assert_array_equal(cnt, bc)
+    np.testing.assert_allclose(P, Pb, rtol=1e-13)
+    assert loss == pytest.approx(lb, rel=1e-13)
+
+
+def test_router_stats_invariants():
+    """P sums to 1; counts equal the expert histogram of the grouping step (no
+    capacity, distinct ids); relabelling the experts permutes counts and P and
+    keeps the loss; shuffling tokens changes nothing; T = 0 gives zeros."""
+    rng = np.random.default_rng(5)
+    T, E, k = 200, 16, 4
+    L = rng.standard_normal((T, E)) + np.log(np.arange(1, E + 1))[None, :]
+    ids = orc.select_topk(L, k)
+    cnt, P, loss = orc.router_stats(L, ids)
+    assert P.sum() == pytest.approx(1.0, rel=1e-14)
+    offsets = orc.permute(ids, E_loc=E)[0]
+    np.testing.assert_array_equal(cnt, np.diff(offsets))
+    perm = rng.permutation(E)
+    inv = np.argsort(perm)
+    cnt2, P2, loss2 = orc.router_stats(L[:, perm], inv[ids])
+    np.testing.assert_array_equal(cnt2, cnt[perm])
+    np.testing.assert_allclose(P2, P[perm], rtol=1e-14)
+    assert loss2 == pytest.approx(loss, rel=1e-14)
+    tp = rng.permutation(T)
+    cnt3, P3, loss3 = orc.router_stats(L[tp], ids[tp])
+    np.testing.assert_array_equal(cnt3, cnt)
+    np.testing.assert_allclose(P3, P, rtol=1e-13)
+    cnt0, P0, loss0 = orc.router_stats(np.zeros((0, E)), np.zeros((0, k), np.int64))
+    assert cnt0.sum() == 0 and not P0.any() and loss0 == 0.0
+
+
+def test_router_stats_p_matches_torch_softmax_column_mean():
+    """P against torch's float64 softmax, with a per-expert bias added."""
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((64, 12)) * 3
+    b = rng.standard_normal(12)
+    _, P, _ = orc.router_stats(L + b, orc.select_topk(L + b, 2))
+    ref = torch.softmax(torch.from_numpy(L + b), dim=-1).mean(0).numpy()
+    np.testing.assert_allclose(P, ref, rtol=1e-13)
+
+
 # ---------------------------------------------------------------- permutation
 @pytest.mark.parametrize("T,k,E,owners", [(64, 2, 8, 1), (333, 4, 192, 1), (512, 16, 896, 32),
                                           (100, 8, 128, 4)])
