@@ -4,6 +4,7 @@
  *
  * The layer (forward only) runs in five steps, each a call below:
  *   moe_route       router logits GEMM, softmax and top-k selection
+ *   moe_router_stats per-expert counts, mean probabilities, balance loss
  *   moe_permute     grouping of (token, slot) pairs by expert
  *   moe_expert_ffn  grouped gated expert GEMMs (SwiGLU / GeGLU; bf16, fp32 or
  *                   signed INT4 with fp16 group scales)
@@ -105,6 +106,35 @@ int moe_route(int T, int d, int E, int k, int act_dtype,
               const void* x, const void* w_router, const float* logits_in,
               const float* expert_bias, int renorm,
               int32_t* topk_ids, float* topk_w, float* logits_out, void* stream);
+
+/*
+ * moe_router_stats - router by-products of one batch (moe_stream.py
+ * MoEFFN.forward, load-balancing part; the balance loss is the batch-local
+ * auxiliary loss that keeps the experts evenly used).
+ *
+ *   L[t,e]            = logits[t,e] + expert_bias[e]   (bias may be NULL)
+ *   expert_counts[e]  = number of tokens t with e among topk_ids[t, 0..k-1]
+ *                       (a token counts once per expert; ids outside [0, E)
+ *                       match no expert)
+ *   prob_mean[e]      = (1/T) sum_t softmax(L[t, .])[e], softmax over all E
+ *   balance_loss[0]   = E * sum_e (expert_counts[e] / T) * prob_mean[e]
+ *
+ *   T, E, k        tokens, experts, top-k; T = 0 writes zero counts, zero
+ *                  means and a zero loss
+ *   logits         [T, E] fp32 (as moe_route's logits_out, or without bias)
+ *   topk_ids       [T, k] int32
+ *   expert_counts  out [E] int32 or NULL;  prob_mean out [E] fp32 or NULL;
+ *   balance_loss   out [1] fp32 or NULL
+ *   ws, ws_bytes   device workspace of at least
+ *                  moe_router_stats_workspace_bytes(T, E) bytes (NULL allowed
+ *                  when that is 0)
+ * Counts are exact; prob_mean and the loss come from fp32 softmax values added
+ * in fp64 in a fixed order, so repeated calls give identical bits.
+ */
+size_t moe_router_stats_workspace_bytes(int T, int E);
+int moe_router_stats(int T, int E, int k, const float* logits, const float* expert_bias,
+                     const int32_t* topk_ids, int32_t* expert_counts, float* prob_mean,
+                     float* balance_loss, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_permute - group the pairs p = t*k + j by local expert (ExpertMesh:
@@ -235,6 +265,11 @@ struct moe_layer_trace {
   int32_t* pair_pos;          /* [T*k]    */
   void* events[MOE_NUM_EVENTS]; /* hipEvent_t handles owned by the caller, each
                                    recorded on `stream` at its step boundary */
+  /* router by-products (written when T > 0), as moe_router_stats over the layer's L and topk_ids
+   * (all E experts and all T tokens, whatever expert_map keeps local): */
+  int32_t* expert_counts;     /* [E]      */
+  float* prob_mean;           /* [E]      */
+  float* balance_loss;        /* [1]      */
 };
 
 /*

@@ -10,8 +10,8 @@ MOE_SWIGLU, MOE_GEGLU = 0, 1
 
 # every symbol the header declares
 EXPORTS = [
-    "moe_route", "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
-    "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
+    "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
+    "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
     "moe_quantize_int4", "moe_strerror", "moe_last_error",
 ]
 
@@ -38,7 +38,8 @@ EVENT_NAMES = ["start", "routed", "grouped", "gate_up", "down", "shared", "end"]
 
 class LayerTrace(ctypes.Structure):
     _fields_ = [("logits", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("expert_offsets", _vp),
-                ("pair_pos", _vp), ("events", _vp * MOE_NUM_EVENTS)]
+                ("pair_pos", _vp), ("events", _vp * MOE_NUM_EVENTS),
+                ("expert_counts", _vp), ("prob_mean", _vp), ("balance_loss", _vp)]
 
 
 _LIB = None
@@ -57,6 +58,9 @@ def load(path: str = LIB_PATH):
     sig = {
         "moe_route": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                _vp, _vp, _vp, _vp]),
+        "moe_router_stats_workspace_bytes": (_c_size, [_c_int, _c_int]),
+        "moe_router_stats": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                      _vp]),
         "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
         "moe_permute": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp,
                                  _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),

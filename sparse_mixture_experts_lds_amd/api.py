@@ -63,6 +63,23 @@ def route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], k: int, r
     return ids, tw, lo
 
 
+def router_stats(logits: torch.Tensor, topk_ids: torch.Tensor, bias: Optional[torch.Tensor] = None):
+    """Router by-products.  Returns (expert_counts int32 [E], prob_mean float32 [E],
+    balance_loss float32 [1])."""
+    lib = load()
+    T, E = logits.shape
+    k = topk_ids.shape[1]
+    dev = logits.device
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    pm = torch.empty(E, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    nb = lib.moe_router_stats_workspace_bytes(T, E)
+    ws = _ws(nb, dev)
+    check("moe_router_stats", lib.moe_router_stats(T, E, k, _p(logits), _p(bias), _p(topk_ids), _p(cnt), _p(pm),
+                                                   _p(loss), _p(ws), nb, _stream(dev)))
+    return cnt, pm, loss
+
+
 def permute_workspace_bytes(T: int, k: int, E_loc: int) -> int:
     return load().moe_permute_workspace_bytes(T, k, E_loc)
 
@@ -191,12 +208,14 @@ def layer_workspace_bytes(weights: LayerWeights, T: int, d: int, act_dtype: int)
 
 def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Tensor] = None,
               trace: bool = False, out: Optional[torch.Tensor] = None,
-              ws: Optional[torch.Tensor] = None, events=None):
-    """Whole layer forward.  Returns out [T, d] (and a dict of intermediates when trace).
+              ws: Optional[torch.Tensor] = None, events=None, stats: bool = False):
+    """Whole layer forward.  Returns out [T, d] (and a dict of intermediates when trace;
+    ``stats`` adds the router by-products expert_counts, prob_mean and balance_loss to it).
 
     ``events``: optional list of MOE_NUM_EVENTS raw hipEvent_t handles (ints, or None),
     recorded on the current stream at the step boundaries."""
     lib = load()
+    trace = trace or stats
     T, d = x.shape
     dev = x.device
     dt = _dt(x)
@@ -225,6 +244,10 @@ def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Ten
         }
         if logits is None:
             tdict["logits"] = torch.empty((T, weights.E), dtype=torch.float32, device=dev)
+        if stats:
+            tdict["expert_counts"] = torch.empty(weights.E, dtype=torch.int32, device=dev)
+            tdict["prob_mean"] = torch.empty(weights.E, dtype=torch.float32, device=dev)
+            tdict["balance_loss"] = torch.empty(1, dtype=torch.float32, device=dev)
         tr = tr if tr is not None else LayerTrace()
         for name, t in tdict.items():
             setattr(tr, name, t.data_ptr())

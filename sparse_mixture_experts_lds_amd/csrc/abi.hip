@@ -236,7 +236,7 @@ struct LayerBufs {
   int4* tiles;
   int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts;
   float *tw, *logits;
-  void *z, *y, *zs, *ys;
+  void *z, *y, *zs, *ys, *stats;
 };
 
 size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
@@ -257,6 +257,7 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->y = c.take<void>(rows * L->d * 4);  // expert outputs stay fp32 until the combine
   b->zs = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->h_shared * eb : 0);
   b->ys = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->d * 4 : 0);
+  b->stats = c.take<void>(router_stats_ws_bytes(L->T, L->E));  // router by-product partials
   return c.used;
 }
 
@@ -291,6 +292,26 @@ int moe_route(int T, int d, int E, int k, int act_dtype, const void* x, const vo
   if (T > 0 && (!topk_ids || !topk_w)) return MOE_EINVAL;
   MOE_HIP(launch_route(T, d, E, k, act_dtype == MOE_BF16, x, w_router, logits_in, expert_bias, renorm,
                        topk_ids, topk_w, logits_out, as_stream(stream)));
+  return MOE_OK;
+}
+
+size_t moe_router_stats_workspace_bytes(int T, int E) {
+  if (T < 0 || E <= 0 || E > kMaxE) return 0;
+  return router_stats_ws_bytes(T, E);
+}
+
+int moe_router_stats(int T, int E, int k, const float* logits, const float* expert_bias, const int32_t* topk_ids,
+                     int32_t* expert_counts, float* prob_mean, float* balance_loss, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_route_dims(T, E, k);
+  if (rc) return rc;
+  if (T > 0 && (!logits || !topk_ids)) return MOE_EINVAL;
+  const size_t need = router_stats_ws_bytes(T, E);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (need > 0 && !ws) return MOE_EINVAL;
+  if (!expert_counts && !prob_mean && !balance_loss) return MOE_OK;
+  MOE_HIP(launch_router_stats(T, E, k, logits, expert_bias, topk_ids, expert_counts, prob_mean, balance_loss, ws,
+                              as_stream(stream)));
   return MOE_OK;
 }
 
@@ -439,6 +460,12 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
       lsrc = lbuf;
     }
     MOE_HIP(launch_select(T, L->E, k, lsrc, L->expert_bias, L->renorm, ids, tw, tr.logits, s));
+    // router by-products; a trace logits buffer already holds the biased L
+    if (tr.expert_counts || tr.prob_mean || tr.balance_loss) {
+      const float* lstat = tr.logits ? tr.logits : lsrc;
+      MOE_HIP(launch_router_stats(T, L->E, k, lstat, tr.logits ? nullptr : L->expert_bias, ids, tr.expert_counts,
+                                  tr.prob_mean, tr.balance_loss, b.stats, s));
+    }
     MOE_HIP(mark(MOE_EV_ROUTED));
     // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
     const FfnPlan plan = layer_plan(L, rows);

@@ -66,6 +66,15 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
 hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
                          float* tw, float* logits_out, hipStream_t s);
 
+// Router by-products: per-expert token counts, mean softmax probabilities and
+// the balance loss from logits (+ bias) and top-k ids; ws holds
+// router_stats_ws_bytes(T, E) bytes of per-block partials.  Any of counts,
+// prob_mean, loss may be NULL.
+int router_stats_blocks(int T, int E);
+size_t router_stats_ws_bytes(int T, int E);
+hipError_t launch_router_stats(int T, int E, int k, const float* logits, const float* bias, const int32_t* ids,
+                               int32_t* counts, float* prob_mean, float* loss, void* ws, hipStream_t s);
+
 // Grouping of pairs by local expert.
 struct PermuteWs {
   int32_t* counts;       // [nblk * E_loc] per-block counts, then per-block bases

@@ -85,6 +85,21 @@ def shared_f64(inp):
     return (as_f64(inp.wsg), as_f64(inp.wsu), as_f64(inp.wsd))
 
 
+# fp32 softmax values (a few ulp each) added in fp64, then one rounding to fp32
+STATS_RTOL = 2e-6
+
+
+def check_router_stats(L, ids, counts, prob_mean, loss):
+    """Counts bit-exact; mean probabilities and loss within STATS_RTOL of the
+    oracle's float64 values on the same logits and ids."""
+    c_o, P_o, l_o = orc.router_stats(L, ids)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_o)
+    P_g = prob_mean.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(P_g - P_o) <= STATS_RTOL * P_o + 1e-30), float(np.abs(P_g - P_o).max())
+    l_g = float(loss.cpu().numpy()[0])
+    assert abs(l_g - l_o) <= STATS_RTOL * abs(l_o), (l_g, l_o)
+
+
 def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
     """Run the GPU layer and check it against the oracle with the comparison
     protocol: selection bit-exact on the GPU's own fp32 logits, grouping
@@ -96,7 +111,7 @@ def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
     wdev = wdev or device_weights(inp, q, dev)
     x = inp.x.to(dev)
     logits_dev = inp.logits.to(dev) if inp.logits is not None else None
-    out, tr = moe.layer_fwd(x, wdev, logits=logits_dev, trace=True)
+    out, tr = moe.layer_fwd(x, wdev, logits=logits_dev, trace=True, stats=True)
     torch.cuda.synchronize()
     ids_g = tr["topk_ids"].cpu().numpy().astype(np.int64)
     tw_g = tr["topk_w"].cpu().numpy().astype(np.float64)
@@ -109,6 +124,8 @@ def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
     np.testing.assert_array_equal(ids_g, ids_a)
     w_a = orc.gates(Lg, ids_a, cfg.renorm)
     assert np.abs(w_a - tw_g).max() <= 1e-6
+    # (a') router by-products of the GPU's own logits and ids
+    check_router_stats(Lg, ids_g, tr["expert_counts"], tr["prob_mean"], tr["balance_loss"])
     # (c) grouping of the GPU's ids, bit-exact
     offs, sp, pos = orc.permute(ids_g, inp.expert_map, cfg.E_loc, inp.capacity)
     np.testing.assert_array_equal(tr["expert_offsets"].cpu().numpy(), offs)

@@ -15,8 +15,8 @@ import torch
 import oracle as orc
 from moe_synth import CONFIGS, make_inputs, scaled
 from moe_synth.generate import as_f64
-from moe_testutil import (TOL, check_layer, device_weights, oracle_weights, out_err, quantize_inputs,
-                          relerr, sample_tokens)
+from moe_testutil import (TOL, check_layer, check_router_stats, device_weights, oracle_weights, out_err,
+                          quantize_inputs, relerr, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -164,6 +164,64 @@ def test_route_ties_from_given_logits():
     ids, tw, _ = moe.route(None, None, 8, True, logits=torch.from_numpy(L).to(DEV))
     ref = np.argsort(-L.astype(np.float64), axis=1, kind="stable")[:, :8]
     np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (257, 192, 4), (4099, 896, 16), (5000, 1024, 32), (33, 33, 5),
+                                   (70000, 64, 1), (8192, 192, 4)])
+def test_router_stats_entry_point(T, E, k):
+    """Seeded logits with a per-expert bias, ids from the oracle's selection;
+    T spans one to several hundred token blocks with ragged tails, E ragged."""
+    moe = _moe()
+    rng = np.random.default_rng(T + E + k)
+    L = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    Lb = L.astype(np.float32) + b  # the fp32 L the kernel forms
+    ids = orc.select_topk(Lb.astype(np.float64), k).astype(np.int32)
+    c, P, loss = moe.router_stats(torch.from_numpy(L).to(DEV), torch.from_numpy(ids).to(DEV),
+                                  bias=torch.from_numpy(b).to(DEV))
+    check_router_stats(Lb.astype(np.float64), ids, c, P, loss)
+    c2, P2, loss2 = moe.router_stats(torch.from_numpy(Lb).to(DEV), torch.from_numpy(ids).to(DEV))
+    assert torch.equal(c, c2)
+    # same L either way; fixed-order sums give identical bits on a repeat
+    c3, P3, loss3 = moe.router_stats(torch.from_numpy(Lb).to(DEV), torch.from_numpy(ids).to(DEV))
+    assert torch.equal(P2, P3) and torch.equal(loss2, loss3)
+
+
+def test_router_stats_duplicate_foreign_ids_and_extremes():
+    moe = _moe()
+    rng = np.random.default_rng(11)
+    T, E, k = 999, 40, 6
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ids = rng.integers(-3, E + 3, size=(T, k)).astype(np.int32)  # repeats and ids outside [0, E)
+    ids[:50] = 7
+    c, P, loss = moe.router_stats(torch.from_numpy(L).to(DEV), torch.from_numpy(ids).to(DEV))
+    check_router_stats(L.astype(np.float64), ids, c, P, loss)
+    # equal logits: P = 1/E and the loss is k
+    Lu = np.zeros((T, E), np.float32)
+    idu = orc.select_topk(Lu.astype(np.float64), k).astype(np.int32)
+    c, P, loss = moe.router_stats(torch.from_numpy(Lu).to(DEV), torch.from_numpy(idu).to(DEV))
+    assert abs(float(loss.cpu()[0]) - k) <= 1e-5 * k
+    # every token on one expert with a wide margin: the loss is E
+    Lo = np.zeros((T, E), np.float32)
+    Lo[:, 3] = 60.0
+    ido = orc.select_topk(Lo.astype(np.float64), 1).astype(np.int32)
+    c, P, loss = moe.router_stats(torch.from_numpy(Lo).to(DEV), torch.from_numpy(ido).to(DEV))
+    assert int(c.cpu()[3]) == T and abs(float(loss.cpu()[0]) - E) <= 1e-5 * E
+
+
+def test_router_stats_empty_batch_writes_zeros():
+    moe = _moe()
+    E, k = 16, 2
+    c = torch.full((E,), 77, dtype=torch.int32, device=DEV)
+    P = torch.full((E,), 5.0, device=DEV)
+    loss = torch.full((1,), 5.0, device=DEV)
+    lib = moe.load()
+    from sparse_mixture_experts_lds_amd.api import _p, _stream
+    assert lib.moe_router_stats_workspace_bytes(0, E) == 0
+    rc = lib.moe_router_stats(0, E, k, None, None, None, _p(c), _p(P), _p(loss), None, 0, _stream(c.device))
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert not c.any() and not P.any() and not loss.any()
 
 
 @pytest.mark.parametrize("T,k,E,owners,cap", [(1000, 2, 8, 1, 0), (8192, 4, 192, 1, 214), (512, 16, 896, 32, 0),
