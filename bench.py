@@ -174,6 +174,30 @@ def cpu_baseline(cfg, target_s):
                       % (Ts, cfg.T, reps, total)}
 
 
+def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=10):
+    """Per-expert counts, mean probabilities and balance loss of this batch's
+    routing (outside the timed step): average time of one call, and the HBM
+    rate on its algorithmic bytes (logits T*E*4 plus ids T*k*4)."""
+    L = tr["logits"] if "logits" in tr else logits
+    b = None if "logits" in tr else bias  # the trace logits already hold the bias
+    ids = tr["topk_ids"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    moe.router_stats(L, ids, bias=b)
+    for e0, e1 in ev:
+        if not args.warm_cache:
+            flush.fill_(1)
+        e0.record()
+        moe.router_stats(L, ids, bias=b)
+        e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    nbytes = cfg.T * cfg.E * 4 + cfg.T * cfg.k * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "router by-products (counts, mean probability, balance loss; two launches)",
+            "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
+            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -275,6 +299,7 @@ def main(argv=None):
                  "avg_ms": seg_ms[dom], "traffic": measured_traffic(cfg.name, dom),
                  "algorithmic": {"bytes": work[dom]["bytes"], "flops": work[dom]["flops"]}})
     layer_roof = roofline_entry(work["layer"], ms, peak)
+    by_products = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
 
     rec = {
         "metric": METRIC,
@@ -299,6 +324,7 @@ def main(argv=None):
         "touched_experts": work["touched"],
         "step_ms": seg_ms,
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / args.steps, 4),
+        "router_stats": by_products,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -10,7 +10,7 @@ dtype and upcast exactly.  See ``moe_oracle`` for the function list and the
 passages each function follows.
 """
 from .moe_oracle import (  # noqa: F401
-    router_logits, select_topk, gates, route, router_stats, permute, silu, gelu_erf, gated_ffn,
+    router_logits, select_topk, gates, route, router_stats, placement, owner_dispatch, permute, silu, gelu_erf, gated_ffn,
     quantize_int4, dequantize_int4, pack_int4, unpack_int4, round_to_dtype,
     moe_layer, LayerWeights, combine,
 )

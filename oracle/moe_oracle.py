@@ -22,6 +22,10 @@ What the layer computes, and where it is stated:
   "Architecture": SwiGLU experts and one shared expert that is always active;
   ExpertMesh runtime list: SwiGLU experts with INT4 weights.  The gated form
   is ``down(act(gate x) * (up x))`` with no biases.
+* Owner-grouped dispatch (sender side of expert parallelism).  ExpertMesh
+  README, feature list and data-flow figure: deterministic placement of the
+  expert pool across stationary owners, and a dispatcher that groups the
+  routed activations by expert owner.
 * Router by-products.  moe_stream.py ``MoEFFN.forward``: per-expert counts of
   the tokens that chose each expert, the mean softmax probability per expert,
   and the batch-local balance loss built from both.
@@ -46,6 +50,8 @@ of the repository):
   surviving gates are not renormalised;
 * GeGLU's GELU is the exact erf form; SiLU(g) = g / (1 + exp(-g));
 * the shared expert is added with weight 1 on every token;
+* placement of experts on owners is round-robin (owner = e mod n, local id
+  e div n) unless stated otherwise; a contiguous rule is also provided;
 * INT4: per (output row, 128-input group) the scale is
   ``fp16(fp32(max|w|) / 7)`` (both roundings to nearest-even), the code is
   ``clip(rint(w / fp32(scale)), -8, 7)`` with the division in float32 and
@@ -205,6 +211,67 @@ def permute(ids, expert_map=None, E_loc: Optional[int] = None, capacity: int = 0
     for e in range(E_loc):
         pair_pos[groups[e]] = offsets[e] + np.arange(groups[e].size)
     return offsets, sorted_pair.astype(np.int64), pair_pos
+
+
+def placement(E: int, n_owners: int, rule: str = "round_robin"):
+    """Owner and local id of every expert.
+
+    ExpertMesh README, feature list: the expert pool is placed
+    deterministically across stationary owners (896 experts on 32 owners), but
+    the rule is not given.  "round_robin": ``owner = e mod n``,
+    ``local = e div n``; "contiguous": ``owner = e div (E/n)``,
+    ``local = e mod (E/n)``.  E must be a multiple of n.  Returns
+    ``(owner int64 [E], local int64 [E])``.
+    """
+    if n_owners <= 0 or E % n_owners:
+        raise ValueError("E must be a positive multiple of n_owners")
+    e = np.arange(E)
+    per = E // n_owners
+    if rule == "round_robin":
+        return e % n_owners, e // n_owners
+    if rule == "contiguous":
+        return e // per, e % per
+    raise ValueError(rule)
+
+
+def owner_dispatch(ids, E: int, n_owners: int, rule: str = "round_robin", capacity: int = 0):
+    """Sender side of expert parallelism: every (token, slot) pair grouped by the
+    owner of its expert, inside an owner by local expert, inside an expert by
+    ascending pair index p = t*k + j; with ``capacity > 0`` only the first
+    ``capacity`` pairs of each expert are kept.
+
+    ExpertMesh README: the dispatcher groups the routed activations by expert
+    owner (feature list and data-flow figure) and keeps each token's id and
+    top-k slot; MoEEvolve "Architecture": capacity-factor dispatch.  Done as one
+    stable sort on the key (owner, local, p).  Returns a dict with
+    ``sorted_pair``, ``pair_pos`` (-1 for dropped pairs and ids outside
+    [0, E)), ``expert_offsets [E+1]`` in (owner, local) order,
+    ``owner_offsets [n+1]`` and ``recv_offsets [n, E/n + 1]`` (each owner's
+    expert offsets counted from its first row).
+    """
+    owner, local = placement(E, n_owners, rule)
+    per = E // n_owners
+    flat = np.asarray(ids).reshape(-1).astype(np.int64)
+    P = flat.size
+    valid = (flat >= 0) & (flat < E)
+    p = np.nonzero(valid)[0]
+    o, l = owner[flat[p]], local[flat[p]]
+    order = np.lexsort((p, l, o))  # last key is the primary one
+    p, o, l = p[order], o[order], l[order]
+    slot = o * per + l  # position of the expert in owner-major order
+    # rank of each pair inside its expert (pairs of one expert are adjacent)
+    start = np.searchsorted(slot, slot, side="left")
+    keep = np.ones(p.size, bool) if capacity <= 0 else (np.arange(p.size) - start) < capacity
+    p, slot = p[keep], slot[keep]
+    counts = np.bincount(slot, minlength=E)
+    expert_offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    pair_pos = np.full(P, -1, np.int64)
+    pair_pos[p] = np.arange(p.size)
+    owner_offsets = expert_offsets[::per].copy()
+    recv = np.stack([expert_offsets[i * per:(i + 1) * per + 1] - expert_offsets[i * per]
+                     for i in range(n_owners)])
+    return {"sorted_pair": p.astype(np.int64), "pair_pos": pair_pos, "expert_offsets": expert_offsets,
+            "owner_offsets": owner_offsets, "recv_offsets": recv}
 
 
 # --------------------------------------------------------------------------

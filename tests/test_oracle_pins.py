@@ -265,6 +265,75 @@ def test_capacity_brute_force_sequential_dispatch():
                 assert (pos >= 0).tolist() == expect
 
 
+# ---------------------------------------------------------------- owner-grouped dispatch
+@pytest.mark.parametrize("rule", ["round_robin", "contiguous"])
+@pytest.mark.parametrize("cap", [0, 2])
+def test_owner_dispatch_brute_force(rule, cap):
+    """Python's sorted() on (owner, local, p) tuples with a per-expert counter,
+    ids outside [0, E) included; capacity keeps the first pairs of each expert."""
+    rng = np.random.default_rng(4)
+    T, k, E, n = 13, 3, 12, 4
+    ids = rng.integers(-1, E + 1, size=(T, k))
+    per = E // n
+    own = (lambda e: e % n) if rule == "round_robin" else (lambda e: e // per)
+    loc = (lambda e: e // n) if rule == "round_robin" else (lambda e: e % per)
+    keys = sorted((own(int(e)), loc(int(e)), p) for p, e in enumerate(ids.reshape(-1)) if 0 <= e < E)
+    seen = {}
+    rows = []
+    for o, l, p in keys:
+        seen[(o, l)] = seen.get((o, l), 0) + 1
+        if cap == 0 or seen[(o, l)] <= cap:
+            rows.append((o, l, p))
+    r = orc.owner_dispatch(ids, E, n, rule, capacity=cap)
+    np.testing.assert_array_equal(r["sorted_pair"], [p for _, _, p in rows])
+    pos = [-1] * (T * k)
+    for i, (_, _, p) in enumerate(rows):
+        pos[p] = i
+    np.testing.assert_array_equal(r["pair_pos"], pos)
+    for o in range(n):
+        mine = [i for i, row in enumerate(rows) if row[0] == o]
+        assert r["owner_offsets"][o + 1] - r["owner_offsets"][o] == len(mine)
+        for l in range(per):
+            cnt = sum(1 for row in rows if row[0] == o and row[1] == l)
+            assert r["recv_offsets"][o, l + 1] - r["recv_offsets"][o, l] == cnt
+    assert r["owner_offsets"][-1] == len(rows) == r["expert_offsets"][-1]
+
+
+def test_owner_dispatch_special_cases():
+    """One owner is the plain grouping by expert; one expert per owner makes
+    owner offsets equal expert offsets; the composed map (owner * E/n + local)
+    handed to the grouping step gives the same rows."""
+    rng = np.random.default_rng(8)
+    T, k, E = 50, 4, 16
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    off, sp, pos = orc.permute(ids, E_loc=E)
+    r = orc.owner_dispatch(ids, E, 1)
+    np.testing.assert_array_equal(r["sorted_pair"], sp)
+    np.testing.assert_array_equal(r["pair_pos"], pos)
+    np.testing.assert_array_equal(r["recv_offsets"][0], off)
+    r = orc.owner_dispatch(ids, E, E, "contiguous")
+    np.testing.assert_array_equal(r["owner_offsets"], off)
+    for n, rule, cap in [(4, "round_robin", 0), (8, "contiguous", 5), (2, "round_robin", 3)]:
+        owner, local = orc.placement(E, n, rule)
+        off, sp, pos = orc.permute(ids, expert_map=owner * (E // n) + local, E_loc=E, capacity=cap)
+        r = orc.owner_dispatch(ids, E, n, rule, capacity=cap)
+        np.testing.assert_array_equal(r["expert_offsets"], off)
+        np.testing.assert_array_equal(r["sorted_pair"], sp)
+        np.testing.assert_array_equal(r["pair_pos"], pos)
+
+
+def test_round_robin_share_of_owner_zero():
+    """896 experts on 32 owners: owner 0 holds 0, 32, ..., 864 with local ids
+    0..27, the share of the INT4 workload recipe."""
+    from moe_synth import CONFIGS
+    owner, local = orc.placement(896, 32)
+    mine = np.nonzero(owner == 0)[0]
+    np.testing.assert_array_equal(mine, np.arange(0, 896, 32))
+    np.testing.assert_array_equal(local[mine], np.arange(28))
+    assert mine.tolist() == CONFIGS["int4_share"].local_experts()
+    assert np.bincount(owner).tolist() == [28] * 32
+
+
 # ---------------------------------------------------------------- expert FFN
 @pytest.mark.parametrize("name,g,v", activation_points())
 def test_activation_textbook_points(name, g, v):
