@@ -193,7 +193,7 @@ def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=10)
     us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
     nbytes = cfg.T * cfg.E * 4 + cfg.T * cfg.k * 4
     gbps = nbytes / (us * 1e-6) / 1e9
-    return {"kernel": "router by-products (counts, mean probability, balance loss; two launches)",
+    return {"kernel": "router by-products (counts, mean probability, balance loss; three launches)",
             "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
 

@@ -6,6 +6,8 @@
  *   moe_route       router logits GEMM, softmax and top-k selection
  *   moe_router_stats per-expert counts, mean probabilities, balance loss
  *   moe_permute     grouping of (token, slot) pairs by expert
+ *   moe_dispatch_owners  the same grouping by owner of the expert (sender
+ *                   side of expert parallelism)
  *   moe_expert_ffn  grouped gated expert GEMMs (SwiGLU / GeGLU; bf16, fp32 or
  *                   signed INT4 with fp16 group scales)
  *   moe_combine     weighted top-k combine plus the optional shared expert
@@ -164,6 +166,43 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids,
                 int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
                 const void* x, int d, int act_dtype, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch_owners - sender side of expert parallelism: every (token, slot)
+ * pair grouped by the owner that holds its expert, in one pass (ExpertMesh
+ * README: deterministic placement of the expert pool across stationary
+ * owners; a dispatcher that groups the routed activations by expert owner and
+ * keeps each token and top-k slot).
+ *
+ *   placement  MOE_PLACE_ROUND_ROBIN: owner(e) = e % n_owners, local(e) = e / n_owners
+ *              MOE_PLACE_CONTIGUOUS:  owner(e) = e / per,      local(e) = e % per
+ *              with per = E / n_owners (E must be a multiple of n_owners)
+ *   rows       ordered by (owner, local expert, p = t*k + j); with capacity > 0
+ *              only the first `capacity` pairs of each expert (ascending p)
+ *              are kept; ids outside [0, E) are dropped
+ *   owner_offsets   out [n_owners+1]: owner o sends rows [owner_offsets[o],
+ *                   owner_offsets[o+1])
+ *   recv_offsets    out [n_owners, per+1] or NULL: owner o's expert offsets
+ *                   counted from its first row (offsets[0] = 0), as the
+ *                   receiving owner passes them to moe_expert_ffn
+ *   expert_offsets  out [E+1] or NULL: the same offsets over the whole buffer,
+ *                   expert (o, l) at index o*per + l
+ *   sorted_pair, pair_pos   as moe_permute, over the whole buffer
+ *   x, d, act_dtype, x_send optional row gather x_send[r, :] = x[sorted_pair[r] / k, :]
+ *                   into x_send [T*k, d] (NULL = no gather)
+ *   ws, ws_bytes    device workspace of at least moe_dispatch_owners_workspace_bytes()
+ * Output is deterministic.
+ */
+enum moe_placement {
+  MOE_PLACE_ROUND_ROBIN = 0,
+  MOE_PLACE_CONTIGUOUS = 1
+};
+size_t moe_dispatch_owners_workspace_bytes(int T, int k, int E);
+int moe_dispatch_owners(int T, int k, int E, int n_owners, int placement, int capacity,
+                        const int32_t* topk_ids, int32_t* owner_offsets, int32_t* recv_offsets,
+                        int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        const void* x, int d, int act_dtype, void* x_send,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_expert_ffn - grouped gated expert FFN ("Deux roles": the three matrix

@@ -7,11 +7,13 @@ from .build import LIB_PATH
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_I4G128 = 0, 1, 2
 MOE_SWIGLU, MOE_GEGLU = 0, 1
+MOE_PLACE_ROUND_ROBIN, MOE_PLACE_CONTIGUOUS = 0, 1
 
 # every symbol the header declares
 EXPORTS = [
     "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
-    "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
+    "moe_permute", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
+    "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
     "moe_quantize_int4", "moe_strerror", "moe_last_error",
 ]
 
@@ -64,6 +66,9 @@ def load(path: str = LIB_PATH):
         "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
         "moe_permute": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp,
                                  _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+        "moe_dispatch_owners_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+        "moe_dispatch_owners": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
         "moe_expert_ffn_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
         "moe_expert_ffn": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),

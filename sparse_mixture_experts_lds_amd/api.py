@@ -109,6 +109,36 @@ def permute(topk_ids: torch.Tensor, E: int, E_loc: Optional[int] = None,
     return offsets, sp, pos, x_perm
 
 
+_PLACE = {"round_robin": _lib.MOE_PLACE_ROUND_ROBIN, "contiguous": _lib.MOE_PLACE_CONTIGUOUS}
+
+
+def dispatch_owners(topk_ids: torch.Tensor, E: int, n_owners: int, placement: str = "round_robin",
+                    capacity: int = 0, x: Optional[torch.Tensor] = None):
+    """Pairs grouped by expert owner (then local expert, then pair index).  Returns a dict
+    with owner_offsets [n+1], recv_offsets [n, E/n+1], expert_offsets [E+1], sorted_pair,
+    pair_pos [T*k] (int32) and, when x is given, x_send [T*k, d]."""
+    lib = load()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    r = {"owner_offsets": torch.empty(n_owners + 1, **i32),
+         "recv_offsets": torch.empty((n_owners, E // max(n_owners, 1) + 1), **i32),
+         "expert_offsets": torch.empty(E + 1, **i32),
+         "sorted_pair": torch.empty(max(T * k, 1), **i32),
+         "pair_pos": torch.empty(max(T * k, 1), **i32)}
+    d, dt = 0, MOE_F32
+    if x is not None:
+        d, dt = x.shape[1], _dt(x)
+        r["x_send"] = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    nb = lib.moe_dispatch_owners_workspace_bytes(T, k, E)
+    ws = _ws(nb, dev)
+    check("moe_dispatch_owners", lib.moe_dispatch_owners(
+        T, k, E, n_owners, _PLACE[placement], int(capacity), _p(topk_ids), _p(r["owner_offsets"]),
+        _p(r["recv_offsets"]), _p(r["expert_offsets"]), _p(r["sorted_pair"]), _p(r["pair_pos"]), _p(x), d, dt,
+        _p(r.get("x_send")), _p(ws), nb, _stream(dev)))
+    return r
+
+
 def expert_ffn_workspace_bytes(E_loc, rows_max, d, h, act_dtype) -> int:
     return load().moe_expert_ffn_workspace_bytes(E_loc, rows_max, d, h, act_dtype)
 

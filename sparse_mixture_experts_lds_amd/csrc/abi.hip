@@ -346,6 +346,41 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* exp
   return MOE_OK;
 }
 
+size_t moe_dispatch_owners_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k <= 0 || E <= 0 || E > kMaxE) return 0;
+  return align_up((size_t)E * 4) + align_up((size_t)(E + 1) * 4) + align_up(permute_ws_bytes(T * k, E));
+}
+
+int moe_dispatch_owners(int T, int k, int E, int n_owners, int placement, int capacity, const int32_t* topk_ids,
+                        int32_t* owner_offsets, int32_t* recv_offsets, int32_t* expert_offsets,
+                        int32_t* sorted_pair, int32_t* pair_pos, const void* x, int d, int act_dtype,
+                        void* x_send, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_route_dims(T, E, k);
+  if (rc) return rc;
+  if (n_owners <= 0 || E % n_owners != 0 || capacity < 0) return MOE_EINVAL;
+  if (placement != MOE_PLACE_ROUND_ROBIN && placement != MOE_PLACE_CONTIGUOUS) return MOE_EINVAL;
+  if (!owner_offsets) return MOE_EINVAL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_EINVAL;
+  if (x_send) {
+    if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
+    if ((rc = check_width(d, act_dtype))) return rc;
+    if (!x) return MOE_EINVAL;
+  }
+  if (ws_bytes < moe_dispatch_owners_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
+  if (!ws) return MOE_EINVAL;
+  Carver c(ws);
+  int32_t* map = c.take<int32_t>((size_t)E * 4);
+  int32_t* eo_ws = c.take<int32_t>((size_t)(E + 1) * 4);
+  int32_t* counts = c.take<int32_t>(permute_ws_bytes(T * k, E));
+  int32_t* eo = expert_offsets ? expert_offsets : eo_ws;
+  hipStream_t s = as_stream(stream);
+  MOE_HIP(launch_owner_dispatch(T, k, E, n_owners, placement, capacity, topk_ids, owner_offsets, recv_offsets, eo,
+                                sorted_pair, pair_pos, map, counts, s));
+  if (x_send && T > 0)
+    MOE_HIP(launch_gather_rows(T * k, d, act_dtype == MOE_BF16, x, sorted_pair, k, eo + E, x_send, s));
+  return MOE_OK;
+}
+
 size_t moe_expert_ffn_workspace_bytes(int E_loc, int rows_max, int d, int h, int act_dtype) {
   (void)d;
   if (E_loc <= 0 || rows_max < 0 || h <= 0 || !act_dtype_ok(act_dtype)) return 0;

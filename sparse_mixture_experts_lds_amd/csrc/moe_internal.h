@@ -51,6 +51,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
+// Every lane of the group ends with the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
+
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dppf<kRowRor8>(x));
+  x = fmaxf(x, dppf<kRowRor4>(x));
+  x = fmaxf(x, dppf<kQuadSwap2>(x));
+  x = fmaxf(x, dppf<kQuadSwap1>(x));
+  if constexpr (G == 64) {
+    x = fmaxf(x, wave_shfl_xor(x, 16));
+    x = fmaxf(x, wave_shfl_xor(x, 32));
+  }
+  return x;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dppf<kRowRor8>(x);
+  x += dppf<kRowRor4>(x);
+  x += dppf<kQuadSwap2>(x);
+  x += dppf<kQuadSwap1>(x);
+  if constexpr (G == 64) {
+    x += wave_shfl_xor(x, 16);
+    x += wave_shfl_xor(x, 32);
+  }
+  return x;
+}
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
 
@@ -87,6 +123,12 @@ int permute_block_pairs();
 hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t* expert_map, int E_loc,
                           int capacity, int BM, int32_t* offsets, int32_t* mtile_start, int4* tile_tab,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* counts, hipStream_t s);
+// Pairs grouped by (owner, local expert, p) under a placement rule (0 round
+// robin, 1 contiguous); map holds E ints and counts permute_ws_bytes(T*k, E).
+hipError_t launch_owner_dispatch(int T, int k, int E, int n_owners, int rule, int capacity, const int32_t* ids,
+                                 int32_t* owner_offsets, int32_t* recv_offsets, int32_t* expert_offsets,
+                                 int32_t* sorted_pair, int32_t* pair_pos, int32_t* map, int32_t* counts,
+                                 hipStream_t s);
 hipError_t launch_gather_rows(int rows_max, int d, bool bf16, const void* x, const int32_t* sorted_pair,
                               int k, const int32_t* offsets_end, void* x_perm, hipStream_t s);
 hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_t* mtile_start,

@@ -18,6 +18,8 @@
 //               ballots over the key bits (a wave multisplit) and takes its
 //               rank from a popcount; per-wave counts become per-wave bases
 //               in LDS, added to the block's base from the scan.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -216,6 +218,28 @@ __global__ void zero_offsets_kernel(int E_loc, int32_t* offsets, int32_t* mtile_
   }
 }
 
+// Owner-grouped dispatch: the composed key owner(e) * (E/n) + local(e) puts
+// every expert at its place in owner-major order, so the grouping above sorts
+// the pairs by (owner, local expert, p) in the same single pass.
+__global__ void placement_map_kernel(int E, int n_owners, int rule, int32_t* __restrict__ map) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int per = E / n_owners;
+  const int o = rule == 0 ? e % n_owners : e / per;
+  const int l = rule == 0 ? e / n_owners : e % per;
+  map[e] = o * per + l;
+}
+
+__global__ void owner_offsets_kernel(int n_owners, int per, const int32_t* __restrict__ eo,
+                                     int32_t* __restrict__ owner_offsets, int32_t* __restrict__ recv) {
+  const int total = n_owners * (per + 1);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int o = i / (per + 1), l = i - o * (per + 1);
+    if (recv) recv[i] = eo[o * per + l] - eo[o * per];
+    if (i <= n_owners) owner_offsets[i] = eo[i * per];
+  }
+}
+
 }  // namespace
 
 int permute_block_pairs() { return kBlockPairs; }
@@ -238,6 +262,22 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t
   scan_kernel<<<1, kScanThreads, 0, s>>>(nblk, E_loc, capacity, BM, counts, offsets, mtile_start, tile_tab);
   scatter_kernel<<<nblk, kBlockPairs, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets,
                                               sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_owner_dispatch(int T, int k, int E, int n_owners, int rule, int capacity, const int32_t* ids,
+                                 int32_t* owner_offsets, int32_t* recv_offsets, int32_t* expert_offsets,
+                                 int32_t* sorted_pair, int32_t* pair_pos, int32_t* map, int32_t* counts,
+                                 hipStream_t s) {
+  placement_map_kernel<<<(E + 255) / 256, 256, 0, s>>>(E, n_owners, rule, map);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_permute(T, k, E, ids, map, E, capacity, 16, expert_offsets, nullptr, nullptr, sorted_pair, pair_pos,
+                     counts, s);
+  if (e != hipSuccess) return e;
+  const int total = n_owners * (E / n_owners + 1);
+  owner_offsets_kernel<<<std::min((total + 255) / 256, 64), 256, 0, s>>>(n_owners, E / n_owners, expert_offsets,
+                                                                          owner_offsets, recv_offsets);
   return hipGetLastError();
 }
 

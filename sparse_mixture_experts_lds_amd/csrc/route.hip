@@ -207,42 +207,6 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
   }
 }
 
-// Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
-// Every lane of the group ends with the result.
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-  return __int_as_float(dpp<CTRL>(__float_as_int(v)));
-}
-constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;
-
-template <int G>
-__device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, dppf<kRowRor8>(x));
-  x = fmaxf(x, dppf<kRowRor4>(x));
-  x = fmaxf(x, dppf<kQuadSwap2>(x));
-  x = fmaxf(x, dppf<kQuadSwap1>(x));
-  if constexpr (G == 64) {
-    x = fmaxf(x, wave_shfl_xor(x, 16));
-    x = fmaxf(x, wave_shfl_xor(x, 32));
-  }
-  return x;
-}
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dppf<kRowRor8>(x);
-  x += dppf<kRowRor4>(x);
-  x += dppf<kQuadSwap2>(x);
-  x += dppf<kQuadSwap1>(x);
-  if constexpr (G == 64) {
-    x += wave_shfl_xor(x, 16);
-    x += wave_shfl_xor(x, 32);
-  }
-  return x;
-}
 __device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
   if (ov > v || (ov == v && oe < e)) {
     v = ov;

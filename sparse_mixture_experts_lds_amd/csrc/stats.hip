@@ -6,13 +6,14 @@
 //   loss     = E * sum_e (count[e] / T) * P[e]
 // with L = logits (+ bias).  Ids outside [0, E) match no expert.
 //
-// Two passes, both in a fixed order so the result does not depend on
+// Three passes, each in a fixed order so the result does not depend on
 // scheduling: each workgroup of the first pass owns a fixed strided set of
 // tokens (one wave per token row; lane l holds experts l + 64i), keeps fp64
 // column sums of the softmax in registers and integer counts in LDS, and
-// writes one [E] row of partials; one workgroup of the second pass adds the
-// rows in block order in fp64 and forms the loss.  The logits are read once,
-// so the first pass is bound by HBM at T*E*4 + T*k*4 bytes.
+// writes one [E] row of partials; the second pass adds the rows column by
+// column (one workgroup per 64 experts); the third folds the per-workgroup
+// loss terms.  The logits are read once: the first pass moves
+// T*E*4 + T*k*4 bytes, the partial rows at most 12*E*256 more.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -20,118 +21,199 @@
 namespace moe {
 namespace {
 
-constexpr int kStatsWaves = 4;
-constexpr int kStatsMinTokensPerBlock = 32;
 constexpr int kStatsMaxBlocks = 256;
 constexpr int kStatsMaxPartials = 65536;  // partial rows * E, bounds the workspace
+constexpr int kColWaves = 16;             // waves of a column-reduction workgroup
 
-template <int NV>
+// First pass.  One group of G lanes per token (G = 16: one DPP row, for
+// E <= 256 and k <= 16; else G = 64, the wave); lane g of a group holds experts
+// g + G*i, so every lane keeps the same columns for all its tokens and adds
+// their probabilities in fp64 registers.  A group takes U tokens at a time so
+// the loads and reductions of the U rows overlap.  Counting a token once per
+// expert: the lanes of its slots swap the token id into a per-group LDS stamp
+// of the expert, and only a lane that finds another value there counts.
+template <int G, int NV, int U>
 __global__ __launch_bounds__(256) void stats_partial_kernel(int T, int E, int k, const float* __restrict__ logits,
                                                             const float* __restrict__ bias,
                                                             const int32_t* __restrict__ ids,
                                                             double* __restrict__ part_p,
                                                             int32_t* __restrict__ part_c) {
-  constexpr int EW = NV * 64;
-  __shared__ double red[kStatsWaves][EW];
+  constexpr int NG = 256 / G;  // groups per workgroup
+  constexpr int EW = NV * G;   // expert columns covered by a group (>= E)
+  __shared__ double red[NG][EW];
+  __shared__ int stamp[NG][EW];
   __shared__ int cnt[EW];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = threadIdx.x & (G - 1), grp = threadIdx.x / G;
   for (int e = threadIdx.x; e < EW; e += blockDim.x) cnt[e] = 0;
+  for (int i = threadIdx.x; i < NG * EW; i += blockDim.x) (&stamp[0][0])[i] = -1;
   __syncthreads();
 
   float b[NV];
   double acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
+    const int e = gl + G * i;
     b[i] = (bias != nullptr && e < E) ? bias[e] : 0.f;
     acc[i] = 0.0;
   }
-  const int stride = gridDim.x * kStatsWaves;
-  for (int t = blockIdx.x * kStatsWaves + wave; t < T; t += stride) {
-    const float* row = logits + (size_t)t * E;
-    float v[NV];
-    float m = -INFINITY;
+  const int stride = gridDim.x * NG;  // groups in the grid
+  for (int t0 = blockIdx.x * NG + grp; t0 < T; t0 += U * stride) {
+    float v[U][NV];
+    float m[U], sum[U];
+    int id[U];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? row[e] + b[i] : -INFINITY;
-      m = fmaxf(m, v[i]);
-    }
-    m = wave_max(m);
-    float s = 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * stride;  // uniform over the group
+      const bool ok = t < T;
+      const float* row = logits + (size_t)(ok ? t : 0) * E;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      v[i] = lane + 64 * i < E ? expf(v[i] - m) : 0.f;
-      s += v[i];
+      for (int i = 0; i < NV; ++i) {
+        const int e = gl + G * i;
+        v[u][i] = (ok && e < E) ? row[e] + b[i] : -INFINITY;
+      }
+      id[u] = (ok && gl < k) ? ids[(size_t)t * k + gl] : -1;
     }
-    s = wave_sum(s);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] += (double)(v[i] / s);
-
-    // lane j < k holds slot j; a slot whose id already appears in a lower
-    // slot of the same token is not counted again
-    const int id = lane < k ? ids[(size_t)t * k + lane] : -1;
-    bool dup = false;
-    for (int j = 0; j < k; ++j) {
-      const int o = __shfl(id, j);
-      dup |= (j < lane) && (o == id);
+    for (int u = 0; u < U; ++u) {
+      float mm = v[u][0];
+#pragma unroll
+      for (int i = 1; i < NV; ++i) mm = fmaxf(mm, v[u][i]);
+      m[u] = group_max<G>(mm);
     }
-    if (lane < k && !dup && id >= 0 && id < E) atomicAdd(&cnt[id], 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = t0 + u * stride < T;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        v[u][i] = (ok && gl + G * i < E) ? expf(v[u][i] - m[u]) : 0.f;
+        ss += v[u][i];
+      }
+      sum[u] = group_sum<G>(ss);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u * stride < T) {  // a row past T has sum 0
+        const float inv = 1.f / sum[u];  // one division per token; p within 1.5 ulp
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] += (double)(v[u][i] * inv);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * stride;
+      if (id[u] >= 0 && id[u] < E) {
+        const int prev = atomicExch(&stamp[grp][id[u]], t);
+        if (prev != t) atomicAdd(&cnt[id[u]], 1);
+      }
+    }
   }
 #pragma unroll
-  for (int i = 0; i < NV; ++i) red[wave][lane + 64 * i] = acc[i];
+  for (int i = 0; i < NV; ++i) red[grp][gl + G * i] = acc[i];
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     double p = red[0][e];
 #pragma unroll
-    for (int w = 1; w < kStatsWaves; ++w) p += red[w][e];
+    for (int g = 1; g < NG; ++g) p += red[g][e];
     part_p[(size_t)blockIdx.x * E + e] = p;
     part_c[(size_t)blockIdx.x * E + e] = cnt[e];
   }
 }
 
-__global__ __launch_bounds__(1024) void stats_final_kernel(int T, int E, int nblk, const double* __restrict__ part_p,
-                                                           const int32_t* __restrict__ part_c,
-                                                           int32_t* __restrict__ counts, float* __restrict__ prob_mean,
-                                                           float* __restrict__ loss) {
-  __shared__ double red[1024];
-  double tot = 0.0;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    // four interleaved chains (blocks b = 0,1,2,3 mod 4) for load parallelism,
-    // added in a fixed order at the end
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    int c = 0;
-    int b = 0;
-    for (; b + 4 <= nblk; b += 4) {
-      s0 += part_p[(size_t)(b + 0) * E + e];
-      s1 += part_p[(size_t)(b + 1) * E + e];
-      s2 += part_p[(size_t)(b + 2) * E + e];
-      s3 += part_p[(size_t)(b + 3) * E + e];
-      c += part_c[(size_t)(b + 0) * E + e] + part_c[(size_t)(b + 1) * E + e] + part_c[(size_t)(b + 2) * E + e] +
-           part_c[(size_t)(b + 3) * E + e];
+// Second pass: workgroup c owns experts 64c..64c+63; wave w adds the partial
+// rows b = w, w + 16, ... (eight independent chains, folded in a fixed order),
+// then wave 0 adds the 16 wave sums in wave order.  Writes the counts and
+// means of its experts and its share of sum_e count[e] * colsum[e].
+__global__ __launch_bounds__(64 * kColWaves) void stats_column_kernel(int T, int E, int nblk,
+                                                                     const double* __restrict__ part_p,
+                                                                     const int32_t* __restrict__ part_c,
+                                                                     int32_t* __restrict__ counts,
+                                                                     float* __restrict__ prob_mean,
+                                                                     double* __restrict__ chunk_loss) {
+  __shared__ double rs[kColWaves][64];
+  __shared__ int rc[kColWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int c = 0;
+  if (e < E) {
+    int b = wave;
+    for (; b + 7 * kColWaves < nblk; b += 8 * kColWaves) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        s[q] += part_p[(size_t)(b + q * kColWaves) * E + e];
+        c += part_c[(size_t)(b + q * kColWaves) * E + e];
+      }
     }
-    for (; b < nblk; ++b) {
-      s0 += part_p[(size_t)b * E + e];
+    for (; b < nblk; b += kColWaves) {
+      s[0] += part_p[(size_t)b * E + e];
       c += part_c[(size_t)b * E + e];
     }
-    const double s = (s0 + s1) + (s2 + s3);
-    if (counts) counts[e] = c;
-    if (prob_mean) prob_mean[e] = T > 0 ? (float)(s / (double)T) : 0.f;
-    tot += (double)c * s;
   }
-  red[threadIdx.x] = tot;
+  rs[wave][lane] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  rc[wave][lane] = c;
   __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
+  if (wave == 0) {
+    double tot = rs[0][lane];
+    int ct = rc[0][lane];
+#pragma unroll
+    for (int w = 1; w < kColWaves; ++w) {
+      tot += rs[w][lane];
+      ct += rc[w][lane];
+    }
+    double term = 0.0;
+    if (e < E) {
+      if (counts) counts[e] = ct;
+      if (prob_mean) prob_mean[e] = T > 0 ? (float)(tot / (double)T) : 0.f;
+      term = (double)ct * tot;
+    }
+    // fixed-order fold of the 64 lane terms (lane 0's result is used)
+    for (int m = 32; m >= 1; m >>= 1) term += __shfl_down(term, m);
+    if (lane == 0) chunk_loss[blockIdx.x] = term;
   }
-  if (threadIdx.x == 0 && loss) loss[0] = T > 0 ? (float)((double)E * red[0] / ((double)T * (double)T)) : 0.f;
 }
 
-template <int NV>
+__global__ void stats_loss_kernel(int T, int E, int nchunk, const double* __restrict__ chunk_loss,
+                                  float* __restrict__ loss) {
+  if (threadIdx.x != 0) return;
+  double tot = 0.0;
+  for (int c = 0; c < nchunk; ++c) tot += chunk_loss[c];
+  loss[0] = T > 0 ? (float)((double)E * tot / ((double)T * (double)T)) : 0.f;
+}
+
+__global__ void stats_empty_kernel(int E, int32_t* __restrict__ counts, float* __restrict__ prob_mean,
+                                   float* __restrict__ loss) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    if (counts) counts[e] = 0;
+    if (prob_mean) prob_mean[e] = 0.f;
+  }
+  if (threadIdx.x == 0 && loss) loss[0] = 0.f;
+}
+
+template <int G, int NV, int U>
 void launch_partial(int nblk, int T, int E, int k, const float* logits, const float* bias, const int32_t* ids,
                     double* part_p, int32_t* part_c, hipStream_t s) {
-  stats_partial_kernel<NV><<<nblk, 64 * kStatsWaves, 0, s>>>(T, E, k, logits, bias, ids, part_p, part_c);
+  stats_partial_kernel<G, NV, U><<<nblk, 256, 0, s>>>(T, E, k, logits, bias, ids, part_p, part_c);
+}
+
+inline int stats_group(int E, int k) { return (E <= 256 && k <= 16) ? 16 : 64; }
+
+struct StatsWs {
+  double* part_p;
+  int32_t* part_c;
+  double* chunk_loss;
+};
+
+inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+StatsWs stats_ws(void* ws, int nblk, int E) {
+  const size_t n = (size_t)nblk * E;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  StatsWs w;
+  w.part_p = reinterpret_cast<double*>(p);
+  w.part_c = reinterpret_cast<int32_t*>(p + al256(n * 8));
+  w.chunk_loss = reinterpret_cast<double*>(p + al256(n * 8) + al256(n * 4));
+  return w;
 }
 
 }  // namespace
@@ -139,37 +221,58 @@ void launch_partial(int nblk, int T, int E, int k, const float* logits, const fl
 int router_stats_blocks(int T, int E) {
   if (T <= 0 || E <= 0) return 0;
   const int cap = std::max(1, std::min(kStatsMaxBlocks, kStatsMaxPartials / E));
-  return std::min(cap, (T + kStatsMinTokensPerBlock - 1) / kStatsMinTokensPerBlock);
+  // two tokens per group at least (a 64-lane group when E > 256): fewer
+  // partial rows than that would cost more to add up than they save
+  const int per_block = 2 * (E <= 256 ? 16 : 4);
+  return std::min(cap, (T + per_block - 1) / per_block);
 }
 
 size_t router_stats_ws_bytes(int T, int E) {
-  const size_t n = (size_t)router_stats_blocks(T, E) * (size_t)std::max(E, 0);
-  return ((n * 8 + 255) & ~(size_t)255) + ((n * 4 + 255) & ~(size_t)255);
+  const int nblk = router_stats_blocks(T, E);
+  if (nblk == 0) return 0;  // an empty batch needs no workspace
+  const size_t n = (size_t)nblk * (size_t)E;
+  return al256(n * 8) + al256(n * 4) + al256(16 * 8);
 }
 
 hipError_t launch_router_stats(int T, int E, int k, const float* logits, const float* bias, const int32_t* ids,
                                int32_t* counts, float* prob_mean, float* loss, void* ws, hipStream_t s) {
   const int nblk = router_stats_blocks(T, E);
-  const size_t n = (size_t)nblk * E;
-  double* part_p = static_cast<double*>(ws);
-  int32_t* part_c = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + ((n * 8 + 255) & ~(size_t)255));
-  if (nblk > 0) {
-    const int nv = (E + 63) / 64;
-    if (nv <= 1)
-      launch_partial<1>(nblk, T, E, k, logits, bias, ids, part_p, part_c, s);
-    else if (nv <= 2)
-      launch_partial<2>(nblk, T, E, k, logits, bias, ids, part_p, part_c, s);
-    else if (nv <= 4)
-      launch_partial<4>(nblk, T, E, k, logits, bias, ids, part_p, part_c, s);
-    else if (nv <= 8)
-      launch_partial<8>(nblk, T, E, k, logits, bias, ids, part_p, part_c, s);
-    else
-      launch_partial<16>(nblk, T, E, k, logits, bias, ids, part_p, part_c, s);
+  if (nblk == 0) {
+    stats_empty_kernel<<<1, 256, 0, s>>>(E, counts, prob_mean, loss);
+    return hipGetLastError();
+  }
+  const StatsWs w = stats_ws(ws, nblk, E);
+  {
+    const int G = stats_group(E, k);
+    const int nv = (E + G - 1) / G;
+#define MOE_STATS(Gv, NVv, Uv) launch_partial<Gv, NVv, Uv>(nblk, T, E, k, logits, bias, ids, w.part_p, w.part_c, s)
+    if (G == 16) {
+      if (nv <= 1) MOE_STATS(16, 1, 4);
+      else if (nv <= 2) MOE_STATS(16, 2, 4);
+      else if (nv <= 4) MOE_STATS(16, 4, 2);
+      else if (nv <= 8) MOE_STATS(16, 8, 2);
+      else MOE_STATS(16, 16, 2);
+    } else {
+      if (nv <= 1) MOE_STATS(64, 1, 4);
+      else if (nv <= 2) MOE_STATS(64, 2, 4);
+      else if (nv <= 4) MOE_STATS(64, 4, 2);
+      else if (nv <= 8) MOE_STATS(64, 8, 2);
+      else MOE_STATS(64, 16, 2);
+    }
+#undef MOE_STATS
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  stats_final_kernel<<<1, 1024, 0, s>>>(T, E, nblk, part_p, part_c, counts, prob_mean, loss);
-  return hipGetLastError();
+  const int nchunk = (E + 63) / 64;  // E <= 1024: at most 16
+  stats_column_kernel<<<nchunk, 64 * kColWaves, 0, s>>>(T, E, nblk, w.part_p, w.part_c, counts, prob_mean,
+                                                        w.chunk_loss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (loss) {
+    stats_loss_kernel<<<1, 64, 0, s>>>(T, E, nchunk, w.chunk_loss, loss);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace moe
