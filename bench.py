@@ -198,6 +198,35 @@ def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=10)
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
+def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
+    """Sender side of expert parallelism on this batch's routing (outside the
+    timed step): all pairs grouped by owner (round-robin placement; the
+    workload's owners, else 8 owners, one node) and their rows gathered into
+    the send buffer.  Algorithmic bytes: each pair's row read and written,
+    plus ids, sorted_pair and pair_pos."""
+    n = cfg.owners if cfg.owners > 1 else 8
+    if cfg.E % n:
+        return None
+    ids = tr["topk_ids"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    moe.dispatch_owners(ids, cfg.E, n, "round_robin", x=x)
+    for e0, e1 in ev:
+        if not args.warm_cache:
+            flush.fill_(1)
+        e0.record()
+        moe.dispatch_owners(ids, cfg.E, n, "round_robin", x=x)
+        e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    P = cfg.T * cfg.k
+    eb = 4 if cfg.dtype == "f32" else 2
+    nbytes = 2 * P * cfg.d * eb + 3 * P * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "owner-grouped dispatch (grouping by owner + row gather)", "owners": n,
+            "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
+            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -300,6 +329,7 @@ def main(argv=None):
                  "algorithmic": {"bytes": work[dom]["bytes"], "flops": work[dom]["flops"]}})
     layer_roof = roofline_entry(work["layer"], ms, peak)
     by_products = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
+    dispatch = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
 
     rec = {
         "metric": METRIC,
@@ -325,6 +355,7 @@ def main(argv=None):
         "step_ms": seg_ms,
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / args.steps, 4),
         "router_stats": by_products,
+        "owner_dispatch": dispatch,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -12,5 +12,5 @@ passages each function follows.
 from .moe_oracle import (  # noqa: F401
     router_logits, select_topk, gates, route, router_stats, placement, owner_dispatch, permute, silu, gelu_erf, gated_ffn,
     quantize_int4, dequantize_int4, pack_int4, unpack_int4, round_to_dtype,
-    moe_layer, LayerWeights, combine,
+    moe_layer, LayerWeights, combine, act_grad, gated_ffn_bwd, moe_layer_bwd,
 )

@@ -26,6 +26,9 @@ What the layer computes, and where it is stated:
   README, feature list and data-flow figure: deterministic placement of the
   expert pool across stationary owners, and a dispatcher that groups the
   routed activations by expert owner.
+* Backward pass.  The trainers among the pages (MoEEvolve, kieve-moe,
+  moe_stream.py) differentiate the layer; the gradients here are the chain
+  rule of the forward definition, with the selection held fixed.
 * Router by-products.  moe_stream.py ``MoEFFN.forward``: per-expert counts of
   the tokens that chose each expert, the mean softmax probability per expert,
   and the batch-local balance loss built from both.
@@ -305,6 +308,115 @@ def gated_ffn(a, wg, wu, wd, act: str) -> np.ndarray:
     u = a @ np.asarray(wu, np.float64).T
     z = _ACTS[act](g) * u
     return z @ np.asarray(wd, np.float64).T
+
+
+def act_grad(g, act: str) -> np.ndarray:
+    """Derivative of the gate activation: SiLU' = s (1 + g (1 - s)) with s the
+    logistic sigmoid; GELU' = Phi(g) + g phi(g) (standard normal cdf and pdf)."""
+    g = np.asarray(g, np.float64)
+    if act == "swiglu":
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-g))
+        return sg * (1.0 + g * (1.0 - sg))
+    if act == "geglu":
+        return 0.5 * (1.0 + _erf(g / np.sqrt(2.0))) + g * np.exp(-0.5 * g * g) / np.sqrt(2.0 * np.pi)
+    raise ValueError(act)
+
+
+def gated_ffn_bwd(a, wg, wu, wd, act: str, dy):
+    """Chain rule through ``y = Wd (act(Wg a) * (Wu a))`` for rows ``a`` with
+    upstream ``dy``: ``dz = dy Wd``, ``dWd = dy^T z``, ``dg = dz * u * act'(g)``,
+    ``du = dz * act(g)``, ``da = dg Wg + du Wu``, ``dWg = dg^T a``,
+    ``dWu = du^T a``.  Returns ``(da, dWg, dWu, dWd)``."""
+    a = np.asarray(a, np.float64)
+    wg, wu, wd = (np.asarray(m, np.float64) for m in (wg, wu, wd))
+    dy = np.asarray(dy, np.float64)
+    g = a @ wg.T
+    u = a @ wu.T
+    ag = _ACTS[act](g)
+    z = ag * u
+    dz = dy @ wd
+    dg = dz * u * act_grad(g, act)
+    du = dz * ag
+    return dg @ wg + du @ wu, dg.T @ a, du.T @ a, dy.T @ z
+
+
+def moe_layer_bwd(x, weights: LayerWeights, k: int, renorm: bool, act: str, dout, *,
+                  w_router=None, logits=None, bias=None, expert_map=None, capacity: int = 0,
+                  shared: Optional[Sequence] = None, balance: float = 0.0):
+    """Gradients of the layer forward (float64) for an upstream gradient ``dout``
+    of its output, plus ``balance`` times the gradient of the batch balance
+    loss (the trainers of moe_stream.py, MoEEvolve and kieve-moe train the
+    layer; moe_stream.py ``MoEFFN.forward`` returns the balance loss next to the
+    output and the model adds it with a small coefficient).
+
+    The selection (top-k ids, capacity drops) and the expert counts of the
+    balance loss are piecewise constant and carry no gradient.  Per kept pair p
+    of token t, slot j, expert e: ``dw[t, j] = <dout[t], y_p>`` and the expert
+    receives ``dy_p = w[t, j] dout[t]``.  Gates: with ``renorm``,
+    ``w_j = pi_j / S`` over the k selected, so ``dpi_i = dw_i / S -
+    sum_j dw_j pi_j / S^2``; without, ``dpi_i = dw_i``.  Balance loss
+    ``E / T^2 sum_e count_e sum_t pi[t, e]``: ``dpi[t, e] += balance * E *
+    count_e / T^2``.  Softmax: ``dL = pi * (dpi - <dpi, pi>)``.  Router:
+    ``dx += dL Wr``, ``dWr = dL^T x``, ``dbias = sum_t dL``; with given logits
+    ``dlogits = dL``.  Returns a dict of the gradients (weights of local
+    experts only; None where the input does not exist).
+    """
+    x = np.asarray(x, np.float64)
+    dout = np.asarray(dout, np.float64)
+    T, d = x.shape
+    L, ids, w = route(k, renorm, x=x, w_router=w_router, bias=bias, logits=logits)
+    E = L.shape[1]
+    E_loc = weights.E_loc
+    offsets, sorted_pair, pair_pos = permute(ids, expert_map, E_loc, capacity)
+    dx = np.zeros((T, d))
+    dw = np.zeros((T, k))
+    wg0, wu0, wd0 = weights.expert(0)
+    dWg = np.zeros((E_loc,) + wg0.shape)
+    dWu = np.zeros((E_loc,) + wu0.shape)
+    dWd = np.zeros((E_loc,) + wd0.shape)
+    for e in range(E_loc):
+        rows = sorted_pair[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        t, j = rows // k, rows % k
+        wg, wu, wd = weights.expert(e)
+        y = gated_ffn(x[t], wg, wu, wd, act)
+        dw[t, j] = np.sum(dout[t] * y, axis=1)
+        da, dWg[e], dWu[e], dWd[e] = gated_ffn_bwd(x[t], wg, wu, wd, act, w[t, j][:, None] * dout[t])
+        np.add.at(dx, t, da)
+    dshared = None
+    if shared is not None:
+        da, gsg, gsu, gsd = gated_ffn_bwd(x, shared[0], shared[1], shared[2], act, dout)
+        dx += da
+        dshared = (gsg, gsu, gsd)
+    m = L.max(axis=1, keepdims=True)
+    ex = np.exp(L - m)
+    pi = ex / ex.sum(axis=1, keepdims=True)
+    dpi = np.zeros((T, E))
+    rows = np.arange(T)[:, None]
+    if renorm:
+        psel = np.take_along_axis(pi, ids, axis=1)
+        S = psel.sum(axis=1, keepdims=True)
+        dsel = dw / S - np.sum(dw * psel, axis=1, keepdims=True) / S ** 2
+    else:
+        dsel = dw
+    np.add.at(dpi, (np.broadcast_to(rows, ids.shape), ids), dsel)
+    if balance:
+        count = router_stats(L, ids)[0]
+        dpi += balance * E * count[None, :] / float(T * T)
+    dL = pi * (dpi - np.sum(dpi * pi, axis=1, keepdims=True))
+    out = {"dx": dx, "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd, "dshared": dshared,
+           "dw_router": None, "dlogits": None, "dbias": None, "dgates": dw, "dL": dL}
+    if logits is None:
+        Wr = np.asarray(w_router, np.float64)
+        out["dx"] = dx + dL @ Wr
+        out["dw_router"] = dL.T @ x
+    else:
+        out["dlogits"] = dL
+    if bias is not None:
+        out["dbias"] = dL.sum(axis=0)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -516,6 +516,133 @@ def test_vectorised_oracle_equals_pure_python_loops(renorm, act, cap, sh):
     np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- backward
+def _bwd_case(seed, T=7, d=8, E=5, k=2, h=6, shared_h=0, given_logits=False, biased=False):
+    x, wr, W, shared = _rand_layer(T, d, E, k, h, shared_h=shared_h, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    logits = rng.standard_normal((T, E)) * 1.5 if given_logits else None
+    bias = rng.standard_normal(E) * 0.3 if biased else None
+    R = rng.standard_normal((T, d))
+    return x, (None if given_logits else wr), W, shared, logits, bias, R
+
+
+def _objective(x, wr, W, shared, logits, bias, R, k, renorm, act, cap, balance, ids_ref):
+    r = orc.moe_layer(x, W, k, renorm, act, w_router=wr, logits=logits, bias=bias, capacity=cap, shared=shared)
+    assert np.array_equal(r["ids"], ids_ref), "selection moved under the perturbation"
+    f = float(np.sum(r["out"] * R))
+    if balance:
+        f += balance * orc.router_stats(r["L"], r["ids"])[2]
+    return f
+
+
+@pytest.mark.parametrize("act,renorm,cap,sh,given,balance", [
+    ("swiglu", True, 0, 0, False, 0.0), ("geglu", False, 0, 4, False, 0.0), ("swiglu", True, 2, 4, False, 0.3),
+    ("geglu", True, 0, 0, True, 0.5), ("swiglu", False, 3, 0, True, 0.0)])
+def test_backward_central_differences(act, renorm, cap, sh, given, balance):
+    """Every gradient output against central differences of
+    F = sum(out * R) + balance * balance_loss (step 1e-5, float64)."""
+    x, wr, W, shared, logits, bias, R = _bwd_case(11, shared_h=sh, given_logits=given, biased=True)
+    k = 2
+    g = orc.moe_layer_bwd(x, W, k, renorm, act, R, w_router=wr, logits=logits, bias=bias, capacity=cap,
+                          shared=shared, balance=balance)
+    ids_ref = orc.moe_layer(x, W, k, renorm, act, w_router=wr, logits=logits, bias=bias, capacity=cap)["ids"]
+    eps = 1e-5
+    rng = np.random.default_rng(0)
+
+    def fd(arr, idx, rebuild):
+        old = arr[idx]
+        arr[idx] = old + eps
+        fp = _objective(*rebuild(), R, k, renorm, act, cap, balance, ids_ref)
+        arr[idx] = old - eps
+        fm = _objective(*rebuild(), R, k, renorm, act, cap, balance, ids_ref)
+        arr[idx] = old
+        return (fp - fm) / (2 * eps)
+
+    def rebuild():
+        return x, wr, W, shared, logits, bias
+
+    checks = [(x, g["dx"])]
+    checks += [(W.wg, g["dw_gate"]), (W.wu, g["dw_up"]), (W.wd, g["dw_down"])]
+    if shared is not None:
+        checks += list(zip(shared, g["dshared"]))
+    if wr is not None:
+        checks.append((wr, g["dw_router"]))
+    if logits is not None:
+        checks.append((logits, g["dlogits"]))
+    checks.append((bias, g["dbias"]))
+    for arr, grad in checks:
+        assert grad.shape == arr.shape
+        flat = [tuple(int(v) for v in np.unravel_index(i, arr.shape))
+                for i in rng.choice(arr.size, size=min(arr.size, 12), replace=False)]
+        for idx in flat:
+            num = fd(arr, idx, rebuild)
+            assert abs(num - grad[idx]) <= 1e-6 * max(1.0, abs(num)), (idx, num, grad[idx])
+
+
+@pytest.mark.parametrize("act,renorm,cap", [("swiglu", True, 0), ("geglu", False, 2), ("geglu", True, 3)])
+def test_backward_matches_torch_autograd(act, renorm, cap):
+    """An independent forward in torch float64 (the oracle's selection and
+    capacity mask held fixed as constants) differentiated by autograd."""
+    T, d, E, k, h, sh = 9, 8, 6, 3, 5, 4
+    x, wr, W, shared, _, bias, R = _bwd_case(5, T, d, E, k, h, shared_h=sh, biased=True)
+    fwd = orc.moe_layer(x, W, k, renorm, act, w_router=wr, bias=bias, capacity=cap, shared=shared)
+    ids = torch.from_numpy(fwd["ids"])
+    kept = torch.from_numpy((fwd["pair_pos"].reshape(T, k) >= 0).astype(np.float64))
+    tt = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+          for n, v in [("x", x), ("wr", wr), ("b", bias), ("wg", W.wg), ("wu", W.wu), ("wd", W.wd),
+                       ("sg", shared[0]), ("su", shared[1]), ("sd", shared[2])]}
+    a = torch.nn.functional.silu if act == "swiglu" else torch.nn.functional.gelu
+    L = tt["x"] @ tt["wr"].T + tt["b"]
+    pi = torch.softmax(L, dim=-1)
+    psel = torch.gather(pi, 1, ids)
+    wgt = psel / psel.sum(-1, keepdim=True) if renorm else psel
+    out = torch.zeros(T, d, dtype=torch.float64)
+    for j in range(k):
+        for t in range(T):
+            e = int(ids[t, j])
+            xt = tt["x"][t]
+            y = tt["wd"][e] @ (a(tt["wg"][e] @ xt) * (tt["wu"][e] @ xt))
+            out[t] = out[t] + kept[t, j] * wgt[t, j] * y
+    out = out + (a(tt["x"] @ tt["sg"].T) * (tt["x"] @ tt["su"].T)) @ tt["sd"].T
+    (out * torch.from_numpy(R)).sum().backward()
+    g = orc.moe_layer_bwd(x, W, k, renorm, act, R, w_router=wr, bias=bias, capacity=cap, shared=shared)
+    pairs = [("x", g["dx"]), ("wr", g["dw_router"]), ("b", g["dbias"]), ("wg", g["dw_gate"]),
+             ("wu", g["dw_up"]), ("wd", g["dw_down"]), ("sg", g["dshared"][0]), ("su", g["dshared"][1]),
+             ("sd", g["dshared"][2])]
+    for n, ours in pairs:
+        np.testing.assert_allclose(ours, tt[n].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=n)
+
+
+def test_backward_special_cases():
+    """One expert (k = E = 1): the softmax is constant 1, so the router gets no
+    gradient and the rest is the dense gated MLP's; the activation derivatives
+    at 0 are 1/2; the sum of the owners' gradients is the full layer's."""
+    x, wr, W, _, _, _, R = _bwd_case(3, T=6, d=8, E=1, k=1, h=4)
+    g = orc.moe_layer_bwd(x, W, 1, True, "swiglu", R, w_router=wr)
+    assert np.abs(g["dw_router"]).max() == 0.0
+    da, dwg, dwu, dwd = orc.gated_ffn_bwd(x, W.wg[0], W.wu[0], W.wd[0], "swiglu", R)
+    np.testing.assert_allclose(g["dx"], da, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(g["dw_down"][0], dwd, rtol=1e-13, atol=1e-14)
+    assert orc.act_grad(0.0, "swiglu") == 0.5 and orc.act_grad(0.0, "geglu") == 0.5
+    # the sum over owner shares of their gradients is the whole layer's gradient
+    T, d, E, k, h, owners = 10, 8, 8, 3, 4, 4
+    x, wr, W, _, _, _, R = _bwd_case(9, T, d, E, k, h)
+    full = orc.moe_layer_bwd(x, W, k, True, "geglu", R, w_router=wr)
+    dx = np.zeros_like(full["dx"])
+    dwr = np.zeros_like(full["dw_router"])
+    for o in range(owners):
+        mine = np.arange(o, E, owners)
+        emap = np.full(E, -1)
+        emap[mine] = np.arange(mine.size)
+        Wo = orc.LayerWeights(wg=W.wg[mine], wu=W.wu[mine], wd=W.wd[mine])
+        go = orc.moe_layer_bwd(x, Wo, k, True, "geglu", R, w_router=wr, expert_map=emap)
+        dx += go["dx"]
+        dwr += go["dw_router"]
+        np.testing.assert_allclose(go["dw_gate"], full["dw_gate"][mine], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dx, full["dx"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dwr, full["dw_router"], rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- INT4
 def test_int4_worked_example():
     c = int4_case()
