@@ -12,6 +12,7 @@
  *                   signed INT4 with fp16 group scales)
  *   moe_combine     weighted top-k combine plus the optional shared expert
  *   moe_layer_fwd   all of the above, fused where it pays, on one stream
+ *   moe_layer_bwd   gradients of the layer (bf16 and fp32 weights)
  *
  * Sources of the operation (web pages; section named where the page has one):
  *   "Sharding d'experts" (Kvasir wiki), section "Deux roles": the backbone /
@@ -323,6 +324,52 @@ size_t moe_layer_workspace_bytes(const struct moe_layer_desc* L);
 int moe_layer_fwd(const struct moe_layer_desc* L, const void* x, const float* logits_in,
                   void* out, const struct moe_layer_trace* trace,
                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_bwd - gradients of moe_layer_fwd (the trainers among the sources,
+ * MoEEvolve, kieve-moe and moe_stream.py, train this layer; moe_stream.py
+ * returns a batch balance loss next to the output).  The routing, the
+ * grouping and the gate/up products are recomputed from x as the forward
+ * computes them (bit-identical), so only x, the weights and dout are needed.
+ * Selection and capacity drops are held fixed (they carry no gradient).
+ *
+ *   loss = <dout, out> + balance * E * sum_e (count[e] / T) * prob_mean[e]
+ *   per kept pair p (token t, slot j, expert e, gate w): the expert's output
+ *   gradient is w * dout[t]; d(loss)/d(w) = <dout[t], y_p>; the gates pass it to
+ *   the softmax as in moe_route (renorm: w_j = pi_j / sum_sel pi), the softmax
+ *   to L, and L = x Wr^T + bias to x, Wr and the bias.
+ *
+ *   L, x, logits_in  as moe_layer_fwd; w_dtype MOE_I4G128 is not supported
+ *   dout       [T, d] act_dtype, upstream gradient of the output
+ *   balance    coefficient of the balance loss (0 = none); with expert_map it
+ *              belongs to one share only, the loss being per layer
+ *   g          output buffers (device, fp32 unless stated; NULL = not wanted):
+ *     dx        [T, d] act_dtype, required
+ *     dlogits   [T, E]: d(loss)/d(logits_in) (only with logits_in)
+ *     dw_router [E, d] (needs w_router);  dbias [E] (needs expert_bias)
+ *     dw_gate, dw_up [E_loc, h, d], dw_down [E_loc, d, h]  (gate and up both or neither)
+ *     dws_gate, dws_up [h_shared, d], dws_down [d, h_shared] (gate and up both or neither)
+ *     dgates    [T, k]: d(loss)/d(topk_w), 0 for pairs not kept
+ *   ws         at least moe_layer_bwd_workspace_bytes(L)
+ * Gradients are accumulated in fp32 in a fixed order: repeated calls give
+ * identical bits.  Expert weight gradients of experts without rows are zero.
+ */
+struct moe_layer_grads {
+  void* dx;
+  float* dlogits;
+  float* dw_router;
+  float* dbias;
+  float* dw_gate;
+  float* dw_up;
+  float* dw_down;
+  float* dws_gate;
+  float* dws_up;
+  float* dws_down;
+  float* dgates;
+};
+size_t moe_layer_bwd_workspace_bytes(const struct moe_layer_desc* L);
+int moe_layer_bwd(const struct moe_layer_desc* L, const void* x, const float* logits_in, const void* dout,
+                  float balance, const struct moe_layer_grads* g, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_quantize_int4 - weight preparation for MOE_I4G128 (ExpertMesh: bit-exact

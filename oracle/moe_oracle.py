@@ -343,7 +343,7 @@ def gated_ffn_bwd(a, wg, wu, wd, act: str, dy):
 
 def moe_layer_bwd(x, weights: LayerWeights, k: int, renorm: bool, act: str, dout, *,
                   w_router=None, logits=None, bias=None, expert_map=None, capacity: int = 0,
-                  shared: Optional[Sequence] = None, balance: float = 0.0):
+                  shared: Optional[Sequence] = None, balance: float = 0.0, ids=None):
     """Gradients of the layer forward (float64) for an upstream gradient ``dout``
     of its output, plus ``balance`` times the gradient of the batch balance
     loss (the trainers of moe_stream.py, MoEEvolve and kieve-moe train the
@@ -359,13 +359,18 @@ def moe_layer_bwd(x, weights: LayerWeights, k: int, renorm: bool, act: str, dout
     ``E / T^2 sum_e count_e sum_t pi[t, e]``: ``dpi[t, e] += balance * E *
     count_e / T^2``.  Softmax: ``dL = pi * (dpi - <dpi, pi>)``.  Router:
     ``dx += dL Wr``, ``dWr = dL^T x``, ``dbias = sum_t dL``; with given logits
-    ``dlogits = dL``.  Returns a dict of the gradients (weights of local
-    experts only; None where the input does not exist).
+    ``dlogits = dL``.  ``ids`` overrides the selection as in ``moe_layer``.
+    Returns a dict of the gradients (weights of local experts only; None
+    where the input does not exist).
     """
     x = np.asarray(x, np.float64)
     dout = np.asarray(dout, np.float64)
     T, d = x.shape
-    L, ids, w = route(k, renorm, x=x, w_router=w_router, bias=bias, logits=logits)
+    L, ids_o, w = route(k, renorm, x=x, w_router=w_router, bias=bias, logits=logits)
+    if ids is not None:
+        ids_o = np.asarray(ids, np.int64)
+        w = gates(L, ids_o, renorm)
+    ids = ids_o
     E = L.shape[1]
     E_loc = weights.E_loc
     offsets, sorted_pair, pair_pos = permute(ids, expert_map, E_loc, capacity)

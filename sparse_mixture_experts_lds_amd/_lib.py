@@ -14,7 +14,7 @@ EXPORTS = [
     "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
     "moe_permute", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
-    "moe_quantize_int4", "moe_strerror", "moe_last_error",
+    "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_quantize_int4", "moe_strerror", "moe_last_error",
 ]
 
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -42,6 +42,11 @@ class LayerTrace(ctypes.Structure):
     _fields_ = [("logits", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("expert_offsets", _vp),
                 ("pair_pos", _vp), ("events", _vp * MOE_NUM_EVENTS),
                 ("expert_counts", _vp), ("prob_mean", _vp), ("balance_loss", _vp)]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("dx", "dlogits", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down",
+                                   "dws_gate", "dws_up", "dws_down", "dgates")]
 
 
 _LIB = None
@@ -76,6 +81,9 @@ def load(path: str = LIB_PATH):
         "moe_layer_workspace_bytes": (_c_size, [ctypes.POINTER(LayerDesc)]),
         "moe_layer_fwd": (_c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, ctypes.POINTER(LayerTrace),
                                    _vp, _c_size, _vp]),
+        "moe_layer_bwd_workspace_bytes": (_c_size, [ctypes.POINTER(LayerDesc)]),
+        "moe_layer_bwd": (_c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, ctypes.c_float,
+                                   ctypes.POINTER(LayerGrads), _vp, _c_size, _vp]),
         "moe_quantize_int4": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp]),
         "moe_strerror": (ctypes.c_char_p, [_c_int]),
         "moe_last_error": (ctypes.c_char_p, []),

@@ -8,7 +8,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MOE_BF16, MOE_F32, MOE_GEGLU, MOE_I4G128, MOE_SWIGLU, LayerDesc, LayerTrace,
+from ._lib import (MOE_BF16, MOE_F32, MOE_GEGLU, MOE_I4G128, MOE_SWIGLU, LayerDesc, LayerGrads, LayerTrace,
                    check, load)
 
 _ACT = {"swiglu": MOE_SWIGLU, "geglu": MOE_GEGLU}
@@ -286,4 +286,53 @@ def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Ten
                                              _stream(dev)))
     if trace:
         return out, tdict
+    return out
+
+
+def layer_bwd_workspace_bytes(weights: LayerWeights, T: int, d: int, act_dtype: int) -> int:
+    L = weights.desc(T, d, act_dtype)
+    return load().moe_layer_bwd_workspace_bytes(ctypes.byref(L))
+
+
+def layer_bwd(x: torch.Tensor, weights: LayerWeights, dout: torch.Tensor, logits: Optional[torch.Tensor] = None,
+              balance: float = 0.0, ws: Optional[torch.Tensor] = None, grads: Optional[dict] = None):
+    """Gradients of layer_fwd for the upstream gradient dout (plus balance times the
+    balance loss).  Returns a dict: dx, dgates, the weight gradients that exist
+    (dw_gate, dw_up, dw_down; dws_* with a shared expert; dw_router with a router;
+    dbias with a bias) and dlogits when logits are given.  ``grads`` may hold
+    preallocated outputs (a missing key is allocated)."""
+    lib = load()
+    T, d = x.shape
+    dev = x.device
+    dt = _dt(x)
+    L = weights.desc(T, d, dt)
+    nb = lib.moe_layer_bwd_workspace_bytes(ctypes.byref(L))
+    if nb == 0:
+        raise _lib.MoEError("moe_layer_bwd_workspace_bytes", _lib.MOE_EINVAL)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb, dev)
+    E, k = weights.E, weights.k
+    E_loc, h = weights.wg.shape[0], weights.wg.shape[1]
+    f32 = dict(dtype=torch.float32, device=dev)
+    shapes = {"dgates": (T, k), "dw_gate": (E_loc, h, d), "dw_up": (E_loc, h, d), "dw_down": (E_loc, d, h)}
+    if weights.wsg is not None:
+        hs = weights.wsg.shape[0]
+        shapes.update(dws_gate=(hs, d), dws_up=(hs, d), dws_down=(d, hs))
+    if weights.w_router is not None and logits is None:
+        shapes["dw_router"] = (E, d)
+    if weights.bias is not None:
+        shapes["dbias"] = (E,)
+    if logits is not None:
+        shapes["dlogits"] = (T, E)
+    out = dict(grads or {})
+    if "dx" not in out:
+        out["dx"] = torch.empty((T, d), dtype=x.dtype, device=dev)
+    for n, shp in shapes.items():
+        if n not in out:
+            out[n] = torch.empty(shp, **f32)
+    g = LayerGrads()
+    for n, t in out.items():
+        setattr(g, n, t.data_ptr())
+    check("moe_layer_bwd", lib.moe_layer_bwd(ctypes.byref(L), _p(x), _p(logits), _p(dout), float(balance),
+                                             ctypes.byref(g), _p(ws), nb, _stream(dev)))
     return out

@@ -4,8 +4,11 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 #include <string>
 
+#include "bwd.h"
 #include "moe_internal.h"
 
 using namespace moe;
@@ -259,6 +262,146 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->ys = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->d * 4 : 0);
   b->stats = c.take<void>(router_stats_ws_bytes(L->T, L->E));  // router by-product partials
   return c.used;
+}
+
+// ---------------------------------------------------------------- backward
+struct BwdBufs {
+  int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts, *mtile_rc, *cnt;
+  int4 *tiles, *tiles_rc;
+  float *tw, *Lraw, *Lw, *G, *U, *dZ, *dgate, *dXp, *Gs, *Us, *dZs, *dXs, *dL, *dXr, *part, *colpart;
+  void *dGU, *ZW, *dGUs, *ZWs, *dLc, *stats;
+};
+
+constexpr int kBwdBM = 64;  // grouped rows per tile of the backward GEMMs (and of the recompute)
+
+inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Row slices of a single-group weight gradient: enough workgroups to fill the
+// chip, at least 256 rows per slice.
+int tn_slices(int rows, int M, int N) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = (512 + tiles - 1) / tiles;
+  S = std::min(S, std::max(1, rows / 256));
+  return std::max(1, std::min(S, 64));
+}
+
+size_t carve_bwd(const moe_layer_desc* L, void* ws, BwdBufs* b) {
+  Carver c(ws);
+  const size_t T = L->T, P = T * L->k, E = L->E, d = L->d, h = L->h, hs = L->h_shared;
+  const size_t rows = (size_t)layer_rows_max(L);
+  const size_t eb = elt_bytes(L->act_dtype);
+  const size_t Epad = (size_t)round_up(L->E, 32);
+  const bool f32 = L->act_dtype == MOE_F32;
+  b->ids = c.take<int32_t>(P * 4);
+  b->tw = c.take<float>(P * 4);
+  b->Lraw = c.take<float>(L->w_router ? T * E * 4 : 0);
+  b->Lw = c.take<float>(T * E * 4);
+  b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
+  b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
+  b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, kBwdBM) * sizeof(int4));
+  b->mtile_rc = c.take<int32_t>(f32 ? (L->E_loc + 1) * 4 : 0);
+  b->tiles_rc = c.take<int4>(f32 ? (size_t)ffn_max_mtiles(L->E_loc, (int)rows, 32) * sizeof(int4) : 0);
+  b->sorted_pair = c.take<int32_t>(P * 4);
+  b->pair_pos = c.take<int32_t>(P * 4);
+  b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
+  b->G = c.take<float>(rows * h * 4);
+  b->U = c.take<float>(rows * h * 4);
+  b->dZ = c.take<float>(rows * h * 4);
+  b->dGU = c.take<void>(rows * 2 * h * eb);
+  b->ZW = c.take<void>(rows * h * eb);
+  b->dgate = c.take<float>(P * 4);
+  b->dXp = c.take<float>(rows * d * 4);
+  b->Gs = c.take<float>(T * hs * 4);
+  b->Us = c.take<float>(T * hs * 4);
+  b->dZs = c.take<float>(T * hs * 4);
+  b->dGUs = c.take<void>(T * 2 * hs * eb);
+  b->ZWs = c.take<void>(T * hs * eb);
+  b->dXs = c.take<float>(hs ? T * d * 4 : 0);
+  b->dL = c.take<float>(T * E * 4);
+  b->dLc = c.take<void>(T * Epad * eb);
+  b->dXr = c.take<float>(L->w_router ? T * d * 4 : 0);
+  b->cnt = c.take<int32_t>(E * 4);
+  b->stats = c.take<void>(router_stats_ws_bytes(L->T, L->E));
+  size_t part = 0;
+  if (L->w_router) part = std::max(part, (size_t)tn_slices(L->T, L->E, L->d) * E * d);
+  if (hs) {
+    part = std::max(part, (size_t)tn_slices(L->T, L->d, (int)hs) * d * hs);
+    part = std::max(part, (size_t)tn_slices(L->T, 2 * (int)hs, L->d) * 2 * hs * d);
+  }
+  b->part = c.take<float>(part * 4);
+  b->colpart = c.take<float>(colsum_ws_floats(L->T, L->E) * 4);
+  return c.used;
+}
+
+int check_bwd(const moe_layer_desc* L) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->w_dtype == MOE_I4G128) return MOE_EUNSUPPORTED;  // packed INT4 experts are not trained
+  if ((size_t)layer_rows_max(L) * 2 * L->h * 4 > 0xFFFFFFFFull) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// One single-group weight gradient C = A^T B over all T rows: row slices into
+// b->part, then their fixed-order sum (rows m >= M1 of the result to C2).
+int tn_single(bool bf, const void* A, int lda, const void* B, int ldb, int T, int M, int N, int M1, float* C1,
+              float* C2, int ldc, float* part, hipStream_t s) {
+  const int S = tn_slices(T, M, N);
+  bwdg::TnArgs t{};
+  t.A = A;
+  t.lda = lda;
+  t.a_div = 1;
+  t.B = B;
+  t.ldb = ldb;
+  t.b_div = 1;
+  t.rows = T;
+  t.slice = round_up((T + S - 1) / S, 32);
+  t.M = M;
+  t.N = N;
+  t.mtiles = (M + bwdg::kTnTile - 1) / bwdg::kTnTile;
+  const int nz = (T + t.slice - 1) / t.slice;
+  if (nz <= 1) {
+    t.C1 = C1;
+    t.C2 = C2;
+    t.M1 = M1;
+    t.ldc = ldc;
+    MOE_HIP(launch_bwd_tn(bf, t, 1, s));
+    return MOE_OK;
+  }
+  t.C1 = t.C2 = part;
+  t.M1 = M;
+  t.ldc = N;
+  t.c_stride = (long long)M * N;
+  MOE_HIP(launch_bwd_tn(bf, t, nz, s));
+  MOE_HIP(launch_sum_slices(nz, M, N, M1, part, C1, C2, ldc, s));
+  return MOE_OK;
+}
+
+// Gate/up pre-activations of one expert set, fp32 [rows, h] each.
+int recompute_gu(int wt, bool grouped, const void* x, int T, int k, const int32_t* sorted_pair,
+                 const int32_t* offsets, const int32_t* mtile, const int4* tiles, int E_loc, int rows, int d, int h,
+                 int BM, const void* wg, const void* wu, float* G, float* U, hipStream_t s) {
+  FfnGemmArgs g{};
+  g.A = x;
+  g.row_index = grouped ? sorted_pair : nullptr;
+  g.row_div = grouped ? k : 1;
+  g.offsets = grouped ? offsets : nullptr;
+  g.mtile_start = grouped ? mtile : nullptr;
+  g.tile_tab = grouped ? tiles : nullptr;
+  g.E_loc = grouped ? E_loc : 1;
+  g.rows_max = rows;
+  g.K = d;
+  g.N = h;
+  g.a_rows = T;
+  g.slot_div = 1;
+  g.out_f32 = 1;
+  const int NF = (wt == W_BF16 && h % 128 == 0) ? 2 : 1;
+  g.W0 = wg;
+  g.out = G;
+  MOE_HIP(launch_ffn_gemm(g, false, wt, false, BM, NF, s));
+  g.W0 = wu;
+  g.out = U;
+  MOE_HIP(launch_ffn_gemm(g, false, wt, false, BM, NF, s));
+  return MOE_OK;
 }
 
 }  // namespace
@@ -526,6 +669,217 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   MOE_HIP(mark(MOE_EV_SHARED));
   MOE_HIP(launch_combine(T, k, L->d, bf16, true, b.y, pair_pos, tw, shared_y, out, s));
   MOE_HIP(mark(MOE_EV_END));
+  return MOE_OK;
+}
+
+size_t moe_layer_bwd_workspace_bytes(const moe_layer_desc* L) {
+  if (check_bwd(L) != MOE_OK) return 0;
+  BwdBufs b;
+  return carve_bwd(L, nullptr, &b);
+}
+
+int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in, const void* dout, float balance,
+                  const moe_layer_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_bwd(L);
+  if (rc) return rc;
+  if (!logits_in && !L->w_router) return MOE_EINVAL;
+  if (!gr || !gr->dx) return MOE_EINVAL;
+  if (L->T > 0 && (!x || !dout)) return MOE_EINVAL;
+  if ((gr->dw_gate == nullptr) != (gr->dw_up == nullptr)) return MOE_EINVAL;
+  if ((gr->dws_gate == nullptr) != (gr->dws_up == nullptr)) return MOE_EINVAL;
+  if (gr->dw_router && !L->w_router) return MOE_EINVAL;
+  if (gr->dbias && !L->expert_bias) return MOE_EINVAL;
+  if (!(balance == balance)) return MOE_EINVAL;  // NaN
+  const size_t need = moe_layer_bwd_workspace_bytes(L);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (L->T == 0) return MOE_OK;
+  if (!ws) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+  BwdBufs b;
+  carve_bwd(L, ws, &b);
+  const bool bf = L->act_dtype == MOE_BF16;
+  const int wt = wtype_of(L->w_dtype);
+  const int T = L->T, k = L->k, E = L->E, E_loc = L->E_loc, d = L->d, h = L->h, hs = L->h_shared;
+  const int rows = layer_rows_max(L);
+  const int Epad = round_up(E, 32);
+  const int grid_m = ffn_max_mtiles(E_loc, rows, kBwdBM);
+
+  // 1. routing, as the forward: logits (GEMM or given) + bias, selection, grouping
+  const float* lsrc = logits_in;
+  if (!lsrc) {
+    MOE_HIP(launch_router_logits(T, d, E, bf, x, L->w_router, b.Lraw, s));
+    lsrc = b.Lraw;
+  }
+  MOE_HIP(launch_select(T, E, k, lsrc, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
+  MOE_HIP(launch_permute(T, k, E, b.ids, L->expert_map, E_loc, L->capacity, kBwdBM, b.offsets, b.mtile, b.tiles,
+                         b.sorted_pair, b.pair_pos, b.counts, s));
+  // the fp32 grouped GEMM of the forward takes at most 32-row tiles
+  const int BMrc = bf ? kBwdBM : 32;
+  if (!bf) MOE_HIP(launch_mtile_prefix(E_loc, 32, b.offsets, b.mtile_rc, b.tiles_rc, s));
+
+  // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients
+  if ((rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, bf ? b.mtile : b.mtile_rc,
+                         bf ? b.tiles : b.tiles_rc, E_loc, rows, d, h, BMrc, L->w_gate, L->w_up, b.G, b.U, s)))
+    return rc;
+  bwdg::NnArgs n{};
+  n.A = dout;
+  n.lda = d;
+  n.a_index = b.sorted_pair;
+  n.a_div = k;
+  n.B1 = L->w_down;
+  n.K1 = d;
+  n.ldb = h;
+  n.b_stride = (long long)d * h;
+  n.K_valid = d;
+  n.C = b.dZ;
+  n.ldc = h;
+  n.mtile_start = b.mtile;
+  n.tile_tab = b.tiles;
+  n.groups = E_loc;
+  n.rows = rows;
+  n.N = h;
+  n.K = d;
+  MOE_HIP(launch_bwd_nn(bf, n, kBwdBM, grid_m, s));
+  MOE_HIP(launch_gate_bwd(bf, L->act, rows, h, b.offsets + E_loc, b.G, b.U, b.dZ, b.sorted_pair, b.tw, b.dGU, b.ZW,
+                          b.dgate, s));
+  if (gr->dw_down) {
+    bwdg::TnArgs t{};
+    t.A = dout;
+    t.lda = d;
+    t.a_index = b.sorted_pair;
+    t.a_div = k;
+    t.B = b.ZW;
+    t.ldb = h;
+    t.b_div = 1;
+    t.offsets = b.offsets;
+    t.C1 = t.C2 = gr->dw_down;
+    t.M1 = d;
+    t.ldc = h;
+    t.c_stride = (long long)d * h;
+    t.M = d;
+    t.N = h;
+    t.mtiles = (d + bwdg::kTnTile - 1) / bwdg::kTnTile;
+    MOE_HIP(launch_bwd_tn(bf, t, E_loc, s));
+  }
+  if (gr->dw_gate) {
+    bwdg::TnArgs t{};
+    t.A = b.dGU;
+    t.lda = 2 * h;
+    t.a_div = 1;
+    t.B = x;
+    t.ldb = d;
+    t.b_index = b.sorted_pair;
+    t.b_div = k;
+    t.offsets = b.offsets;
+    t.C1 = gr->dw_gate;
+    t.C2 = gr->dw_up;
+    t.M1 = h;
+    t.ldc = d;
+    t.c_stride = (long long)h * d;
+    t.M = 2 * h;
+    t.N = d;
+    t.mtiles = (2 * h + bwdg::kTnTile - 1) / bwdg::kTnTile;
+    MOE_HIP(launch_bwd_tn(bf, t, E_loc, s));
+  }
+  n = bwdg::NnArgs{};
+  n.A = b.dGU;
+  n.lda = 2 * h;
+  n.a_div = 1;
+  n.B1 = L->w_gate;
+  n.B2 = L->w_up;
+  n.K1 = h;
+  n.ldb = d;
+  n.b_stride = (long long)h * d;
+  n.K_valid = 2 * h;
+  n.C = b.dXp;
+  n.ldc = d;
+  n.mtile_start = b.mtile;
+  n.tile_tab = b.tiles;
+  n.groups = E_loc;
+  n.rows = rows;
+  n.N = d;
+  n.K = 2 * h;
+  MOE_HIP(launch_bwd_nn(bf, n, kBwdBM, grid_m, s));
+
+  // 3. shared expert on every token (gate 1)
+  if (hs > 0) {
+    const int swt = wtype_of(L->act_dtype);
+    if ((rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMrc, L->ws_gate,
+                           L->ws_up, b.Gs, b.Us, s)))
+      return rc;
+    const int BMs = (bf && T >= 4096) ? 128 : 64;
+    const int gm = (T + BMs - 1) / BMs;
+    n = bwdg::NnArgs{};
+    n.A = dout;
+    n.lda = d;
+    n.a_div = 1;
+    n.B1 = L->ws_down;
+    n.K1 = d;
+    n.ldb = hs;
+    n.K_valid = d;
+    n.C = b.dZs;
+    n.ldc = hs;
+    n.rows = T;
+    n.N = hs;
+    n.K = d;
+    MOE_HIP(launch_bwd_nn(bf, n, BMs, gm, s));
+    MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs, nullptr,
+                            s));
+    if (gr->dws_down && (rc = tn_single(bf, dout, d, b.ZWs, hs, T, d, hs, d, gr->dws_down, gr->dws_down, hs, b.part,
+                                        s)))
+      return rc;
+    if (gr->dws_gate && (rc = tn_single(bf, b.dGUs, 2 * hs, x, d, T, 2 * hs, d, hs, gr->dws_gate, gr->dws_up, d,
+                                        b.part, s)))
+      return rc;
+    n = bwdg::NnArgs{};
+    n.A = b.dGUs;
+    n.lda = 2 * hs;
+    n.a_div = 1;
+    n.B1 = L->ws_gate;
+    n.B2 = L->ws_up;
+    n.K1 = hs;
+    n.ldb = d;
+    n.K_valid = 2 * hs;
+    n.C = b.dXs;
+    n.ldc = d;
+    n.rows = T;
+    n.N = d;
+    n.K = 2 * hs;
+    MOE_HIP(launch_bwd_nn(bf, n, BMs, gm, s));
+  }
+
+  // 4. gates, softmax and balance loss back to the logits; router GEMMs
+  if (balance != 0.f)
+    MOE_HIP(launch_router_stats(T, E, k, b.Lw, nullptr, b.ids, b.cnt, nullptr, nullptr, b.stats, s));
+  const float bal = (float)((double)balance * E / ((double)T * (double)T));
+  float* dLt = (logits_in && gr->dlogits) ? gr->dlogits : b.dL;
+  MOE_HIP(launch_router_bwd(bf, T, E, Epad, k, L->renorm, b.Lw, b.ids, b.pair_pos, b.dgate,
+                            balance != 0.f ? b.cnt : nullptr, bal, dLt, b.dLc, gr->dgates, s));
+  if (!logits_in) {
+    n = bwdg::NnArgs{};
+    n.A = b.dLc;
+    n.lda = Epad;
+    n.a_div = 1;
+    n.B1 = L->w_router;
+    n.K1 = Epad;
+    n.ldb = d;
+    n.K_valid = E;
+    n.C = b.dXr;
+    n.ldc = d;
+    n.rows = T;
+    n.N = d;
+    n.K = Epad;
+    const int BMr = (bf && T >= 4096) ? 128 : 64;
+    MOE_HIP(launch_bwd_nn(bf, n, BMr, (T + BMr - 1) / BMr, s));
+    if (gr->dw_router &&
+        (rc = tn_single(bf, b.dLc, Epad, x, d, T, E, d, E, gr->dw_router, gr->dw_router, d, b.part, s)))
+      return rc;
+  }
+  if (gr->dbias) MOE_HIP(launch_colsum(T, E, dLt, b.colpart, gr->dbias, s));
+
+  // 5. dx = routed pairs + shared expert + router
+  MOE_HIP(launch_dx_assemble(bf, T, k, d, b.dXp, b.pair_pos, hs > 0 ? b.dXs : nullptr, logits_in ? nullptr : b.dXr,
+                             gr->dx, s));
   return MOE_OK;
 }
 

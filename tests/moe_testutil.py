@@ -154,3 +154,87 @@ def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
     assert err <= TOL[cfg.w_dtype if cfg.w_dtype != "bf16" else "bf16"], \
         "relative error %.3g above tolerance (flipped %d)" % (err, flipped)
     return out, tr, err
+
+
+BF16_U = 2.0 ** -8  # unit roundoff of bf16: 8 significand bits, round to nearest even
+
+
+def bwd_error_bounds(inp, dout, ids, balance=0.0):
+    """First-order bounds on the error of the bf16 backward, element by element.
+
+    The bf16 path feeds its GEMMs bf16 operands: z (as the forward does), w*z,
+    dg, du and dL are rounded once (w*z twice) and all sums are in fp32.  A sum
+    of products whose operand carries a relative error of at most n U (U =
+    2^-8) is off by at most n U sum |a||b|, so each bound below is that
+    absolute-term sum, taken from float64 values; the gate gradients' errors
+    are carried through the gate normalisation and the softmax to the router
+    gradients.  Returns name -> bound array, for the gradients present.
+    """
+    cfg = inp.cfg
+    U = BF16_U
+    k = cfg.k
+    x = as_f64(inp.x)
+    dout = as_f64(dout)
+    W = oracle_weights(inp)
+    L = orc.route(k, cfg.renorm, x=x, w_router=as_f64(inp.w_router), bias=as_f64(inp.bias),
+                  logits=as_f64(inp.logits))[0]
+    ids = np.asarray(ids, np.int64)
+    w = orc.gates(L, ids, cfg.renorm)
+    offsets, sp, pos = orc.permute(ids, inp.expert_map, cfg.E_loc, inp.capacity)
+    act = {"swiglu": orc.silu, "geglu": orc.gelu_erf}[cfg.act]
+    T, E = L.shape
+    b = {"dw_gate": np.zeros((cfg.E_loc, cfg.h, cfg.d)), "dw_up": np.zeros((cfg.E_loc, cfg.h, cfg.d)),
+         "dw_down": np.zeros((cfg.E_loc, cfg.d, cfg.h)), "dgates": np.zeros((T, k))}
+    a_gate = np.zeros((T, k))  # sum_c |dz'_c| |z_c| per kept pair
+    for e in range(cfg.E_loc):
+        rows = sp[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        t, j = rows // k, rows % k
+        wg, wu, wd = W.expert(e)
+        a = x[t]
+        g, u = a @ wg.T, a @ wu.T
+        A = act(g)
+        z = A * u
+        dzp = dout[t] @ wd
+        ww = w[t, j][:, None]
+        dz = ww * dzp
+        dg = dz * u * orc.act_grad(g, cfg.act)
+        du = dz * A
+        a_gate[t, j] = np.sum(np.abs(dzp) * np.abs(z), axis=1)
+        b["dw_down"][e] = 2 * U * np.abs(dout[t]).T @ np.abs(ww * z)
+        b["dw_gate"][e] = U * np.abs(dg).T @ np.abs(a)
+        b["dw_up"][e] = U * np.abs(du).T @ np.abs(a)
+    b["dgates"] = U * a_gate
+    if inp.wsg is not None:
+        sg, su, sd = (as_f64(m) for m in (inp.wsg, inp.wsu, inp.wsd))
+        g, u = x @ sg.T, x @ su.T
+        A = act(g)
+        dz = dout @ sd
+        b["dws_down"] = 2 * U * np.abs(dout).T @ np.abs(A * u)
+        b["dws_gate"] = U * np.abs(dz * u * orc.act_grad(g, cfg.act)).T @ np.abs(x)
+        b["dws_up"] = U * np.abs(dz * A).T @ np.abs(x)
+    # router: gate errors through the normalisation and the softmax
+    m = L.max(axis=1, keepdims=True)
+    pi = np.exp(L - m)
+    pi /= pi.sum(axis=1, keepdims=True)
+    delta = b["dgates"] * (pos.reshape(T, k) >= 0)
+    psel = np.take_along_axis(pi, ids, axis=1)
+    if cfg.renorm:
+        S = psel.sum(axis=1, keepdims=True)
+        ddsel = delta / S + np.sum(delta * psel, axis=1, keepdims=True) / S ** 2
+    else:
+        ddsel = delta
+    ddpi = np.zeros((T, E))
+    np.add.at(ddpi, (np.broadcast_to(np.arange(T)[:, None], ids.shape), ids), ddsel)
+    dL = orc.moe_layer_bwd(x, W, k, cfg.renorm, cfg.act, dout, w_router=as_f64(inp.w_router),
+                           logits=as_f64(inp.logits), bias=as_f64(inp.bias), expert_map=inp.expert_map,
+                           capacity=inp.capacity, balance=balance, ids=ids)["dL"]
+    ddL = pi * (ddpi + np.sum(ddpi * pi, axis=1, keepdims=True))
+    if inp.logits is not None:
+        b["dlogits"] = ddL
+    else:
+        b["dw_router"] = (ddL + U * np.abs(dL)).T @ np.abs(x)
+    if inp.bias is not None:
+        b["dbias"] = ddL.sum(axis=0)
+    return b
