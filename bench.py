@@ -227,6 +227,39 @@ def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
+def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
+    """Layer backward on this batch (outside the timed forward step; not for
+    INT4 weights): average time of one moe_layer_bwd with preallocated
+    gradients and workspace, and its rate on the algorithmic FLOPs of its
+    GEMMs: per kept pair 16 d h (gate/up again, dz = dy Wd, dWd, dWg and dWu,
+    dx), the shared expert 16 T d h_s, the router 6 T d E."""
+    if cfg.w_dtype == "i4g128":
+        return None
+    g0 = torch.Generator(device=x.device)
+    g0.manual_seed(7)
+    dout = torch.randn(x.shape, generator=g0, device=x.device, dtype=torch.float32).to(x.dtype)
+    act_dt = 0 if cfg.dtype == "f32" else 1
+    ws = torch.empty(moe.layer_bwd_workspace_bytes(W, cfg.T, cfg.d, act_dt), dtype=torch.uint8, device=x.device)
+    grads = moe.layer_bwd(x, W, dout, logits=logits, balance=0.01, ws=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        if not args.warm_cache:
+            flush.fill_(2)
+        e0.record()
+        moe.layer_bwd(x, W, dout, logits=logits, balance=0.01, ws=ws, grads=grads)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    flops = 16.0 * work["P"] * cfg.d * cfg.h + 16.0 * cfg.T * cfg.d * cfg.h_shared
+    if cfg.has_router:
+        flops += 6.0 * cfg.T * cfg.d * cfg.E
+    peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "layer backward (recomputed routing and gate/up, dgrad and wgrad GEMMs, router)",
+            "ms": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "flops": flops,
+            "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": peak, "frac": round(tf / peak, 4)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -330,6 +363,7 @@ def main(argv=None):
     layer_roof = roofline_entry(work["layer"], ms, peak)
     by_products = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
     dispatch = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
+    backward = backward_timing(moe, torch, cfg, W, x, logits, work, flush, args)
 
     rec = {
         "metric": METRIC,
@@ -356,6 +390,7 @@ def main(argv=None):
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / args.steps, 4),
         "router_stats": by_products,
         "owner_dispatch": dispatch,
+        "backward": backward,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
