@@ -137,6 +137,29 @@ constexpr int kMaxDevices = 64;
 // free CUs; measured on MI355X with the granular workload (1/4 and 3/4 were
 // slower).
 constexpr int kSharedSlotDiv = 2;
+
+constexpr int kSharedWideMinRows = 2048;
+
+// Where the shared expert is forked onto the side stream.  On the narrow
+// persistent kernel (capped at part of the resident slots) it fits beside
+// routing and grouping, so it starts with the layer; its wide 256-row tiles
+// each need a whole CU, so they start once the grouping is issued and fill the
+// CUs the routed GEMMs' last partial wave of tiles leaves idle.  Measured on
+// MI355X: granular 0.228 ms forked after grouping against 0.236 at the start
+// and 0.243 after selection; decode 0.497 at the start against 0.542 after
+// grouping.
+enum class SharedFork { kAtStart, kAfterGrouping };
+inline SharedFork shared_fork(const FfnPlan& sp) {
+  return sp.BM == 256 ? SharedFork::kAfterGrouping : SharedFork::kAtStart;
+}
+
+// The shared expert is one group of T rows.  With bf16 weights and enough
+// rows it takes the wide 256-row tiles: they finish its GEMMs in fewer, fuller
+// workgroups that slot in beside the routed GEMMs' own wide tiles.
+FfnPlan shared_plan(int T, int d, int hs, int wt) {
+  if (wt == W_BF16 && T >= kSharedWideMinRows && hs % 128 == 0 && d % 256 == 0) return FfnPlan{256, 4, 4, false};
+  return plan_ffn((double)T, 1, d, hs, wt);
+}
 thread_local SideStream g_side[kMaxDevices];
 
 int side_stream(hipStream_t caller, SideStream** out) {
@@ -607,27 +630,34 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const int rows = layer_rows_max(L);
 
   MOE_HIP(mark(MOE_EV_START));
-  // 5a: shared expert on every token, forked onto the side stream
+  // 5a: shared expert on every token, forked onto the side stream (where:
+  // shared_fork)
   const void* shared_y = nullptr;
   SideStream* side = nullptr;
-  if (L->h_shared > 0) {
-    if ((rc = side_stream(s, &side))) return rc;
+  const int swt = L->act_dtype;  // shared weights are in the activation dtype
+  const FfnPlan sp = L->h_shared > 0 ? shared_plan(T, L->d, L->h_shared, wtype_of(swt)) : FfnPlan{16, 1, 1, false};
+  const SharedFork fork_at = shared_fork(sp);
+  auto launch_shared = [&]() -> int {
+    if (L->h_shared <= 0) return MOE_OK;
+    int r = side_stream(s, &side);
+    if (r) return r;
     MOE_HIP(hipEventRecord(side->fork, s));
     MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
-    const int swt = L->act_dtype;  // shared weights are in the activation dtype
-    const FfnPlan sp = plan_ffn((double)T, 1, L->d, L->h_shared, wtype_of(swt));
-    rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
-                 L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s, nullptr,
-                 kSharedSlotDiv);
+    r = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
+                L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s, nullptr,
+                kSharedSlotDiv);
     // the join is recorded even if a launch failed; on failure the caller's
     // stream waits for whatever the side stream did take before returning
     const hipError_t e = hipEventRecord(side->join, side->s);
-    if (rc || e != hipSuccess) {
+    if (r || e != hipSuccess) {
       if (e == hipSuccess) (void)hipStreamWaitEvent(s, side->join, 0);
-      return rc ? rc : hip_fail(e);
+      side = nullptr;
+      return r ? r : hip_fail(e);
     }
     shared_y = b.ys;
-  }
+    return MOE_OK;
+  };
+  if (fork_at == SharedFork::kAtStart && (rc = launch_shared())) return rc;
   // 1-4 on the caller's stream; the side stream is joined whatever their outcome
   auto routed = [&]() -> int {
     // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
@@ -649,6 +679,10 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     const FfnPlan plan = layer_plan(L, rows);
     MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
                            b.tiles, b.sorted_pair, pair_pos, b.counts, s));
+    if (fork_at == SharedFork::kAfterGrouping) {
+      const int r = launch_shared();
+      if (r) return r;
+    }
     MOE_HIP(mark(MOE_EV_GROUPED));
     // 4: routed experts, activations gathered straight from x by pair index
     const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
