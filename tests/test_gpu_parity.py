@@ -35,6 +35,9 @@ SCALED = {
     "wide_geglu_small": scaled("wide_geglu_bf16", T=1024, d=256, E=8, h=512),
     "decode_small": scaled("decode_bf16", T=136, d=512, E=32, h=256, h_shared=256),
     "int4_small": scaled("int4_share", T=72, d=512, E=64, h=256, owners=8),
+    # 2304 tokens: the shared expert takes the wide 256-row tiles and is
+    # forked after the grouping step; every output is compared
+    "shared_wide": scaled("granular_bf16", T=2304, d=256, E=16, h=128, h_shared=256),
 }
 
 
