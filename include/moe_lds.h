@@ -310,6 +310,12 @@ struct moe_layer_trace {
   int32_t* expert_counts;     /* [E]      */
   float* prob_mean;           /* [E]      */
   float* balance_loss;        /* [1]      */
+  /* hipEvent_t start/stop pairs (timing-enabled, caller-owned) attached to the
+   * launches of the routed gate/up and down GEMMs themselves
+   * (hipExtLaunchKernel): they time exactly those kernels and, unlike the
+   * step events above, put no extra packet on the stream */
+  void* gate_up_kernel_events[2];
+  void* down_kernel_events[2];
 };
 
 /*

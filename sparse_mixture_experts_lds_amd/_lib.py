@@ -41,7 +41,8 @@ EVENT_NAMES = ["start", "routed", "grouped", "gate_up", "down", "shared", "end"]
 class LayerTrace(ctypes.Structure):
     _fields_ = [("logits", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("expert_offsets", _vp),
                 ("pair_pos", _vp), ("events", _vp * MOE_NUM_EVENTS),
-                ("expert_counts", _vp), ("prob_mean", _vp), ("balance_loss", _vp)]
+                ("expert_counts", _vp), ("prob_mean", _vp), ("balance_loss", _vp),
+                ("gate_up_kernel_events", _vp * 2), ("down_kernel_events", _vp * 2)]
 
 
 class LayerGrads(ctypes.Structure):

@@ -238,12 +238,14 @@ def layer_workspace_bytes(weights: LayerWeights, T: int, d: int, act_dtype: int)
 
 def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Tensor] = None,
               trace: bool = False, out: Optional[torch.Tensor] = None,
-              ws: Optional[torch.Tensor] = None, events=None, stats: bool = False):
+              ws: Optional[torch.Tensor] = None, events=None, stats: bool = False, kernel_events=None):
     """Whole layer forward.  Returns out [T, d] (and a dict of intermediates when trace;
     ``stats`` adds the router by-products expert_counts, prob_mean and balance_loss to it).
 
     ``events``: optional list of MOE_NUM_EVENTS raw hipEvent_t handles (ints, or None),
-    recorded on the current stream at the step boundaries."""
+    recorded on the current stream at the step boundaries.  ``kernel_events``: optional
+    (gate_up_start, gate_up_stop, down_start, down_stop) raw handles attached to the
+    routed GEMM launches themselves."""
     lib = load()
     trace = trace or stats
     T, d = x.shape
@@ -259,10 +261,13 @@ def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Ten
         out = torch.empty((T, d), dtype=x.dtype, device=dev)
     tr = None
     tdict = None
-    if events is not None:
+    if events is not None or kernel_events is not None:
         tr = LayerTrace()
-        for i, ev in enumerate(events):
+        for i, ev in enumerate(events or []):
             tr.events[i] = ev
+        if kernel_events is not None:
+            tr.gate_up_kernel_events[0], tr.gate_up_kernel_events[1] = kernel_events[0], kernel_events[1]
+            tr.down_kernel_events[0], tr.down_kernel_events[1] = kernel_events[2], kernel_events[3]
     if trace:
         E_loc = weights.wg.shape[0]
         k = weights.k

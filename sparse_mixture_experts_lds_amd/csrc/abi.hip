@@ -80,9 +80,13 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
             const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
-            void* mid_event = nullptr, int slot_div = 1) {
+            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr) {
   const int wt = wtype_of(w_dtype);
   FfnGemmArgs g{};
+  if (kernel_events) {
+    g.ev_start = kernel_events[0];
+    g.ev_stop = kernel_events[1];
+  }
   g.A = A;
   g.row_index = row_index;
   g.row_div = row_div > 0 ? row_div : 1;
@@ -117,6 +121,8 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   dn.a_rows = rows_max;
   dn.K = h;
   dn.N = d;
+  dn.ev_start = kernel_events ? kernel_events[2] : nullptr;
+  dn.ev_stop = kernel_events ? kernel_events[3] : nullptr;
   MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BM, plan.NF_down, s));
   return MOE_OK;
 }
@@ -692,9 +698,11 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     }
     MOE_HIP(mark(MOE_EV_GROUPED));
     // 4: routed experts, activations gathered straight from x by pair index
+    void* kev[4] = {tr.gate_up_kernel_events[0], tr.gate_up_kernel_events[1], tr.down_kernel_events[0],
+                    tr.down_kernel_events[1]};
     const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
                           b.tiles, plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down,
-                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP]);
+                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP], 1, kev);
     if (r) return r;
     MOE_HIP(mark(MOE_EV_DOWN));
     return MOE_OK;

@@ -557,7 +557,7 @@ hipError_t launch_one(const FfnGemmArgs& a, hipStream_t s) {
   long long S = std::max<long long>(slots, (per_ub + NT_MAX - 1) / NT_MAX);
   S = std::min<long long>(S, per_ub);
   const long long g = 8 * S;
-  ffn_gemm_kernel<WT, MF, NF, GU, SPLIT><<<dim3((unsigned)g), 256, 0, s>>>(a);
+  launch_gemm(ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>, dim3((unsigned)g), dim3(256), s, a);
   return hipGetLastError();
 }
 

@@ -363,9 +363,9 @@ hipError_t launch_bw(const FfnGemmArgs& a, hipStream_t s) {
   long long g = (long long)mt * (a.N / BNO);
   g = (g + 7) / 8 * 8;
   if (g == 0) return hipSuccess;
-  if (!GATEUP && a.out_f32) wide_kernel<false, true, 0, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
-  else if (GATEUP && a.act == 1) wide_kernel<GATEUP, false, 1, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
-  else wide_kernel<GATEUP, false, 0, BW><<<dim3((unsigned)g), 512, 0, s>>>(a);
+  if (!GATEUP && a.out_f32) launch_gemm(wide_kernel<false, true, 0, BW>, dim3((unsigned)g), dim3(512), s, a);
+  else if (GATEUP && a.act == 1) launch_gemm(wide_kernel<GATEUP, false, 1, BW>, dim3((unsigned)g), dim3(512), s, a);
+  else launch_gemm(wide_kernel<GATEUP, false, 0, BW>, dim3((unsigned)g), dim3(512), s, a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // Nothing here is exported from the shared library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -152,7 +153,20 @@ struct FfnGemmArgs {
   int slot_div;              // persistent grid = resident workgroup slots / slot_div (0, 1: all)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
+  void* ev_start;            // hipEvent_t pair carried by the launch itself (NULL: none):
+  void* ev_stop;             //   they time exactly this kernel and add no packet to the stream
 };
+
+// Launch a GEMM kernel, with the argument block's start/stop events attached
+// to its dispatch when it has any.
+template <typename Kern>
+inline void launch_gemm(Kern kernel, dim3 grid, dim3 block, hipStream_t s, const FfnGemmArgs& a) {
+  if (a.ev_start || a.ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(a.ev_start),
+                          static_cast<hipEvent_t>(a.ev_stop), 0, a);
+  else
+    kernel<<<grid, block, 0, s>>>(a);
+}
 struct FfnPlan {
   int BM;                    // rows per tile (16 * MF)
   int NF_up, NF_down;        // 16-col fragments per wave
