@@ -49,21 +49,43 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_r
   const size_t t = i / v8_per_row;
   if (t >= (size_t)T) return;
   const int c = (int)(i - t * v8_per_row);
+  constexpr bool YF = Y_F32 || !OUT_BF16;
   float acc[8];
 #pragma unroll
   for (int v = 0; v < 8; ++v) acc[v] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int pos = pair_pos[t * k + j];
-    if (pos < 0) continue;
-    const float w = tw[t * k + j];
-    float yv[8];
-    load8<Y_F32 || !OUT_BF16>(y, (size_t)pos * v8_per_row + c, yv);
+  // the shared row's load is issued first; slots go four at a time: their
+  // indices and gates, then the rows of the kept ones, all in flight together,
+  // then the sums in ascending slot order (the order of the definition)
+  float sv[8];
+  if (shared_y) load8<YF>(shared_y, t * v8_per_row + c, sv);
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int pos[4];
+    float w[4];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) acc[v] = fmaf(w, yv[v], acc[v]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      pos[u] = j < k ? pair_pos[t * k + j] : -1;
+      w[u] = pos[u] >= 0 ? tw[t * k + j] : 0.f;
+    }
+    float yv[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (pos[u] >= 0) {
+        load8<YF>(y, (size_t)pos[u] * v8_per_row + c, yv[u]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) yv[u][v] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (pos[u] >= 0) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[v] = fmaf(w[u], yv[u][v], acc[v]);
+      }
+    }
   }
   if (shared_y) {
-    float sv[8];
-    load8<Y_F32 || !OUT_BF16>(shared_y, t * v8_per_row + c, sv);
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[v] += sv[v];
   }
