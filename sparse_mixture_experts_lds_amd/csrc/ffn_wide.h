@@ -273,84 +273,73 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   wait_vm<0>();  // the dummy loads land before the stages become the epilogue's buffer
   lds_barrier();
 
-  // ---------------- epilogue: the output columns in slices of 32 (gate/up) or
-  // 64 (down), staged through the (now free) stage memory; a wave column owns
-  // QPW consecutive slices
+  // ---------------- epilogue: the output tile is staged through the (now free)
+  // stage memory so that the stores go out as 16-byte row chunks
   unsigned char* const lds = &stg[0][0];
   unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * (OUT_F32 ? 4 : 2);
   if constexpr (GATEUP) {
-    // g and u go to LDS as fp32; every thread then forms act(g)*u for 8
-    // columns at a time and stores them as 16 bytes of bf16, which keeps the
-    // activation's temporaries out of the accumulator-heavy code
-    constexpr int GS = 32 + 4;     // fp32 row stride of a staged slice
-    constexpr int NQ = BNO / 32;   // slices
-    constexpr int QPW = NQ / 2;    // slices per wave column
-    float* Gs = reinterpret_cast<float*>(lds);
-    float* U = Gs + BM * GS;
+    // g and u of an output sit in the same lane, so z = act(g) * u is formed
+    // in registers and the whole bf16 z tile (256 x BNO) goes to LDS in one
+    // pass; then every thread stores 16-byte row chunks
+    constexpr int ZS = BNO * 2 + 16;  // LDS row stride of the staged z tile (bytes)
+    constexpr int cpr = BNO * 2 / 16; // 16-byte chunks per row
+    static_assert(BM * ZS <= NS * STAGE, "z tile fits the stage memory");
+    if (active) {
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      if (wc == qq / QPW && active) {
+      for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
+        for (int f = 0; f < NF / 2; ++f)
 #pragma unroll
-          for (int ff = 0; ff < 2; ++ff) {
-            const int f = 2 * (qq % QPW) + ff;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int o = (64 * wr + 16 * mi + 4 * q + r) * GS + 16 * ff + lrow;
-              Gs[o] = acc[mi][f][r];
-              U[o] = acc[mi][f + NF / 2][r];
-            }
+          for (int r = 0; r < 4; ++r) {
+            const float z = act_fn<ACT>(acc[mi][f][r]) * acc[mi][f + NF / 2][r];
+            *reinterpret_cast<uint16_t*>(lds + (64 * wr + 16 * mi + 4 * q + r) * ZS + (HW / 2 * wc + 16 * f + lrow) * 2) =
+                (uint16_t)f32_to_bf16_bits(z);
           }
-      }
-      lds_barrier();
-      for (int c = tid; c < nrows * 4; c += 512) {
-        const int row = c >> 2, cc = c & 3;
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(Gs + row * GS + cc * 8);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(Gs + row * GS + cc * 8 + 4);
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8);
-        const f32x4 u1 = *reinterpret_cast<const f32x4*>(U + row * GS + cc * 8 + 4);
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          o[i] = pack_bf16x2(act_fn<ACT>(g0[2 * i]) * u0[2 * i], act_fn<ACT>(g0[2 * i + 1]) * u0[2 * i + 1]);
-          o[i + 2] = pack_bf16x2(act_fn<ACT>(g1[2 * i]) * u1[2 * i], act_fn<ACT>(g1[2 * i + 1]) * u1[2 * i + 1]);
-        }
-        *reinterpret_cast<u32x4*>(obase + ((size_t)row * N + 32 * qq + cc * 8) * 2) = o;
-      }
-      lds_barrier();
+    }
+    lds_barrier();
+    for (int c = tid; c < nrows * cpr; c += 512) {
+      const int row = c / cpr;
+      const int cc = c - row * cpr;
+      *reinterpret_cast<u32x4*>(obase + ((size_t)row * N) * 2 + cc * 16) =
+          *reinterpret_cast<const u32x4*>(lds + row * ZS + cc * 16);
     }
   } else {
+    // every wave stages its own 64 x HW block of the output through a private
+    // LDS region, in two halves of HW/2 columns, and stores 16-byte row
+    // chunks; a wave's LDS accesses complete in order, so no workgroup barrier
+    // is needed between the writes and the reads
     constexpr int osz = OUT_F32 ? 4 : 2;
-    constexpr int QC = 64;              // output columns per slice
-    constexpr int OS = QC * osz + 16;   // LDS row stride of a staged slice
-    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row of a slice
-    constexpr int NQ = BNO / QC;        // slices
-    constexpr int QPW = NQ / 2;         // slices per wave column
+    constexpr int QC = HW / 2;          // output columns per half
+    constexpr int OS = QC * osz + 16;   // LDS row stride of a wave's block (bytes)
+    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row
+    static_assert(8 * 64 * OS <= NS * STAGE, "the waves' blocks fit the stage memory");
+    unsigned char* const wl = lds + wave * 64 * OS;
+    const int rows_w = min(64, nrows - 64 * wr);
+    if (active) {
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      if (wc == qq / QPW && active) {
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
-          for (int ff = 0; ff < 4; ++ff) {
-            const int f = 4 * (qq % QPW) + ff;
+          for (int ff = 0; ff < NF / 2; ++ff)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              unsigned char* dst = lds + (64 * wr + 16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
-              if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = acc[mi][f][r];
-              else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(acc[mi][f][r]);
+              const float v = acc[mi][(NF / 2) * hh + ff][r];
+              unsigned char* dst = wl + (16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
+              if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = v;
+              else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
             }
-          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        unsigned char* const ob = obase + ((size_t)(64 * wr) * N + HW * wc + QC * hh) * osz;
+        for (int c = lane; c < rows_w * cpr; c += 64) {
+          const int row = c / cpr;
+          const int cc = c - row * cpr;
+          *reinterpret_cast<u32x4*>(ob + (size_t)row * N * osz + cc * 16) =
+              *reinterpret_cast<const u32x4*>(wl + row * OS + cc * 16);
+        }
+        // the reads land before the next half overwrites the block
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      lds_barrier();
-      for (int c = tid; c < nrows * cpr; c += 512) {
-        const int row = c / cpr;
-        const int cc = c - row * cpr;
-        *reinterpret_cast<u32x4*>(obase + ((size_t)row * N + qq * QC) * osz + cc * 16) =
-            *reinterpret_cast<const u32x4*>(lds + row * OS + cc * 16);
-      }
-      lds_barrier();
     }
   }
 }
