@@ -71,13 +71,18 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
           "bytes": touched * wb_gu + kept_tokens * d * ab + P * h * zb}
     dn = {"flops": 2.0 * d * h * P,
           "bytes": touched * wb_dn + P * h * zb + P * d * 4}
+    # the shared expert's GEMMs over all T tokens (z in bf16 or fp32 like the
+    # routed one, y in fp32)
+    T = cfg.T
+    sgu = {"flops": 4.0 * d * hs * T, "bytes": 2 * hs * d * ab + T * d * ab + T * hs * zb}
+    sdn = {"flops": 2.0 * d * hs * T, "bytes": d * hs * ab + T * hs * zb + T * d * 4}
     router_f = 2.0 * cfg.T * d * cfg.E if cfg.has_router else 0.0
     router_b = cfg.E * d * ab if cfg.has_router else cfg.T * cfg.E * 4
     layer_f = router_f + 6.0 * d * h * P + (6.0 * d * hs * cfg.T if hs else 0.0)
     layer_b = (touched * (wb_gu + wb_dn) + router_b + (3 * hs * d * ab if hs else 0)
                + cfg.T * d * ab + cfg.T * d * ab)
-    return {"gate_up": gu, "down": dn, "layer": {"flops": layer_f, "bytes": layer_b},
-            "P": P, "touched": touched}
+    return {"gate_up": gu, "down": dn, "shared_gate_up": sgu, "shared_down": sdn,
+            "layer": {"flops": layer_f, "bytes": layer_b}, "P": P, "touched": touched}
 
 
 GEMM_SOURCES = ("ffn_kernel.h", "ffn_wide.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
@@ -385,10 +390,17 @@ def main(argv=None):
     dom_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in kev]))
     ms = float(np.mean(layer_ms))
     peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
-    roof = roofline_entry(work[dom], dom_ms, peak)
-    roof.update({"kernel": "grouped expert GEMM (routed %s)" % dom.replace("_", "/"),
+    # when the shared expert's GEMMs ride in the routed launches, the timed
+    # launch does both problems' work
+    paired = bool(moe.layer_plan(W, cfg.T, cfg.d, act_dt)["shared_in_routed_launches"])
+    dom_work = dict(work[dom])
+    if paired:
+        dom_work = {key: work[dom][key] + work["shared_" + dom][key] for key in ("flops", "bytes")}
+    roof = roofline_entry(dom_work, dom_ms, peak)
+    roof.update({"kernel": "grouped expert GEMM (%s %s)" % ("routed + shared, one launch," if paired else "routed",
+                                                            dom.replace("_", "/")),
                  "avg_ms": round(dom_ms, 4), "traffic": measured_traffic(cfg.name, dom),
-                 "algorithmic": {"bytes": work[dom]["bytes"], "flops": work[dom]["flops"]}})
+                 "algorithmic": {"bytes": dom_work["bytes"], "flops": dom_work["flops"]}})
     layer_roof = roofline_entry(work["layer"], ms, peak)
     by_products = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
     dispatch = dispatch_timing(moe, torch, cfg, tr, x, flush, args)

@@ -319,6 +319,24 @@ struct moe_layer_trace {
 };
 
 /*
+ * moe_layer_plan - how moe_layer_fwd runs the expert GEMMs of layer L (host
+ * only; reads the descriptor's sizes and types, no device memory): the tile
+ * shapes it picks and whether the shared expert's gate/up and down GEMMs run
+ * inside the routed GEMMs' own launches (then the kernel events of
+ * moe_layer_trace time those combined launches, and MOE_EV_GATE_UP and
+ * MOE_EV_DOWN fall after the shared expert's GEMMs too).  Returns what
+ * moe_layer_workspace_bytes would reject L with, else MOE_OK.
+ */
+struct moe_layer_plan_info {
+  int tile_m;                     /* rows per tile of the routed GEMMs (256: wide kernel) */
+  int tile_n_up;                  /* output columns per tile of the routed gate/up GEMM   */
+  int tile_n_down;                /* output columns per tile of the routed down GEMM      */
+  int shared_tile_m;              /* rows per tile of the shared expert's GEMMs, 0 if none */
+  int shared_in_routed_launches;  /* 1: the shared expert shares the routed launches      */
+};
+int moe_layer_plan(const struct moe_layer_desc* L, struct moe_layer_plan_info* out);
+
+/*
  *   x          [T, d] act_dtype (always read: the experts run on it)
  *   logits_in  [T, E] fp32 routing logits (a share that receives its routing
  *              from upstream), or NULL to run the router GEMM on w_router

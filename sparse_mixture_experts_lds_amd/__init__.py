@@ -7,7 +7,7 @@ arithmetic runs in the library's HIP kernels; nothing here computes.
 """
 from .api import (  # noqa: F401
     route, router_stats, permute, dispatch_owners, expert_ffn, combine, layer_fwd, quantize_int4, LayerWeights,
-    permute_workspace_bytes, expert_ffn_workspace_bytes, layer_workspace_bytes, layer_bwd,
+    permute_workspace_bytes, expert_ffn_workspace_bytes, layer_workspace_bytes, layer_plan, layer_bwd,
     layer_bwd_workspace_bytes,
 )
 from ._lib import MoEError, load  # noqa: F401

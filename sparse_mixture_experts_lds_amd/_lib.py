@@ -13,7 +13,8 @@ MOE_PLACE_ROUND_ROBIN, MOE_PLACE_CONTIGUOUS = 0, 1
 EXPORTS = [
     "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
     "moe_permute", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
-    "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_fwd",
+    "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_plan",
+    "moe_layer_fwd",
     "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_quantize_int4", "moe_strerror", "moe_last_error",
 ]
 
@@ -43,6 +44,11 @@ class LayerTrace(ctypes.Structure):
                 ("pair_pos", _vp), ("events", _vp * MOE_NUM_EVENTS),
                 ("expert_counts", _vp), ("prob_mean", _vp), ("balance_loss", _vp),
                 ("gate_up_kernel_events", _vp * 2), ("down_kernel_events", _vp * 2)]
+
+
+class LayerPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("tile_m", "tile_n_up", "tile_n_down", "shared_tile_m",
+                                            "shared_in_routed_launches")]
 
 
 class LayerGrads(ctypes.Structure):
@@ -80,6 +86,7 @@ def load(path: str = LIB_PATH):
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
         "moe_combine": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
         "moe_layer_workspace_bytes": (_c_size, [ctypes.POINTER(LayerDesc)]),
+        "moe_layer_plan": (_c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerPlanInfo)]),
         "moe_layer_fwd": (_c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, ctypes.POINTER(LayerTrace),
                                    _vp, _c_size, _vp]),
         "moe_layer_bwd_workspace_bytes": (_c_size, [ctypes.POINTER(LayerDesc)]),

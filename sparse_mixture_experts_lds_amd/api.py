@@ -8,8 +8,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MOE_BF16, MOE_F32, MOE_GEGLU, MOE_I4G128, MOE_SWIGLU, LayerDesc, LayerGrads, LayerTrace,
-                   check, load)
+from ._lib import (MOE_BF16, MOE_F32, MOE_GEGLU, MOE_I4G128, MOE_SWIGLU, LayerDesc, LayerGrads, LayerPlanInfo,
+                   LayerTrace, check, load)
 
 _ACT = {"swiglu": MOE_SWIGLU, "geglu": MOE_GEGLU}
 
@@ -234,6 +234,14 @@ class LayerWeights:
 def layer_workspace_bytes(weights: LayerWeights, T: int, d: int, act_dtype: int) -> int:
     L = weights.desc(T, d, act_dtype)
     return load().moe_layer_workspace_bytes(ctypes.byref(L))
+
+
+def layer_plan(weights: LayerWeights, T: int, d: int, act_dtype: int) -> dict:
+    """How layer_fwd runs the expert GEMMs for this layer (moe_layer_plan)."""
+    L = weights.desc(T, d, act_dtype)
+    info = LayerPlanInfo()
+    check("moe_layer_plan", load().moe_layer_plan(ctypes.byref(L), ctypes.byref(info)))
+    return {n: int(getattr(info, n)) for n, _ in LayerPlanInfo._fields_}
 
 
 def layer_fwd(x: torch.Tensor, weights: LayerWeights, logits: Optional[torch.Tensor] = None,

@@ -74,19 +74,14 @@ int check_route_dims(int T, int E, int k) {
   return MOE_OK;
 }
 
-// Gate/up then down over grouped rows; `offsets` NULL means one group.
-int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A, int a_rows,
-            const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
-            const int4* tile_tab, int BM,
-            const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
-            const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
-            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr) {
-  const int wt = wtype_of(w_dtype);
+// Argument blocks of the gate/up GEMM (z = act(A Wg^T) * (A Wu^T) over
+// grouped rows; `offsets` NULL means one group) and of the down GEMM that
+// follows it (y = z Wd^T).
+FfnGemmArgs gate_up_args(int E_loc, int rows_max, int d, int h, int act, const void* A, int a_rows,
+                         const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
+                         const int4* tile_tab, const FfnPlan& plan, const void* wg, const void* wu,
+                         const void* sg, const void* su, void* z) {
   FfnGemmArgs g{};
-  if (kernel_events) {
-    g.ev_start = kernel_events[0];
-    g.ev_stop = kernel_events[1];
-  }
   g.A = A;
   g.row_index = row_index;
   g.row_div = row_div > 0 ? row_div : 1;
@@ -104,12 +99,14 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   g.K = d;
   g.N = h;
   g.act = act == MOE_GEGLU ? 1 : 0;
-  g.slot_div = slot_div;
+  g.slot_div = 1;
   g.out_f32 = plan.split_z ? 1 : 0;
-  MOE_HIP(launch_ffn_gemm(g, true, wt, false, BM, plan.NF_up, s));
-  if (mid_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(mid_event), s));
-  FfnGemmArgs dn = g;
-  dn.A = z;
+  return g;
+}
+
+FfnGemmArgs down_args(const FfnGemmArgs& gu, const void* wd, const void* sd, void* y, bool y_f32) {
+  FfnGemmArgs dn = gu;
+  dn.A = gu.out;
   dn.row_index = nullptr;
   dn.row_div = 1;
   dn.W0 = wd;
@@ -118,9 +115,30 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   dn.S1 = nullptr;
   dn.out = y;
   dn.out_f32 = y_f32 ? 1 : 0;
-  dn.a_rows = rows_max;
-  dn.K = h;
-  dn.N = d;
+  dn.a_rows = gu.rows_max;
+  dn.K = gu.N;
+  dn.N = gu.K;
+  return dn;
+}
+
+// Gate/up then down over grouped rows; `offsets` NULL means one group.
+int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A, int a_rows,
+            const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
+            const int4* tile_tab, int BM,
+            const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
+            const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
+            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr) {
+  const int wt = wtype_of(w_dtype);
+  FfnGemmArgs g = gate_up_args(E_loc, rows_max, d, h, act, A, a_rows, row_index, row_div, offsets, mtile,
+                               tile_tab, plan, wg, wu, sg, su, z);
+  g.slot_div = slot_div;
+  if (kernel_events) {
+    g.ev_start = kernel_events[0];
+    g.ev_stop = kernel_events[1];
+  }
+  MOE_HIP(launch_ffn_gemm(g, true, wt, false, BM, plan.NF_up, s));
+  if (mid_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(mid_event), s));
+  FfnGemmArgs dn = down_args(g, wd, sd, y, y_f32);
   dn.ev_start = kernel_events ? kernel_events[2] : nullptr;
   dn.ev_stop = kernel_events ? kernel_events[3] : nullptr;
   MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BM, plan.NF_down, s));
@@ -166,6 +184,15 @@ FfnPlan shared_plan(int T, int d, int hs, int wt) {
   if (wt == W_BF16 && T >= kSharedWideMinRows && hs % 128 == 0 && d % 256 == 0) return FfnPlan{256, 4, 4, false};
   return plan_ffn((double)T, 1, d, hs, wt);
 }
+// The shared expert's GEMMs ride in the routed GEMMs' own launches when both
+// run on the wide kernel with the same tile widths: the two problems' tiles
+// then fill the CUs as one grid (granular: 384 + 128 gate/up tiles, exactly
+// two rounds of 256 CUs), with no second stream and no fork or join events.
+bool shared_paired(const moe_layer_desc* L, const FfnPlan& plan, const FfnPlan& sp) {
+  return L->h_shared > 0 && L->w_dtype == MOE_BF16 && L->act_dtype == MOE_BF16 && plan.BM == 256 &&
+         sp.BM == 256 && !plan.split_z && plan.NF_up == sp.NF_up && plan.NF_down == sp.NF_down;
+}
+
 thread_local SideStream g_side[kMaxDevices];
 
 int side_stream(hipStream_t caller, SideStream** out) {
@@ -616,6 +643,25 @@ size_t moe_layer_workspace_bytes(const moe_layer_desc* L) {
   return carve_layer(L, nullptr, &b);
 }
 
+int moe_layer_plan(const moe_layer_desc* L, moe_layer_plan_info* out) {
+  if (!out) return MOE_EINVAL;
+  const int rc = check_layer(L);
+  if (rc) return rc;
+  const FfnPlan p = layer_plan(L, layer_rows_max(L));
+  const bool wide = p.BM == 256;
+  moe_layer_plan_info r{};
+  r.tile_m = p.BM;
+  r.tile_n_up = wide ? 32 * p.NF_up : 64 * p.NF_up;
+  r.tile_n_down = 64 * p.NF_down;
+  if (L->h_shared > 0) {
+    const FfnPlan sp = shared_plan(L->T, L->d, L->h_shared, wtype_of(L->act_dtype));
+    r.shared_tile_m = sp.BM;
+    r.shared_in_routed_launches = shared_paired(L, p, sp) ? 1 : 0;
+  }
+  *out = r;
+  return MOE_OK;
+}
+
 int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in, void* out,
                   const moe_layer_trace* trace, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
@@ -643,15 +689,17 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const int rows = layer_rows_max(L);
 
   MOE_HIP(mark(MOE_EV_START));
-  // 5a: shared expert on every token, forked onto the side stream (where:
-  // shared_fork)
+  const FfnPlan plan = layer_plan(L, rows);
+  // 5a: shared expert on every token: inside the routed GEMM launches
+  // (shared_paired), else forked onto the side stream (where: shared_fork)
   const void* shared_y = nullptr;
   SideStream* side = nullptr;
   const int swt = L->act_dtype;  // shared weights are in the activation dtype
   const FfnPlan sp = L->h_shared > 0 ? shared_plan(T, L->d, L->h_shared, wtype_of(swt)) : FfnPlan{16, 1, 1, false};
+  const bool paired = shared_paired(L, plan, sp);
   const SharedFork fork_at = shared_fork(sp);
   auto launch_shared = [&]() -> int {
-    if (L->h_shared <= 0) return MOE_OK;
+    if (L->h_shared <= 0 || paired) return MOE_OK;
     int r = side_stream(s, &side);
     if (r) return r;
     MOE_HIP(hipEventRecord(side->fork, s));
@@ -689,7 +737,6 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     }
     MOE_HIP(mark(MOE_EV_ROUTED));
     // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
-    const FfnPlan plan = layer_plan(L, rows);
     MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
                            b.tiles, b.sorted_pair, pair_pos, b.counts, s));
     if (fork_at == SharedFork::kAfterGrouping) {
@@ -700,6 +747,22 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     // 4: routed experts, activations gathered straight from x by pair index
     void* kev[4] = {tr.gate_up_kernel_events[0], tr.gate_up_kernel_events[1], tr.down_kernel_events[0],
                     tr.down_kernel_events[1]};
+    if (paired) {
+      const FfnGemmArgs rg = gate_up_args(L->E_loc, rows, L->d, L->h, L->act, x, T, b.sorted_pair, k, offsets,
+                                          b.mtile, b.tiles, plan, L->w_gate, L->w_up, nullptr, nullptr, b.z);
+      const FfnGemmArgs sg = gate_up_args(1, T, L->d, L->h_shared, L->act, x, T, nullptr, 1, nullptr, nullptr,
+                                          nullptr, sp, L->ws_gate, L->ws_up, nullptr, nullptr, b.zs);
+      MOE_HIP(launch_ffn_gemm_wide_pair(rg, sg, true, plan.NF_up, kev[0], kev[1], s));
+      MOE_HIP(mark(MOE_EV_GATE_UP));
+      const FfnGemmArgs rd = down_args(rg, L->w_down, nullptr, b.y, true);
+      const FfnGemmArgs sd = down_args(sg, L->ws_down, nullptr, b.ys, true);
+      // the deeper problem's tiles are dispatched first
+      if (L->h_shared > L->h) MOE_HIP(launch_ffn_gemm_wide_pair(sd, rd, false, plan.NF_down, kev[2], kev[3], s));
+      else MOE_HIP(launch_ffn_gemm_wide_pair(rd, sd, false, plan.NF_down, kev[2], kev[3], s));
+      shared_y = b.ys;
+      MOE_HIP(mark(MOE_EV_DOWN));
+      return MOE_OK;
+    }
     const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
                           b.tiles, plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down,
                           b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP], 1, kev);

@@ -65,12 +65,22 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   if (BM == ffn_wide::BM) {
     if (w_type != W_BF16 || split) return hipErrorInvalidValue;
     // NF: weight rows per tile / 64 (4 -> 256, 2 -> 128)
-    return gateup ? ffn_wide::launch_wide<true>(a, 64 * NF, s) : ffn_wide::launch_wide<false>(a, 64 * NF, s);
+    return gateup ? ffn_wide::launch_wide<true>(&a, 1, 64 * NF, a.ev_start, a.ev_stop, s)
+                  : ffn_wide::launch_wide<false>(&a, 1, 64 * NF, a.ev_start, a.ev_stop, s);
   }
   if (w_type == W_F32) return gateup ? launch_mf_nf<W_F32, true, false>(a, BM, NF, s) : launch_mf_nf<W_F32, false, false>(a, BM, NF, s);
   if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);
   if (gateup) return launch_mf_nf<W_BF16, true, false>(a, BM, NF, s);
   return split ? launch_mf_nf<W_BF16, false, true>(a, BM, NF, s) : launch_mf_nf<W_BF16, false, false>(a, BM, NF, s);
+}
+
+hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int NF,
+                                     void* ev_start, void* ev_stop, hipStream_t s) {
+  const FfnGemmArgs a[2] = {a0, a1};
+  for (const FfnGemmArgs& p : a)
+    if (p.a_rows < 0 || (size_t)p.a_rows * (size_t)p.K * 2 > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  return gateup ? ffn_wide::launch_wide<true>(a, 2, 64 * NF, ev_start, ev_stop, s)
+                : ffn_wide::launch_wide<false>(a, 2, 64 * NF, ev_start, ev_stop, s);
 }
 
 }  // namespace moe

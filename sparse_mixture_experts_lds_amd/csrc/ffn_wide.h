@@ -93,8 +93,23 @@ __device__ __forceinline__ void dma16(const unsigned char* src, uint32_t lds_add
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
 
+// One launch covers one or two GEMM problems of the same kind (the routed
+// experts' grouped rows and the shared expert's dense rows): each XCD takes a
+// contiguous range of problem 0's tiles, then of problem 1's, so both spread
+// evenly over the XCDs and problem 0's tiles are dispatched first.
+struct WideArgs {
+  FfnGemmArgs p[2];
+  int np;  // 1 or 2
+};
+
+// tiles of one problem: m-tiles x weight-row blocks
+__device__ __forceinline__ int wide_tiles(const FfnGemmArgs& a, int NBLK) {
+  const int mt = a.offsets ? a.mtile_start[a.E_loc] : (a.rows_max + BM - 1) / BM;
+  return mt * NBLK;
+}
+
 template <bool GATEUP, bool OUT_F32, int ACT, int BW>
-__global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
+__global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
   using G = Geo<BW>;
   constexpr int OPB = G::OPB, STAGE = G::STAGE, NS = G::NS, LPS = G::LPS, LB = G::LB;
   constexpr int BNO = GATEUP ? BW / 2 : BW;  // output columns per tile
@@ -109,20 +124,29 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
   const int q = lane >> 4;
   const int wr = wave & 3;
   const int wc = wave >> 2;
-  const int N = args.N, K = args.K;
-  const int NBLK = N / BNO;
   static_assert(NS >= 4, "the loop keeps two k-blocks out of the load window");
 
-  // ---------------- tile of this workgroup (XCD-contiguous ranges, grouped-M order)
-  int total_mt;
-  if (args.offsets) total_mt = args.mtile_start[args.E_loc];
-  else total_mt = (args.rows_max + BM - 1) / BM;
-  const int total = total_mt * NBLK;
-  const int per = (total + 7) / 8;
+  // ---------------- problem and tile of this workgroup (XCD-contiguous ranges,
+  // grouped-M order within a problem)
   const int slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int R = (blockIdx.x & 7) * per + slot;
+  const int xcd = blockIdx.x & 7;
+  FfnGemmArgs args = wa.p[0];
+  int total = wide_tiles(args, args.N / BNO);
+  int per = (total + 7) / 8;
+  int sl = slot;
+  if (sl >= per) {
+    if (wa.np < 2) return;
+    sl -= per;
+    args = wa.p[1];
+    total = wide_tiles(args, args.N / BNO);
+    per = (total + 7) / 8;
+    if (sl >= per) return;
+  }
+  const int R = xcd * per + sl;
   if (R >= total) return;
+  const int N = args.N, K = args.K;
+  const int NBLK = N / BNO;
+  const int total_mt = total / NBLK;
   int e = 0, row0, nrows, nb;
   {
     const int grp = R / (kGroupM * NBLK);
@@ -345,26 +369,45 @@ __global__ __launch_bounds__(512) void wide_kernel(FfnGemmArgs args) {
 }
 
 template <bool GATEUP, int BW>
-hipError_t launch_bw(const FfnGemmArgs& a, hipStream_t s) {
+hipError_t launch_bw(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, hipStream_t s) {
   constexpr int BNO = GATEUP ? BW / 2 : BW;
-  if (a.N % BNO || a.K % (2 * KB) || (size_t)a.N * a.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
-  long long g = (long long)mt * (a.N / BNO);
-  g = (g + 7) / 8 * 8;
+  WideArgs w{};
+  w.np = np;
+  long long slots = 0;
+  for (int i = 0; i < np; ++i) {
+    const FfnGemmArgs& p = a[i];
+    if (p.N % BNO || p.K % (2 * KB) || (size_t)p.N * p.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (i > 0 && (p.out_f32 != a[0].out_f32 || p.act != a[0].act)) return hipErrorInvalidValue;
+    const int mt = p.offsets ? ffn_max_mtiles(p.E_loc, p.rows_max, BM) : (p.rows_max + BM - 1) / BM;
+    slots += ((long long)mt * (p.N / BNO) + 7) / 8;  // per-XCD slots of problem i
+    w.p[i] = p;
+  }
+  const long long g = 8 * slots;
   if (g == 0) return hipSuccess;
-  if (!GATEUP && a.out_f32) launch_gemm(wide_kernel<false, true, 0, BW>, dim3((unsigned)g), dim3(512), s, a);
-  else if (GATEUP && a.act == 1) launch_gemm(wide_kernel<GATEUP, false, 1, BW>, dim3((unsigned)g), dim3(512), s, a);
-  else launch_gemm(wide_kernel<GATEUP, false, 0, BW>, dim3((unsigned)g), dim3(512), s, a);
+  if (g > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  auto go = [&](auto kernel) {
+    if (ev_start || ev_stop)
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)g), dim3(512), 0, s, static_cast<hipEvent_t>(ev_start),
+                            static_cast<hipEvent_t>(ev_stop), 0, w);
+    else
+      kernel<<<dim3((unsigned)g), dim3(512), 0, s>>>(w);
+  };
+  if (!GATEUP && a[0].out_f32) go(wide_kernel<false, true, 0, BW>);
+  else if (GATEUP && a[0].act == 1) go(wide_kernel<GATEUP, false, 1, BW>);
+  else go(wide_kernel<GATEUP, false, 0, BW>);
   return hipGetLastError();
 }
 
-// bw: weight rows per tile (256 or 128)
+// bw: weight rows per tile (256 or 128); np problems of the same kind in one
+// launch (their tiles in the order given); the events, if any, are attached to
+// the launch
 template <bool GATEUP>
-hipError_t launch_wide(const FfnGemmArgs& a, int bw, hipStream_t s) {
+hipError_t launch_wide(const FfnGemmArgs* a, int np, int bw, void* ev_start, void* ev_stop, hipStream_t s) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
   // gate/up writes z in bf16 (the fp32 z of the INT4 path never comes here)
-  if (GATEUP && a.out_f32) return hipErrorInvalidValue;
-  if (bw == 256) return launch_bw<GATEUP, 256>(a, s);
-  if (bw == 128) return launch_bw<GATEUP, 128>(a, s);
+  if (GATEUP && a[0].out_f32) return hipErrorInvalidValue;
+  if (bw == 256) return launch_bw<GATEUP, 256>(a, np, ev_start, ev_stop, s);
+  if (bw == 128) return launch_bw<GATEUP, 128>(a, np, ev_start, ev_stop, s);
   return hipErrorInvalidValue;
 }
 

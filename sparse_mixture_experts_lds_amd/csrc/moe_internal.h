@@ -178,6 +178,11 @@ int ffn_max_mtiles(int E_loc, int rows_max, int BM);
 // split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
 hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,
                            int NF, hipStream_t s);
+// Two problems of the same kind (bf16 weights, wide 256-row tiles, 64 * NF
+// weight rows per tile, same activation and output type) in one launch, the
+// tiles of a0 dispatched first; the events, if any, time the launch.
+hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int NF,
+                                     void* ev_start, void* ev_stop, hipStream_t s);
 
 // Weighted combine.
 // y and shared_y are fp32 when y_f32, else in the output dtype.

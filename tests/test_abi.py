@@ -105,3 +105,46 @@ def test_empty_batch_layer_is_a_no_op(T):
     L = _desc(T=T)
     nb = lib.moe_layer_workspace_bytes(ctypes.byref(L))
     assert lib.moe_layer_fwd(ctypes.byref(L), None, None, None, None, None, nb, None) == _lib.MOE_OK
+
+
+def _plan(L):
+    lib = moe.load()
+    info = _lib.LayerPlanInfo()
+    rc = lib.moe_layer_plan(ctypes.byref(L), ctypes.byref(info))
+    return rc, {n: getattr(info, n) for n, _ in _lib.LayerPlanInfo._fields_}
+
+
+def _cfg_desc(name, **over):
+    from moe_synth import CONFIGS
+    c = CONFIGS[name]
+    f = dict(T=c.T, d=c.d, E=c.E, k=c.k, h=c.h, act=0 if c.act == "swiglu" else 1,
+             act_dtype=0 if c.dtype == "f32" else 1, w_dtype={"f32": 0, "bf16": 1, "i4g128": 2}[c.w_dtype],
+             E_loc=c.E, h_shared=c.h_shared)
+    f.update(over)
+    L = _desc(**f)
+    if L.h_shared:
+        L.ws_gate = L.ws_up = L.ws_down = 16
+    return L
+
+
+def test_layer_plan():
+    # granular: routed and shared GEMMs both on 256-row tiles, in shared launches
+    rc, p = _plan(_cfg_desc("granular_bf16"))
+    assert rc == _lib.MOE_OK
+    assert p == dict(tile_m=256, tile_n_up=128, tile_n_down=256, shared_tile_m=256, shared_in_routed_launches=1)
+    # narrow tiles asked for: the shared expert keeps its own launches
+    rc, p = _plan(_cfg_desc("granular_bf16", tile_m=128))
+    assert rc == _lib.MOE_OK and p["tile_m"] == 128 and p["shared_in_routed_launches"] == 0
+    # decode: a few rows per expert, narrow tiles, shared expert on its own
+    rc, p = _plan(_cfg_desc("decode_bf16"))
+    assert rc == _lib.MOE_OK and p["tile_m"] < 256 and p["shared_in_routed_launches"] == 0
+    # no shared expert
+    rc, p = _plan(_cfg_desc("granular_bf16", h_shared=0))
+    assert rc == _lib.MOE_OK and p["shared_tile_m"] == 0 and p["shared_in_routed_launches"] == 0
+    # fp32 layers never take the wide kernel
+    rc, p = _plan(_cfg_desc("tiny_fp32"))
+    assert rc == _lib.MOE_OK and p["tile_m"] <= 32 and p["shared_in_routed_launches"] == 0
+    # rejected as the workspace query rejects it; no output struct is an error
+    rc, _ = _plan(_desc(E_loc=4))
+    assert rc == _lib.MOE_EINVAL
+    assert moe.load().moe_layer_plan(ctypes.byref(_desc()), None) == _lib.MOE_EINVAL

@@ -72,6 +72,28 @@ def test_layer_wide_tiles(name, tiles):
     print(name, tiles, rep)
 
 
+# ------------------------------------------------------------------ shared expert in the routed launches
+PAIRED = {
+    # routed and shared GEMMs both on 256-row tiles in one launch each; some
+    # experts past 256 rows (two m-tiles); the routed down tiles are the deeper
+    "routed_deeper": scaled("granular_bf16", T=4096, d=256, E=64, h=512, h_shared=256),
+    # the shared expert's down tiles are the deeper and are dispatched first
+    "shared_deeper": scaled("granular_bf16", T=8192, d=256, E=128, h=256, h_shared=512),
+}
+
+
+@pytest.mark.parametrize("name", list(PAIRED))
+def test_layer_shared_in_routed_launches(name):
+    moe = _moe()
+    inp = make_inputs(PAIRED[name])
+    w = device_weights(inp)
+    plan = moe.layer_plan(w, inp.cfg.T, inp.cfg.d, 1)
+    assert plan["tile_m"] == 256 and plan["shared_in_routed_launches"] == 1, plan
+    rep = {}
+    check_layer(inp, wdev=w, report=rep)
+    print(name, rep)
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("T", [1, 17, 100])
 def test_ragged_and_single_token_batches(T):
