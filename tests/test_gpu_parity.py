@@ -163,12 +163,15 @@ def test_layer_is_deterministic():
 
 
 # ------------------------------------------------------------------ entry points one by one
-@pytest.mark.parametrize("E,k,dt", [(8, 2, torch.float32), (192, 4, torch.bfloat16), (896, 16, torch.bfloat16),
-                                    (33, 5, torch.bfloat16), (1024, 32, torch.bfloat16)])
-def test_route_entry_point(E, k, dt):
+# T >= 8161 (bf16): 32 tokens per workgroup, ragged last workgroup
+@pytest.mark.parametrize("E,k,dt,T", [(8, 2, torch.float32, 131), (192, 4, torch.bfloat16, 131),
+                                      (896, 16, torch.bfloat16, 131), (33, 5, torch.bfloat16, 131),
+                                      (1024, 32, torch.bfloat16, 131), (192, 4, torch.bfloat16, 8200),
+                                      (64, 1, torch.bfloat16, 9001), (256, 8, torch.bfloat16, 8199)])
+def test_route_entry_point(E, k, dt, T):
     moe = _moe()
     rng = np.random.default_rng(E + k)
-    T, d = 131, 128
+    d = 128
     x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dt)
     w = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(dt)
     b = torch.from_numpy(rng.standard_normal(E).astype(np.float32))
