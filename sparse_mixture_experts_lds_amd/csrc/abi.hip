@@ -305,7 +305,10 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   const size_t eb = elt_bytes(L->act_dtype);
   b->ids = c.take<int32_t>(P * 4);
   b->tw = c.take<float>(P * 4);
-  b->logits = c.take<float>(L->w_router ? (size_t)L->T * L->E * 4 : 0);  // router GEMM output
+  // router GEMM output: its partial arrays over input slices
+  b->logits = c.take<float>(L->w_router ? (size_t)router_logits_splits(L->T, L->d, L->E, L->act_dtype == MOE_BF16) *
+                                              L->T * L->E * 4
+                                        : 0);
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
   b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, 16) * sizeof(int4));
@@ -357,7 +360,9 @@ size_t carve_bwd(const moe_layer_desc* L, void* ws, BwdBufs* b) {
   const bool f32 = L->act_dtype == MOE_F32;
   b->ids = c.take<int32_t>(P * 4);
   b->tw = c.take<float>(P * 4);
-  b->Lraw = c.take<float>(L->w_router ? T * E * 4 : 0);
+  b->Lraw = c.take<float>(L->w_router ? (size_t)router_logits_splits(L->T, L->d, L->E, L->act_dtype == MOE_BF16) *
+                                            T * E * 4
+                                      : 0);
   b->Lw = c.take<float>(T * E * 4);
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
@@ -723,18 +728,22 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   auto routed = [&]() -> int {
     // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
     const float* lsrc = logits_in;
+    int nsplit = 1;
     if (!lsrc) {
-      float* lbuf = tr.logits ? tr.logits : b.logits;
-      MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, s));
+      nsplit = router_logits_splits(T, L->d, L->E, bf16);
+      float* lbuf = (tr.logits && nsplit == 1) ? tr.logits : b.logits;
+      MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, nsplit, s));
       lsrc = lbuf;
     }
-    MOE_HIP(launch_select(T, L->E, k, lsrc, L->expert_bias, L->renorm, ids, tw, tr.logits, s));
-    // router by-products; a trace logits buffer already holds the biased L
-    if (tr.expert_counts || tr.prob_mean || tr.balance_loss) {
-      const float* lstat = tr.logits ? tr.logits : lsrc;
-      MOE_HIP(launch_router_stats(T, L->E, k, lstat, tr.logits ? nullptr : L->expert_bias, ids, tr.expert_counts,
-                                  tr.prob_mean, tr.balance_loss, b.stats, s));
-    }
+    const bool want_stats = tr.expert_counts || tr.prob_mean || tr.balance_loss;
+    // the summed, biased logits go to the trace buffer, else (partial arrays)
+    // over the first partial array when the by-products read them
+    float* lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
+    MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
+    // router by-products
+    if (want_stats)
+      MOE_HIP(launch_router_stats(T, L->E, k, lout ? lout : lsrc, lout ? nullptr : L->expert_bias, ids,
+                                  tr.expert_counts, tr.prob_mean, tr.balance_loss, b.stats, s));
     MOE_HIP(mark(MOE_EV_ROUTED));
     // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
     MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
@@ -819,11 +828,13 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
 
   // 1. routing, as the forward: logits (GEMM or given) + bias, selection, grouping
   const float* lsrc = logits_in;
+  int nsplit = 1;
   if (!lsrc) {
-    MOE_HIP(launch_router_logits(T, d, E, bf, x, L->w_router, b.Lraw, s));
+    nsplit = router_logits_splits(T, d, E, bf);
+    MOE_HIP(launch_router_logits(T, d, E, bf, x, L->w_router, b.Lraw, nsplit, s));
     lsrc = b.Lraw;
   }
-  MOE_HIP(launch_select(T, E, k, lsrc, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
+  MOE_HIP(launch_select(T, E, k, lsrc, nsplit, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
   MOE_HIP(launch_permute(T, k, E, b.ids, L->expert_map, E_loc, L->capacity, BMb, b.offsets, b.mtile, b.tiles,
                          b.sorted_pair, b.pair_pos, b.counts, s));
   // the fp32 grouped GEMM of the forward takes at most 32-row tiles

@@ -95,13 +95,20 @@ __device__ __forceinline__ float group_sum(float x) {
 hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                         const float* logits_in, const float* bias, int renorm, int32_t* ids,
                         float* tw, float* logits_out, hipStream_t s);
-// Router logits without bias: L[t,e] = sum_i x[t,i] w[e,i], fp32 [T, E].
-hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits,
-                                hipStream_t s);
-// Softmax + top-k from logits rows src[T, E] plus bias; logits_out (may alias
-// src or be NULL) receives src + bias.
-hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
-                         float* tw, float* logits_out, hipStream_t s);
+// Router logits without bias, L[t,e] = sum_i x[t,i] w[e,i] in fp32, written
+// as nsplit partial sums over consecutive input slices: part[s][t][e], [nsplit,
+// T, E] (nsplit 1: the logits themselves).  router_logits_splits picks nsplit
+// (1 .. kMaxRouterSplits) for the shape.
+constexpr int kMaxRouterSplits = 8;
+int router_logits_splits(int T, int d, int E, bool bf16);
+hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* part,
+                                int nsplit, hipStream_t s);
+// Softmax + top-k from logits given as nsplit partial arrays src[s][T][E]
+// (added in ascending s) plus bias; logits_out (NULL, or aliasing the first
+// partial array: every element is read and written by the same lane) receives
+// the sum + bias.
+hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
+                         int32_t* ids, float* tw, float* logits_out, hipStream_t s);
 
 // Router by-products: per-expert token counts, mean softmax probabilities and
 // the balance loss from logits (+ bias) and top-k ids; ws holds

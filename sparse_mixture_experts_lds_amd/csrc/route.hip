@@ -17,7 +17,10 @@
 // pick the experts.  When the activations are bf16 and E is a multiple of 64
 // the logits of a whole layer come from the grouped GEMM kernel (one group,
 // fp32 output) instead, which reuses each router weight slice across 16-64
-// tokens per workgroup rather than 16.
+// tokens per workgroup rather than 16.  Few tokens with long rows (decode)
+// leave most CUs idle on either kernel; there the logits kernel splits the
+// inputs into slices, each workgroup sums one slice into its own partial
+// array, and the select kernel adds the partials in ascending slice order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -80,9 +83,11 @@ __device__ __forceinline__ void select_token(const float (&v)[NF], int E, int k,
 }
 
 // SELECT false: only the logits (without bias) are written, to logits_out.
+// Without SELECT the inputs are split into gridDim.y slices of kspan: slice s
+// = blockIdx.y sums inputs [s kspan, (s+1) kspan) into logits_out + s T E.
 template <int NF, bool BF16, bool SELECT>
-__global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, const void* __restrict__ xv,
-                                                    const void* __restrict__ wv,
+__global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, int kspan,
+                                                    const void* __restrict__ xv, const void* __restrict__ wv,
                                                     const float* __restrict__ bias, int renorm,
                                                     int32_t* __restrict__ ids, float* __restrict__ tw,
                                                     float* __restrict__ logits_out) {
@@ -91,6 +96,9 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kTokTile;
+  const int kbeg = blockIdx.y * kspan;
+  const int kend = kbeg + kspan;
+  if (!SELECT && logits_out) logits_out += (size_t)blockIdx.y * T * E;
 
   {
     const int row = lane & 15;  // A row (token) / B column (expert) inside a fragment
@@ -115,8 +123,8 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
         e_ok[i] = e < E;
         wrow[i] = w + (size_t)(e_ok[i] ? e : 0) * d + 8 * q;
       }
-      for (int k0 = 0; k0 < d; k0 += 32 * KC) {
-        const int nk = min(KC, (d - k0) / 32);
+      for (int k0 = kbeg; k0 < kend; k0 += 32 * KC) {
+        const int nk = min(KC, (kend - k0) / 32);
         u32x4 av[KC], bv[KC][NF];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
@@ -149,8 +157,8 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
         e_ok[i] = e < E;
         wrow[i] = w + (size_t)(e_ok[i] ? e : 0) * d + q;
       }
-      for (int k0 = 0; k0 < d; k0 += 4 * KC) {
-        const int nk = min(KC, (d - k0) / 4);
+      for (int k0 = kbeg; k0 < kend; k0 += 4 * KC) {
+        const int nk = min(KC, (kend - k0) / 4);
         float av[KC], bv[KC][NF];
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
@@ -229,8 +237,11 @@ __device__ __forceinline__ void group_argmax(float& v, int& e) {  // larger valu
 // written back with the bias added (logits_out may alias src).  Lane g of the
 // group holds experts g + G*i in v[i]; k rounds of a group arg-max pick the
 // experts, lane j of the group keeps the j-th pick.
-template <int G, int NV>
-__global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const float* src,
+// SPLIT: the logits come as nsplit (2 .. kMaxRouterSplits) partial arrays;
+// every partial is loaded before the first addition (the loads overlap), then
+// they are added in ascending slice order.
+template <int G, int NV, bool SPLIT>
+__global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const float* src, int nsplit,
                                                      const float* __restrict__ bias, int renorm,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
                                                      float* logits_out) {
@@ -239,11 +250,36 @@ __global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const 
   if (t >= T) return;  // whole groups leave together
   const float* row = src + (size_t)t * E;
   float v[NV];
+  if constexpr (SPLIT) {
+    const size_t split_stride = (size_t)T * E;
+    float part[kMaxRouterSplits][NV];
+#pragma unroll
+    for (int sl = 0; sl < kMaxRouterSplits; ++sl)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = gl + G * i;
+        part[sl][i] = sl < nsplit ? row[sl * split_stride + (e < E ? e : E - 1)] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float l = part[0][i];
+#pragma unroll
+      for (int sl = 1; sl < kMaxRouterSplits; ++sl)
+        if (sl < nsplit) l += part[sl][i];
+      v[i] = l;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = gl + G * i;
+      v[i] = row[e < E ? e : E - 1];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = gl + G * i;
     const int ec = e < E ? e : E - 1;
-    const float x = row[ec] + (bias ? bias[ec] : 0.f);
+    const float x = v[i] + (bias ? bias[ec] : 0.f);
     v[i] = e < E ? x : -INFINITY;
   }
   if (logits_out) {
@@ -297,30 +333,38 @@ template <int NF>
 hipError_t launch_nf(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                      const float* logits_in, const float* bias, int renorm, int32_t* ids, float* tw,
                      float* logits_out, hipStream_t s) {
-  if (logits_in != nullptr) return launch_select(T, E, k, logits_in, bias, renorm, ids, tw, logits_out, s);
+  if (logits_in != nullptr) return launch_select(T, E, k, logits_in, 1, bias, renorm, ids, tw, logits_out, s);
   const dim3 grid((T + kTokTile - 1) / kTokTile);
   if (bf16)
-    route_kernel<NF, true, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out);
+    route_kernel<NF, true, true><<<grid, 256, 0, s>>>(T, d, E, k, d, x, wr, bias, renorm, ids, tw, logits_out);
   else
-    route_kernel<NF, false, true><<<grid, 256, 0, s>>>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out);
+    route_kernel<NF, false, true><<<grid, 256, 0, s>>>(T, d, E, k, d, x, wr, bias, renorm, ids, tw, logits_out);
   return hipGetLastError();
 }
 
 template <int NF>
-hipError_t logits_nf(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits, hipStream_t s) {
-  const dim3 grid((T + kTokTile - 1) / kTokTile);
+hipError_t logits_nf(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits, int nsplit,
+                     hipStream_t s) {
+  const dim3 grid((T + kTokTile - 1) / kTokTile, nsplit);
+  const int kspan = d / nsplit;
   if (bf16)
-    route_kernel<NF, true, false><<<grid, 256, 0, s>>>(T, d, E, 1, x, wr, nullptr, 0, nullptr, nullptr, logits);
+    route_kernel<NF, true, false><<<grid, 256, 0, s>>>(T, d, E, 1, kspan, x, wr, nullptr, 0, nullptr, nullptr,
+                                                        logits);
   else
-    route_kernel<NF, false, false><<<grid, 256, 0, s>>>(T, d, E, 1, x, wr, nullptr, 0, nullptr, nullptr, logits);
+    route_kernel<NF, false, false><<<grid, 256, 0, s>>>(T, d, E, 1, kspan, x, wr, nullptr, 0, nullptr, nullptr,
+                                                         logits);
   return hipGetLastError();
 }
 
 template <int G, int NV>
-hipError_t select_gn(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
-                     float* tw, float* logits_out, hipStream_t s) {
+hipError_t select_gn(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
+                     int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
   constexpr int TPB = 256 / G;  // tokens per workgroup
-  select_kernel<G, NV><<<dim3((T + TPB - 1) / TPB), 256, 0, s>>>(T, E, k, src, bias, renorm, ids, tw, logits_out);
+  const dim3 grid((T + TPB - 1) / TPB);
+  if (nsplit > 1)
+    select_kernel<G, NV, true><<<grid, 256, 0, s>>>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out);
+  else
+    select_kernel<G, NV, false><<<grid, 256, 0, s>>>(T, E, k, src, 1, bias, renorm, ids, tw, logits_out);
   return hipGetLastError();
 }
 
@@ -347,9 +391,34 @@ int router_logits_tile_m(int T, int E) {
   return 16;
 }
 
+int router_logits_splits(int T, int d, int E, bool bf16) {
+  // workgroups without a split: the grouped GEMM's tiles, else 16-token tiles
+  const long long tiles16 = ((long long)T + kTokTile - 1) / kTokTile;
+  const long long wgs = (bf16 && E % 64 == 0) ? ((long long)T + router_logits_tile_m(T, E) - 1) /
+                                                    router_logits_tile_m(T, E) * (E / 64)
+                                              : tiles16;
+  if (T == 0 || wgs >= 256) return 1;
+  // few tokens and long rows: split the inputs until 16-token tiles fill the
+  // CUs, keeping every slice a multiple of 32 inputs and at least 256 long
+  int ns = 1;
+  while (ns < kMaxRouterSplits && tiles16 * ns < 256 && d % (64 * ns) == 0 && d / (2 * ns) >= 256) ns *= 2;
+  return ns;
+}
+
 hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* logits,
-                                hipStream_t s) {
+                                int nsplit, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (nsplit < 1 || d % nsplit || (d / nsplit) % (bf16 ? 32 : 4)) return hipErrorInvalidValue;
+  if (nsplit > 1) {
+    const int nf = (E + 63) / 64;
+#define MOE_CALL(NFv) logits_nf<NFv>(T, d, E, bf16, x, wr, logits, nsplit, s)
+    if (nf <= 1) return MOE_CALL(1);
+    if (nf <= 2) return MOE_CALL(2);
+    if (nf <= 4) return MOE_CALL(4);
+    if (nf <= 8) return MOE_CALL(8);
+    return MOE_CALL(16);
+#undef MOE_CALL
+  }
   if (bf16 && E % 64 == 0) {
     FfnGemmArgs g{};
     g.A = x;
@@ -365,7 +434,7 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
     return launch_ffn_gemm(g, false, W_BF16, false, router_logits_tile_m(T, E), 1, s);
   }
   const int nf = (E + 63) / 64;
-#define MOE_CALL(NFv) logits_nf<NFv>(T, d, E, bf16, x, wr, logits, s)
+#define MOE_CALL(NFv) logits_nf<NFv>(T, d, E, bf16, x, wr, logits, 1, s)
   if (nf <= 1) return MOE_CALL(1);
   if (nf <= 2) return MOE_CALL(2);
   if (nf <= 4) return MOE_CALL(4);
@@ -374,14 +443,15 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
 #undef MOE_CALL
 }
 
-hipError_t launch_select(int T, int E, int k, const float* src, const float* bias, int renorm, int32_t* ids,
-                         float* tw, float* logits_out, hipStream_t s) {
+hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
+                         int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (nsplit < 1 || nsplit > kMaxRouterSplits) return hipErrorInvalidValue;
   // 16 lanes per token while a lane holds at most 16 logits and the k picks fit
   // in the group; the whole wave otherwise
   if (E <= 256 && k <= 16) {
     const int nv = (E + 15) / 16;
-#define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
+#define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, s)
     if (nv <= 2) return MOE_CALL(2);
     if (nv <= 4) return MOE_CALL(4);
     if (nv <= 8) return MOE_CALL(8);
@@ -389,7 +459,7 @@ hipError_t launch_select(int T, int E, int k, const float* src, const float* bia
 #undef MOE_CALL
   }
   const int nv = (E + 63) / 64;
-#define MOE_CALL(NVv) select_gn<64, NVv>(T, E, k, src, bias, renorm, ids, tw, logits_out, s)
+#define MOE_CALL(NVv) select_gn<64, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, s)
   if (nv <= 1) return MOE_CALL(1);
   if (nv <= 2) return MOE_CALL(2);
   if (nv <= 4) return MOE_CALL(4);
