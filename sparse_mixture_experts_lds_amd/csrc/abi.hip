@@ -342,6 +342,20 @@ inline int bwd_bm(const moe_layer_desc* L, bool bf16) {
 
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
+// Weight rows per tile (64 * NF) of the wide recompute of g and u for hidden
+// width h (N = h), or 0 when the wide kernel does not take it.
+inline int wide_rc_nf(bool bf16, int d, int h) {
+  if (!bf16 || d % 64) return 0;
+  return h % 256 == 0 ? 4 : (h % 128 == 0 ? 2 : 0);
+}
+
+// The backward recomputes the routed g and u on the wide kernel when the
+// forward's routed gate/up runs on it (bf16 weights).
+inline bool bwd_wide_rc(const moe_layer_desc* L) {
+  return L->act_dtype == MOE_BF16 && L->w_dtype == MOE_BF16 && layer_plan(L, layer_rows_max(L)).BM == 256 &&
+         wide_rc_nf(true, L->d, L->h) > 0;
+}
+
 // Row slices of a single-group weight gradient: enough workgroups to fill the
 // chip, at least 256 rows per slice.
 int tn_slices(int rows, int M, int N) {
@@ -367,8 +381,11 @@ size_t carve_bwd(const moe_layer_desc* L, void* ws, BwdBufs* b) {
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
   b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, kBwdBM) * sizeof(int4));
-  b->mtile_rc = c.take<int32_t>(f32 ? (L->E_loc + 1) * 4 : 0);
-  b->tiles_rc = c.take<int4>(f32 ? (size_t)ffn_max_mtiles(L->E_loc, (int)rows, 32) * sizeof(int4) : 0);
+  // m-tiles of the recompute of g and u when they differ from the backward's own
+  // (fp32: at most 32 rows; wide bf16: 256 rows)
+  const bool own_rc = f32 || bwd_wide_rc(L);
+  b->mtile_rc = c.take<int32_t>(own_rc ? (L->E_loc + 1) * 4 : 0);
+  b->tiles_rc = c.take<int4>(own_rc ? (size_t)ffn_max_mtiles(L->E_loc, (int)rows, f32 ? 32 : 256) * sizeof(int4) : 0);
   b->sorted_pair = c.take<int32_t>(P * 4);
   b->pair_pos = c.take<int32_t>(P * 4);
   b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
@@ -445,6 +462,9 @@ int tn_single(bool bf, const void* A, int lda, const void* B, int ldb, int T, in
 }
 
 // Gate/up pre-activations of one expert set, fp32 [rows, h] each.
+// g = a Wg^T and u = a Wu^T in fp32, as the forward's gate/up GEMM forms them
+// before the activation.  BM 256: both in one launch of the wide kernel (two
+// problems); else two launches of the narrow kernel.
 int recompute_gu(int wt, bool grouped, const void* x, int T, int k, const int32_t* sorted_pair,
                  const int32_t* offsets, const int32_t* mtile, const int4* tiles, int E_loc, int rows, int d, int h,
                  int BM, const void* wg, const void* wu, float* G, float* U, hipStream_t s) {
@@ -462,6 +482,17 @@ int recompute_gu(int wt, bool grouped, const void* x, int T, int k, const int32_
   g.a_rows = T;
   g.slot_div = 1;
   g.out_f32 = 1;
+  if (BM == 256) {
+    const int nfw = wide_rc_nf(wt == W_BF16, d, h);
+    if (!nfw) return MOE_EUNSUPPORTED;
+    FfnGemmArgs u = g;
+    g.W0 = wg;
+    g.out = G;
+    u.W0 = wu;
+    u.out = U;
+    MOE_HIP(launch_ffn_gemm_wide_pair(g, u, false, nfw, nullptr, nullptr, s));
+    return MOE_OK;
+  }
   const int NF = (wt == W_BF16 && h % 128 == 0) ? 2 : 1;
   g.W0 = wg;
   g.out = G;
@@ -837,13 +868,16 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   MOE_HIP(launch_select(T, E, k, lsrc, nsplit, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
   MOE_HIP(launch_permute(T, k, E, b.ids, L->expert_map, E_loc, L->capacity, BMb, b.offsets, b.mtile, b.tiles,
                          b.sorted_pair, b.pair_pos, b.counts, s));
-  // the fp32 grouped GEMM of the forward takes at most 32-row tiles
-  const int BMrc = bf ? BMb : 32;
-  if (!bf) MOE_HIP(launch_mtile_prefix(E_loc, 32, b.offsets, b.mtile_rc, b.tiles_rc, s));
+  // the fp32 grouped GEMM of the forward takes at most 32-row tiles; the wide
+  // recompute takes 256-row tiles
+  const bool wide_rc = bwd_wide_rc(L);
+  const int BMrc = !bf ? 32 : (wide_rc ? 256 : BMb);
+  const bool own_rc = !bf || wide_rc;
+  if (own_rc) MOE_HIP(launch_mtile_prefix(E_loc, BMrc, b.offsets, b.mtile_rc, b.tiles_rc, s));
 
   // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients
-  if ((rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, bf ? b.mtile : b.mtile_rc,
-                         bf ? b.tiles : b.tiles_rc, E_loc, rows, d, h, BMrc, L->w_gate, L->w_up, b.G, b.U, s)))
+  if ((rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, own_rc ? b.mtile_rc : b.mtile,
+                         own_rc ? b.tiles_rc : b.tiles, E_loc, rows, d, h, BMrc, L->w_gate, L->w_up, b.G, b.U, s)))
     return rc;
   bwdg::NnArgs n{};
   n.A = dout;
@@ -928,7 +962,9 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   // 3. shared expert on every token (gate 1)
   if (hs > 0) {
     const int swt = wtype_of(L->act_dtype);
-    if ((rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMrc, L->ws_gate,
+    // the forward's shared plan: wide tiles take it to the wide kernel here too
+    const int BMsr = (shared_plan(T, d, hs, swt).BM == 256 && wide_rc_nf(bf, d, hs)) ? 256 : (bf ? BMb : 32);
+    if ((rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMsr, L->ws_gate,
                            L->ws_up, b.Gs, b.Us, s)))
       return rc;
     const int BMs = (bf && T >= 4096) ? 128 : 64;

@@ -37,6 +37,8 @@ BWD = {
                          owners=4),
     "fp32_geglu_bias": scaled("tiny_fp32", T=100, E=12, k=3, act="geglu", zipf_bias=0.7, h_shared=64,
                               renorm=False),
+    # routed and shared g, u recomputed on the wide 256-row tiles
+    "wide_recompute": scaled("granular_bf16", T=4096, d=256, E=64, h=512, h_shared=256),
 }
 
 
