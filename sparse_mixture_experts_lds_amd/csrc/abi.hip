@@ -875,6 +875,21 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const bool own_rc = !bf || wide_rc;
   if (own_rc) MOE_HIP(launch_mtile_prefix(E_loc, BMrc, b.offsets, b.mtile_rc, b.tiles_rc, s));
 
+  // The routed experts' data and weight gradient GEMMs take the wide 256 x 256
+  // tiles where the forward's gate/up does (its recompute built the 256-row
+  // m-tile table), else the 128-wide kernels.
+  auto run_nn = [&](bwdg::NnArgs a) -> hipError_t {
+    if (wide_rc && bwd_nn_wide_ok(a)) {
+      a.mtile_start = b.mtile_rc;
+      a.tile_tab = b.tiles_rc;
+      return launch_bwd_nn_wide(a, s);
+    }
+    return launch_bwd_nn(bf, a, BMb, grid_m, s);
+  };
+  auto run_tn = [&](const bwdg::TnArgs& a) -> hipError_t {
+    return (wide_rc && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
+  };
+
   // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients
   if ((rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, own_rc ? b.mtile_rc : b.mtile,
                          own_rc ? b.tiles_rc : b.tiles, E_loc, rows, d, h, BMrc, L->w_gate, L->w_up, b.G, b.U, s)))
@@ -897,7 +912,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   n.rows = rows;
   n.N = h;
   n.K = d;
-  MOE_HIP(launch_bwd_nn(bf, n, BMb, grid_m, s));
+  MOE_HIP(run_nn(n));
   MOE_HIP(launch_gate_bwd(bf, L->act, rows, h, b.offsets + E_loc, b.G, b.U, b.dZ, b.sorted_pair, b.tw, b.dGU, b.ZW,
                           b.dgate, s));
   if (gr->dw_down) {
@@ -917,7 +932,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     t.M = d;
     t.N = h;
     t.mtiles = (d + bwdg::kTnTile - 1) / bwdg::kTnTile;
-    MOE_HIP(launch_bwd_tn(bf, t, E_loc, s));
+    MOE_HIP(run_tn(t));
   }
   if (gr->dw_gate) {
     bwdg::TnArgs t{};
@@ -937,7 +952,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     t.M = 2 * h;
     t.N = d;
     t.mtiles = (2 * h + bwdg::kTnTile - 1) / bwdg::kTnTile;
-    MOE_HIP(launch_bwd_tn(bf, t, E_loc, s));
+    MOE_HIP(run_tn(t));
   }
   n = bwdg::NnArgs{};
   n.A = b.dGU;
@@ -957,7 +972,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   n.rows = rows;
   n.N = d;
   n.K = 2 * h;
-  MOE_HIP(launch_bwd_nn(bf, n, BMb, grid_m, s));
+  MOE_HIP(run_nn(n));
 
   // 3. shared expert on every token (gate 1)
   if (hs > 0) {
@@ -969,6 +984,12 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
       return rc;
     const int BMs = (bf && T >= 4096) ? 128 : 64;
     const int gm = (T + BMs - 1) / BMs;
+    // the shared expert's rows are one dense group: wide tiles from as many
+    // tokens as the forward gives it wide tiles
+    auto run_nn_shared = [&](const bwdg::NnArgs& a) -> hipError_t {
+      return (bf && T >= kSharedWideMinRows && bwd_nn_wide_ok(a)) ? launch_bwd_nn_wide(a, s)
+                                                                  : launch_bwd_nn(bf, a, BMs, gm, s);
+    };
     n = bwdg::NnArgs{};
     n.A = dout;
     n.lda = d;
@@ -982,7 +1003,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     n.rows = T;
     n.N = hs;
     n.K = d;
-    MOE_HIP(launch_bwd_nn(bf, n, BMs, gm, s));
+    MOE_HIP(run_nn_shared(n));
     MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs, nullptr,
                             s));
     if (gr->dws_down && (rc = tn_single(bf, dout, d, b.ZWs, hs, T, d, hs, d, gr->dws_down, gr->dws_down, hs, b.part,
@@ -1005,7 +1026,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     n.rows = T;
     n.N = d;
     n.K = 2 * hs;
-    MOE_HIP(launch_bwd_nn(bf, n, BMs, gm, s));
+    MOE_HIP(run_nn_shared(n));
   }
 
   // 4. gates, softmax and balance loss back to the logits; router GEMMs

@@ -58,6 +58,13 @@ constexpr int kNnBN = 128;    // nn tiles are BM x 128
 hipError_t launch_bwd_nn(bool bf16, const bwdg::NnArgs& a, int BM, int grid_m, hipStream_t s);
 // grid_z: groups (with offsets) or row slices
 hipError_t launch_bwd_tn(bool bf16, const bwdg::TnArgs& a, int grid_z, hipStream_t s);
+// The same two GEMMs on 256 x 256 tiles (bf16 operands only; ok tells whether
+// the shapes fit: N a multiple of 256, K of 64 and K1 of 32 for nn; M, N and
+// M1 multiples of 256 for tn).  The nn tile table, if any, is for 256-row tiles.
+bool bwd_nn_wide_ok(const bwdg::NnArgs& a);
+hipError_t launch_bwd_nn_wide(const bwdg::NnArgs& a, hipStream_t s);
+bool bwd_tn_wide_ok(const bwdg::TnArgs& a);
+hipError_t launch_bwd_tn_wide(const bwdg::TnArgs& a, int grid_z, hipStream_t s);
 // Per grouped row: dgate (pair gradient), dGU = [dg | du], ZW = w * z.
 hipError_t launch_gate_bwd(bool bf16, int act, int rows, int h, const int32_t* n_rows, const float* G,
                            const float* U, const float* dZ, const int32_t* sorted_pair, const float* tw,

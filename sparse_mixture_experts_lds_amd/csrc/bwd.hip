@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "bwd_gemm.h"
+#include "bwd_wide.h"
 
 namespace moe {
 namespace {
@@ -279,6 +280,34 @@ hipError_t launch_bwd_nn(bool bf16, const bwdg::NnArgs& a, int BM, int grid_m, h
   } else {
     bwdg::nn_kernel<float, 64><<<grid, bwdg::NTH, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+bool bwd_nn_wide_ok(const bwdg::NnArgs& a) {
+  return a.N % bwdw::BT == 0 && a.K % (2 * bwdw::KB) == 0 && a.K1 % bwdw::KB == 0 && a.K_valid > 0;
+}
+
+hipError_t launch_bwd_nn_wide(const bwdg::NnArgs& a, hipStream_t s) {
+  if (!bwd_nn_wide_ok(a)) return hipErrorInvalidValue;
+  const long long mt = a.tile_tab ? ffn_max_mtiles(a.groups, a.rows, bwdw::BT) : (a.rows + bwdw::BT - 1) / bwdw::BT;
+  const long long g = (mt * (a.N / bwdw::BT) + 7) / 8 * 8;
+  if (g == 0) return hipSuccess;
+  if (g > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  bwdw::wide_nn_kernel<<<dim3((unsigned)g), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+bool bwd_tn_wide_ok(const bwdg::TnArgs& a) {
+  return a.M % bwdw::BT == 0 && a.N % bwdw::BT == 0 && (a.M1 % bwdw::BT == 0 || a.M1 >= a.M);
+}
+
+hipError_t launch_bwd_tn_wide(const bwdg::TnArgs& a, int grid_z, hipStream_t s) {
+  if (!bwd_tn_wide_ok(a)) return hipErrorInvalidValue;
+  if (grid_z <= 0) return hipSuccess;
+  const long long total = (long long)grid_z * (a.M / bwdw::BT) * (a.N / bwdw::BT);
+  const long long g = (total + 7) / 8 * 8;
+  if (g > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  bwdw::wide_tn_kernel<<<dim3((unsigned)g), 512, 0, s>>>(a, grid_z);
   return hipGetLastError();
 }
 

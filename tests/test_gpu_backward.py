@@ -37,8 +37,13 @@ BWD = {
                          owners=4),
     "fp32_geglu_bias": scaled("tiny_fp32", T=100, E=12, k=3, act="geglu", zipf_bias=0.7, h_shared=64,
                               renorm=False),
-    # routed and shared g, u recomputed on the wide 256-row tiles
+    # routed and shared g, u recomputed, and the data and weight gradient GEMMs
+    # run, on the wide 256 x 256 tiles
     "wide_recompute": scaled("granular_bf16", T=4096, d=256, E=64, h=512, h_shared=256),
+    # the same tiles with skewed routing: experts from several 256-row tiles to
+    # none (their weight gradients are zero)
+    "wide_skewed": scaled("granular_bf16", T=4096, d=256, E=64, h=512, h_shared=0, capacity_factor=None,
+                          zipf_bias=1.5),
 }
 
 
