@@ -875,9 +875,12 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   const bool own_rc = !bf || wide_rc;
   if (own_rc) MOE_HIP(launch_mtile_prefix(E_loc, BMrc, b.offsets, b.mtile_rc, b.tiles_rc, s));
 
-  // The routed experts' data and weight gradient GEMMs take the wide 256 x 256
-  // tiles where the forward's gate/up does (its recompute built the 256-row
-  // m-tile table), else the 128-wide kernels.
+  // The routed experts' data gradient GEMMs take the wide 256 x 256 tiles where
+  // the forward's gate/up does (its recompute built the 256-row m-tile table);
+  // their weight gradient GEMMs take them whenever the shapes fit (bf16): a
+  // tile's contraction runs over its expert's rows however few, and the wide
+  // tile stores its fp32 gradient as 16-byte row chunks (decode: 1.77 against
+  // 1.92 ms per backward).  Else the 128-wide kernels.
   auto run_nn = [&](bwdg::NnArgs a) -> hipError_t {
     if (wide_rc && bwd_nn_wide_ok(a)) {
       a.mtile_start = b.mtile_rc;
@@ -887,7 +890,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     return launch_bwd_nn(bf, a, BMb, grid_m, s);
   };
   auto run_tn = [&](const bwdg::TnArgs& a) -> hipError_t {
-    return (wide_rc && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
+    return (bf && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
   };
 
   // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients
