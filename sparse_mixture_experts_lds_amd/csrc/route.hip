@@ -583,6 +583,7 @@ hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, cons
     if (nv <= 2) return MOE_CALL(2);
     if (nv <= 4) return MOE_CALL(4);
     if (nv <= 8) return MOE_CALL(8);
+    if (nv <= 12) return MOE_CALL(12);
     return MOE_CALL(16);
 #undef MOE_CALL
   }

@@ -148,3 +148,16 @@ def test_layer_plan():
     rc, _ = _plan(_desc(E_loc=4))
     assert rc == _lib.MOE_EINVAL
     assert moe.load().moe_layer_plan(ctypes.byref(_desc()), None) == _lib.MOE_EINVAL
+
+
+def test_layer_workspace_covers_router_slices():
+    # 512 tokens x 3072 inputs x 128 experts: the router splits its inputs into
+    # 8 slices whose partial logits the workspace holds next to the rest
+    lib = moe.load()
+    L = _cfg_desc("decode_bf16")
+    nb = lib.moe_layer_workspace_bytes(ctypes.byref(L))
+    assert nb >= 8 * 512 * 128 * 4
+    # without a router (logits given) no logits buffer is needed at all
+    L2 = _cfg_desc("decode_bf16")
+    L2.w_router = None
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(L2)) <= nb - 8 * 512 * 128 * 4
