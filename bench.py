@@ -238,9 +238,11 @@ def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
 def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
     """Layer backward on this batch (outside the timed forward step; not for
     INT4 weights): average time of one moe_layer_bwd with preallocated
-    gradients and workspace, and its rate on the algorithmic FLOPs of its
-    GEMMs: per kept pair 16 d h (gate/up again, dz = dy Wd, dWd, dWg and dWu,
-    dx), the shared expert 16 T d h_s, the router 6 T d E."""
+    gradients and workspace, and its roofline on the algorithmic FLOPs of its
+    GEMMs (per kept pair 16 d h: gate/up again, dz = dy Wd, dWd, dWg and dWu,
+    dx; the shared expert 16 T d h_s; the router 6 T d E) and algorithmic bytes
+    (inputs and weights read once, dx and the fp32 weight gradients written
+    once)."""
     if cfg.w_dtype == "i4g128":
         return None
     g0 = torch.Generator(device=x.device)
@@ -261,11 +263,21 @@ def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
     flops = 16.0 * work["P"] * cfg.d * cfg.h + 16.0 * cfg.T * cfg.d * cfg.h_shared
     if cfg.has_router:
         flops += 6.0 * cfg.T * cfg.d * cfg.E
+    # algorithmic bytes: x and dout read once, the touched experts', shared and
+    # router weights read once, dx written once, every weight gradient written
+    # once in fp32
+    ab = 4 if cfg.dtype == "f32" else 2
+    wb = 4 if cfg.w_dtype == "f32" else 2
+    nw = 3 * work["touched"] * cfg.h * cfg.d + 3 * cfg.h_shared * cfg.d + (cfg.E * cfg.d if cfg.has_router else 0)
+    nbytes = 3 * cfg.T * cfg.d * ab + 3 * work["touched"] * cfg.h * cfg.d * wb + 3 * cfg.h_shared * cfg.d * ab
+    nbytes += (cfg.E * cfg.d * ab if cfg.has_router else 0) + 4 * nw
     peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
     tf = flops / (ms * 1e-3) / 1e12
-    return {"kernel": "layer backward (recomputed routing and gate/up, dgrad and wgrad GEMMs, router)",
-            "ms": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "flops": flops,
-            "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": peak, "frac": round(tf / peak, 4)}
+    rec = {"kernel": "layer backward (recomputed routing and gate/up, dgrad and wgrad GEMMs, router)",
+           "ms": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "flops": flops, "bytes": nbytes,
+           "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": peak}
+    rec["roofline"] = roofline_entry({"flops": flops, "bytes": nbytes}, ms, peak)
+    return rec
 
 
 def main(argv=None):
