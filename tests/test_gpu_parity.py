@@ -38,6 +38,10 @@ SCALED = {
     # 2304 tokens: the shared expert takes the wide 256-row tiles and is
     # forked after the grouping step; every output is compared
     "shared_wide": scaled("granular_bf16", T=2304, d=256, E=16, h=128, h_shared=256),
+    # decode-like: ~30 rows per expert against many weight rows, one with
+    # GeGLU and a ragged batch; every output compared
+    "stream_swiglu": scaled("decode_bf16", T=512, d=256, E=64, k=4, h=1024, h_shared=256),
+    "stream_geglu_ragged": scaled("decode_bf16", T=300, d=512, E=64, k=6, h=512, act="geglu", h_shared=0),
 }
 
 
