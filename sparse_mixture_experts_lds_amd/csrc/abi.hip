@@ -122,12 +122,15 @@ FfnGemmArgs down_args(const FfnGemmArgs& gu, const void* wd, const void* sd, voi
 }
 
 // Gate/up then down over grouped rows; `offsets` NULL means one group.
+// With plan.BM_down set, the down GEMM takes its own tile height and m-tile
+// tables (mtile_dn, tiles_dn, for grouped rows).
 int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const void* A, int a_rows,
             const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
             const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
-            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr) {
+            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr,
+            const int32_t* mtile_dn = nullptr, const int4* tiles_dn = nullptr) {
   const int wt = wtype_of(w_dtype);
   FfnGemmArgs g = gate_up_args(E_loc, rows_max, d, h, act, A, a_rows, row_index, row_div, offsets, mtile,
                                tile_tab, plan, wg, wu, sg, su, z);
@@ -141,7 +144,16 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   FfnGemmArgs dn = down_args(g, wd, sd, y, y_f32);
   dn.ev_start = kernel_events ? kernel_events[2] : nullptr;
   dn.ev_stop = kernel_events ? kernel_events[3] : nullptr;
-  MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BM, plan.NF_down, s));
+  int BMd = BM;
+  if (plan.BM_down && plan.BM_down != BM) {
+    BMd = plan.BM_down;
+    if (offsets) {
+      if (!mtile_dn || !tiles_dn) return MOE_EINVAL;
+      dn.mtile_start = mtile_dn;
+      dn.tile_tab = tiles_dn;
+    }
+  }
+  MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BMd, plan.NF_down, s));
   return MOE_OK;
 }
 
@@ -282,8 +294,10 @@ FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
     if (L->tile_n_down) w.NF_down = L->tile_n_down / 64;
     return w;
   }
-  // narrow tiles: the hinted sizes, the planner's choice for the rest
+  // narrow tiles: the hinted sizes, the planner's choice for the rest (one
+  // tile height for both GEMMs)
   if (p.BM == 256) p = FfnPlan{128, 1, L->d % 128 == 0 ? 2 : 1, false};
+  p.BM_down = 0;
   if (L->tile_m) p.BM = L->tile_m;
   if (L->tile_n_up) p.NF_up = L->tile_n_up / 64;
   if (L->tile_n_down) p.NF_down = L->tile_n_down / 64;
@@ -293,7 +307,8 @@ FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
 
 struct LayerBufs {
   int4* tiles;
-  int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts;
+  int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts, *mtile_dn;
+  int4* tiles_dn;
   float *tw, *logits;
   void *z, *y, *zs, *ys, *stats;
 };
@@ -312,6 +327,10 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->offsets = c.take<int32_t>((L->E_loc + 1) * 4);
   b->mtile = c.take<int32_t>((L->E_loc + 1) * 4);
   b->tiles = c.take<int4>((size_t)ffn_max_mtiles(L->E_loc, (int)rows, 16) * sizeof(int4));
+  // the down GEMM's own m-tiles when its tile height differs
+  const bool own_dn = layer_plan(L, (int)rows).BM_down > 0;
+  b->mtile_dn = c.take<int32_t>(own_dn ? (L->E_loc + 1) * 4 : 0);
+  b->tiles_dn = c.take<int4>(own_dn ? (size_t)ffn_max_mtiles(L->E_loc, (int)rows, 16) * sizeof(int4) : 0);
   b->sorted_pair = c.take<int32_t>(P * 4);
   b->pair_pos = c.take<int32_t>(P * 4);
   b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
@@ -626,8 +645,9 @@ int moe_dispatch_owners(int T, int k, int E, int n_owners, int placement, int ca
 size_t moe_expert_ffn_workspace_bytes(int E_loc, int rows_max, int d, int h, int act_dtype) {
   (void)d;
   if (E_loc <= 0 || rows_max < 0 || h <= 0 || !act_dtype_ok(act_dtype)) return 0;
-  return align_up((size_t)rows_max * h * 4) + align_up((size_t)(E_loc + 1) * 4) +
-         align_up((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
+  // z, then two m-tile tables (gate/up, and down when its tile height differs)
+  return align_up((size_t)rows_max * h * 4) +
+         2 * (align_up((size_t)(E_loc + 1) * 4) + align_up((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4)));
 }
 
 int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype, int w_dtype,
@@ -653,12 +673,16 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   void* z = c.take<void>((size_t)rows_max * h * 4);
   int32_t* mtile = c.take<int32_t>((size_t)(E_loc + 1) * 4);
   int4* tab = c.take<int4>((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
+  int32_t* mtile_dn = c.take<int32_t>((size_t)(E_loc + 1) * 4);
+  int4* tab_dn = c.take<int4>((size_t)ffn_max_mtiles(E_loc, rows_max, 16) * sizeof(int4));
   const int wt = wtype_of(w_dtype);
   const FfnPlan plan = plan_ffn((double)rows_max / E_loc, E_loc, d, h, wt);
+  const bool own_dn = plan.BM_down && plan.BM_down != plan.BM;
   if (expert_offsets) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM, expert_offsets, mtile, tab, s));
+  if (expert_offsets && own_dn) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM_down, expert_offsets, mtile_dn, tab_dn, s));
   return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, rows_max, nullptr, 1, expert_offsets,
                  expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
-                 w_down, s_gate, s_up, s_down, z, y_perm, false, s);
+                 w_down, s_gate, s_up, s_down, z, y_perm, false, s, nullptr, 1, nullptr, mtile_dn, tab_dn);
 }
 
 int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const int32_t* pair_pos,
@@ -779,6 +803,8 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
     MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
                            b.tiles, b.sorted_pair, pair_pos, b.counts, s));
+    if (plan.BM_down && plan.BM_down != plan.BM)
+      MOE_HIP(launch_mtile_prefix(L->E_loc, plan.BM_down, offsets, b.mtile_dn, b.tiles_dn, s));
     if (fork_at == SharedFork::kAfterGrouping) {
       const int r = launch_shared();
       if (r) return r;
@@ -805,7 +831,7 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     }
     const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
                           b.tiles, plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down,
-                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP], 1, kev);
+                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP], 1, kev, b.mtile_dn, b.tiles_dn);
     if (r) return r;
     MOE_HIP(mark(MOE_EV_DOWN));
     return MOE_OK;

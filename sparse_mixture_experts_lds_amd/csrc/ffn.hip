@@ -23,7 +23,7 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   // expert (weights are then re-read from L2 at most a few times), 64-column
   // gate/up tiles once tiles are tall (halves the live accumulators), 128-column
   // down tiles whenever d allows.
-  FfnPlan p;
+  FfnPlan p{};
   // Wide tiles (256 rows x 256 weight rows, bf16): half the bytes per FLOP of
   // the narrow tiles; worth it once experts average ~100 rows and there are
   // enough tiles to give every CU one.
@@ -45,6 +45,19 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   else if (avg_rows <= 112) BM = 64;
   else BM = 128;
   if (w_type == W_I4 && BM > 64) BM = 64;
+  // INT4 with up to ~32 rows per expert: gate/up on 32-row tiles of 64
+  // columns (each weight slice read once per expert, two workgroups per CU),
+  // down on 16-row tiles of 128 columns, whose 32-row version holds one
+  // workgroup per CU.  Measured on MI355X (28-of-896-expert share, ~26 rows
+  // per expert): 0.40 against 0.50 ms per layer.
+  if (w_type == W_I4 && avg_rows <= 32) {
+    p.BM = 32;
+    p.NF_up = 1;
+    p.BM_down = 16;
+    p.NF_down = d % 128 == 0 ? 2 : 1;
+    p.split_z = true;
+    return p;
+  }
   if (w_type == W_F32 && BM > 32) BM = 32;
   p.BM = BM;
   p.NF_up = (BM <= 64 && h % 128 == 0) ? 2 : 1;

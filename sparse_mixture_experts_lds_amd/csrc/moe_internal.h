@@ -178,6 +178,7 @@ struct FfnPlan {
   int BM;                    // rows per tile (16 * MF)
   int NF_up, NF_down;        // 16-col fragments per wave
   bool split_z;              // z kept in fp32, down projection on its hi/lo bf16 parts
+  int BM_down;               // rows per tile of the down GEMM when it differs (its own m-tile table), else 0
 };
 // avg_rows: expected rows per group (local expert); groups: number of groups.
 FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type);
