@@ -784,17 +784,24 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
     const float* lsrc = logits_in;
     int nsplit = 1;
-    if (!lsrc) {
-      nsplit = router_logits_splits(T, L->d, L->E, bf16);
-      float* lbuf = (tr.logits && nsplit == 1) ? tr.logits : b.logits;
-      MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, nsplit, s));
-      lsrc = lbuf;
-    }
     const bool want_stats = tr.expert_counts || tr.prob_mean || tr.balance_loss;
-    // the summed, biased logits go to the trace buffer, else (partial arrays)
-    // over the first partial array when the by-products read them
-    float* lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
-    MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
+    float* lout = nullptr;
+    if (!lsrc && router_fused_ok(T, L->d, L->E, k, bf16)) {
+      // one launch: the biased logits reach memory only when something reads them
+      lout = tr.logits ? tr.logits : (want_stats ? b.logits : nullptr);
+      MOE_HIP(launch_router_fused(T, L->d, L->E, k, x, L->w_router, L->expert_bias, L->renorm, ids, tw, lout, s));
+    } else {
+      if (!lsrc) {
+        nsplit = router_logits_splits(T, L->d, L->E, bf16);
+        float* lbuf = (tr.logits && nsplit == 1) ? tr.logits : b.logits;
+        MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, nsplit, s));
+        lsrc = lbuf;
+      }
+      // the summed, biased logits go to the trace buffer, else (partial arrays)
+      // over the first partial array when the by-products read them
+      lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
+      MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
+    }
     // router by-products
     if (want_stats)
       MOE_HIP(launch_router_stats(T, L->E, k, lout ? lout : lsrc, lout ? nullptr : L->expert_bias, ids,
@@ -886,12 +893,16 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   // 1. routing, as the forward: logits (GEMM or given) + bias, selection, grouping
   const float* lsrc = logits_in;
   int nsplit = 1;
-  if (!lsrc) {
-    nsplit = router_logits_splits(T, d, E, bf);
-    MOE_HIP(launch_router_logits(T, d, E, bf, x, L->w_router, b.Lraw, nsplit, s));
-    lsrc = b.Lraw;
+  if (!lsrc && router_fused_ok(T, d, E, k, bf)) {
+    MOE_HIP(launch_router_fused(T, d, E, k, x, L->w_router, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
+  } else {
+    if (!lsrc) {
+      nsplit = router_logits_splits(T, d, E, bf);
+      MOE_HIP(launch_router_logits(T, d, E, bf, x, L->w_router, b.Lraw, nsplit, s));
+      lsrc = b.Lraw;
+    }
+    MOE_HIP(launch_select(T, E, k, lsrc, nsplit, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
   }
-  MOE_HIP(launch_select(T, E, k, lsrc, nsplit, L->expert_bias, L->renorm, b.ids, b.tw, b.Lw, s));
   MOE_HIP(launch_permute(T, k, E, b.ids, L->expert_map, E_loc, L->capacity, BMb, b.offsets, b.mtile, b.tiles,
                          b.sorted_pair, b.pair_pos, b.counts, s));
   // the fp32 grouped GEMM of the forward takes at most 32-row tiles; the wide

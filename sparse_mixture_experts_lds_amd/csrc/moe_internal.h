@@ -41,16 +41,21 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, wave_shfl_xor(v, m));
-  return v;
+// The xor-16 and xor-32 lane exchanges of a wave in registers (gfx950's
+// v_permlane16_swap / v_permlane32_swap) rather than through LDS permutes.
+// Lane mapping, checked on the GPU: from r = permlane32_swap(x, x) lane l
+// takes r[1] for l < 32 and r[0] above; from r = permlane16_swap(x, x), r[1]
+// in the even 16-lane rows and r[0] in the odd ones.
+__device__ __forceinline__ int xor32_lanes(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (__lane_id() & 32) ? r[0] : r[1];
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += wave_shfl_xor(v, m);
-  return v;
+__device__ __forceinline__ int xor16_lanes(int x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (__lane_id() & 16) ? r[0] : r[1];
 }
+__device__ __forceinline__ float xor32_lanes(float x) { return __int_as_float(xor32_lanes(__float_as_int(x))); }
+__device__ __forceinline__ float xor16_lanes(float x) { return __int_as_float(xor16_lanes(__float_as_int(x))); }
 
 // Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
 // Every lane of the group ends with the result.
@@ -71,8 +76,8 @@ __device__ __forceinline__ float group_max(float x) {
   x = fmaxf(x, dppf<kQuadSwap2>(x));
   x = fmaxf(x, dppf<kQuadSwap1>(x));
   if constexpr (G == 64) {
-    x = fmaxf(x, wave_shfl_xor(x, 16));
-    x = fmaxf(x, wave_shfl_xor(x, 32));
+    x = fmaxf(x, xor16_lanes(x));
+    x = fmaxf(x, xor32_lanes(x));
   }
   return x;
 }
@@ -83,11 +88,13 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dppf<kQuadSwap2>(x);
   x += dppf<kQuadSwap1>(x);
   if constexpr (G == 64) {
-    x += wave_shfl_xor(x, 16);
-    x += wave_shfl_xor(x, 32);
+    x += xor16_lanes(x);
+    x += xor32_lanes(x);
   }
   return x;
 }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already checked.
 
@@ -103,6 +110,12 @@ constexpr int kMaxRouterSplits = 8;
 int router_logits_splits(int T, int d, int E, bool bf16);
 hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* part,
                                 int nsplit, hipStream_t s);
+// Router logits (+ bias), softmax and top-k in one launch for bf16 layers with
+// many tokens (router_fused_ok); logits_out (NULL allowed) receives the biased
+// logits.
+bool router_fused_ok(int T, int d, int E, int k, bool bf16);
+hipError_t launch_router_fused(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
+                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s);
 // Softmax + top-k from logits given as nsplit partial arrays src[s][T][E]
 // (added in ascending s) plus bias; logits_out (NULL, or aliasing the first
 // partial array: every element is read and written by the same lane) receives

@@ -22,7 +22,9 @@
 // inputs into slices, each workgroup sums one slice into its own partial
 // array, and the select kernel adds the partials in ascending slice order.
 // When the whole router weight fits in LDS (few experts), a third logits
-// kernel keeps it there and streams only the token rows.
+// kernel keeps it there and streams only the token rows.  With many tokens
+// and at most 64 experts (bf16), a fourth kernel computes a 32-token tile's
+// logits and selects its tokens' experts in the same launch.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -31,6 +33,25 @@ namespace moe {
 namespace {
 
 constexpr int kTokTile = 16;
+constexpr int kSelectGroupMinTok = 4096;  // 16-lane selection groups from here on
+
+__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
+  if (ov > v || (ov == v && oe < e)) {
+    v = ov;
+    e = oe;
+  }
+}
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& e) {  // larger value, then lower id
+  take_better(v, e, dppf<kRowRor8>(v), dpp<kRowRor8>(e));
+  take_better(v, e, dppf<kRowRor4>(v), dpp<kRowRor4>(e));
+  take_better(v, e, dppf<kQuadSwap2>(v), dpp<kQuadSwap2>(e));
+  take_better(v, e, dppf<kQuadSwap1>(v), dpp<kQuadSwap1>(e));
+  if constexpr (G == 64) {
+    take_better(v, e, xor16_lanes(v), xor16_lanes(e));
+    take_better(v, e, xor32_lanes(v), xor32_lanes(e));
+  }
+}
 
 // Softmax and top-k of one token held by one wave: lane l holds experts l+64i in
 // v[i] (-inf past E).  Writes k ids (descending logit, ties to the lower id) and
@@ -63,15 +84,7 @@ __device__ __forceinline__ void select_token(const float (&v)[NF], int E, int k,
         be = e;
       }
     }
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) {
-      const float ov = wave_shfl_xor(bv, msk);
-      const int oe = wave_shfl_xor(be, msk);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    group_argmax<64>(bv, be);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == j) {
       my_v = bv;
@@ -219,21 +232,49 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
   }
 }
 
-__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
-  if (ov > v || (ov == v && oe < e)) {
-    v = ov;
-    e = oe;
+// Softmax and top-k of one token held by a group of G lanes: lane gl holds
+// experts gl + G i in v[i] (-inf past E).  k rounds of a group arg-max pick
+// the experts; lane j keeps the j-th pick and writes its id and gate.
+template <int G, int NV>
+__device__ __forceinline__ void select_group(const float (&v)[NV], int gl, int E, int k, int renorm,
+                                             int32_t* ids_row, float* tw_row) {
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) m = fmaxf(m, v[i]);
+  m = group_max<G>(m);
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (gl + G * i < E) se += expf(v[i] - m);
+  const float sum_all = group_sum<G>(se);
+
+  uint32_t taken = 0;
+  float my_v = -INFINITY;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = gl + G * i;
+      // ascending e within the lane: strict '>' keeps the lower id among equal values
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    group_argmax<G>(bv, be);
+    if (be % G == gl) taken |= 1u << (be / G);
+    if (gl == j) {
+      my_v = bv;
+      my_e = be;
+    }
   }
-}
-template <int G>
-__device__ __forceinline__ void group_argmax(float& v, int& e) {  // larger value, then lower id
-  take_better(v, e, dppf<kRowRor8>(v), dpp<kRowRor8>(e));
-  take_better(v, e, dppf<kRowRor4>(v), dpp<kRowRor4>(e));
-  take_better(v, e, dppf<kQuadSwap2>(v), dpp<kQuadSwap2>(e));
-  take_better(v, e, dppf<kQuadSwap1>(v), dpp<kQuadSwap1>(e));
-  if constexpr (G == 64) {
-    take_better(v, e, wave_shfl_xor(v, 16), wave_shfl_xor(e, 16));
-    take_better(v, e, wave_shfl_xor(v, 32), wave_shfl_xor(e, 32));
+  const float ex = gl < k ? expf(my_v - m) : 0.f;
+  const float denom = renorm ? group_sum<G>(ex) : sum_all;
+  if (gl < k) {
+    ids_row[gl] = my_e;
+    tw_row[gl] = ex / denom;
   }
 }
 
@@ -293,44 +334,7 @@ __global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const 
       if (e < E) logits_out[(size_t)t * E + e] = v[i];
     }
   }
-  float m = v[0];
-#pragma unroll
-  for (int i = 1; i < NV; ++i) m = fmaxf(m, v[i]);
-  m = group_max<G>(m);
-  float se = 0.f;
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (gl + G * i < E) se += expf(v[i] - m);
-  const float sum_all = group_sum<G>(se);
-
-  uint32_t taken = 0;
-  float my_v = -INFINITY;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = gl + G * i;
-      // ascending e within the lane: strict '>' keeps the lower id among equal values
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    group_argmax<G>(bv, be);
-    if (be % G == gl) taken |= 1u << (be / G);
-    if (gl == j) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float ex = gl < k ? expf(my_v - m) : 0.f;
-  const float denom = renorm ? group_sum<G>(ex) : sum_all;
-  if (gl < k) {
-    ids[(size_t)t * k + gl] = my_e;
-    tw[(size_t)t * k + gl] = ex / denom;
-  }
+  select_group<G, NV>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
 }
 
 template <int NF>
@@ -476,12 +480,159 @@ hipError_t router_lds_nf(int T, int d, int E, int nsplit, const void* x, const v
   return hipGetLastError();
 }
 
+// Router logits and selection in one pass (bf16 x and router weight, E <= 64
+// NFW experts): a workgroup takes kRfTok tokens and every expert.  Its x rows
+// go to LDS once.  Wave w owns the 16-expert fragments w, w + 4, w + 8, ... and
+// streams their router rows from memory straight into MFMA B fragments, kRfPf
+// 32-input steps ahead of the MFMAs.  The tile's logits (+ bias) land in LDS;
+// 16-lane groups then pick each token's top k from there, and the logits are
+// copied out in row order when asked for.  Against a logits GEMM followed by a
+// selection pass, the logits make no round trip through memory and one launch
+// goes; in exchange every workgroup takes in the whole router weight, so the
+// path is taken for few experts only.  Measured on MI355X (cold cache, bench
+// timing of the routing step): 16384 tokens x 768 inputs x 32 experts, 19.8
+// against 22.9 us for the LDS-resident logits kernel plus selection; 8192 x
+// 768 x 192, 25.7 against 25.0 us for the grouped GEMM with 64-token tiles
+// plus selection, where each CU takes in 344 KB against 295 KB.
+constexpr int kRfTok = 32;     // tokens per workgroup: two 16-row A fragments
+constexpr int kRfPf = 4;       // 32-input steps of router rows in flight per wave
+constexpr int kRfMaxD = 1024;  // longest x row the LDS tile holds
+constexpr int kRfMinTok = 4096;
+constexpr int kRfMaxE = 64;
+
+template <int NFW>
+__global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, int k,
+                                                           const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w,
+                                                           const float* __restrict__ bias, int renorm,
+                                                           int32_t* __restrict__ ids, float* __restrict__ tw,
+                                                           float* __restrict__ logits_out) {
+  constexpr int ES = 64 * NFW + 4;  // logits row stride in LDS (floats)
+  __shared__ __attribute__((aligned(16))) unsigned char Xl[kRfTok * (2 * kRfMaxD + 16)];
+  __shared__ float Ls[kRfTok * ES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.x * kRfTok;
+  const int XRS = 2 * d + 16;  // x row stride in LDS (bytes); the pad spreads rows over the banks
+  const int cpr = d / 8;       // 16-byte chunks per x row
+  const int nk = d / 32;       // MFMA input steps (a multiple of kRfPf)
+
+  // x rows of the tile (rows past T re-read row T-1; their logits are not
+  // used).  Straight-line code: a chunk index past the tile repeats the last
+  // chunk, which writes the same bytes to the same place again.
+  constexpr int XCH = kRfTok * kRfMaxD / 8 / 256;
+  const int nch = kRfTok * cpr;
+  u32x4 xv[XCH];
+#pragma unroll
+  for (int u = 0; u < XCH; ++u) {
+    const int c = min((int)threadIdx.x + 256 * u, nch - 1);
+    const int r = c / cpr;
+    xv[u] = *reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + r, T - 1) * d + 8 * (c - r * cpr));
+  }
+  // the first kRfPf steps of this wave's router rows (rows past E re-read row E-1)
+  const uint16_t* wp[NFW];
+  u32x4 wb[kRfPf][NFW];
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) wp[i] = w + (size_t)min(16 * (wave + 4 * i) + row, E - 1) * d + 8 * q;
+#pragma unroll
+  for (int s = 0; s < kRfPf; ++s)
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) wb[s][i] = *reinterpret_cast<const u32x4*>(wp[i] + 32 * s);
+#pragma unroll
+  for (int u = 0; u < XCH; ++u) {
+    const int c = min((int)threadIdx.x + 256 * u, nch - 1);
+    const int r = c / cpr;
+    *reinterpret_cast<u32x4*>(Xl + r * XRS + 16 * (c - r * cpr)) = xv[u];
+  }
+  __syncthreads();
+
+  // Waves whose fragments lie past E run on row E-1 as well (their columns are
+  // not read); keeping every wave on one straight path keeps the loads where
+  // they are written.
+  {
+    f32x4 acc[2][NFW];
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) acc[0][i] = acc[1][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A fragment: token row (+16 for the second), inputs 8 q .. 8 q + 7 of the step
+    const unsigned char* xa = Xl + row * XRS + 16 * q;
+    int kb = 0;
+    do {  // nk >= kRfPf; no guard branch for the first router loads to sink behind
+#pragma unroll
+      for (int s = 0; s < kRfPf; ++s) {
+        const int kk = kb + s;
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + 64 * kk));
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + 16 * XRS + 64 * kk));
+#pragma unroll
+        for (int i = 0; i < NFW; ++i) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, wb[s][i]);
+          acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][i], 0, 0, 0);
+          acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][i], 0, 0, 0);
+        }
+        // refill the slot kRfPf steps ahead (the last steps re-read a valid one)
+        const int kn = min(kk + kRfPf, nk - 1);
+#pragma unroll
+        for (int i = 0; i < NFW; ++i) wb[s][i] = *reinterpret_cast<const u32x4*>(wp[i] + 32 * kn);
+        // keep each step's refill behind its MFMAs, so kRfPf - 1 steps of
+        // loads stay in flight throughout the loop
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      kb += kRfPf;
+    } while (kb < nk);
+    // D: lane holds expert 16 f + row for tokens 16 m + 4 q + r
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) {
+      const int e = 16 * (wave + 4 * i) + row;
+      const float be = (bias && e < E) ? bias[e] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ls[(16 * m + 4 * q + r) * ES + e] = acc[m][i][r] + be;
+    }
+  }
+  __syncthreads();
+
+  // selection: 16 groups of 16 lanes, two tokens each
+  const int gl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+#pragma unroll
+  for (int hh = 0; hh < kRfTok / 16; ++hh) {
+    const int r = grp + 16 * hh, t = t0 + r;
+    if (t < T) {  // uniform over the group
+      float v[4 * NFW];
+#pragma unroll
+      for (int i = 0; i < 4 * NFW; ++i) {
+        const int e = gl + 16 * i;
+        v[i] = e < E ? Ls[r * ES + e] : -INFINITY;
+      }
+      select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
+    }
+  }
+  if (logits_out) {
+    const int n = min(kRfTok, T - t0) * E;
+    for (int c = threadIdx.x; c < n; c += 256) {
+      const int r = c / E;
+      logits_out[(size_t)(t0 + r) * E + (c - r * E)] = Ls[r * ES + (c - r * E)];
+    }
+  }
+}
+
+template <int NFW>
+hipError_t router_fused_nf(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
+                           int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+  const dim3 grid((unsigned)((T + kRfTok - 1) / kRfTok));
+  router_fused_kernel<NFW><<<grid, 256, 0, s>>>(T, d, E, k, static_cast<const uint16_t*>(x),
+                                                static_cast<const uint16_t*>(wr), bias, renorm, ids, tw,
+                                                logits_out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
                         const float* logits_in, const float* bias, int renorm, int32_t* ids,
                         float* tw, float* logits_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (!logits_in && router_fused_ok(T, d, E, k, bf16))
+    return launch_router_fused(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, s);
   const int nf = (E + 63) / 64;
 #define MOE_CALL(NFv) launch_nf<NFv>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s)
   if (nf <= 1) return MOE_CALL(1);
@@ -494,8 +645,10 @@ hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, co
 
 int router_logits_tile_m(int T, int E) {
   const long long nb = E / 64;
+  // the largest tile that still gives every CU one: the tiles' operand bytes
+  // (tile rows of x plus 64 router rows) are what a CU has to take in
   for (int bm : {64, 32})
-    if ((long long)((T + bm - 1) / bm) * nb >= 512) return bm;
+    if ((long long)((T + bm - 1) / bm) * nb >= 256) return bm;
   return 16;
 }
 
@@ -571,13 +724,28 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
 #undef MOE_CALL
 }
 
+bool router_fused_ok(int T, int d, int E, int k, bool bf16) {
+  return bf16 && T >= kRfMinTok && E >= 1 && E <= kRfMaxE && k >= 1 && k <= 16 && d >= 32 * kRfPf &&
+         d % (32 * kRfPf) == 0 && d <= kRfMaxD;
+}
+
+hipError_t launch_router_fused(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
+                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+  if (!router_fused_ok(T, d, E, k, true)) return hipErrorInvalidValue;
+  static_assert(kRfMaxE <= 64, "one 16-expert fragment per wave");
+  return router_fused_nf<1>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, s);
+}
+
 hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
                          int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (nsplit < 1 || nsplit > kMaxRouterSplits) return hipErrorInvalidValue;
-  // 16 lanes per token while a lane holds at most 16 logits and the k picks fit
-  // in the group; the whole wave otherwise
-  if (E <= 256 && k <= 16) {
+  // 16 lanes per token while a lane holds at most 16 logits, the k picks fit in
+  // the group and there are tokens enough for a wave per SIMD; the whole wave
+  // otherwise.  Measured on MI355X, routing step: 8192 tokens x 192 experts,
+  // 24.6 us with 16 lanes against 28.3 with 64; 512 x 128 (four partial
+  // arrays), 34.5 against 30.0.
+  if (E <= 256 && k <= 16 && T >= kSelectGroupMinTok) {
     const int nv = (E + 15) / 16;
 #define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, s)
     if (nv <= 2) return MOE_CALL(2);

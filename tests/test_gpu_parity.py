@@ -189,6 +189,32 @@ def test_route_entry_point(E, k, dt, T):
         assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
 
 
+# bf16, T >= 4096, d a multiple of 128 up to 1024, E <= 64, k <= 16: logits
+# and selection come from one launch (32 tokens and every expert per
+# workgroup).  Cases: ragged last workgroup, waves holding no expert (E = 32,
+# E = 7), the longest row (1024) with k = 16, the shortest (128).  The
+# E = 160 .. 256 cases at the same sizes take the grouped logits GEMM and the
+# selection kernel.
+@pytest.mark.parametrize("E,k,d,T", [(32, 2, 768, 16385), (7, 3, 512, 4100), (64, 1, 128, 5000),
+                                     (48, 16, 1024, 4097), (192, 4, 768, 8192), (160, 16, 768, 4133),
+                                     (256, 8, 1024, 4097)])
+def test_route_one_launch_path(E, k, d, T):
+    moe = _moe()
+    rng = np.random.default_rng(1000 + E + k + d)
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(E).astype(np.float32))
+    for renorm, bias in ((True, b), (False, None)):
+        ids, tw, L = moe.route(x.to(DEV), w.to(DEV), k, renorm, bias=None if bias is None else bias.to(DEV),
+                               want_logits=True)
+        Lg = L.cpu().numpy().astype(np.float64)
+        Lo = orc.router_logits(as_f64(x), as_f64(w), None if bias is None else as_f64(bias))
+        assert relerr(Lg, Lo) <= 1e-4
+        ids_o = orc.select_topk(Lg, k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+        assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
+
+
 def test_route_ties_from_given_logits():
     moe = _moe()
     rng = np.random.default_rng(3)
