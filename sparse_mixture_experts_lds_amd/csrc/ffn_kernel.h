@@ -84,8 +84,8 @@ struct Traits<W_I4> {
 };
 
 __device__ __forceinline__ float act_fn(float g, int act) {
-  if (act == 0) return g / (1.0f + expf(-g));
-  return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  if (act == 0) return silu_hw(g);
+  return gelu_hw(g);
 }
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {

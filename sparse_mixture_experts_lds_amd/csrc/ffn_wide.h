@@ -78,8 +78,8 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int ACT>  // 0 SiLU, 1 exact-erf GELU
 __device__ __forceinline__ float act_fn(float g) {
-  if constexpr (ACT == 0) return g / (1.0f + expf(-g));
-  else return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));
+  if constexpr (ACT == 0) return silu_hw(g);
+  else return gelu_hw(g);
 }
 
 // 16 bytes per lane from global memory into LDS at byte address lds_addr +

@@ -57,6 +57,35 @@ __device__ __forceinline__ int xor16_lanes(int x) {
 __device__ __forceinline__ float xor32_lanes(float x) { return __int_as_float(xor32_lanes(__float_as_int(x))); }
 __device__ __forceinline__ float xor16_lanes(float x) { return __int_as_float(xor16_lanes(__float_as_int(x))); }
 
+// SiLU from the hardware base-2 exponential and reciprocal (v_exp_f32,
+// v_rcp_f32, about 1 ulp each): g / (1 + e^-g) = g * rcp(1 + 2^(-g log2 e)).
+// Large positive g gives g, large negative g gives -0.  Five instructions
+// against about twenty for expf and an IEEE division; the result feeds a z
+// that is rounded to bf16, or kept in fp32 where outputs are held to 1e-5 of
+// their RMS.
+__device__ __forceinline__ float silu_hw(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
+// Exact-erf GELU, 0.5 g (1 + erf(g / sqrt 2)), with erf from Abramowitz and
+// Stegun's rational approximation 7.1.26 (Handbook of Mathematical
+// Functions; |error| <= 1.5e-7 for x >= 0, erf odd):
+//   1 - erf(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-x^2),
+//   t = 1 / (1 + p x).
+// With c = 1 - erf(|g| / sqrt 2) the result is g - g c / 2 for g >= 0 and
+// g c / 2 below, which avoids the cancellation in 1 + erf for negative g.
+__device__ __forceinline__ float gelu_hw(float g) {
+  const float x = fabsf(g) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  const float c = t * p * __builtin_amdgcn_exp2f(x * x * -1.4426950408889634f);
+  const float h = 0.5f * g * c;
+  return g >= 0.f ? g - h : h;
+}
+
 // Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
 // Every lane of the group ends with the result.
 template <int CTRL>
