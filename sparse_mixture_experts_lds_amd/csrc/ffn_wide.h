@@ -19,8 +19,11 @@
 // as 4 x BW/32 MFMA 16x16x32 fragments (up to 128 fp32 accumulators per lane).
 // For gate/up the tile's weight rows are BW/2 gate rows then the BW/2 up rows
 // of the same outputs, and wave wc takes gate and up rows of the same output
-// columns, so g and u of an output meet in one lane.  For down the weight
-// rows are output columns, BW/2 per wave column.  The half-width tile exists
+// columns, so g and u of an output meet in one lane; its MFMAs take the
+// weight fragment as the A operand, so a lane ends with four consecutive
+// outputs of one row and stores their z straight from registers.  For down
+// the weight rows are output columns, BW/2 per wave column, and the output
+// goes out through LDS as whole row pieces.  The half-width tile exists
 // for workloads whose full-width tiles would leave the last round of
 // workgroups mostly empty.
 //
@@ -259,7 +262,10 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
       for (int f = g * NF / LPS; f < (g + 1) * NF / LPS; ++f)
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi)
-          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[f], acc[mi][f], 0, 0, 0);
+          // gate/up: the weight fragment is the A operand (rows of D are
+          // outputs); down: the activation fragment is (rows of D are tokens)
+          acc[mi][f] = GATEUP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[f], fa[mi], acc[mi][f], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[f], acc[mi][f], 0, 0, 0);
       issue_one(g, st, kb, real);
     }
   };
@@ -294,40 +300,36 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
     read_frags(fa0, fb0, cst);
     mfmas_issue(fa1, fb1, st1, (j + NS) * KB, j + NS < NKB);
   }
-  wait_vm<0>();  // the dummy loads land before the stages become the epilogue's buffer
-  lds_barrier();
-
-  // ---------------- epilogue: the output tile is staged through the (now free)
-  // stage memory so that the stores go out as 16-byte row chunks
-  unsigned char* const lds = &stg[0][0];
+  wait_vm<0>();  // the dummy loads land in LDS before its last use
   unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * (OUT_F32 ? 4 : 2);
   if constexpr (GATEUP) {
-    // g and u of an output sit in the same lane, so z = act(g) * u is formed
-    // in registers and the whole bf16 z tile (256 x BNO) goes to LDS in one
-    // pass; then every thread stores 16-byte row chunks
-    constexpr int ZS = BNO * 2 + 16;  // LDS row stride of the staged z tile (bytes)
-    constexpr int cpr = BNO * 2 / 16; // 16-byte chunks per row
-    static_assert(BM * ZS <= NS * STAGE, "z tile fits the stage memory");
+    // ---------------- gate/up epilogue.  Lane (lrow, q) holds, for tile row
+    // 64 wr + 16 mi + lrow, g (fragment f) and u (fragment f + NF / 2) of the
+    // four consecutive outputs 16 f + 4 q .. 16 f + 4 q + 3: z = act(g) u
+    // goes out straight from registers, 8 bytes per lane and 4 lanes side by
+    // side per row.  Rows past the tile end are not stored.
     if (active) {
 #pragma unroll
-      for (int mi = 0; mi < MF; ++mi)
+      for (int mi = 0; mi < MF; ++mi) {
+        const int row = 64 * wr + 16 * mi + lrow;
+        if (row < nrows) {
+          uint16_t* orow = reinterpret_cast<uint16_t*>(obase) + (size_t)row * N + HW / 2 * wc + 4 * q;
 #pragma unroll
-        for (int f = 0; f < NF / 2; ++f)
+          for (int f = 0; f < NF / 2; ++f) {
+            float z[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float z = act_fn<ACT>(acc[mi][f][r]) * acc[mi][f + NF / 2][r];
-            *reinterpret_cast<uint16_t*>(lds + (64 * wr + 16 * mi + 4 * q + r) * ZS + (HW / 2 * wc + 16 * f + lrow) * 2) =
-                (uint16_t)f32_to_bf16_bits(z);
+            for (int r = 0; r < 4; ++r) z[r] = act_fn<ACT>(acc[mi][f][r]) * acc[mi][f + NF / 2][r];
+            *reinterpret_cast<uint2*>(orow + 16 * f) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
           }
-    }
-    lds_barrier();
-    for (int c = tid; c < nrows * cpr; c += 512) {
-      const int row = c / cpr;
-      const int cc = c - row * cpr;
-      *reinterpret_cast<u32x4*>(obase + ((size_t)row * N) * 2 + cc * 16) =
-          *reinterpret_cast<const u32x4*>(lds + row * ZS + cc * 16);
+        }
+      }
     }
   } else {
+    // ---------------- down epilogue (lane (lrow, q) holds output column
+    // 16 f + lrow of tile rows 64 wr + 16 mi + 4 q + r).  Straight 64-byte
+    // row pieces from registers ran slower here than full rows staged in LDS.
+    lds_barrier();
+    unsigned char* const lds = &stg[0][0];
     // every wave stages its own 64 x HW block of the output through a private
     // LDS region, in two halves of HW/2 columns, and stores 16-byte row
     // chunks; a wave's LDS accesses complete in order, so no workgroup barrier

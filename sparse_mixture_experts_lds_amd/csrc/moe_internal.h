@@ -26,14 +26,15 @@ constexpr int kI4Group = 128;
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Round-to-nearest-even float -> bf16 bit pattern (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// fp32 -> bf16, rounded to nearest even (gfx950's v_cvt_pk_bf16_f32, one
+// instruction per pair)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename T>
