@@ -44,14 +44,18 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int rows, int h, const in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float a, ad;
+      // a as the forward's epilogue forms it (silu_hw, gelu_hw)
       if constexpr (ACT == 0) {
-        const float sg = 1.f / (1.f + expf(-g[i]));
+        const float sg = sigmoid_hw(g[i]);
         a = g[i] * sg;
         ad = sg * (1.f + g[i] * (1.f - sg));
       } else {
-        const float phi = 0.5f * (1.f + erff(g[i] * 0.70710678118654752f));
-        a = g[i] * phi;
-        ad = phi + g[i] * expf(-0.5f * g[i] * g[i]) * 0.39894228040143268f;
+        float e;
+        const float c = gelu_tail(g[i], e);
+        const float h = 0.5f * g[i] * c;
+        a = g[i] >= 0.f ? g[i] - h : h;
+        const float phi = g[i] >= 0.f ? 1.f - 0.5f * c : 0.5f * c;
+        ad = phi + g[i] * e * 0.39894228040143268f;
       }
       float z = a * u[i];
       if constexpr (sizeof(T) == 2) z = bf16_bits_to_f32(f32_to_bf16_bits(z));

@@ -64,9 +64,10 @@ __device__ __forceinline__ float xor16_lanes(float x) { return __int_as_float(xo
 // against about twenty for expf and an IEEE division; the result feeds a z
 // that is rounded to bf16, or kept in fp32 where outputs are held to 1e-5 of
 // their RMS.
-__device__ __forceinline__ float silu_hw(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+__device__ __forceinline__ float sigmoid_hw(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
 }
+__device__ __forceinline__ float silu_hw(float g) { return g * sigmoid_hw(g); }
 
 // Exact-erf GELU, 0.5 g (1 + erf(g / sqrt 2)), with erf from Abramowitz and
 // Stegun's rational approximation 7.1.26 (Handbook of Mathematical
@@ -75,15 +76,21 @@ __device__ __forceinline__ float silu_hw(float g) {
 //   t = 1 / (1 + p x).
 // With c = 1 - erf(|g| / sqrt 2) the result is g - g c / 2 for g >= 0 and
 // g c / 2 below, which avoids the cancellation in 1 + erf for negative g.
-__device__ __forceinline__ float gelu_hw(float g) {
+// gelu_tail returns c = 1 - erf(|g| / sqrt 2) and sets e = exp(-g^2 / 2),
+// which the derivative reuses (GELU'(g) = Phi(g) + g e / sqrt(2 pi)).
+__device__ __forceinline__ float gelu_tail(float g, float& e) {
   const float x = fabsf(g) * 0.70710678118654752f;
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
   float p = fmaf(t, 1.061405429f, -1.453152027f);
   p = fmaf(t, p, 1.421413741f);
   p = fmaf(t, p, -0.284496736f);
   p = fmaf(t, p, 0.254829592f);
-  const float c = t * p * __builtin_amdgcn_exp2f(x * x * -1.4426950408889634f);
-  const float h = 0.5f * g * c;
+  e = __builtin_amdgcn_exp2f(x * x * -1.4426950408889634f);
+  return t * p * e;
+}
+__device__ __forceinline__ float gelu_hw(float g) {
+  float e;
+  const float h = 0.5f * g * gelu_tail(g, e);
   return g >= 0.f ? g - h : h;
 }
 
