@@ -6,9 +6,10 @@
 // capacity-factor dispatch, overflow dropped): pairs of each local expert are laid out in ascending p;
 // with a capacity C only the first C of them are kept.
 //
-// Three launches (two when the block histograms fit in one workgroup's LDS:
-// that workgroup then counts too), none of which depends on the order of
-// atomic operations:
+// Three launches, none of which depends on the order of atomic operations
+// (two when the block histograms fit in one workgroup's LDS: that workgroup
+// then counts too; two as well for up to 64 blocks, where every scatter
+// workgroup does the scan's work for itself):
 //   1. count:   one wave per block of kBlockPairs pairs builds the block's
 //               per-expert histogram in LDS and writes it out;
 //   2. scan:    one workgroup turns the histograms into per-block bases (an
@@ -103,6 +104,7 @@ __device__ void write_tiles(int e, int off, int n, int BM, int mstart, int4* __r
 // workgroup's reads and LDS atomics then outweighing the saved launch.
 constexpr int kFusedHistInts = 24576;  // blocks x local experts held in LDS
 constexpr int kFusedMaxBlocks = 4;
+constexpr int kScatterBasesMaxBlocks = 64;
 
 template <bool COUNT>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int P, const int32_t* __restrict__ ids,
@@ -169,22 +171,71 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int P, const int32_t
 // One workgroup of kBlockPairs threads per block: wave w ranks chunk w (64
 // pairs) by a ballot multisplit, the per-wave counts are turned into per-wave
 // bases in LDS, and every lane then places its pair.
+// BASES false: counts holds the scan's per-block bases and offsets the
+// expert offsets.  BASES true (no scan launch): counts holds the raw block
+// histograms; every workgroup sums them itself (thread e: expert e, the
+// blocks before its own and all blocks) and scans the clamped totals into the
+// offsets, and workgroup 0 writes the offsets and the m-tile table, the same
+// integers the scan kernel writes.  Each workgroup then reads nblk x E_loc
+// counts, so this form is for few blocks.
+template <bool BASES>
 __global__ __launch_bounds__(kBlockPairs) void scatter_kernel(int P, const int32_t* __restrict__ ids,
                                                               const int32_t* __restrict__ emap, int E, int E_loc,
-                                                              int capacity, const int32_t* __restrict__ counts,
-                                                              const int32_t* __restrict__ offsets,
+                                                              int capacity, int nblk, int BM,
+                                                              const int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ mtile_start,
+                                                              int4* __restrict__ tile_tab,
                                                               int32_t* __restrict__ sorted_pair,
                                                               int32_t* __restrict__ pair_pos) {
+  static_assert(kBlockPairs == kScanThreads, "the block scan takes every thread of the workgroup");
   constexpr int NW = kBlockPairs / 64;
   __shared__ int32_t base[kMaxE];            // block's first rank per expert (exclusive over blocks)
   __shared__ int32_t off[kMaxE];             // expert's first grouped row
   __shared__ uint16_t wbase[NW][kMaxE];      // per-wave counts, then per-wave bases within the block
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int32_t* cb = counts + (size_t)blockIdx.x * E_loc;
-  for (int e = tid; e < E_loc; e += kBlockPairs) {
-    base[e] = cb[e];
-    off[e] = offsets[e];
+  if constexpr (BASES) {
+    __shared__ int sh[kScanThreads / 64 + 1];
+    const int e = tid;
+    int pre = 0, run = 0;
+    if (e < E_loc) {
+      constexpr int U = 16;  // blocks read per batch, all loads in flight together
+      for (int b0 = 0; b0 < nblk; b0 += U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = b0 + u < nblk ? counts[(size_t)(b0 + u) * E_loc + e] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (b0 + u == (int)blockIdx.x) pre = run;
+          run += v[u];
+        }
+      }
+    }
+    const int kept = capacity > 0 ? min(run, capacity) : run;
+    int total;
+    const int o = block_exclusive_scan(kept, &total, sh);
+    if (e < E_loc) {
+      base[e] = pre;
+      off[e] = o;
+    }
+    if (blockIdx.x == 0) {
+      if (e < E_loc) offsets[e] = o;
+      if (e == 0) offsets[E_loc] = total;
+      if (mtile_start != nullptr) {
+        int mtotal;
+        const int moff = block_exclusive_scan((kept + BM - 1) / BM, &mtotal, sh);
+        if (e < E_loc) mtile_start[e] = moff;
+        if (e == 0) mtile_start[E_loc] = mtotal;
+        if (tile_tab != nullptr && e < E_loc) write_tiles(e, o, kept, BM, moff, tile_tab);
+      }
+    }
+  } else {
+    const int32_t* cb = counts + (size_t)blockIdx.x * E_loc;
+    for (int e = tid; e < E_loc; e += kBlockPairs) {
+      base[e] = cb[e];
+      off[e] = offsets[e];
+    }
   }
   for (int i = tid; i < NW * E_loc; i += kBlockPairs) wbase[i / E_loc][i % E_loc] = 0;
   const int p = blockIdx.x * kBlockPairs + tid;
@@ -298,13 +349,19 @@ hipError_t launch_permute(int T, int k, int E, const int32_t* ids, const int32_t
     // few blocks: one workgroup counts and scans (one launch fewer)
     scan_kernel<true><<<1, kScanThreads, 0, s>>>(P, ids, expert_map, E, nblk, E_loc, capacity, BM, counts, offsets,
                                                  mtile_start, tile_tab);
+  } else if (nblk <= kScatterBasesMaxBlocks) {
+    // few blocks: the scatter workgroups form their own bases (one launch fewer)
+    count_kernel<<<nblk, 256, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
+    scatter_kernel<true><<<nblk, kBlockPairs, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, nblk, BM, counts,
+                                                      offsets, mtile_start, tile_tab, sorted_pair, pair_pos);
+    return hipGetLastError();
   } else {
     count_kernel<<<nblk, 256, 0, s>>>(P, ids, expert_map, E, E_loc, counts);
     scan_kernel<false><<<1, kScanThreads, 0, s>>>(P, ids, expert_map, E, nblk, E_loc, capacity, BM, counts,
                                                   offsets, mtile_start, tile_tab);
   }
-  scatter_kernel<<<nblk, kBlockPairs, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, counts, offsets,
-                                              sorted_pair, pair_pos);
+  scatter_kernel<false><<<nblk, kBlockPairs, 0, s>>>(P, ids, expert_map, E, E_loc, capacity, nblk, BM, counts,
+                                                     offsets, mtile_start, tile_tab, sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

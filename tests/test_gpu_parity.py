@@ -283,8 +283,9 @@ def test_router_stats_empty_batch_writes_zeros():
 
 
 # up to 4 blocks of 1024 pairs (whose histograms fit in LDS): count and scan in
-# one workgroup, else a separate count launch ((40000, 2, 64): 79 blocks,
-# (16000, 4, 512): 63 blocks)
+# one workgroup; up to 64 blocks: count, then scatter workgroups that form
+# their own bases ((16000, 4, 512): 63 blocks, (4500, 2, 1024): 9 blocks of
+# 1024 experts); more: count, scan, scatter ((40000, 2, 64): 79 blocks)
 @pytest.mark.parametrize("T,k,E,owners,cap", [(1000, 2, 8, 1, 0), (8192, 4, 192, 1, 214), (512, 16, 896, 32, 0),
                                               (3000, 8, 128, 4, 40), (5, 3, 7, 1, 1), (4500, 2, 1024, 1, 0),
                                               (40000, 2, 64, 1, 0), (16000, 4, 512, 1, 150)])
