@@ -12,9 +12,10 @@
 // and builds the logits tile [16, E] in LDS (MFMA 16x16x32 bf16 or 16x16x4 f32,
 // each wave a strided set of 16-expert column fragments); it either selects
 // for its tokens directly or only writes the logits.  The select kernel takes
-// logits from memory with one wave per token.  Selection: every lane holds
-// E/64 logits in registers and k rounds of a (value, lower-id) wave arg-max
-// pick the experts.  When the activations are bf16 and E is a multiple of 64
+// logits from memory with a group of G lanes per token (16 with many tokens
+// and E <= 256, else the whole wave).  Selection: every lane of the group
+// holds E/G logits in registers and k rounds of a (value, lower-id) group
+// arg-max pick the experts.  When the activations are bf16 and E is a multiple of 64
 // the logits of a whole layer come from the grouped GEMM kernel (one group,
 // fp32 output) instead, which reuses each router weight slice across 16-64
 // tokens per workgroup rather than 16.  Few tokens with long rows (decode)
