@@ -85,15 +85,49 @@ __device__ __forceinline__ float act_fn(float g) {
   else return gelu_hw(g);
 }
 
-// 16 bytes per lane from global memory into LDS at byte address lds_addr +
-// 16 * lane (lds_addr uniform).  Written as asm so that the compiler, which
-// cannot tell the stages apart, adds no waits of its own; the kernel waits
-// explicitly (wait_vm + lds_barrier) before it reads a stage.  The asm has no
-// register outputs, and the "memory" clobber keeps every LDS access on its side.
+// 16 bytes per lane from base + off (base uniform, off a per-lane 32-bit byte
+// offset) into LDS at byte address lds_addr + 16 * lane (lds_addr uniform).
+// Written as asm so that the compiler, which cannot tell the stages apart,
+// adds no waits of its own; the kernel waits explicitly (wait_vm +
+// lds_barrier) before it reads a stage.  The asm has no register outputs, and
+// the "memory" clobber keeps every LDS access on its side.
+__device__ __forceinline__ void dma16(const unsigned char* base, uint32_t off, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  // the base is uniform; readfirstlane keeps it in scalar registers (the
+  // builtin returns int: each half goes through uint32_t before widening, or
+  // the low half would be sign-extended into the high one)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+  base = reinterpret_cast<const unsigned char*>(ub);
+  // one wait state between the SALU write of M0 and the LDS-writing load
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
+// The same from a per-lane 64-bit address.
 __device__ __forceinline__ void dma16(const unsigned char* src, uint32_t lds_addr) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  // one wait state between the SALU write of M0 and the LDS-writing load
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+// p[i] for a wave-uniform i, read through the scalar cache (s_load, counted by
+// lgkmcnt): the tile table and gathered row indices of a workgroup's next tile
+// are read while its operand loads are in flight, and those loads' vmcnt waits
+// are counted exactly.  The arrays are written by earlier launches only.
+__device__ __forceinline__ int sload(const int32_t* p, int i) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  return reinterpret_cast<cint*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+__device__ __forceinline__ int4 sload4(const int4* p, int i) {
+  const int32_t* w = reinterpret_cast<const int32_t*>(p) + 4 * i;
+  int4 r;
+  r.x = sload(w, 0);
+  r.y = sload(w, 1);
+  r.z = sload(w, 2);
+  r.w = sload(w, 3);
+  return r;
 }
 
 // One launch covers one or two GEMM problems of the same kind (the routed
@@ -107,9 +141,21 @@ struct WideArgs {
 
 // tiles of one problem: m-tiles x weight-row blocks
 __device__ __forceinline__ int wide_tiles(const FfnGemmArgs& a, int NBLK) {
-  const int mt = a.offsets ? a.mtile_start[a.E_loc] : (a.rows_max + BM - 1) / BM;
+  const int mt = a.offsets ? sload(a.mtile_start, a.E_loc) : (a.rows_max + BM - 1) / BM;
   return mt * NBLK;
 }
+
+// A tile: problem, expert, first grouped row, rows, first output column.
+struct Tile {
+  int pi, e, row0, nrows, n0;
+};
+
+// A tile's operand addresses: uniform bases, per-lane A row offsets.
+struct Ops {
+  const unsigned char* abase;
+  const unsigned char* bbase;
+  uint32_t a_off[2];
+};
 
 template <bool GATEUP, bool OUT_F32, int ACT, int BW>
 __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
@@ -122,97 +168,142 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int lrow = lane & 15;
   const int q = lane >> 4;
   const int wr = wave & 3;
   const int wc = wave >> 2;
   static_assert(NS >= 4, "the loop keeps two k-blocks out of the load window");
 
-  // ---------------- problem and tile of this workgroup (XCD-contiguous ranges,
-  // grouped-M order within a problem)
-  const int slot = blockIdx.x >> 3;
+  // ---------------- slots.  XCD x = blockIdx % 8 owns a contiguous range of
+  // each problem's tiles (grouped-M order within a problem): slot s < per0 is
+  // problem 0's tile x per0 + s, slot per0 + s problem 1's tile x per1 + s.
+  // Workgroup b takes slots b / 8, b / 8 + S, ... (S = workgroups per XCD).
+  // Down launches one workgroup per slot.  Gate/up launches one per CU, and
+  // each carries its operand pipeline from one tile into the next: the next
+  // tile's first k-blocks are loaded during the current tile's last ones, and
+  // the epilogue stores from registers, leaving the stages to those loads.
   const int xcd = blockIdx.x & 7;
-  FfnGemmArgs args = wa.p[0];
-  int total = wide_tiles(args, args.N / BNO);
-  int per = (total + 7) / 8;
-  int sl = slot;
-  if (sl >= per) {
-    if (wa.np < 2) return;
-    sl -= per;
-    args = wa.p[1];
-    total = wide_tiles(args, args.N / BNO);
-    per = (total + 7) / 8;
-    if (sl >= per) return;
-  }
-  const int R = xcd * per + sl;
-  if (R >= total) return;
-  const int N = args.N, K = args.K;
-  const int NBLK = N / BNO;
-  const int total_mt = total / NBLK;
-  int e = 0, row0, nrows, nb;
-  {
+  const int S = gridDim.x >> 3;
+  const int total0 = wide_tiles(wa.p[0], wa.p[0].N / BNO);
+  const int total1 = wa.np > 1 ? wide_tiles(wa.p[1], wa.p[1].N / BNO) : 0;
+  const int per0 = (total0 + 7) / 8, per1 = (total1 + 7) / 8;
+  const int nslots = per0 + per1;
+  auto decode = [&](int sl, Tile& t) -> bool {
+    const int pi = sl < per0 ? 0 : 1;
+    const int R = pi ? xcd * per1 + (sl - per0) : xcd * per0 + sl;
+    const int total = pi ? total1 : total0;
+    if (R >= total) return false;
+    const FfnGemmArgs& a = wa.p[pi];
+    const int NBLK = a.N / BNO;
+    const int total_mt = total / NBLK;
     const int grp = R / (kGroupM * NBLK);
     const int t0 = grp * kGroupM;
     const int gm = min(kGroupM, total_mt - t0);
     const int rr = R - grp * kGroupM * NBLK;
-    nb = rr / gm;
-    const int t = t0 + (rr - nb * gm);
-    if (args.tile_tab) {
-      const int4 ti = args.tile_tab[t];
-      e = ti.x;
-      row0 = ti.y;
-      nrows = ti.z;
+    const int nb = rr / gm;
+    const int mt = t0 + (rr - nb * gm);
+    if (a.tile_tab) {
+      const int4 ti = sload4(a.tile_tab, mt);
+      t.e = ti.x;
+      t.row0 = ti.y;
+      t.nrows = ti.z;
     } else {
-      row0 = t * BM;
-      nrows = min(BM, args.rows_max - row0);
+      t.e = 0;
+      t.row0 = mt * BM;
+      t.nrows = min(BM, a.rows_max - t.row0);
     }
-  }
-  e = __builtin_amdgcn_readfirstlane(e);
-  nrows = __builtin_amdgcn_readfirstlane(nrows);
-  const int n0 = nb * BNO;
+    t.pi = pi;
+    t.n0 = nb * BNO;
+    return true;
+  };
+  // the first slot from sl on (in steps of S) that holds a tile, else nslots
+  auto next_slot = [&](int sl, Tile& t) -> int {
+    while (sl < nslots && !decode(sl, t)) sl += S;
+    return sl;
+  };
 
   // ---------------- load addresses.  Load i (0, 1) of wave w fills 1 KB = 16
   // rows of an operand: rows 16 (2w + i) + lane / 4, stored chunk lane % 4,
   // holding logical chunk (lane % 4) ^ ((row / 2) % 4) of the row.  Rows
   // past the tile end re-read the tile's last row (their results are never
-  // stored; a row of the product depends only on the same row of A).
-  const size_t wslice = (size_t)N * K * 2;  // one expert's matrix, bytes
-  const unsigned char* w0 = static_cast<const unsigned char*>(args.W0) + (size_t)e * wslice;
-  const unsigned char* w1 = GATEUP ? static_cast<const unsigned char*>(args.W1) + (size_t)e * wslice : w0;
-  const unsigned char* a_ptr[2];
-  const unsigned char* b_ptr[LB];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * (2 * wave + i) + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
-    const int gr = row0 + min(row, nrows - 1);
-    const int src = args.row_index ? args.row_index[gr] / args.row_div : gr;
-    a_ptr[i] = static_cast<const unsigned char*>(args.A) + ((size_t)src * K + chunk * 8) * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
+  // stored; a row of the product depends only on the same row of A).  The
+  // A offsets are 32-bit (the launcher checks the matrix size); a B load is
+  // the tile's weight base plus a fixed per-lane offset.
+  Tile tc, tn;
+  int sl = next_slot(blockIdx.x >> 3, tc);
+  if (sl >= nslots) return;
+  // K of this workgroup's tiles (a gate/up workgroup with several tiles only
+  // runs where both problems have the same K; the launcher checks)
+  const int K = wa.p[tc.pi].K;
+  const int NKB = K / KB;
+  // per-lane offset of B load i in the tile's weight rows (recomputed at each
+  // issue rather than held: registers are the scarce resource here)
+  auto b_off = [&](int i) -> uint32_t {
     const int row = 16 * (LB * wave + i) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 1) & 3);
     // gate/up: tile rows 0..BW/2-1 are gate rows, BW/2..BW-1 the up rows of the same outputs
-    const unsigned char* w = (GATEUP && row >= BW / 2) ? w1 : w0;
-    b_ptr[i] = w + ((size_t)(n0 + (GATEUP ? row % (BW / 2) : row)) * K + chunk * 8) * 2;
-  }
-  // k-block kb into stage st; past the last k-block every lane reads the same
-  // 16 bytes (one cached line) into the stage, which is never read again
-  const unsigned char* const dummy = static_cast<const unsigned char*>(args.A);
+    return (uint32_t)(((GATEUP ? row % (BW / 2) : row) * K + chunk * 8) * 2);
+  };
+  const bool up_rows = GATEUP && 16 * LB * wave >= BW / 2;  // this wave's B rows (wave-uniform)
+  auto make_ops = [&](const Tile& t, Ops& o) {
+    const FfnGemmArgs& a = wa.p[t.pi];
+    o.abase = static_cast<const unsigned char*>(a.A);
+    o.bbase = static_cast<const unsigned char*>(up_rows ? a.W1 : a.W0) + ((size_t)t.e * a.N + t.n0) * (size_t)K * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * (2 * wave + i) + (lane >> 2);
+      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      int src;
+      if (a.row_index) {
+        // the 16 rows of this load, read wave-uniformly; lane keeps row lane / 4
+        int v = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = sload(a.row_index, t.row0 + min(16 * (2 * wave + i) + j, t.nrows - 1));
+          v = (lane >> 2) == j ? r : v;
+        }
+        src = v / a.row_div;
+      } else {
+        src = t.row0 + min(row, t.nrows - 1);
+      }
+      o.a_off[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)(chunk * 16);
+    }
+  };
+
+  Ops cur, nxt;
+  make_ops(tc, cur);
+  int sln = GATEUP ? next_slot(sl + S, tn) : nslots;
+  bool has_next = sln < nslots;
+  nxt = cur;
+  if (has_next) make_ops(tn, nxt);
+
+  // k-block qb of the running sequence into stage st: block qb of the current
+  // tile, block qb - NKB of the next one, and past both every lane reads the
+  // same 16 bytes (one cached line) into the stage, which is never read again,
+  // so that every step issues the same loads and the wait counts never change
+  const unsigned char* const dummy = static_cast<const unsigned char*>(wa.p[0].A);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)&stg[0][0]);
   // load l of a stage: A rows (l = 0, 1), then B rows (l = 2 .. 1 + LB)
-  auto issue_one = [&](int l, int st, int kb, bool real) {
+  auto issue_one = [&](int l, int st, int qb) {
     const uint32_t dst = l < 2 ? lds_base + (uint32_t)(st * STAGE + (2 * wave + l) * 1024)
                                : lds_base + (uint32_t)(st * STAGE + OPA + (LB * wave + l - 2) * 1024);
-    const unsigned char* src = l < 2 ? a_ptr[l] : b_ptr[l - 2];
-    dma16(real ? src + kb * 2 : dummy, dst);
+    const bool in_cur = qb < NKB;
+    const bool in_next = !in_cur && has_next && qb < 2 * NKB;
+    // field by field (uniform selects), no branches
+    const unsigned char* const base_c = l < 2 ? cur.abase : cur.bbase;
+    const unsigned char* const base_n = l < 2 ? nxt.abase : nxt.bbase;
+    const uint32_t off_c = l < 2 ? cur.a_off[l & 1] : b_off(l - 2);
+    const uint32_t off_n = l < 2 ? nxt.a_off[l & 1] : b_off(l - 2);
+    const unsigned char* const base = in_cur ? base_c : (in_next ? base_n : dummy);
+    const uint32_t off = in_cur ? off_c + (uint32_t)(qb * KB * 2)
+                                : (in_next ? off_n + (uint32_t)((qb - NKB) * KB * 2) : 0u);
+    dma16(base, off, dst);
   };
-  auto issue = [&](int st, int kb, bool real) {
+  auto issue = [&](int st, int qb) {
 #pragma unroll
-    for (int l = 0; l < LPS; ++l) issue_one(l, st, kb, real);
+    for (int l = 0; l < LPS; ++l) issue_one(l, st, qb);
   };
 
   // fragment reads: lane (lrow, q) needs logical chunk q of its row; rows of a
@@ -222,14 +313,8 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
   // wave column wc: gate/up -> gate rows [BW/4 wc, BW/4 (wc+1)) and the same up
   // rows at +BW/2; down -> rows [BW/2 wc, BW/2 (wc+1))
   const int b_rd = (GATEUP ? HW / 2 : HW) * wc * ROWB + rd;
-  const bool active = 64 * wr < nrows;  // wave-uniform
 
   f32x4 acc[MF][NF];
-#pragma unroll
-  for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // MFMA fragments of one k-block, double-buffered in registers (two named
   // sets): the fragments of k-block j+1 are read from LDS while k-block j's
   // MFMAs run
@@ -251,9 +336,10 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
   // issued after each group: a load issue that waits for the address unit
   // (64 B/clk per CU) then overlaps the MFMAs already in the matrix pipe
   // instead of holding up the whole k-block.
-  auto mfmas_issue = [&](const bf16x8 (&fa)[MF], const bf16x8 (&fb)[NF], int st, int kb, bool real) {
+  bool active = false;  // this wave has rows in the current tile (wave-uniform)
+  auto mfmas_issue = [&](const bf16x8 (&fa)[MF], const bf16x8 (&fb)[NF], int st, int qb) {
     if (!active) {
-      issue(st, kb, real);
+      issue(st, qb);
       return;
     }
 #pragma unroll
@@ -266,108 +352,146 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
           // outputs); down: the activation fragment is (rows of D are tokens)
           acc[mi][f] = GATEUP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[f], fa[mi], acc[mi][f], 0, 0, 0)
                               : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[f], acc[mi][f], 0, 0, 0);
-      issue_one(g, st, kb, real);
+      issue_one(g, st, qb);
     }
   };
 
-  // ---------------- k-loop.  At the top of k-block j the fragments of j are in
-  // registers and the k-blocks j+1..j+NS-2 are in flight; waiting until at most
-  // NS-3 stages' loads remain, then a barrier, makes stage j+1 complete for
-  // every wave and frees stage j-1 (last read one iteration ago), which then
-  // receives k-block j+NS-1 (a dummy load past the end, so that every
-  // iteration issues the same loads and the wait count never changes).  The
-  // fragments of j+1 are read while j's MFMAs run (past the last k-block they
-  // read a stale stage and are never used).  K / KB is even.
-  const int NKB = K / KB;
+  // ---------------- k-loop.  k-block q of the running sequence sits in stage
+  // q % NS.  At the top of k-block j the fragments of j are in registers and
+  // the k-blocks j+1..j+NS-2 are in flight; waiting until at most NS-3
+  // stages' loads remain, then a barrier, makes stage j+1 complete for every
+  // wave and frees stage j-1 (last read one iteration ago), which then
+  // receives k-block j+NS-1.  The fragments of j+1 are read while j's MFMAs
+  // run (past the tile's last k-block they read a stage that is not complete
+  // and are never used).  K / KB is even.  A tile starts with k-blocks
+  // 0..NS-2 in flight (issued here for the first tile, during the previous
+  // tile's last k-blocks for the others); the global stores of an epilogue
+  // are counted by vmcnt as well, which only makes the next waits stricter.
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st) issue(st, st * KB, st < NKB);
-  wait_vm<(NS - 2) * LPS>();
-  lds_barrier();
-  read_frags(fa0, fb0, 0);
-  int cst = 0;  // stage of k-block j
-  for (int j = 0; j < NKB; j += 2) {
-    wait_vm<(NS - 3) * LPS>();
+  for (int st = 0; st < NS - 1; ++st) issue(st, st);
+  int cst = 0;  // stage of the tile's k-block j
+  for (;;) {
+    const FfnGemmArgs& args = wa.p[tc.pi];
+    const int N = args.N, nrows = tc.nrows;
+    active = 64 * wr < nrows;
+#pragma unroll
+    for (int mi = 0; mi < MF; ++mi)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    wait_vm<(NS - 2) * LPS>();
     lds_barrier();
-    const int st0 = cst == 0 ? NS - 1 : cst - 1;  // free stage (k-block j-1)
-    cst = cst + 1 == NS ? 0 : cst + 1;             // stage of k-block j+1
-    read_frags(fa1, fb1, cst);
-    mfmas_issue(fa0, fb0, st0, (j + NS - 1) * KB, j + NS - 1 < NKB);
-
-    wait_vm<(NS - 3) * LPS>();
-    lds_barrier();
-    const int st1 = cst == 0 ? NS - 1 : cst - 1;
-    cst = cst + 1 == NS ? 0 : cst + 1;  // stage of k-block j+2
     read_frags(fa0, fb0, cst);
-    mfmas_issue(fa1, fb1, st1, (j + NS) * KB, j + NS < NKB);
-  }
-  wait_vm<0>();  // the dummy loads land in LDS before its last use
-  unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * (OUT_F32 ? 4 : 2);
-  if constexpr (GATEUP) {
-    // ---------------- gate/up epilogue.  Lane (lrow, q) holds, for tile row
-    // 64 wr + 16 mi + lrow, g (fragment f) and u (fragment f + NF / 2) of the
-    // four consecutive outputs 16 f + 4 q .. 16 f + 4 q + 3: z = act(g) u
-    // goes out straight from registers, 8 bytes per lane and 4 lanes side by
-    // side per row.  Rows past the tile end are not stored.
-    if (active) {
+    for (int j = 0; j < NKB; j += 2) {
+      wait_vm<(NS - 3) * LPS>();
+      lds_barrier();
+      const int st0 = cst == 0 ? NS - 1 : cst - 1;  // free stage (k-block j-1)
+      cst = cst + 1 == NS ? 0 : cst + 1;             // stage of k-block j+1
+      read_frags(fa1, fb1, cst);
+      mfmas_issue(fa0, fb0, st0, j + NS - 1);
+
+      wait_vm<(NS - 3) * LPS>();
+      lds_barrier();
+      const int st1 = cst == 0 ? NS - 1 : cst - 1;
+      cst = cst + 1 == NS ? 0 : cst + 1;  // stage of k-block j+2
+      read_frags(fa0, fb0, cst);
+      mfmas_issue(fa1, fb1, st1, j + NS);
+    }
+    // cst is now the stage of the next tile's k-block 0
+
+    unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT_F32 ? 4 : 2);
+    if constexpr (GATEUP) {
+      // ---------------- gate/up epilogue.  Lane (lrow, q) holds, for tile row
+      // 64 wr + 16 mi + lrow, g (fragment f) and u (fragment f + NF / 2) of the
+      // four consecutive outputs 16 f + 4 q .. 16 f + 4 q + 3: z = act(g) u
+      // goes out straight from registers, 8 bytes per lane and 4 lanes side by
+      // side per row.  Rows past the tile end are not stored.
+      if (active) {
 #pragma unroll
-      for (int mi = 0; mi < MF; ++mi) {
-        const int row = 64 * wr + 16 * mi + lrow;
-        if (row < nrows) {
-          uint16_t* orow = reinterpret_cast<uint16_t*>(obase) + (size_t)row * N + HW / 2 * wc + 4 * q;
+        for (int mi = 0; mi < MF; ++mi) {
+          const int row = 64 * wr + 16 * mi + lrow;
+          if (row < nrows) {
+            uint16_t* orow = reinterpret_cast<uint16_t*>(obase) + (size_t)row * N + HW / 2 * wc + 4 * q;
 #pragma unroll
-          for (int f = 0; f < NF / 2; ++f) {
-            float z[4];
+            for (int f = 0; f < NF / 2; ++f) {
+              float z[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = act_fn<ACT>(acc[mi][f][r]) * acc[mi][f + NF / 2][r];
-            *reinterpret_cast<uint2*>(orow + 16 * f) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+              for (int r = 0; r < 4; ++r) z[r] = act_fn<ACT>(acc[mi][f][r]) * acc[mi][f + NF / 2][r];
+              *reinterpret_cast<uint2*>(orow + 16 * f) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+            }
           }
         }
       }
-    }
-  } else {
-    // ---------------- down epilogue (lane (lrow, q) holds output column
-    // 16 f + lrow of tile rows 64 wr + 16 mi + 4 q + r).  Straight 64-byte
-    // row pieces from registers ran slower here than full rows staged in LDS.
-    lds_barrier();
-    unsigned char* const lds = &stg[0][0];
-    // every wave stages its own 64 x HW block of the output through a private
-    // LDS region, in two halves of HW/2 columns, and stores 16-byte row
-    // chunks; a wave's LDS accesses complete in order, so no workgroup barrier
-    // is needed between the writes and the reads
-    constexpr int osz = OUT_F32 ? 4 : 2;
-    constexpr int QC = HW / 2;          // output columns per half
-    constexpr int OS = QC * osz + 16;   // LDS row stride of a wave's block (bytes)
-    constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row
-    static_assert(8 * 64 * OS <= NS * STAGE, "the waves' blocks fit the stage memory");
-    unsigned char* const wl = lds + wave * 64 * OS;
-    const int rows_w = min(64, nrows - 64 * wr);
-    if (active) {
+      if (!has_next) break;
+      // the next tile becomes the current one; the one after is decoded
+      // through the scalar cache while the next tile's loads are in flight
+      tc = tn;
+      cur = nxt;
+      sln = next_slot(sln + S, tn);
+      has_next = sln < nslots;
+      if (has_next) make_ops(tn, nxt);
+    } else {
+      // ---------------- down epilogue (lane (lrow, q) holds output column
+      // 16 f + lrow of tile rows 64 wr + 16 mi + 4 q + r).  Straight 64-byte
+      // row pieces from registers ran slower here than full rows staged in LDS.
+      // One tile per workgroup: the dummy loads land before the stages become
+      // the staging buffer.
+      wait_vm<0>();
+      lds_barrier();
+      unsigned char* const lds = &stg[0][0];
+      // every wave stages its own 64 x HW block of the output through a private
+      // LDS region, in two halves of HW/2 columns, and stores 16-byte row
+      // chunks; a wave's LDS accesses complete in order, so no workgroup barrier
+      // is needed between the writes and the reads
+      constexpr int osz = OUT_F32 ? 4 : 2;
+      constexpr int QC = HW / 2;          // output columns per half
+      constexpr int OS = QC * osz + 16;   // LDS row stride of a wave's block (bytes)
+      constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row
+      static_assert(8 * 64 * OS <= NS * STAGE, "the waves' blocks fit the stage memory");
+      unsigned char* const wl = lds + wave * 64 * OS;
+      const int rows_w = min(64, nrows - 64 * wr);
+      if (active) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int mi = 0; mi < MF; ++mi)
+          for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
-          for (int ff = 0; ff < NF / 2; ++ff)
+            for (int ff = 0; ff < NF / 2; ++ff)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float v = acc[mi][(NF / 2) * hh + ff][r];
-              unsigned char* dst = wl + (16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
-              if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = v;
-              else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
-            }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        unsigned char* const ob = obase + ((size_t)(64 * wr) * N + HW * wc + QC * hh) * osz;
-        for (int c = lane; c < rows_w * cpr; c += 64) {
-          const int row = c / cpr;
-          const int cc = c - row * cpr;
-          *reinterpret_cast<u32x4*>(ob + (size_t)row * N * osz + cc * 16) =
-              *reinterpret_cast<const u32x4*>(wl + row * OS + cc * 16);
+              for (int r = 0; r < 4; ++r) {
+                const float v = acc[mi][(NF / 2) * hh + ff][r];
+                unsigned char* dst = wl + (16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
+                if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = v;
+                else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
+              }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          unsigned char* const ob = obase + ((size_t)(64 * wr) * N + HW * wc + QC * hh) * osz;
+          for (int c = lane; c < rows_w * cpr; c += 64) {
+            const int row = c / cpr;
+            const int cc = c - row * cpr;
+            *reinterpret_cast<u32x4*>(ob + (size_t)row * N * osz + cc * 16) =
+                *reinterpret_cast<const u32x4*>(wl + row * OS + cc * 16);
+          }
+          // the reads land before the next half overwrites the block
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        // the reads land before the next half overwrites the block
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
+      break;
     }
   }
+  wait_vm<0>();  // every load has landed in LDS before the workgroup ends
+}
+
+// compute units per XCD of the current device (8 XCDs), at least 1
+inline int cus_per_xcd() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cached = n / 8;
+  }
+  return cached;
 }
 
 template <bool GATEUP, int BW>
@@ -384,9 +508,17 @@ hipError_t launch_bw(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop
     slots += ((long long)mt * (p.N / BNO) + 7) / 8;  // per-XCD slots of problem i
     w.p[i] = p;
   }
-  const long long g = 8 * slots;
+  long long g = 8 * slots;
   if (g == 0) return hipSuccess;
   if (g > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  // gate/up: one workgroup per CU, each running several tiles back to back,
+  // where the pipeline can run from tile to tile (the same K in every problem
+  // and at least NS - 1 k-blocks per tile); otherwise one workgroup per tile
+  if (GATEUP) {
+    bool same_k = true;
+    for (int i = 1; i < np; ++i) same_k = same_k && a[i].K == a[0].K;
+    if (same_k && a[0].K / KB >= Geo<BW>::NS - 1 && g > 8LL * cus_per_xcd()) g = 8LL * cus_per_xcd();
+  }
   auto go = [&](auto kernel) {
     if (ev_start || ev_stop)
       hipExtLaunchKernelGGL(kernel, dim3((unsigned)g), dim3(512), 0, s, static_cast<hipEvent_t>(ev_start),
