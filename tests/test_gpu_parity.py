@@ -350,6 +350,29 @@ def test_expert_ffn_entry_point(wdt, act, counts):
     assert out_err(yg, ref, "f32" if wdt == "f32" else "bf16") <= TOL[wdt]
 
 
+# Enough 256-row wide tiles (10 m-tiles x 32 n-blocks) that the gate/up launch
+# runs several tiles back to back per workgroup, the next tile's operands
+# loaded during the current one's last k-blocks; ragged experts, so tiles end
+# mid-expert and the last m-tile of each expert is short.
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+def test_expert_ffn_wide_tiles_several_per_workgroup(act):
+    moe = _moe()
+    rng = np.random.default_rng(21)
+    counts, d, h = [1100, 700, 300], 256, 4096
+    E_loc, rows = len(counts), sum(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = torch.from_numpy(rng.standard_normal((rows, d)).astype(np.float32)).to(torch.bfloat16)
+    ws = [torch.from_numpy((rng.standard_normal(s) / np.sqrt(s[-1])).astype(np.float32)).to(torch.bfloat16)
+          for s in [(E_loc, h, d), (E_loc, h, d), (E_loc, d, h)]]
+    y = moe.expert_ffn(a.to(DEV), torch.from_numpy(offs).to(DEV), *[w.to(DEV) for w in ws], act=act)
+    a64 = as_f64(a)
+    ref = np.zeros((rows, d))
+    for e in range(E_loc):
+        sl = slice(offs[e], offs[e + 1])
+        ref[sl] = orc.gated_ffn(a64[sl], as_f64(ws[0][e]), as_f64(ws[1][e]), as_f64(ws[2][e]), act)
+    assert out_err(y.float().cpu().numpy(), ref, "bf16") <= 2e-2
+
+
 def test_expert_ffn_single_group_without_offsets():
     moe = _moe()
     rng = np.random.default_rng(11)
