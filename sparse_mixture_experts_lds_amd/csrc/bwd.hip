@@ -220,9 +220,19 @@ __global__ __launch_bounds__(256) void dx_assemble_kernel(int Tn, int k, int d, 
   if (i >= (size_t)Tn * d4) return;
   const int t = (int)(i / d4), c = (int)(i % d4) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int pos = pair_pos[(size_t)t * k + j];
-    if (pos >= 0) acc += *reinterpret_cast<const f32x4*>(dXp + (size_t)pos * d + c);
+  // slots four at a time: their positions, then the rows of the kept ones,
+  // all in flight together, then the sums in ascending slot order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int pos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pos[u] = j0 + u < k ? pair_pos[(size_t)t * k + j0 + u] : -1;
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = pos[u] >= 0 ? *reinterpret_cast<const f32x4*>(dXp + (size_t)pos[u] * d + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (pos[u] >= 0) acc += v[u];
   }
   if (dXs) acc += *reinterpret_cast<const f32x4*>(dXs + (size_t)t * d + c);
   if (dXr) acc += *reinterpret_cast<const f32x4*>(dXr + (size_t)t * d + c);
