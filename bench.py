@@ -12,11 +12,20 @@ that kernel.  A separate untimed pass with an event at every step boundary
 splits the time by step (each event record idles the GPU for a few
 microseconds, so the timed steps carry no others).
 
-Prints one JSON line.  ``value`` is routed tokens per second (T / layer time).
-``roofline`` describes the dominant kernel: algorithmic bytes (or FLOPs) per
-launch divided by its average event-timed duration, against MI355X's
-published peak.  ``cpu_baseline`` times the float64 CPU oracle on a bounded
-sample of the same workload.
+The headline workload (default: the wide GeGLU layer, 16384 tokens, the
+largest of the five) is timed over exactly --steps steps after --warmup
+untimed ones; the other four workloads follow in the same run as sub-records
+under "configs", each over at least 50 steps after at least 10 warm-ups.
+Step times are medians of the per-step event times (means are reported too).
+
+Prints one JSON line.  ``value`` is routed tokens per second (T / median layer
+time).  ``roofline`` describes the dominant kernel: algorithmic bytes (the
+launch's weight matrices of every touched expert, plus the activation rows it
+reads, once) or FLOPs (4 d h per kept pair for gate/up) per launch divided by
+its median event-timed duration, against MI355X's published peak; staging
+traffic (the z and y intermediates) is reported apart as ``overhead_bytes``.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the
+headline workload.
 """
 import argparse
 import json
@@ -34,14 +43,20 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 FLUSH_BYTES = 512 << 20
+HEADLINE = "wide_geglu_bf16"
+SUB_MIN_STEPS, SUB_MIN_WARMUP = 50, 10
 
 
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="granular_bf16")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=HEADLINE, help="headline workload")
+    p.add_argument("--only", action="store_true", help="time the headline workload only (no sub-records)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the backward, router by-products and owner dispatch timings")
+    p.add_argument("--no-peaks", action="store_true", help="skip the on-box copy and GEMM rate measurements")
     p.add_argument("--warm-cache", action="store_true", help="do not flush the Infinity Cache between steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -51,11 +66,19 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
+def median(v):
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
 def algorithmic_work(cfg, counts, kept_tokens, split_z):
-    """FLOPs and bytes that the layer (and each GEMM kernel) must move, from the
-    actual routing: weights of touched experts read once, activations read
-    once, outputs written once; staging buffers and padding excluded."""
-    d, h, hs = cfg.d, cfg.h, cfg.h_shared
+    """FLOPs and bytes that the layer and each GEMM launch must move, from the
+    actual routing.  Algorithmic bytes: the weight matrices of every touched
+    expert read once, the activation rows read once, the layer output written
+    once.  The intermediates a launch writes or reads (z, y) are overhead and
+    kept apart."""
+    d, h, hs, T = cfg.d, cfg.h, cfg.h_shared, cfg.T
     ab = 4 if cfg.dtype == "f32" else 2
     if cfg.w_dtype == "i4g128":
         wb_gu = 2 * h * (d // 2 + 2 * (d // 128))   # packed codes + fp16 scales, gate + up
@@ -67,30 +90,30 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
     P = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
     zb = 4 if (split_z or cfg.dtype == "f32") else 2
-    gu = {"flops": 4.0 * d * h * P,
-          "bytes": touched * wb_gu + kept_tokens * d * ab + P * h * zb}
-    dn = {"flops": 2.0 * d * h * P,
-          "bytes": touched * wb_dn + P * h * zb + P * d * 4}
-    # the shared expert's GEMMs over all T tokens (z in bf16 or fp32 like the
-    # routed one, y in fp32)
-    T = cfg.T
-    sgu = {"flops": 4.0 * d * hs * T, "bytes": 2 * hs * d * ab + T * d * ab + T * hs * zb}
-    sdn = {"flops": 2.0 * d * hs * T, "bytes": d * hs * ab + T * hs * zb + T * d * 4}
-    router_f = 2.0 * cfg.T * d * cfg.E if cfg.has_router else 0.0
-    router_b = cfg.E * d * ab if cfg.has_router else cfg.T * cfg.E * 4
-    layer_f = router_f + 6.0 * d * h * P + (6.0 * d * hs * cfg.T if hs else 0.0)
-    layer_b = (touched * (wb_gu + wb_dn) + router_b + (3 * hs * d * ab if hs else 0)
-               + cfg.T * d * ab + cfg.T * d * ab)
+    gu = {"flops": 4.0 * d * h * P, "bytes": touched * wb_gu + kept_tokens * d * ab,
+          "overhead_bytes": P * h * zb}
+    dn = {"flops": 2.0 * d * h * P, "bytes": touched * wb_dn, "overhead_bytes": P * h * zb + P * d * 4}
+    # the shared expert's GEMMs over all T tokens
+    sgu = {"flops": 4.0 * d * hs * T, "bytes": 2 * hs * d * ab, "overhead_bytes": T * hs * zb}
+    sdn = {"flops": 2.0 * d * hs * T, "bytes": d * hs * ab, "overhead_bytes": T * hs * zb + T * d * 4}
+    router_f = 2.0 * T * d * cfg.E if cfg.has_router else 0.0
+    router_b = cfg.E * d * ab if cfg.has_router else T * cfg.E * 4
+    layer_f = router_f + 6.0 * d * h * P + (6.0 * d * hs * T if hs else 0.0)
+    # x: every token's row is read once (by the router, or as an expert input);
+    # a share with given logits reads only the rows of its kept tokens
+    x_rows = T if (cfg.has_router or hs) else kept_tokens
+    layer_b = (touched * (wb_gu + wb_dn) + router_b + (3 * hs * d * ab if hs else 0) + x_rows * d * ab + T * d * ab)
     return {"gate_up": gu, "down": dn, "shared_gate_up": sgu, "shared_down": sdn,
-            "layer": {"flops": layer_f, "bytes": layer_b}, "P": P, "touched": touched}
+            "layer": {"flops": layer_f, "bytes": layer_b}, "P": P, "touched": touched,
+            "kept_tokens": kept_tokens}
 
 
 GEMM_SOURCES = ("ffn_kernel.h", "ffn_wide.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
 
 
 def gemm_source_hash():
-    """sha256 over the sources of the grouped GEMM kernel, to tell whether a
-    stored counter profile was taken on the kernel as it is now."""
+    """sha256 over the sources of the grouped GEMM kernels, to tell whether a
+    stored counter profile was taken on the kernels as they are now."""
     import hashlib
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
@@ -134,21 +157,35 @@ def roofline_entry(work, ms, peak_tflops):
             "frac": round(ach / peak_tflops, 4)}
 
 
+def blas_info():
+    """BLAS vendor and thread count of NumPy's BLAS (threadpoolctl)."""
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return info[0].get("internal_api", "?"), int(info[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", 1
+
+
 def cpu_baseline(cfg, target_s):
     """The oracle as it stands, on the first T' tokens of the workload (same
     weights, shapes and distributions; capacity scaled to the sample), T'
-    grown until one forward takes about a quarter of ``target_s``."""
-    import numpy as np
+    grown until one forward takes about a quarter of ``target_s``.  NumPy's
+    BLAS runs on every core of this process's affinity set."""
+    import numpy as np  # noqa: F401
 
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        limiter = threadpoolctl.threadpool_limits(limits=cores, user_api="blas")
+    except Exception:  # pragma: no cover
+        limiter = None
     import oracle as orc
     from moe_synth import make_inputs
     from moe_synth.generate import as_f64
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    vendor, threads = blas_info()
 
     inp = make_inputs(cfg)
     if cfg.w_dtype == "i4g128":
@@ -173,40 +210,48 @@ def cpu_baseline(cfg, target_s):
     while dt < target_s / 4 and Ts < cfg.T:
         Ts = min(cfg.T, int(Ts * max(2.0, min(8.0, 0.5 * target_s / max(dt, 1e-3)))))
         dt = run(Ts)
-    reps, total = 1, dt
-    while total < target_s * 0.75:
-        total += run(Ts)
-        reps += 1
-    return {"value": round(reps * Ts / total, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 oracle layer forward on the first %d of %d tokens, %d runs, %.1f s"
-                      % (Ts, cfg.T, reps, total)}
+    times = [dt]
+    while sum(times) < target_s * 0.75:
+        times.append(run(Ts))
+    if limiter is not None:
+        limiter.restore_original_limits()
+    total = sum(times)
+    return {"value": round(Ts / median(times), 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas": vendor, "blas_threads": threads,
+            "sample": "float64 oracle layer forward on the first %d of %d tokens of %s, median of %d runs "
+                      "(%.1f s in all)" % (Ts, cfg.T, cfg.name, len(times), total)}
 
 
-def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=10):
+def timed_calls(torch, fn, flush, args, reps):
+    """Median time in ms of `fn()` over `reps` calls, each after a cache flush."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    for i, (e0, e1) in enumerate(ev):
+        if not args.warm_cache:
+            flush.fill_(i & 0xFF)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return median([e0.elapsed_time(e1) for e0, e1 in ev])
+
+
+def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=20):
     """Per-expert counts, mean probabilities and balance loss of this batch's
-    routing (outside the timed step): average time of one call, and the HBM
-    rate on its algorithmic bytes (logits T*E*4 plus ids T*k*4)."""
+    routing (outside the timed step), and the HBM rate on its algorithmic
+    bytes (logits T*E*4 plus ids T*k*4)."""
     L = tr["logits"] if "logits" in tr else logits
     b = None if "logits" in tr else bias  # the trace logits already hold the bias
     ids = tr["topk_ids"]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    moe.router_stats(L, ids, bias=b)
-    for e0, e1 in ev:
-        if not args.warm_cache:
-            flush.fill_(1)
-        e0.record()
-        moe.router_stats(L, ids, bias=b)
-        e1.record()
-    torch.cuda.synchronize()
-    us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    us = 1e3 * timed_calls(torch, lambda: moe.router_stats(L, ids, bias=b), flush, args, reps)
     nbytes = cfg.T * cfg.E * 4 + cfg.T * cfg.k * 4
     gbps = nbytes / (us * 1e-6) / 1e9
-    return {"kernel": "router by-products (counts, mean probability, balance loss; three launches)",
+    return {"kernel": "router by-products (counts, mean probability, balance loss)",
             "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
-def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
+def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=20):
     """Sender side of expert parallelism on this batch's routing (outside the
     timed step): all pairs grouped by owner (round-robin placement; the
     workload's owners, else 8 owners, one node) and their rows gathered into
@@ -216,16 +261,8 @@ def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
     if cfg.E % n:
         return None
     ids = tr["topk_ids"]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    moe.dispatch_owners(ids, cfg.E, n, "round_robin", x=x)
-    for e0, e1 in ev:
-        if not args.warm_cache:
-            flush.fill_(1)
-        e0.record()
-        moe.dispatch_owners(ids, cfg.E, n, "round_robin", x=x)
-        e1.record()
-    torch.cuda.synchronize()
-    us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    us = 1e3 * timed_calls(torch, lambda: moe.dispatch_owners(ids, cfg.E, n, "round_robin", x=x), flush, args,
+                           reps)
     P = cfg.T * cfg.k
     eb = 4 if cfg.dtype == "f32" else 2
     nbytes = 2 * P * cfg.d * eb + 3 * P * 4
@@ -235,9 +272,9 @@ def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=10):
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
-def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
+def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=10):
     """Layer backward on this batch (outside the timed forward step; not for
-    INT4 weights): average time of one moe_layer_bwd with preallocated
+    INT4 weights): median time of one moe_layer_bwd with preallocated
     gradients and workspace, and its roofline on the algorithmic FLOPs of its
     GEMMs (per kept pair 16 d h: gate/up again, dz = dy Wd, dWd, dWg and dWu,
     dx; the shared expert 16 T d h_s; the router 6 T d E) and algorithmic bytes
@@ -251,21 +288,11 @@ def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
     act_dt = 0 if cfg.dtype == "f32" else 1
     ws = torch.empty(moe.layer_bwd_workspace_bytes(W, cfg.T, cfg.d, act_dt), dtype=torch.uint8, device=x.device)
     grads = moe.layer_bwd(x, W, dout, logits=logits, balance=0.01, ws=ws)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
-        if not args.warm_cache:
-            flush.fill_(2)
-        e0.record()
-        moe.layer_bwd(x, W, dout, logits=logits, balance=0.01, ws=ws, grads=grads)
-        e1.record()
-    torch.cuda.synchronize()
-    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    ms = timed_calls(torch, lambda: moe.layer_bwd(x, W, dout, logits=logits, balance=0.01, ws=ws, grads=grads),
+                     flush, args, reps)
     flops = 16.0 * work["P"] * cfg.d * cfg.h + 16.0 * cfg.T * cfg.d * cfg.h_shared
     if cfg.has_router:
         flops += 6.0 * cfg.T * cfg.d * cfg.E
-    # algorithmic bytes: x and dout read once, the touched experts', shared and
-    # router weights read once, dx written once, every weight gradient written
-    # once in fp32
     ab = 4 if cfg.dtype == "f32" else 2
     wb = 4 if cfg.w_dtype == "f32" else 2
     nw = 3 * work["touched"] * cfg.h * cfg.d + 3 * cfg.h_shared * cfg.d + (cfg.E * cfg.d if cfg.has_router else 0)
@@ -280,36 +307,47 @@ def backward_timing(moe, torch, cfg, W, x, logits, work, flush, args, reps=5):
     return rec
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the layer runs on a single MI355X here (across GPUs it "
-              "would shard by expert, with one all-to-all each way). Run with --gpus 1.", file=sys.stderr)
-        return 2
+def measured_peaks(torch, flush):
+    """Rates measured on this GPU beside the published peaks: a 1 GiB device
+    copy (read + write bytes over time) and dense bf16 GEMMs through torch's
+    library path (hipBLASLt), one square and one of the wide GeGLU gate/up
+    shape (16384 x 768 times 768 x 8192)."""
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    dst = torch.empty_like(src)
+    ms = median([_time_once(torch, lambda: dst.copy_(src)) for _ in range(10)])
+    out["copy_GBps"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    for name, (M, K, N) in (("gemm_bf16_8192cube_TFLOPs", (8192, 8192, 8192)),
+                            ("gemm_bf16_16384x768x8192_TFLOPs", (16384, 768, 8192))):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16).t().contiguous()
+        ms = median([_time_once(torch, lambda: torch.matmul(a, b)) for _ in range(10)])
+        out[name] = round(2.0 * M * K * N / (ms * 1e-3) / 1e12, 1)
+        del a, b
+    out["note"] = "measured on this GPU (warm cache); published peaks: HBM 8000 GB/s, bf16 MFMA 2500 TFLOP/s"
+    return out
 
-    import numpy as np
-    import torch
 
-    import sparse_mixture_experts_lds_amd as moe
+def _time_once(torch, fn):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=True):
+    """Build the workload's inputs on the GPU, time `steps` layer forwards after
+    `warmup` untimed ones, and return its record."""
     from moe_synth import CONFIGS, make_inputs
     from sparse_mixture_experts_lds_amd._lib import EVENT_NAMES
 
-    moe.load()  # fails loudly when the HIP library is missing
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        return 3
-    if args.copy_calibration:
-        n = args.copy_calibration
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
-        return 0
-    cfg = CONFIGS[args.workload]
+    cfg = CONFIGS[name]
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     big = cfg.w_dtype == "i4g128" or cfg.E_loc * cfg.h * cfg.d * 3 > 400_000_000
     inp = make_inputs(cfg, fast_weights=big, device=dev if big else "cpu")
 
@@ -332,122 +370,175 @@ def main(argv=None):
     act_dt = 0 if cfg.dtype == "f32" else 1
     ws = torch.empty(moe.layer_workspace_bytes(W, cfg.T, cfg.d, act_dt), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.d), dtype=x.dtype, device=dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     # routing of this batch (untimed): kept pairs per expert, tokens with a kept pair
     _, tr = moe.layer_fwd(x, W, logits=logits, trace=True, ws=ws)
     torch.cuda.synchronize()
-    offs = tr["expert_offsets"].cpu().numpy()
-    counts = np.diff(offs)
+    counts = np.diff(tr["expert_offsets"].cpu().numpy())
     kept_tokens = int(((tr["pair_pos"].cpu().numpy().reshape(cfg.T, cfg.k) >= 0).any(1)).sum())
-    split_z = cfg.w_dtype == "i4g128"
-    work = algorithmic_work(cfg, counts, kept_tokens, split_z)
+    work = algorithmic_work(cfg, counts, kept_tokens, cfg.w_dtype == "i4g128")
 
     n_ev = len(EVENT_NAMES)
     stream = torch.cuda.current_stream()
 
-    def make_events(n):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n)]
+    def make_events(n, m):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(m)] for _ in range(n)]
         for row in ev:
             for e in row:
                 e.record(stream)
         torch.cuda.synchronize()
         return ev
 
-    def step(i, ev):
+    def step(i, **kw):
         if not args.warm_cache:
             flush.fill_(i & 0xFF)
-        moe.layer_fwd(x, W, logits=logits, out=out, ws=ws, events=ev)
+        moe.layer_fwd(x, W, logits=logits, out=out, ws=ws, **kw)
 
-    for i in range(args.warmup):
-        step(i, None)
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     # Breakdown pass (untimed): every step boundary carries an event.  Each
     # event record is a barrier packet that idles the GPU for a few
     # microseconds, so the timed steps below carry only the layer's start and
     # end events, plus a start/stop pair attached to the launch of the dominant
-    # GEMM itself (hipExtLaunchKernel), which times exactly that kernel at a
-    # smaller cost than two more step events.
-    n_bd = max(3, min(args.steps, 10))
-    bd = make_events(n_bd)
+    # GEMM itself (hipExtLaunchKernel), which times exactly that kernel.
+    n_bd = max(3, min(steps, 10))
+    bd = make_events(n_bd, n_ev)
     for i in range(n_bd):
-        step(i, [e.cuda_event for e in bd[i]])
+        step(i, events=[e.cuda_event for e in bd[i]])
     torch.cuda.synchronize()
-    seg_ms = {EVENT_NAMES[j]: round(float(np.mean([row[j - 1].elapsed_time(row[j]) for row in bd])), 4)
+    seg_ms = {EVENT_NAMES[j]: round(median([row[j - 1].elapsed_time(row[j]) for row in bd]), 4)
               for j in range(1, n_ev)}
     dom = max(("gate_up", "down"), key=lambda n: seg_ms[n])
-    events = make_events(args.steps)
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for row in kev:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    handles = [[e.cuda_event if j in (0, n_ev - 1) else None for j, e in enumerate(row)] for row in events]
+    events = make_events(steps, 2)
+    kev = make_events(steps, 2)
+    handles = [[row[0].cuda_event] + [None] * (n_ev - 2) + [row[1].cuda_event] for row in events]
     khandles = [([r[0].cuda_event, r[1].cuda_event, None, None] if dom == "gate_up"
                  else [None, None, r[0].cuda_event, r[1].cuda_event]) for r in kev]
-
-    def tstep(i):
-        if not args.warm_cache:
-            flush.fill_(i & 0xFF)
-        moe.layer_fwd(x, W, logits=logits, out=out, ws=ws, events=handles[i], kernel_events=khandles[i])
-
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        tstep(i)
+    for i in range(steps):
+        step(i, events=handles[i], kernel_events=khandles[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    layer_ms = [row[0].elapsed_time(row[-1]) for row in events]
-    dom_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in kev]))
-    ms = float(np.mean(layer_ms))
+    layer_ms = [row[0].elapsed_time(row[1]) for row in events]
+    dom_ms_all = [r[0].elapsed_time(r[1]) for r in kev]
+    ms, dom_ms = median(layer_ms), median(dom_ms_all)
     peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
     # when the shared expert's GEMMs ride in the routed launches, the timed
-    # launch does both problems' work
+    # launch does both problems' work (x read once for both)
     paired = bool(moe.layer_plan(W, cfg.T, cfg.d, act_dt)["shared_in_routed_launches"])
     dom_work = dict(work[dom])
     if paired:
-        dom_work = {key: work[dom][key] + work["shared_" + dom][key] for key in ("flops", "bytes")}
+        sh = work["shared_" + dom]
+        dom_work = {"flops": dom_work["flops"] + sh["flops"], "bytes": dom_work["bytes"] + sh["bytes"],
+                    "overhead_bytes": dom_work["overhead_bytes"] + sh["overhead_bytes"]}
+        if dom == "gate_up":
+            dom_work["bytes"] += (cfg.T - kept_tokens) * cfg.d * (4 if cfg.dtype == "f32" else 2)
     roof = roofline_entry(dom_work, dom_ms, peak)
     roof.update({"kernel": "grouped expert GEMM (%s %s)" % ("routed + shared, one launch," if paired else "routed",
                                                             dom.replace("_", "/")),
-                 "avg_ms": round(dom_ms, 4), "traffic": measured_traffic(cfg.name, dom),
-                 "algorithmic": {"bytes": dom_work["bytes"], "flops": dom_work["flops"]}})
-    layer_roof = roofline_entry(work["layer"], ms, peak)
-    by_products = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
-    dispatch = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
-    backward = backward_timing(moe, torch, cfg, W, x, logits, work, flush, args)
-
+                 "avg_ms": round(dom_ms, 4), "mean_ms": round(float(np.mean(dom_ms_all)), 4),
+                 "traffic": measured_traffic(cfg.name, dom),
+                 "algorithmic": {"bytes": dom_work["bytes"], "flops": dom_work["flops"]},
+                 "overhead_bytes": dom_work["overhead_bytes"]})
+    if roof["traffic"] is not None:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / dom_work["bytes"], 3)
     rec = {
-        "metric": METRIC,
         "value": round(cfg.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "mean_ms_per_step": round(float(np.mean(layer_ms)), 4),
+        "steps": steps,
+        "warmup": warmup,
         "dtype": {"f32": "f32", "bf16": "bf16"}[cfg.dtype] if cfg.w_dtype != "i4g128" else "bf16xint4",
-        "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "experts_local": cfg.E_loc, "top_k": cfg.k, "hidden": cfg.h, "shared_hidden": cfg.h_shared,
                    "act": cfg.act, "weights": cfg.w_dtype, "capacity": inp.capacity,
                    "cache": "warm" if args.warm_cache else "cold (512 MiB flush before each step)"},
         "roofline": roof,
-        "layer_roofline": layer_roof,
+        "layer_roofline": roofline_entry(work["layer"], ms, peak),
+        "layer_algorithmic": {"bytes": work["layer"]["bytes"], "flops": work["layer"]["flops"]},
         "kept_pairs": work["P"],
         "touched_experts": work["touched"],
         "step_ms": seg_ms,
-        "step_ms_note": "per-segment means from an untimed pass with an event at every boundary",
-        "wall_ms_per_step_incl_flush": round(wall * 1e3 / args.steps, 4),
-        "router_stats": by_products,
-        "owner_dispatch": dispatch,
-        "backward": backward,
+        "step_ms_note": "per-segment medians from an untimed pass with an event at every boundary",
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 4),
     }
+    if extras:
+        rec["router_stats"] = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
+        rec["owner_dispatch"] = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
+        rec["backward"] = backward_timing(moe, torch, cfg, W, x, logits, work, flush, args)
+    del W, ws, out, x, tr
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X here (across GPUs it "
+              "would shard by expert, with one all-to-all each way). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_lds_amd as moe
+    from moe_synth import CONFIGS, WORKLOADS
+
+    moe.load()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
+    if args.workload not in CONFIGS:
+        print("unknown workload %r (one of %s)" % (args.workload, ", ".join(WORKLOADS)), file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+
+    head = measure_workload(moe, torch, np, args.workload, args.steps, args.warmup, args, flush,
+                            extras=not args.no_extras)
+    print("headline %s: %.4f ms per step" % (args.workload, head["ms_per_step"]), file=sys.stderr, flush=True)
+    subs = {}
+    if not args.only:
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            subs[name] = measure_workload(moe, torch, np, name, max(args.steps, SUB_MIN_STEPS),
+                                          max(args.warmup, SUB_MIN_WARMUP), args, flush, extras=not args.no_extras)
+            print("%s: %.4f ms per step" % (name, subs[name]["ms_per_step"]), file=sys.stderr, flush=True)
+    rec = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+    }
+    rec.update({k: v for k, v in head.items() if k not in rec and k not in ("steps", "warmup")})
+    if subs:
+        rec["configs"] = subs
+    if not args.no_peaks:
+        rec["measured_peaks"] = measured_peaks(torch, flush)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(CONFIGS[args.workload], args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
 

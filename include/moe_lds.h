@@ -34,8 +34,10 @@
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers unless stated otherwise; the
  *     caller owns every buffer (inputs, outputs, workspace).  The library never
- *     allocates or frees memory, keeps no pointer after returning and has no
- *     mutable global state; calls on different streams may run concurrently.
+ *     allocates or frees memory, creates no stream or event, keeps no pointer
+ *     after returning and has no mutable global state (apart from the
+ *     per-thread text of the last HIP error); each call enqueues all of its
+ *     work on `stream`, and calls on different streams may run concurrently.
  *   - Arrays are dense and row-major; weight matrices are [out, in].
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; no call synchronises the device or reads device memory
@@ -332,7 +334,8 @@ struct moe_layer_plan_info {
   int tile_n_up;                  /* output columns per tile of the routed gate/up GEMM   */
   int tile_n_down;                /* output columns per tile of the routed down GEMM      */
   int shared_tile_m;              /* rows per tile of the shared expert's GEMMs, 0 if none */
-  int shared_in_routed_launches;  /* 1: the shared expert shares the routed launches      */
+  int shared_in_routed_launches;  /* 1: the shared expert shares the routed launches;
+                                     0: it runs after them, on the same stream          */
 };
 int moe_layer_plan(const struct moe_layer_desc* L, struct moe_layer_plan_info* out);
 

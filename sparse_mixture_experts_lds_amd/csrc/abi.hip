@@ -99,7 +99,6 @@ FfnGemmArgs gate_up_args(int E_loc, int rows_max, int d, int h, int act, const v
   g.K = d;
   g.N = h;
   g.act = act == MOE_GEGLU ? 1 : 0;
-  g.slot_div = 1;
   g.out_f32 = plan.split_z ? 1 : 0;
   return g;
 }
@@ -129,12 +128,11 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
             const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
-            void* mid_event = nullptr, int slot_div = 1, void* const* kernel_events = nullptr,
+            void* mid_event = nullptr, void* const* kernel_events = nullptr,
             const int32_t* mtile_dn = nullptr, const int4* tiles_dn = nullptr) {
   const int wt = wtype_of(w_dtype);
   FfnGemmArgs g = gate_up_args(E_loc, rows_max, d, h, act, A, a_rows, row_index, row_div, offsets, mtile,
                                tile_tab, plan, wg, wu, sg, su, z);
-  g.slot_div = slot_div;
   if (kernel_events) {
     g.ev_start = kernel_events[0];
     g.ev_stop = kernel_events[1];
@@ -157,37 +155,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   return MOE_OK;
 }
 
-// Second stream of the layer forward: the shared expert depends on x only, so it
-// runs beside routing, grouping and the routed experts and is joined back into
-// the caller's stream before the combine.  One stream and two events per
-// (host thread, device), created on first use, default priority, kept for the
-// life of the thread.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-// The side stream's GEMMs take half of the resident workgroup slots, so that
-// routing and grouping on the caller's stream (the critical path) still find
-// free CUs; measured on MI355X with the granular workload (1/4 and 3/4 were
-// slower).
-constexpr int kSharedSlotDiv = 2;
-
 constexpr int kSharedWideMinRows = 2048;
-
-// Where the shared expert is forked onto the side stream.  On the narrow
-// persistent kernel (capped at part of the resident slots) it fits beside
-// routing and grouping, so it starts with the layer; its wide 256-row tiles
-// each need a whole CU, so they start once the grouping is issued and fill the
-// CUs the routed GEMMs' last partial wave of tiles leaves idle.  Measured on
-// MI355X: granular 0.228 ms forked after grouping against 0.236 at the start
-// and 0.243 after selection; decode 0.497 at the start against 0.542 after
-// grouping.
-enum class SharedFork { kAtStart, kAfterGrouping };
-inline SharedFork shared_fork(const FfnPlan& sp) {
-  return sp.BM == 256 ? SharedFork::kAfterGrouping : SharedFork::kAtStart;
-}
 
 // The shared expert is one group of T rows.  With bf16 weights and enough
 // rows it takes the wide 256-row tiles: they finish its GEMMs in fewer, fuller
@@ -196,38 +164,28 @@ FfnPlan shared_plan(int T, int d, int hs, int wt) {
   if (wt == W_BF16 && T >= kSharedWideMinRows && hs % 128 == 0 && d % 256 == 0) return FfnPlan{256, 4, 4, false};
   return plan_ffn((double)T, 1, d, hs, wt);
 }
-// The shared expert's GEMMs ride in the routed GEMMs' own launches when both
-// run on the wide kernel with the same tile widths: the two problems' tiles
-// then fill the CUs as one grid (granular: 384 + 128 gate/up tiles, exactly
-// two rounds of 256 CUs), with no second stream and no fork or join events.
-bool shared_paired(const moe_layer_desc* L, const FfnPlan& plan, const FfnPlan& sp) {
-  return L->h_shared > 0 && L->w_dtype == MOE_BF16 && L->act_dtype == MOE_BF16 && plan.BM == 256 &&
-         sp.BM == 256 && !plan.split_z && plan.NF_up == sp.NF_up && plan.NF_down == sp.NF_down;
-}
 
-thread_local SideStream g_side[kMaxDevices];
-
-int side_stream(hipStream_t caller, SideStream** out) {
-  int dev = 0;
-  if (caller) MOE_HIP(hipStreamGetDevice(caller, &dev));
-  else MOE_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
-  SideStream& ss = g_side[dev];
-  if (!ss.s) {
-    int cur = 0;
-    MOE_HIP(hipGetDevice(&cur));
-    if (cur != dev) MOE_HIP(hipSetDevice(dev));
-    hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
-    if (cur != dev) (void)hipSetDevice(cur);
-    if (e != hipSuccess) {
-      ss = SideStream{};
-      return hip_fail(e);
-    }
-  }
-  *out = &ss;
-  return MOE_OK;
+// How the layer forward runs the shared expert.  Its GEMMs ride in the routed
+// GEMMs' own launches as a second problem whenever one kernel can take both:
+//  - the wide kernel, when both take its tiles with the same tile widths
+//    (granular: 384 + 128 gate/up tiles, exactly two rounds of 256 CUs);
+//  - the narrow kernel at the routed tile shape, when the weights are of the
+//    activation dtype and the shared hidden width equals the routed one (both
+//    problems then have the same K and N; decode: 768 tiles of routed gate/up
+//    plus 48 shared ones).
+// Otherwise (an INT4 share with a bf16 shared expert, or other widths) the
+// shared expert runs after the routed experts on the same stream.  There is
+// no second stream and no fork or join event: the layer is one stream's work.
+enum class SharedMode { kNone, kWidePair, kNarrowPair, kSerial };
+SharedMode shared_mode(const moe_layer_desc* L, const FfnPlan& plan, const FfnPlan& sp) {
+  if (L->h_shared <= 0) return SharedMode::kNone;
+  if (L->w_dtype == MOE_BF16 && L->act_dtype == MOE_BF16 && plan.BM == 256 && sp.BM == 256 && !plan.split_z &&
+      plan.NF_up == sp.NF_up && plan.NF_down == sp.NF_down)
+    return SharedMode::kWidePair;
+  if (plan.BM != 256 && L->w_dtype == L->act_dtype && L->w_dtype != MOE_I4G128 && L->h_shared == L->h &&
+      !plan.split_z && (!plan.BM_down || plan.BM_down == plan.BM))
+    return SharedMode::kNarrowPair;
+  return SharedMode::kSerial;
 }
 
 // Rows a grouped GEMM may see: at most T*k pairs, and at most capacity per expert.
@@ -499,7 +457,6 @@ int recompute_gu(int wt, bool grouped, const void* x, int T, int k, const int32_
   g.K = d;
   g.N = h;
   g.a_rows = T;
-  g.slot_div = 1;
   g.out_f32 = 1;
   if (BM == 256) {
     const int nfw = wide_rc_nf(wt == W_BF16, d, h);
@@ -682,7 +639,7 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   if (expert_offsets && own_dn) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM_down, expert_offsets, mtile_dn, tab_dn, s));
   return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, rows_max, nullptr, 1, expert_offsets,
                  expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
-                 w_down, s_gate, s_up, s_down, z, y_perm, false, s, nullptr, 1, nullptr, mtile_dn, tab_dn);
+                 w_down, s_gate, s_up, s_down, z, y_perm, false, s, nullptr, nullptr, mtile_dn, tab_dn);
 }
 
 int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const int32_t* pair_pos,
@@ -715,8 +672,9 @@ int moe_layer_plan(const moe_layer_desc* L, moe_layer_plan_info* out) {
   r.tile_n_down = 64 * p.NF_down;
   if (L->h_shared > 0) {
     const FfnPlan sp = shared_plan(L->T, L->d, L->h_shared, wtype_of(L->act_dtype));
-    r.shared_tile_m = sp.BM;
-    r.shared_in_routed_launches = shared_paired(L, p, sp) ? 1 : 0;
+    const SharedMode m = shared_mode(L, p, sp);
+    r.shared_tile_m = m == SharedMode::kNarrowPair ? p.BM : sp.BM;
+    r.shared_in_routed_launches = (m == SharedMode::kWidePair || m == SharedMode::kNarrowPair) ? 1 : 0;
   }
   *out = r;
   return MOE_OK;
@@ -750,108 +708,92 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
 
   MOE_HIP(mark(MOE_EV_START));
   const FfnPlan plan = layer_plan(L, rows);
-  // 5a: shared expert on every token: inside the routed GEMM launches
-  // (shared_paired), else forked onto the side stream (where: shared_fork)
-  const void* shared_y = nullptr;
-  SideStream* side = nullptr;
   const int swt = L->act_dtype;  // shared weights are in the activation dtype
   const FfnPlan sp = L->h_shared > 0 ? shared_plan(T, L->d, L->h_shared, wtype_of(swt)) : FfnPlan{16, 1, 1, false};
-  const bool paired = shared_paired(L, plan, sp);
-  const SharedFork fork_at = shared_fork(sp);
-  auto launch_shared = [&]() -> int {
-    if (L->h_shared <= 0 || paired) return MOE_OK;
-    int r = side_stream(s, &side);
-    if (r) return r;
-    MOE_HIP(hipEventRecord(side->fork, s));
-    MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0));
-    r = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
-                L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, side->s, nullptr,
-                kSharedSlotDiv);
-    // the join is recorded even if a launch failed; on failure the caller's
-    // stream waits for whatever the side stream did take before returning
-    const hipError_t e = hipEventRecord(side->join, side->s);
-    if (r || e != hipSuccess) {
-      if (e == hipSuccess) (void)hipStreamWaitEvent(s, side->join, 0);
-      side = nullptr;
-      return r ? r : hip_fail(e);
+  const SharedMode smode = shared_mode(L, plan, sp);
+
+  // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
+  const float* lsrc = logits_in;
+  int nsplit = 1;
+  const bool want_stats = tr.expert_counts || tr.prob_mean || tr.balance_loss;
+  float* lout = nullptr;
+  if (!lsrc && router_fused_ok(T, L->d, L->E, k, bf16)) {
+    // one launch: the biased logits reach memory only when something reads them
+    lout = tr.logits ? tr.logits : (want_stats ? b.logits : nullptr);
+    MOE_HIP(launch_router_fused(T, L->d, L->E, k, x, L->w_router, L->expert_bias, L->renorm, ids, tw, lout, s));
+  } else {
+    if (!lsrc) {
+      nsplit = router_logits_splits(T, L->d, L->E, bf16);
+      float* lbuf = (tr.logits && nsplit == 1) ? tr.logits : b.logits;
+      MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, nsplit, s));
+      lsrc = lbuf;
     }
-    shared_y = b.ys;
-    return MOE_OK;
-  };
-  if (fork_at == SharedFork::kAtStart && (rc = launch_shared())) return rc;
-  // 1-4 on the caller's stream; the side stream is joined whatever their outcome
-  auto routed = [&]() -> int {
-    // 1-2: router logits (GEMM, or the caller's), then softmax + top-k per token
-    const float* lsrc = logits_in;
-    int nsplit = 1;
-    const bool want_stats = tr.expert_counts || tr.prob_mean || tr.balance_loss;
-    float* lout = nullptr;
-    if (!lsrc && router_fused_ok(T, L->d, L->E, k, bf16)) {
-      // one launch: the biased logits reach memory only when something reads them
-      lout = tr.logits ? tr.logits : (want_stats ? b.logits : nullptr);
-      MOE_HIP(launch_router_fused(T, L->d, L->E, k, x, L->w_router, L->expert_bias, L->renorm, ids, tw, lout, s));
-    } else {
-      if (!lsrc) {
-        nsplit = router_logits_splits(T, L->d, L->E, bf16);
-        float* lbuf = (tr.logits && nsplit == 1) ? tr.logits : b.logits;
-        MOE_HIP(launch_router_logits(T, L->d, L->E, bf16, x, L->w_router, lbuf, nsplit, s));
-        lsrc = lbuf;
-      }
-      // the summed, biased logits go to the trace buffer, else (partial arrays)
-      // over the first partial array when the by-products read them
-      lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
-      MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
-    }
-    // router by-products
-    if (want_stats)
-      MOE_HIP(launch_router_stats(T, L->E, k, lout ? lout : lsrc, lout ? nullptr : L->expert_bias, ids,
-                                  tr.expert_counts, tr.prob_mean, tr.balance_loss, b.stats, s));
-    MOE_HIP(mark(MOE_EV_ROUTED));
-    // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
-    MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile,
-                           b.tiles, b.sorted_pair, pair_pos, b.counts, s));
-    if (plan.BM_down && plan.BM_down != plan.BM)
-      MOE_HIP(launch_mtile_prefix(L->E_loc, plan.BM_down, offsets, b.mtile_dn, b.tiles_dn, s));
-    if (fork_at == SharedFork::kAfterGrouping) {
-      const int r = launch_shared();
-      if (r) return r;
-    }
-    MOE_HIP(mark(MOE_EV_GROUPED));
-    // 4: routed experts, activations gathered straight from x by pair index
-    void* kev[4] = {tr.gate_up_kernel_events[0], tr.gate_up_kernel_events[1], tr.down_kernel_events[0],
-                    tr.down_kernel_events[1]};
-    if (paired) {
-      const FfnGemmArgs rg = gate_up_args(L->E_loc, rows, L->d, L->h, L->act, x, T, b.sorted_pair, k, offsets,
-                                          b.mtile, b.tiles, plan, L->w_gate, L->w_up, nullptr, nullptr, b.z);
-      const FfnGemmArgs sg = gate_up_args(1, T, L->d, L->h_shared, L->act, x, T, nullptr, 1, nullptr, nullptr,
-                                          nullptr, sp, L->ws_gate, L->ws_up, nullptr, nullptr, b.zs);
+    // the summed, biased logits go to the trace buffer, else (partial arrays)
+    // over the first partial array when the by-products read them
+    lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
+    MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
+  }
+  // router by-products
+  if (want_stats)
+    MOE_HIP(launch_router_stats(T, L->E, k, lout ? lout : lsrc, lout ? nullptr : L->expert_bias, ids,
+                                tr.expert_counts, tr.prob_mean, tr.balance_loss, b.stats, s));
+  MOE_HIP(mark(MOE_EV_ROUTED));
+  // 3: grouping (the m-tile table of the grouped GEMMs comes out of the same scan)
+  MOE_HIP(launch_permute(T, k, L->E, ids, L->expert_map, L->E_loc, L->capacity, plan.BM, offsets, b.mtile, b.tiles,
+                         b.sorted_pair, pair_pos, b.counts, s));
+  if (plan.BM_down && plan.BM_down != plan.BM)
+    MOE_HIP(launch_mtile_prefix(L->E_loc, plan.BM_down, offsets, b.mtile_dn, b.tiles_dn, s));
+  MOE_HIP(mark(MOE_EV_GROUPED));
+  // 4 (+ 5 when paired): routed experts, activations gathered straight from x
+  // by pair index; the shared expert as the second problem of the same launches
+  void* kev[4] = {tr.gate_up_kernel_events[0], tr.gate_up_kernel_events[1], tr.down_kernel_events[0],
+                  tr.down_kernel_events[1]};
+  const void* shared_y = nullptr;
+  if (smode == SharedMode::kWidePair || smode == SharedMode::kNarrowPair) {
+    const bool wide = smode == SharedMode::kWidePair;
+    const FfnPlan& shp = wide ? sp : plan;
+    FfnGemmArgs rg = gate_up_args(L->E_loc, rows, L->d, L->h, L->act, x, T, b.sorted_pair, k, offsets, b.mtile,
+                                  b.tiles, plan, L->w_gate, L->w_up, nullptr, nullptr, b.z);
+    const FfnGemmArgs sg = gate_up_args(1, T, L->d, L->h_shared, L->act, x, T, nullptr, 1, nullptr, nullptr,
+                                        nullptr, shp, L->ws_gate, L->ws_up, nullptr, nullptr, b.zs);
+    if (wide) {
       MOE_HIP(launch_ffn_gemm_wide_pair(rg, sg, true, plan.NF_up, kev[0], kev[1], s));
-      MOE_HIP(mark(MOE_EV_GATE_UP));
-      const FfnGemmArgs rd = down_args(rg, L->w_down, nullptr, b.y, true);
-      const FfnGemmArgs sd = down_args(sg, L->ws_down, nullptr, b.ys, true);
+    } else {
+      rg.ev_start = kev[0];
+      rg.ev_stop = kev[1];
+      MOE_HIP(launch_ffn_gemm_pair(rg, sg, true, wtype_of(L->w_dtype), plan.BM, plan.NF_up, s));
+      rg.ev_start = rg.ev_stop = nullptr;
+    }
+    MOE_HIP(mark(MOE_EV_GATE_UP));
+    FfnGemmArgs rd = down_args(rg, L->w_down, nullptr, b.y, true);
+    const FfnGemmArgs sd = down_args(sg, L->ws_down, nullptr, b.ys, true);
+    if (wide) {
       // the deeper problem's tiles are dispatched first
       if (L->h_shared > L->h) MOE_HIP(launch_ffn_gemm_wide_pair(sd, rd, false, plan.NF_down, kev[2], kev[3], s));
       else MOE_HIP(launch_ffn_gemm_wide_pair(rd, sd, false, plan.NF_down, kev[2], kev[3], s));
-      shared_y = b.ys;
-      MOE_HIP(mark(MOE_EV_DOWN));
-      return MOE_OK;
+    } else {
+      rd.ev_start = kev[2];
+      rd.ev_stop = kev[3];
+      MOE_HIP(launch_ffn_gemm_pair(rd, sd, false, wtype_of(L->w_dtype), plan.BM, plan.NF_down, s));
     }
-    const int r = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile,
-                          b.tiles, plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down,
-                          b.z, b.y, true, s, tr.events[MOE_EV_GATE_UP], 1, kev, b.mtile_dn, b.tiles_dn);
-    if (r) return r;
+    shared_y = b.ys;
     MOE_HIP(mark(MOE_EV_DOWN));
-    return MOE_OK;
-  };
-  rc = routed();
-  // 5b: join the shared expert, then the weighted combine
-  if (side) {
-    const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
+  } else {
+    rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile, b.tiles,
+                 plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, true, s,
+                 tr.events[MOE_EV_GATE_UP], kev, b.mtile_dn, b.tiles_dn);
     if (rc) return rc;
-    if (e != hipSuccess) return hip_fail(e);
+    MOE_HIP(mark(MOE_EV_DOWN));
+    // 5: the shared expert on every token, on the same stream
+    if (smode == SharedMode::kSerial) {
+      rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
+                   L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, s);
+      if (rc) return rc;
+      shared_y = b.ys;
+    }
   }
-  if (rc) return rc;
   MOE_HIP(mark(MOE_EV_SHARED));
+  // 6: the weighted combine
   MOE_HIP(launch_combine(T, k, L->d, bf16, true, b.y, pair_pos, tw, shared_y, out, s));
   MOE_HIP(mark(MOE_EV_END));
   return MOE_OK;

@@ -9,8 +9,8 @@ namespace moe {
 using ffn_detail::launch_mf_nf;
 
 hipError_t launch_ffn_gemm_i4(const FfnGemmArgs& a, bool gateup, bool split, int BM, int NF, hipStream_t s) {
-  if (gateup) return launch_mf_nf<W_I4, true, false>(a, BM, NF, s);
-  return split ? launch_mf_nf<W_I4, false, true>(a, BM, NF, s) : launch_mf_nf<W_I4, false, false>(a, BM, NF, s);
+  if (gateup) return launch_mf_nf<W_I4, true, false>(&a, 1, BM, NF, s);
+  return split ? launch_mf_nf<W_I4, false, true>(&a, 1, BM, NF, s) : launch_mf_nf<W_I4, false, false>(&a, 1, BM, NF, s);
 }
 
 }  // namespace moe

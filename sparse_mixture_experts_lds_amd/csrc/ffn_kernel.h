@@ -9,6 +9,12 @@
 //   down:     y[r, n] = sum_k z[r,k] Wd[e,n,k]
 // for every grouped row r of local expert e (rows offsets[e] .. offsets[e+1]).
 //
+// Two problems per launch.  A launch covers one or two GEMM problems with the
+// same K and N (the routed experts' grouped rows and the shared expert's dense
+// rows, when the shared hidden width equals the routed one); each XCD takes a
+// contiguous range of problem 0's tiles, then of problem 1's, so both spread
+// evenly over the XCDs.
+//
 // Work decomposition.  A tile is (expert e, 16*MF rows, 64*NF output columns);
 // the four waves of a workgroup split the columns, 16*NF each, and share the
 // activation rows.  Tiles of one expert are consecutive, rows fastest, so the
@@ -126,8 +132,15 @@ struct TileCap {
   static constexpr int NT_MAX = 2048 / BM;
 };
 
+// One or two problems of one launch (same K, N, activation and output type).
+struct GemmPair {
+  FfnGemmArgs p[2];
+  int np;  // 1 or 2
+};
+
 template <int WT, int MF, int NF, bool GATEUP, bool SPLIT>
-__global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
+__global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
+  const FfnGemmArgs& args = gp.p[0];  // K, N, act, out_f32: common to both problems
   using Tr = Traits<WT>;
   constexpr int BM = 16 * MF;
   constexpr int BN = 64 * NF;
@@ -172,24 +185,35 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
   const int NBLK = N / BN;
 
   // ---------------- work range of this workgroup
-  // Tiles are numbered R = 0..total-1 in grouped-M order; XCD x = blockIdx % 8
-  // owns the contiguous range [x*per, (x+1)*per) and its S workgroups stride
-  // through it, so the tiles that share a weight slice or activation rows run
-  // side by side on one XCD and hit its L2.
-  int total_mt;
-  if (args.offsets) total_mt = args.mtile_start[args.E_loc];
-  else total_mt = (args.rows_max + BM - 1) / BM;
-  const int total = total_mt * NBLK;
+  // Tiles of a problem are numbered R = 0..total-1 in grouped-M order; XCD
+  // x = blockIdx % 8 owns the contiguous range [x*per, (x+1)*per) of each
+  // problem (n0x tiles of problem 0, then n1x of problem 1: its local slots
+  // 0..n0x+n1x-1) and its S workgroups stride through those slots, so the
+  // tiles that share a weight slice or activation rows run side by side on
+  // one XCD and hit its L2.
+  auto total_mtiles = [&](const FfnGemmArgs& a) -> int {
+    return a.offsets ? a.mtile_start[a.E_loc] : (a.rows_max + BM - 1) / BM;
+  };
+  const int total0 = total_mtiles(gp.p[0]) * NBLK;
+  const int total1 = gp.np > 1 ? total_mtiles(gp.p[1]) * NBLK : 0;
   const int S = gridDim.x >> 3;  // grid is a multiple of 8
-  const int per = (total + 7) / 8;
-  const int lo = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int hi = min(((int)(blockIdx.x & 7) + 1) * per, total);
-  const int ntiles = lo < hi ? min((hi - lo + S - 1) / S, NT_MAX) : 0;
+  const int xcd = blockIdx.x & 7;
+  const int per0 = (total0 + 7) / 8, per1 = (total1 + 7) / 8;
+  const int n0x = max(0, min(per0, total0 - xcd * per0));
+  const int n1x = max(0, min(per1, total1 - xcd * per1));
+  const int first = blockIdx.x >> 3;
+  const int nx = n0x + n1x;
+  const int ntiles = first < nx ? min((nx - first + S - 1) / S, NT_MAX) : 0;
   if (ntiles == 0) return;
 
-  // ---------------- decode every tile of this workgroup into LDS (once)
+  // ---------------- decode every tile of this workgroup into LDS (once);
+  // the problem index rides in bits 24+ of the n-block field
   if (tid < ntiles) {
-    const int R = lo + tid * S;
+    const int sl = first + tid * S;
+    const int pi = sl < n0x ? 0 : 1;
+    const FfnGemmArgs& a = gp.p[pi];
+    const int R = pi ? xcd * per1 + (sl - n0x) : xcd * per0 + sl;
+    const int total_mt = (pi ? total1 : total0) / NBLK;
     // groups of kGroupM m-tiles, m-tile fastest inside a group
     const int grp = R / (kGroupM * NBLK);
     const int t0 = grp * kGroupM;
@@ -198,14 +222,14 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
     const int nb = rr / gm;
     const int t = t0 + (rr - nb * gm);
     int4 ti;
-    if (args.tile_tab) {
-      ti = args.tile_tab[t];
+    if (a.tile_tab) {
+      ti = a.tile_tab[t];
     } else {
       ti.x = 0;
       ti.y = t * BM;
-      ti.z = min(BM, args.rows_max - t * BM);
+      ti.z = min(BM, a.rows_max - t * BM);
     }
-    ti.w = nb;
+    ti.w = nb | (pi << 24);
     lds_tile[tid] = ti;
   }
   __syncthreads();
@@ -213,8 +237,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
     const int i = idx / BM;
     const int r = idx - i * BM;
     const int4 ti = lds_tile[i];
+    const FfnGemmArgs& a = gp.p[ti.w >> 24];
     const int gr = ti.y + min(r, max(ti.z - 1, 0));
-    lds_src[i][r] = args.row_index ? args.row_index[gr] / args.row_div : gr;
+    lds_src[i][r] = a.row_index ? a.row_index[gr] / a.row_div : gr;
   }
   __syncthreads();
 
@@ -253,8 +278,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
       s_lane[f] = 0;
     }
   }
-  const unsigned char* const Abase = static_cast<const unsigned char*>(args.A);
   struct Ptrs {
+    const unsigned char* abase;
     uint32_t a[NCH];
     const unsigned char* w0;
     const unsigned char* w1;
@@ -264,7 +289,10 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
   auto setup = [&](int i, Ptrs& P) {
     const int4 ti = lds_tile[i];
     const int e = __builtin_amdgcn_readfirstlane(ti.x);
-    const int n0 = __builtin_amdgcn_readfirstlane(ti.w) * BN;
+    const int pi = __builtin_amdgcn_readfirstlane(ti.w) >> 24;
+    const int n0 = (__builtin_amdgcn_readfirstlane(ti.w) & 0xFFFFFF) * BN;
+    const FfnGemmArgs& args = gp.p[pi];
+    P.abase = static_cast<const unsigned char*>(args.A);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) P.a[j] = (uint32_t)lds_src[i][a_row[j]] * (uint32_t)(K * GELT) + a_col[j];
     const size_t row_first = (size_t)e * N + n0;  // first weight row of the tile
@@ -285,7 +313,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
   float sbuf[NS][NB_FR];
   auto load_a = [&](int st, const Ptrs& P, int kb) {
     const bool kin = kb < K;
-    const unsigned char* base = Abase + (size_t)(kin ? kb : K - KB) * GELT;
+    const unsigned char* base = P.abase + (size_t)(kin ? kb : K - KB) * GELT;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
 #pragma unroll
@@ -489,7 +517,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
     // epilogue: results -> LDS tile (output dtype) -> 16-byte row stores
     {
       const int4 ti = lds_tile[it];
-      const int row0 = ti.y, nrows = ti.z, n0 = ti.w * BN;
+      const int row0 = ti.y, nrows = ti.z, n0 = (ti.w & 0xFFFFFF) * BN;
+      void* const out = gp.p[__builtin_amdgcn_readfirstlane(ti.w) >> 24].out;
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi) {
 #pragma unroll
@@ -507,7 +536,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(FfnGemmArgs args) {
         }
       }
       lds_barrier();
-      unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)row0 * N + n0) * osz;
+      unsigned char* obase = static_cast<unsigned char*>(out) + ((size_t)row0 * N + n0) * osz;
       for (int c = tid; c < nrows * cpr; c += 256) {
         const int row = c / cpr;
         const int cc = c - row * cpr;
@@ -541,30 +570,46 @@ int resident_groups(int& cus) {
 }
 
 template <int WT, int MF, int NF, bool GU, bool SPLIT>
-hipError_t launch_one(const FfnGemmArgs& a, hipStream_t s) {
+hipError_t launch_one(const FfnGemmArgs* a, int np, hipStream_t s) {
   const int BM = 16 * MF, BN = 64 * NF;
-  const int mt = a.offsets ? ffn_max_mtiles(a.E_loc, a.rows_max, BM) : (a.rows_max + BM - 1) / BM;
-  const long long total_ub = (long long)mt * (a.N / BN);
-  if (total_ub == 0) return hipSuccess;
+  GemmPair gp{};
+  gp.np = np;
+  long long per_ub = 0;  // per-XCD tiles, upper bound
+  for (int i = 0; i < np; ++i) {
+    const FfnGemmArgs& p = a[i];
+    if (p.N % BN || (i > 0 && (p.K != a[0].K || p.N != a[0].N || p.act != a[0].act || p.out_f32 != a[0].out_f32)))
+      return hipErrorInvalidValue;
+    const int mt = p.offsets ? ffn_max_mtiles(p.E_loc, p.rows_max, BM) : (p.rows_max + BM - 1) / BM;
+    per_ub += ((long long)mt * (p.N / BN) + 7) / 8;
+    gp.p[i] = p;
+  }
+  if (per_ub == 0) return hipSuccess;
   // Persistent grid: every resident slot once, but no more than the tiles there
   // can be, and enough workgroups that none holds more than NT_MAX tiles.
   int cus = 256;
   const int occ = resident_groups<WT, MF, NF, GU, SPLIT>(cus);
   constexpr int NT_MAX = TileCap<16 * MF>::NT_MAX;
-  const long long per_ub = (total_ub + 7) / 8;
-  long long slots = (long long)occ * cus / 8;
-  if (a.slot_div > 1) slots = std::max<long long>(1, slots / a.slot_div);
+  const long long slots = (long long)occ * cus / 8;
   long long S = std::max<long long>(slots, (per_ub + NT_MAX - 1) / NT_MAX);
   S = std::min<long long>(S, per_ub);
   const long long g = 8 * S;
-  launch_gemm(ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>, dim3((unsigned)g), dim3(256), s, a);
+  const dim3 grid((unsigned)g), block(256);
+  auto kernel = ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>;
+  if (a[0].ev_start || a[0].ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(a[0].ev_start),
+                          static_cast<hipEvent_t>(a[0].ev_stop), 0, gp);
+  else
+    kernel<<<grid, block, 0, s>>>(gp);
   return hipGetLastError();
 }
 
+// np problems (1 or 2) of the same K and N in one launch, problem 0's tiles
+// dispatched first
 template <int WT, bool GU, bool SPLIT>
-hipError_t launch_mf_nf(const FfnGemmArgs& a, int BM, int NF, hipStream_t s) {
+hipError_t launch_mf_nf(const FfnGemmArgs* a, int np, int BM, int NF, hipStream_t s) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
 #define MOE_CASE(MFv, NFv) \
-  if (BM == 16 * MFv && NF == NFv) return launch_one<WT, MFv, NFv, GU, SPLIT>(a, s);
+  if (BM == 16 * MFv && NF == NFv) return launch_one<WT, MFv, NFv, GU, SPLIT>(a, np, s);
   if constexpr (WT == W_F32) {
     MOE_CASE(1, 1) MOE_CASE(1, 2) MOE_CASE(2, 1) MOE_CASE(2, 2)
   } else if constexpr (WT == W_I4) {

@@ -207,23 +207,12 @@ struct FfnGemmArgs {
   const int4* tile_tab;      // per m-tile {expert, first row, rows, 0}, or NULL with offsets == NULL
   int E_loc, rows_max, K, N;
   int a_rows;                // rows of A as addressed (a_rows * K elements must stay below 4 GiB)
-  int slot_div;              // persistent grid = resident workgroup slots / slot_div (0, 1: all)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
   void* ev_start;            // hipEvent_t pair carried by the launch itself (NULL: none):
   void* ev_stop;             //   they time exactly this kernel and add no packet to the stream
 };
 
-// Launch a GEMM kernel, with the argument block's start/stop events attached
-// to its dispatch when it has any.
-template <typename Kern>
-inline void launch_gemm(Kern kernel, dim3 grid, dim3 block, hipStream_t s, const FfnGemmArgs& a) {
-  if (a.ev_start || a.ev_stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(a.ev_start),
-                          static_cast<hipEvent_t>(a.ev_stop), 0, a);
-  else
-    kernel<<<grid, block, 0, s>>>(a);
-}
 struct FfnPlan {
   int BM;                    // rows per tile (16 * MF)
   int NF_up, NF_down;        // 16-col fragments per wave
@@ -236,6 +225,11 @@ int ffn_max_mtiles(int E_loc, int rows_max, int BM);
 // split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
 hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,
                            int NF, hipStream_t s);
+// Two problems of the same kind, K and N on the narrow kernel (fp32 or bf16
+// weights, BM rows per tile), problem 0's tiles dispatched first; a0's events,
+// if any, time the launch.
+hipError_t launch_ffn_gemm_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int w_type, int BM,
+                                int NF, hipStream_t s);
 // Two problems of the same kind (bf16 weights, wide 256-row tiles, 64 * NF
 // weight rows per tile, same activation and output type) in one launch, the
 // tiles of a0 dispatched first; the events, if any, time the launch.

@@ -149,8 +149,12 @@ def check_layer(inp, q=None, tokens=None, wdev=None, report=None):
         r = orc.moe_layer(x64, Wo, cfg.k, cfg.renorm, cfg.act, ids=ids_g, **kw)
     got = out.float().cpu().numpy()[r["tokens"]]
     err = out_err(got, r["out"], cfg.dtype)
+    raw = relerr(got, r["out"])
     if report is not None:
-        report.update(err=err, flipped=flipped, tokens=len(r["tokens"]))
+        # floor: the raw figure of the exact result itself, rounded once to the
+        # output dtype (what the output format alone costs)
+        floor = relerr(orc.round_to_dtype(r["out"], cfg.dtype), r["out"])
+        report.update(err=err, raw=raw, floor=floor, flipped=flipped, tokens=len(r["tokens"]))
     assert err <= TOL[cfg.w_dtype if cfg.w_dtype != "bf16" else "bf16"], \
         "relative error %.3g above tolerance (flipped %d)" % (err, flipped)
     return out, tr, err

@@ -135,8 +135,13 @@ def test_layer_plan():
     # narrow tiles asked for: the shared expert keeps its own launches
     rc, p = _plan(_cfg_desc("granular_bf16", tile_m=128))
     assert rc == _lib.MOE_OK and p["tile_m"] == 128 and p["shared_in_routed_launches"] == 0
-    # decode: a few rows per expert, narrow tiles, shared expert on its own
+    # decode: a few rows per expert, narrow tiles; the shared expert (same
+    # hidden width) is the second problem of the routed launches, on their tiles
     rc, p = _plan(_cfg_desc("decode_bf16"))
+    assert rc == _lib.MOE_OK and p["tile_m"] < 256 and p["shared_in_routed_launches"] == 1
+    assert p["shared_tile_m"] == p["tile_m"]
+    # another shared width on narrow tiles: after the routed experts
+    rc, p = _plan(_cfg_desc("decode_bf16", h_shared=512))
     assert rc == _lib.MOE_OK and p["tile_m"] < 256 and p["shared_in_routed_launches"] == 0
     # no shared expert
     rc, p = _plan(_cfg_desc("granular_bf16", h_shared=0))

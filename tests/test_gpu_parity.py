@@ -16,7 +16,7 @@ import oracle as orc
 from moe_synth import CONFIGS, make_inputs, scaled
 from moe_synth.generate import as_f64
 from moe_testutil import (TOL, check_layer, check_router_stats, device_weights, oracle_weights, out_err,
-                          quantize_inputs, relerr, sample_tokens)
+                          quantize_inputs, relerr)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -35,8 +35,9 @@ SCALED = {
     "wide_geglu_small": scaled("wide_geglu_bf16", T=1024, d=256, E=8, h=512),
     "decode_small": scaled("decode_bf16", T=136, d=512, E=32, h=256, h_shared=256),
     "int4_small": scaled("int4_share", T=72, d=512, E=64, h=256, owners=8),
-    # 2304 tokens: the shared expert takes the wide 256-row tiles and is
-    # forked after the grouping step; every output is compared
+    # 2304 tokens: the routed experts take the narrow tiles and the shared
+    # expert (another hidden width) the wide 256-row tiles, after the routed
+    # experts; every output is compared
     "shared_wide": scaled("granular_bf16", T=2304, d=256, E=16, h=128, h_shared=256),
     # decode-like: ~30 rows per expert against many weight rows, one with
     # GeGLU and a ragged batch; every output compared
@@ -423,9 +424,61 @@ def test_quantize_entry_point_bit_exact():
 @pytest.mark.parametrize("name", ["tiny_fp32", "granular_bf16", "wide_geglu_bf16", "decode_bf16",
                                   "int4_share"])
 def test_layer_full_size(name):
+    """Every output row of the full-size workload, in the launch configuration
+    the bench times, against the oracle.  Three figures are reported: the raw
+    max|d|/RMS, the one net of the final rounding's half ulp (which gates),
+    and the raw figure of the exact result rounded once to the output dtype
+    (the floor the output format alone sets: with millions of bf16 outputs
+    the largest ones sit where half an ulp is 1.6e-2 to 3.1e-2 of RMS)."""
     _moe()
     cfg = CONFIGS[name]
     inp = make_inputs(cfg)
     rep = {}
-    check_layer(inp, tokens=sample_tokens(cfg.T, 48), report=rep)
+    check_layer(inp, report=rep)
     print(name, rep)
+    assert rep["tokens"] == cfg.T
+    # the raw error stays within the bar on top of what the format forces
+    assert rep["raw"] <= rep["floor"] + TOL[cfg.w_dtype if cfg.w_dtype != "bf16" else "bf16"], rep
+
+
+# ------------------------------------------------------------------ streams and the shared expert's launches
+SHARED_MODES = {
+    # h == h_shared on the narrow tiles: the shared expert is the second
+    # problem of the routed gate/up and down launches
+    "decode_small": (SCALED["decode_small"], 1),
+    # other widths: the shared expert runs after the routed experts, same stream
+    "stream_swiglu": (SCALED["stream_swiglu"], 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED_MODES))
+def test_shared_expert_launch_mode(name):
+    moe = _moe()
+    cfg, paired = SHARED_MODES[name]
+    inp = make_inputs(cfg)
+    w = device_weights(inp)
+    plan = moe.layer_plan(w, cfg.T, cfg.d, 1)
+    assert plan["tile_m"] < 256 and plan["shared_in_routed_launches"] == paired, plan
+    check_layer(inp, wdev=w)
+
+
+def test_two_layers_on_two_streams_from_one_thread():
+    """The library keeps no stream or event of its own: two layers enqueued
+    from one thread on two streams, interleaved, give the same bits as the
+    same layers run one after the other on the default stream."""
+    moe = _moe()
+    cases = []
+    for cfg in (SCALED["decode_small"], SCALED["stream_swiglu"], PAIRED["routed_deeper"]):
+        inp = make_inputs(cfg)
+        cases.append((inp.x.to(DEV), device_weights(inp)))
+    ref = [moe.layer_fwd(x, w) for x, w in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for i, (x, w) in enumerate(cases):
+            with torch.cuda.stream(streams[(i + rep) % 2]):
+                outs.append((i, moe.layer_fwd(x, w)))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        assert torch.equal(o, ref[i]), i
