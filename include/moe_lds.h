@@ -36,8 +36,10 @@
  *     caller owns every buffer (inputs, outputs, workspace).  The library never
  *     allocates or frees memory, creates no stream or event, keeps no pointer
  *     after returning and has no mutable global state (apart from the
- *     per-thread text of the last HIP error); each call enqueues all of its
- *     work on `stream`, and calls on different streams may run concurrently.
+ *     per-thread text of the last HIP error, and the one static scratch array
+ *     of moe_permute_noalloc); each call enqueues all of its work on `stream`,
+ *     and calls on different streams may run concurrently (except
+ *     moe_permute_noalloc calls on one GPU, which share its scratch).
  *   - Arrays are dense and row-major; weight matrices are [out, in].
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; no call synchronises the device or reads device memory
@@ -169,6 +171,29 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids,
                 int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
                 const void* x, int d, int act_dtype, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_noalloc - moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, outputs
+ * and errors as moe_permute, minus ws / ws_bytes.
+ *
+ * Its scratch (the grouping step's per-block expert histograms and bases) is
+ * a static device array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy per GPU, held from the first call on that GPU until the
+ * process ends; no call allocates or frees anything.  Sizes whose
+ * moe_permute_workspace_bytes(T, k, E_loc) exceeds it (1024 * E_loc * 4 bytes
+ * per block of 1024 pairs: T*k*E_loc up to about 1e9) return
+ * MOE_EUNSUPPORTED.  Every call on one GPU uses that GPU's one array, which
+ * keeps the last call's contents: two calls that may overlap on the same GPU
+ * (e.g. on two streams without an order between them) race and give
+ * undefined results; the caller must order them.
+ */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_permute_noalloc(int T, int k, int E, const int32_t* topk_ids,
+                        const int32_t* expert_map, int E_loc, int capacity,
+                        int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        const void* x, int d, int act_dtype, void* x_perm, void* stream);
 
 /*
  * moe_dispatch_owners - sender side of expert parallelism: every (token, slot)

@@ -12,7 +12,7 @@ MOE_PLACE_ROUND_ROBIN, MOE_PLACE_CONTIGUOUS = 0, 1
 # every symbol the header declares
 EXPORTS = [
     "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
-    "moe_permute", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
+    "moe_permute", "moe_permute_noalloc", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_plan",
     "moe_layer_fwd",
     "moe_layer_bwd_workspace_bytes", "moe_layer_bwd", "moe_quantize_int4", "moe_strerror", "moe_last_error",
@@ -78,6 +78,8 @@ def load(path: str = LIB_PATH):
         "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
         "moe_permute": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp,
                                  _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+        "moe_permute_noalloc": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp,
+                                         _vp, _c_int, _c_int, _vp, _vp]),
         "moe_dispatch_owners_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
         "moe_dispatch_owners": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),

@@ -109,6 +109,31 @@ def permute(topk_ids: torch.Tensor, E: int, E_loc: Optional[int] = None,
     return offsets, sp, pos, x_perm
 
 
+def permute_noalloc(topk_ids: torch.Tensor, E: int, E_loc: Optional[int] = None,
+                    expert_map: Optional[torch.Tensor] = None, capacity: int = 0,
+                    x: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+    """The grouping step without a workspace (moe_permute_noalloc: the library's
+    static scratch).  ``out`` may hold preallocated (expert_offsets, sorted_pair,
+    pair_pos, x_perm) tensors; then nothing is allocated here either.  Returns
+    the same tuple as ``permute``."""
+    lib = load()
+    T, k = topk_ids.shape
+    E_loc = E if E_loc is None else E_loc
+    dev = topk_ids.device
+    if out is None:
+        offsets = torch.empty(E_loc + 1, dtype=torch.int32, device=dev)
+        sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+        pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+        x_perm = torch.zeros((T * k, x.shape[1]), dtype=x.dtype, device=dev) if x is not None else None
+    else:
+        offsets, sp, pos, x_perm = out
+    d, dt = (x.shape[1], _dt(x)) if x is not None else (0, MOE_BF16)
+    check("moe_permute_noalloc", lib.moe_permute_noalloc(T, k, E, _p(topk_ids), _p(expert_map), E_loc, capacity,
+                                                         _p(offsets), _p(sp), _p(pos), _p(x), d, dt, _p(x_perm),
+                                                         _stream(dev)))
+    return offsets, sp, pos, x_perm
+
+
 _PLACE = {"round_robin": _lib.MOE_PLACE_ROUND_ROBIN, "contiguous": _lib.MOE_PLACE_CONTIGUOUS}
 
 

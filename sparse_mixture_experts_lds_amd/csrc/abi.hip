@@ -5,7 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
-
+#include <mutex>
 #include <string>
 
 #include "bwd.h"
@@ -479,6 +479,62 @@ int recompute_gu(int wt, bool grouped, const void* x, int T, int k, const int32_
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free grouping
+// Scratch of moe_permute_noalloc (the per-block expert histograms and bases of
+// the grouping step): one static device array per GPU, held until the process
+// ends.  Its name is a host-side stand-in in host code; the device address of
+// each GPU's copy is looked up once per device (hipGetSymbolAddress with that
+// device current) and only that address reaches kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)MOE_PERMUTE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) int32_t scratch[kNoallocScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null until looked up)
+
+// Device address of this stream's device's copy of `scratch`.
+int scratch_ptr(hipStream_t s, int32_t** out) {
+  int dev = 0;
+  if (s) MOE_HIP(hipStreamGetDevice(s, &dev));
+  else MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    MOE_HIP(hipGetDevice(&cur));
+    if (cur != dev) MOE_HIP(hipSetDevice(dev));
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_fail(e2);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return MOE_EHIP;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Argument checks shared by moe_permute and moe_permute_noalloc.
+int check_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* expert_map, int E_loc, int capacity,
+                  const int32_t* expert_offsets, const int32_t* sorted_pair, const int32_t* pair_pos, const void* x,
+                  int d, int act_dtype, const void* x_perm) {
+  int rc = check_route_dims(T, E, k);
+  if (rc) return rc;
+  if (E_loc <= 0 || E_loc > E || capacity < 0) return MOE_EINVAL;
+  if (!expert_map && E_loc != E) return MOE_EINVAL;
+  if (!expert_offsets) return MOE_EINVAL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_EINVAL;
+  if (x_perm) {
+    if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
+    if ((rc = check_width(d, act_dtype))) return rc;
+    if (!x) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -542,22 +598,34 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* exp
                 int capacity, int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
                 const void* x, int d, int act_dtype, void* x_perm, void* ws, size_t ws_bytes,
                 void* stream) {
-  int rc = check_route_dims(T, E, k);
+  const int rc = check_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, expert_offsets, sorted_pair, pair_pos,
+                               x, d, act_dtype, x_perm);
   if (rc) return rc;
-  if (E_loc <= 0 || E_loc > E || capacity < 0) return MOE_EINVAL;
-  if (!expert_map && E_loc != E) return MOE_EINVAL;
-  if (!expert_offsets) return MOE_EINVAL;
-  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_EINVAL;
-  if (x_perm) {
-    if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
-    if ((rc = check_width(d, act_dtype))) return rc;
-    if (!x) return MOE_EINVAL;
-  }
   if (ws_bytes < moe_permute_workspace_bytes(T, k, E_loc)) return MOE_EWORKSPACE;
   if (T > 0 && !ws) return MOE_EINVAL;
   hipStream_t s = as_stream(stream);
   MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr, nullptr,
                          sorted_pair, pair_pos, static_cast<int32_t*>(ws), s));
+  if (x_perm && T > 0)
+    MOE_HIP(launch_gather_rows(T * k, d, act_dtype == MOE_BF16, x, sorted_pair, k, expert_offsets + E_loc,
+                               x_perm, s));
+  return MOE_OK;
+}
+
+int moe_permute_noalloc(int T, int k, int E, const int32_t* topk_ids, const int32_t* expert_map, int E_loc,
+                        int capacity, int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        const void* x, int d, int act_dtype, void* x_perm, void* stream) {
+  int rc = check_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, expert_offsets, sorted_pair, pair_pos, x,
+                         d, act_dtype, x_perm);
+  if (rc) return rc;
+  // every scratch entry the kernels read is written first in the same call
+  // (histograms, then bases), so nothing needs clearing between calls
+  if (permute_ws_bytes(T * k, E_loc) > kNoallocScratchBytes) return MOE_EUNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  int32_t* ws = nullptr;
+  if ((rc = scratch_ptr(s, &ws))) return rc;
+  MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr, nullptr,
+                         sorted_pair, pair_pos, ws, s));
   if (x_perm && T > 0)
     MOE_HIP(launch_gather_rows(T * k, d, act_dtype == MOE_BF16, x, sorted_pair, k, expert_offsets + E_loc,
                                x_perm, s));

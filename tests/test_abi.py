@@ -49,6 +49,12 @@ def test_argument_errors_before_launch():
     assert lib.moe_permute(100, 2, 8, P, None, 8, 0, P, P, P, None, 0, 1, None, P, need - 1, None) == _lib.MOE_EWORKSPACE
     assert lib.moe_permute(100, 2, 8, P, None, 4, 0, P, P, P, None, 0, 1, None, P, need, None) == _lib.MOE_EINVAL
     assert lib.moe_permute(100, 2, 8, P, None, 8, -1, P, P, P, None, 0, 1, None, P, need, None) == _lib.MOE_EINVAL
+    # the allocation-free grouping: the same checks, and sizes beyond its static
+    # scratch (2^22 pairs over 1024 experts: 4096 blocks x 1024 x 4 B = 16 MiB)
+    assert lib.moe_permute_noalloc(100, 2, 8, P, None, 4, 0, P, P, P, None, 0, 1, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute_noalloc(100, 2, 8, P, None, 8, -1, P, P, P, None, 0, 1, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_permute_noalloc(1 << 20, 4, 1024, P, None, 1024, 0, P, P, P, None, 0, 1, None,
+                                   None) == _lib.MOE_EUNSUPPORTED
     # expert FFN: fp32 activations with bf16 weights; INT4 with d % 128 != 0; missing scales
     nb = lib.moe_expert_ffn_workspace_bytes(4, 64, 256, 128, 1)
     assert lib.moe_expert_ffn(4, 64, 256, 128, 0, 0, 1, P, P, P, P, P, None, None, None, P, P, nb, None) == _lib.MOE_EUNSUPPORTED
