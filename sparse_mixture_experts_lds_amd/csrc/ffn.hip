@@ -4,6 +4,7 @@
 // in ordinary VGPRs instead of being shuffled between register files.
 #include "ffn_kernel.h"
 #include "ffn_wide.h"
+#include "ffn_wide64.h"
 
 namespace moe {
 
@@ -77,7 +78,11 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   if (a.a_rows < 0 || (size_t)a.a_rows * (size_t)a.K * gelt > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (BM == ffn_wide::BM) {
     if (w_type != W_BF16 || split) return hipErrorInvalidValue;
-    // NF: weight rows per tile / 64 (4 -> 256, 2 -> 128)
+    // NF: weight rows per tile / 64 (4 -> 256, 2 -> 128); 256 weight rows and
+    // K a multiple of 128 take the 64-deep k-blocks
+    if (NF == 4 && a.K % 128 == 0)
+      return gateup ? ffn_wide64::launch<true>(&a, 1, a.ev_start, a.ev_stop, s)
+                    : ffn_wide64::launch<false>(&a, 1, a.ev_start, a.ev_stop, s);
     return gateup ? ffn_wide::launch_wide<true>(&a, 1, 64 * NF, a.ev_start, a.ev_stop, s)
                   : ffn_wide::launch_wide<false>(&a, 1, 64 * NF, a.ev_start, a.ev_stop, s);
   }
@@ -105,6 +110,9 @@ hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a
   const FfnGemmArgs a[2] = {a0, a1};
   for (const FfnGemmArgs& p : a)
     if (p.a_rows < 0 || (size_t)p.a_rows * (size_t)p.K * 2 > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  if (NF == 4 && a0.K % 128 == 0 && a1.K % 128 == 0)
+    return gateup ? ffn_wide64::launch<true>(a, 2, ev_start, ev_stop, s)
+                  : ffn_wide64::launch<false>(a, 2, ev_start, ev_stop, s);
   return gateup ? ffn_wide::launch_wide<true>(a, 2, 64 * NF, ev_start, ev_stop, s)
                 : ffn_wide::launch_wide<false>(a, 2, 64 * NF, ev_start, ev_stop, s);
 }
