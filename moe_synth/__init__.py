@@ -5,5 +5,5 @@ layer's arithmetic (no routing, no permutation, no expert math, no quantiser).
 Both the CPU oracle and the HIP path are fed from here, and nothing else is
 shared between them.
 """
-from .configs import CONFIGS, WORKLOADS, scaled, config_by_name  # noqa: F401
-from .generate import make_inputs, MoEInputs  # noqa: F401
+from .configs import CONFIGS, TREE_CONFIGS, WORKLOADS, TreeRouteConfig, scaled, config_by_name  # noqa: F401
+from .generate import make_inputs, make_tree_inputs, MoEInputs  # noqa: F401

@@ -85,6 +85,34 @@ CONFIGS = {
 WORKLOADS = ["tiny_fp32", "granular_bf16", "wide_geglu_bf16", "decode_bf16", "int4_share"]
 
 
+@dataclasses.dataclass(frozen=True)
+class TreeRouteConfig:
+    """Shape of a hierarchical (expert-tree) routing step: T tokens of width d
+    routed to k of E experts, the leaves of a tree with ``branch`` children per
+    node and ``levels`` levels (kieve-moe "Features", fractal tiling routing)."""
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    branch: int
+    levels: int
+    dtype: str       # "f32" | "bf16": x and the gate rows
+    renorm: bool
+    seed: int = 0
+
+
+# The 896-expert pool of the INT4 share (512 tokens of width 7168, top-16) as a
+# 32-ary tree of two levels (28 inner nodes), and a pool of 32,768 experts
+# (a 32-ary tree of three levels) at the width of the flagship's larger sibling.
+TREE_CONFIGS = {
+    "tree_route_896": TreeRouteConfig("tree_route_896", T=512, d=7168, E=896, k=16, branch=32, levels=2,
+                                      dtype="bf16", renorm=True),
+    "tree_route_32k": TreeRouteConfig("tree_route_32k", T=8192, d=2048, E=32768, k=8, branch=32, levels=3,
+                                      dtype="bf16", renorm=True),
+}
+
+
 def config_by_name(name: str) -> MoEConfig:
     return CONFIGS[name]
 

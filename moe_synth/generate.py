@@ -127,6 +127,17 @@ def make_inputs(cfg: MoEConfig, fast_weights: bool = False, device: str = "cpu")
                      wd=wd, wsg=wsg, wsu=wsu, wsd=wsd, expert_map=emap, capacity=cfg.capacity)
 
 
+def make_tree_inputs(cfg, rows: int):
+    """Inputs of a hierarchical routing step: x ``[T, d]`` ~ N(0, 1), then the
+    ``rows`` gate rows ``[rows, d]`` ~ N(0, 1/sqrt(d)), from ``default_rng(seed)``
+    in that order, cast to the config's dtype.  The row count is the caller's
+    (it follows from the tree's shape, which is the method's business)."""
+    rng = np.random.default_rng(cfg.seed)
+    x = _to_dtype(_normal(rng, (cfg.T, cfg.d), 1.0), cfg.dtype)
+    w = _to_dtype(_normal(rng, (rows, cfg.d), 1.0 / np.sqrt(cfg.d)), cfg.dtype)
+    return x, w
+
+
 def as_f64(t) -> Optional[np.ndarray]:
     """Exact float64 copy of a float32/bf16 tensor (or None)."""
     if t is None:

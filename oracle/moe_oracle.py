@@ -40,6 +40,12 @@ What the layer computes, and where it is stated:
 * INT4 weights.  ExpertMesh README: group-scaled signed INT4 weights with FP16
   group scales, laid out ``[expert, output, packed_input]``, plus a bit-exact
   NumPy quantiser and dequantiser.
+* Hierarchical (fractal) router.  kieve-moe "Features": a cheap router for very
+  large expert pools that routes self-similarly down an expert tree of
+  ``branch`` children per node and ``levels`` levels.  The page gives that one
+  sentence and no formula: ``tree_route`` is this repository's reading of it
+  (below), and its parity is UNPINNED against the page; the pins hold it to the
+  reading only.
 
 Readings taken where the pages are silent (each is listed in the design notes
 of the repository):
@@ -60,10 +66,25 @@ of the repository):
   ``clip(rint(w / fp32(scale)), -8, 7)`` with the division in float32 and
   ties to even, an all-zero group (or a scale that rounds to zero) gets code
   0; byte i of a packed row holds input 2i in its low nibble and 2i+1 in its
-  high nibble, two's complement; the weight is ``float(scale) * code``.
+  high nibble, two's complement; the weight is ``float(scale) * code``;
+* hierarchical router: the E experts are the leaves of a tree with ``branch``
+  children per node and ``levels`` levels (E <= branch**levels); leaf e is
+  reached by the base-``branch`` digits of e, most significant first; node i at
+  depth l has children i*branch + c, and a node exists when a leaf below it
+  does, so depth l holds ``ceil(E / branch**(levels - l))`` nodes.  Every
+  internal node scores its existing children with its own bias-free linear gate
+  (one weight row per non-root node) and takes the softmax over them; a leaf's
+  probability is the product of the child probabilities on its path.
+  Selection is a beam search of width k: at each depth the kept nodes' children
+  are ranked by path log-probability (higher first, ties to the lower node id)
+  and the best ``min(k, nodes at that depth)`` are kept; the k leaves kept at
+  the last depth are the selected experts, slot j the j-th best, and a gate is
+  the leaf's path probability, divided by the sum over the k when ``renorm``.
 
 Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
 against closed forms, library routines, brute force and invariants.
+``tree_route`` and ``tree_path_logprob`` are parity unpinned against the page
+(one sentence, no formula): their pins check the reading above.
 """
 from __future__ import annotations
 
@@ -580,3 +601,88 @@ def combine(y_slots, pair_pos, w, shared_y=None) -> np.ndarray:
     if shared_y is not None:
         out += np.asarray(shared_y, np.float64)
     return out
+
+
+# --------------------------------------------------------------------------
+# Hierarchical (fractal) router: reading of kieve-moe "Features"; parity
+# unpinned against the page
+# --------------------------------------------------------------------------
+def tree_nodes(E: int, branch: int, levels: int):
+    """Existing nodes per depth, ``n[l] = ceil(E / branch**(levels - l))`` for
+    l = 0..levels (n[0] = 1 root, n[levels] = E leaves), and the first gate row
+    of each depth's children: ``first[l] = branch * (n[0] + ... + n[l-1])``.
+    The child j of depth l+1 (j < branch * n[l]) has gate row ``first[l] + j``;
+    the table has ``first[levels]`` rows."""
+    if branch < 2 or levels < 1 or not (1 <= E <= branch ** levels):
+        raise ValueError("need branch >= 2, levels >= 1, 1 <= E <= branch**levels")
+    n = [-(-E // branch ** (levels - l)) for l in range(levels + 1)]
+    first = [branch * sum(n[:l]) for l in range(levels + 1)]
+    return n, first
+
+
+def _children_logprob(xt, W, first_l, node, branch, n_next):
+    """log-softmax of one node's existing children: (child ids, log p)."""
+    kids = np.arange(node * branch, min(node * branch + branch, n_next))
+    z = W[first_l + kids] @ xt
+    m = z.max()
+    return kids, z - (m + np.log(np.sum(np.exp(z - m))))
+
+
+def tree_route(k: int, renorm: bool, x, w_tree, branch: int, levels: int, E: int):
+    """Beam-search routing down the expert tree, one token at a time.
+
+    Returns ``(ids [T, k] int64, w [T, k] float64, margin [T] float64)``;
+    ``margin[t]`` is the smallest log-probability gap on which the token's
+    result depends: at every depth between the last kept and the first dropped
+    candidate, and at the last depth also between consecutive kept ones
+    (+inf when nothing is dropped and k = 1)."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(w_tree, np.float64)
+    n, first = tree_nodes(E, branch, levels)
+    if W.shape != (first[levels], x.shape[1]):
+        raise ValueError("w_tree must be [%d, d]" % first[levels])
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    T = x.shape[0]
+    ids = np.empty((T, k), np.int64)
+    w = np.empty((T, k), np.float64)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        beam = [(0.0, 0)]  # (path log-probability, node id) at depth 0
+        for l in range(levels):
+            cand = []
+            for score, node in beam:
+                kids, lp = _children_logprob(x[t], W, first[l], node, branch, n[l + 1])
+                cand += [(score + v, int(c)) for c, v in zip(kids, lp)]
+            cand.sort(key=lambda sv: (-sv[0], sv[1]))
+            keep = min(k, n[l + 1])
+            if len(cand) > keep:
+                margin[t] = min(margin[t], cand[keep - 1][0] - cand[keep][0])
+            if l == levels - 1:
+                for a, b in zip(cand[:keep - 1], cand[1:keep]):
+                    margin[t] = min(margin[t], a[0] - b[0])
+            beam = cand[:keep]
+        ids[t] = [node for _, node in beam]
+        p = np.exp([score for score, _ in beam])
+        w[t] = p / p.sum() if renorm else p
+    return ids, w, margin
+
+
+def tree_path_logprob(x, w_tree, branch: int, levels: int, E: int, ids):
+    """Path log-probability of given leaves: ``lp[t, j] = log P(ids[t, j] | x[t])``,
+    the sum over the path's depths of the child's log-softmax within its
+    parent (the same definition as ``tree_route``'s scores, for any leaf)."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(w_tree, np.float64)
+    n, first = tree_nodes(E, branch, levels)
+    ids = np.asarray(ids)
+    lp = np.zeros(ids.shape, np.float64)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            for l in range(levels):
+                node = e // branch ** (levels - l)
+                child = e // branch ** (levels - l - 1)
+                kids, v = _children_logprob(x[t], W, first[l], node, branch, n[l + 1])
+                lp[t, j] += v[child - kids[0]]
+    return lp

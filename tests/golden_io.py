@@ -60,3 +60,31 @@ def activation_points():
         name, g, v = ln.split()
         pts.append((name, float(g), float(v)))
     return pts
+
+
+def tree_route_cases():
+    """Cases of tree_route_worked_example.txt: dicts with branch, levels, E, x,
+    rows and a list of (k, ids, w_raw, w_renorm, margin or None)."""
+    cases, cur, sub = [], None, None
+    for ln in _lines("tree_route_worked_example.txt"):
+        key, _, val = ln.partition(":")
+        toks = val.split()
+        if key == "branch":
+            cur = {"branch": int(toks[0]), "rows": [], "subs": []}
+            cases.append(cur)
+        elif key in ("levels", "E"):
+            cur[key] = int(toks[0])
+        elif key == "x":
+            cur["x"] = [_logit(t) for t in toks]
+        elif key == "row":
+            cur["rows"].append([_logit(t) for t in toks])
+        elif key == "k":
+            sub = {"k": int(toks[0]), "margin": None}
+            cur["subs"].append(sub)
+        elif key == "ids":
+            sub["ids"] = [int(t) for t in toks]
+        elif key == "margin":
+            sub["margin"] = float(toks[0])
+        else:
+            sub[key] = [float(Fraction(t)) for t in toks]
+    return cases

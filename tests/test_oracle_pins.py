@@ -14,7 +14,7 @@ import scipy.special
 import torch
 
 import oracle as orc
-from golden_io import activation_points, int4_case, route_cases
+from golden_io import activation_points, int4_case, route_cases, tree_route_cases
 
 RNG = np.random.default_rng(1234)
 
@@ -709,3 +709,140 @@ def test_round_bf16_ties_and_single_rounding():
     r = orc.round_to_dtype(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, -(1 + 2 ** -8)]), "bf16")
     # ties go to even; a float64 value just above a tie rounds up (no detour via float32)
     assert r.tolist() == [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0]
+
+
+
+# ---------------------------------------------------------------- hierarchical router
+# The page (kieve-moe "Features") gives one sentence and no formula, so these
+# pins hold tree_route to the reading written in the oracle's header, not to
+# the page: parity unpinned against the page.
+def _tree_case(B, L, E, d, T, seed):
+    rng = np.random.default_rng(seed)
+    n, first = orc.tree_nodes(E, B, L)
+    return rng.standard_normal((T, d)), rng.standard_normal((first[L], d)) / np.sqrt(d)
+
+
+def _leaf_probs_brute_force(xt, W, B, L, E):
+    """Probability of every leaf by enumerating the whole tree: a node at depth
+    l exists when its first leaf (id * B**(L - l)) is below E; each node's
+    children share a softmax of x . row over the existing ones."""
+    first = 0
+    probs = {(): 1.0}  # digit prefix -> probability
+    for l in range(L):
+        nxt = {}
+        row_base = first
+        for prefix, p in probs.items():
+            node = sum(dg * B ** (len(prefix) - 1 - i) for i, dg in enumerate(prefix))
+            kids = [c for c in range(B) if (node * B + c) * B ** (L - l - 1) < E]
+            z = [math.fsum(xt[i] * W[row_base + node * B + c, i] for i in range(len(xt))) for c in kids]
+            m = max(z)
+            den = math.fsum(math.exp(v - m) for v in z)
+            for c, v in zip(kids, z):
+                nxt[prefix + (c,)] = p * math.exp(v - m) / den
+        first += B * len({sum(dg * B ** (len(pr) - 1 - i) for i, dg in enumerate(pr)) for pr in probs})
+        probs = nxt
+    out = np.zeros(E)
+    for prefix, p in probs.items():
+        out[sum(dg * B ** (L - 1 - i) for i, dg in enumerate(prefix))] = p
+    return out
+
+
+@pytest.mark.parametrize("case", tree_route_cases(), ids=lambda c: "B%d_L%d_E%d" % (c["branch"], c["levels"], c["E"]))
+def test_tree_route_worked_examples(case):
+    x = np.array([case["x"]])
+    W = np.array(case["rows"])
+    for sub in case["subs"]:
+        for renorm, key in ((False, "w_raw"), (True, "w_renorm")):
+            ids, w, margin = orc.tree_route(sub["k"], renorm, x, W, case["branch"], case["levels"], case["E"])
+            assert ids[0].tolist() == sub["ids"], (sub["k"], ids)
+            np.testing.assert_allclose(w[0], sub[key], rtol=0, atol=1e-14)
+            if sub["margin"] is not None:
+                assert abs(margin[0] - sub["margin"]) < 1e-14
+        lp = orc.tree_path_logprob(x, W, case["branch"], case["levels"], case["E"], np.array([sub["ids"]]))
+        np.testing.assert_allclose(np.exp(lp[0]), sub["w_raw"], rtol=0, atol=1e-14)
+
+
+def test_tree_layout_sizes():
+    # a full tree has B + B^2 + ... + B^L gate rows; a trimmed one drops the
+    # nodes with no leaf below them
+    assert orc.tree_nodes(16, 2, 4) == ([1, 2, 4, 8, 16], [0, 2, 6, 14, 30])
+    assert orc.tree_nodes(896, 32, 2) == ([1, 28, 896], [0, 32, 928])
+    assert orc.tree_nodes(20, 3, 3) == ([1, 3, 7, 20], [0, 3, 12, 33])
+    for bad in ((5, 2, 2), (4, 1, 2), (4, 2, 0), (0, 2, 2)):
+        with pytest.raises(ValueError):
+            orc.tree_nodes(*bad)
+
+
+@pytest.mark.parametrize("E,B,renorm", [(5, 8, True), (8, 8, False), (3, 4, True)])
+def test_tree_route_one_level_is_the_flat_router(E, B, renorm):
+    # one level: the root's softmax over its E children is the flat router's
+    # softmax over E experts, and a beam of width k is plain top-k
+    x, W = _tree_case(B, 1, E, 16, 60, seed=E)
+    for k in range(1, E + 1):
+        ids, w, _ = orc.tree_route(k, renorm, x, W, B, 1, E)
+        _, ids_f, w_f = orc.route(k, renorm, x=x, w_router=W[:E])
+        assert np.array_equal(ids, ids_f)
+        np.testing.assert_allclose(w, w_f, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("B,L,E", [(3, 3, 20), (2, 4, 16), (4, 2, 13), (2, 3, 5)])
+def test_tree_route_wide_beam_equals_exhaustive_top_k(B, L, E):
+    # a beam as wide as the widest inner depth keeps every node, so the result
+    # is the exact top-k of the whole leaf distribution
+    n, _ = orc.tree_nodes(E, B, L)
+    x, W = _tree_case(B, L, E, 8, 25, seed=B * 100 + E)
+    for k in sorted({n[L - 1], E}):
+        ids, w, _ = orc.tree_route(k, False, x, W, B, L, E)
+        for t in range(x.shape[0]):
+            p = _leaf_probs_brute_force(x[t], W, B, L, E)
+            assert abs(p.sum() - 1) < 1e-12  # the hierarchical softmax is a distribution
+            order = sorted(range(E), key=lambda e: (-p[e], e))[:k]
+            assert ids[t].tolist() == order
+            np.testing.assert_allclose(w[t], p[order], rtol=1e-12, atol=1e-15)
+        if k == E:
+            np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_tree_route_narrow_beam_is_greedy_per_depth():
+    # width 1 follows the most probable child at every depth (the first one on
+    # ties); checked against the brute-force leaf probabilities
+    B, L, E = 3, 3, 27
+    x, W = _tree_case(B, L, E, 8, 40, seed=7)
+    ids, w, _ = orc.tree_route(1, False, x, W, B, L, E)
+    _, first = orc.tree_nodes(E, B, L)
+    for t in range(x.shape[0]):
+        node = 0
+        for l in range(L):
+            z = W[first[l] + node * B: first[l] + node * B + B] @ x[t]
+            node = node * B + int(np.argmax(z))
+        assert ids[t, 0] == node
+        assert abs(w[t, 0] - _leaf_probs_brute_force(x[t], W, B, L, E)[node]) < 1e-12
+
+
+def test_tree_route_subtree_relabelling():
+    # swapping the root's children 0 and 2 (their gate rows and the blocks of
+    # rows that score their children) swaps the leading digit of every leaf
+    B, L, E = 3, 2, 9
+    x, W = _tree_case(B, L, E, 12, 50, seed=3)
+    W2 = W.copy()
+    W2[[0, 2]] = W[[2, 0]]
+    W2[3:6], W2[9:12] = W[9:12], W[3:6]
+    for k in (1, 2, 4, 9):
+        ids, w, _ = orc.tree_route(k, True, x, W, B, L, E)
+        ids2, w2, _ = orc.tree_route(k, True, x, W2, B, L, E)
+        swap = np.array([(2 - e // 3) * 3 + e % 3 if e // 3 != 1 else e for e in range(9)])
+        assert np.array_equal(swap[ids2], ids)
+        np.testing.assert_allclose(w2, w, rtol=1e-12)
+
+
+def test_tree_route_gates_and_margins():
+    B, L, E = 4, 3, 50
+    x, W = _tree_case(B, L, E, 16, 30, seed=11)
+    ids, w, margin = orc.tree_route(6, False, x, W, B, L, E)
+    lp = orc.tree_path_logprob(x, W, B, L, E, ids)
+    np.testing.assert_allclose(w, np.exp(lp), rtol=1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0) and np.all(margin >= 0)
+    assert all(len(set(r)) == 6 for r in ids.tolist()) and ids.min() >= 0 and ids.max() < E
+    ids_n, w_n, _ = orc.tree_route(6, True, x, W, B, L, E)
+    assert np.array_equal(ids_n, ids)
+    np.testing.assert_allclose(w_n, w / w.sum(axis=1, keepdims=True), rtol=1e-12)
