@@ -5,6 +5,8 @@
  * The layer (forward only) runs in five steps, each a call below:
  *   moe_route       router logits GEMM, softmax and top-k selection
  *   moe_router_stats per-expert counts, mean probabilities, balance loss
+ *   moe_route_tree  hierarchical routing down an expert tree (a router for
+ *                   very large expert pools)
  *   moe_permute     grouping of (token, slot) pairs by expert
  *   moe_dispatch_owners  the same grouping by owner of the expert (sender
  *                   side of expert parallelism)
@@ -25,7 +27,10 @@
  *     division of the k gates by their sum, per-expert gather / scatter-add.
  *   MoEEvolve, "Architecture": SwiGLU experts, one always-active shared
  *     expert, capacity-factor static-shape dispatch.
- *   kieve-moe, "Features": top-k GeGLU experts.
+ *   kieve-moe, "Features": top-k GeGLU experts; fractal tiling routing, a
+ *     self-similar routing down a branch^levels expert tree for very large
+ *     expert pools (one sentence, no formula: moe_route_tree states the
+ *     reading it implements).
  *   ExpertMesh README: group-scaled signed INT4 weights with FP16 group
  *     scales in the [expert, output, packed_input] layout, a stable C ABI,
  *     per-expert grouping of activations that keeps each token and top-k
@@ -142,6 +147,51 @@ size_t moe_router_stats_workspace_bytes(int T, int E);
 int moe_router_stats(int T, int E, int k, const float* logits, const float* expert_bias,
                      const int32_t* topk_ids, int32_t* expert_counts, float* prob_mean,
                      float* balance_loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_tree - hierarchical routing down an expert tree (kieve-moe
+ * "Features", fractal tiling routing: self-similar routing over a
+ * branch^levels expert tree, a cheap router for very large expert pools).
+ * The page gives no formula; this is the reading implemented:
+ *
+ *   tree     the E experts are the leaves of a tree with B = branch children
+ *            per node and L = levels levels (E <= B^L); leaf e is reached by
+ *            the base-B digits of e, most significant first; node i at depth
+ *            l has children i*B + c; depth l holds n_l = ceil(E / B^(L-l))
+ *            nodes (those with a leaf below them)
+ *   gates    one row of w_tree per non-root node: child j of depth l+1 has
+ *            row first_l + j, first_l = B * (n_0 + ... + n_{l-1}); the table
+ *            has moe_tree_gate_rows(E, branch, levels) = first_L rows (rows of
+ *            children that do not exist are never read)
+ *   scores   s(child) = sum_i x[t,i] * w_tree[row(child), i] (fp32 accumulate);
+ *            each node's existing children share a softmax, and a leaf's
+ *            log-probability is the sum of its path's log-softmax terms
+ *   select   beam search of width k: at each depth the kept nodes' children
+ *            are ranked by path log-probability (higher first, ties to the
+ *            lower node id) and the best min(k, n_{l+1}) kept; topk_ids[t,j]
+ *            = the j-th leaf kept at the last depth, topk_w[t,j] = its path
+ *            probability, divided by the sum over the k when renorm != 0.
+ *            With levels = 1 this is moe_route with w_router = the first E
+ *            rows and no bias.
+ *
+ *   T, d           tokens (T = 0 is a no-op), model width (a multiple of 64)
+ *   E, k           experts (leaves), picks: 1 <= k <= min(E, 32), k*branch <= 1024
+ *   branch, levels 2 <= branch <= 64, 1 <= levels <= 16, E <= branch^levels,
+ *                  and at most 1024 nodes above the leaves (E <= 1024 * branch)
+ *   act_dtype      MOE_F32 or MOE_BF16: dtype of x and w_tree
+ *   x              [T, d];  w_tree [moe_tree_gate_rows(E, branch, levels), d]
+ *   topk_ids       out [T, k] int32;  topk_w out [T, k] fp32
+ *   ws, ws_bytes   device workspace of at least
+ *                  moe_route_tree_workspace_bytes(T, d, E, k, branch, levels, act_dtype)
+ * Deterministic: repeated calls give identical bits.  Errors: MOE_EINVAL for
+ * a NULL buffer or k outside [1, E]; MOE_EUNSUPPORTED outside the limits;
+ * MOE_EWORKSPACE for a short workspace.
+ */
+long long moe_tree_gate_rows(int E, int branch, int levels);   /* < 0: error code */
+size_t moe_route_tree_workspace_bytes(int T, int d, int E, int k, int branch, int levels, int act_dtype);
+int moe_route_tree(int T, int d, int E, int k, int branch, int levels, int act_dtype,
+                   const void* x, const void* w_tree, int renorm,
+                   int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_permute - group the pairs p = t*k + j by local expert (ExpertMesh:

@@ -6,7 +6,7 @@ outputs and workspace with torch, and passes torch's current HIP stream.  All
 arithmetic runs in the library's HIP kernels; nothing here computes.
 """
 from .api import (  # noqa: F401
-    route, router_stats, permute, permute_noalloc, dispatch_owners, expert_ffn, combine, layer_fwd, quantize_int4, LayerWeights,
+    route, route_tree, route_tree_workspace_bytes, tree_gate_rows, router_stats, permute, permute_noalloc, dispatch_owners, expert_ffn, combine, layer_fwd, quantize_int4, LayerWeights,
     permute_workspace_bytes, expert_ffn_workspace_bytes, layer_workspace_bytes, layer_plan, layer_bwd,
     layer_bwd_workspace_bytes,
 )

@@ -11,7 +11,8 @@ MOE_PLACE_ROUND_ROBIN, MOE_PLACE_CONTIGUOUS = 0, 1
 
 # every symbol the header declares
 EXPORTS = [
-    "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_permute_workspace_bytes",
+    "moe_route", "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_tree_gate_rows",
+    "moe_route_tree_workspace_bytes", "moe_route_tree", "moe_permute_workspace_bytes",
     "moe_permute", "moe_permute_noalloc", "moe_dispatch_owners_workspace_bytes", "moe_dispatch_owners",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_workspace_bytes", "moe_layer_plan",
     "moe_layer_fwd",
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH):
         "moe_router_stats_workspace_bytes": (_c_size, [_c_int, _c_int]),
         "moe_router_stats": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                                       _vp]),
+        "moe_tree_gate_rows": (ctypes.c_longlong, [_c_int, _c_int, _c_int]),
+        "moe_route_tree_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+        "moe_route_tree": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int,
+                                    _vp, _vp, _vp, _c_size, _vp]),
         "moe_permute_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
         "moe_permute": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp,
                                  _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),

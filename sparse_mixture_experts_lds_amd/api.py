@@ -63,6 +63,37 @@ def route(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], k: int, r
     return ids, tw, lo
 
 
+def tree_gate_rows(E: int, branch: int, levels: int) -> int:
+    """Rows of the gate table of an expert tree (one per non-root node)."""
+    n = load().moe_tree_gate_rows(E, branch, levels)
+    check("moe_tree_gate_rows", n if n < 0 else 0)
+    return int(n)
+
+
+def route_tree_workspace_bytes(T: int, d: int, E: int, k: int, branch: int, levels: int,
+                               dtype: torch.dtype = torch.bfloat16) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_route_tree_workspace_bytes(T, d, E, k, branch, levels, dt))
+
+
+def route_tree(x: torch.Tensor, w_tree: torch.Tensor, E: int, k: int, branch: int, levels: int, renorm: bool,
+               ws: Optional[torch.Tensor] = None, out=None):
+    """Hierarchical routing down an expert tree.  Returns (topk_ids int32 [T,k],
+    topk_w float32 [T,k]); ``ws`` (bytes) and ``out`` (ids, w) may be given."""
+    lib = load()
+    T, d = x.shape
+    dev = x.device
+    ids, tw = out if out is not None else (torch.empty((T, k), dtype=torch.int32, device=dev),
+                                            torch.empty((T, k), dtype=torch.float32, device=dev))
+    nb = lib.moe_route_tree_workspace_bytes(T, d, E, k, branch, levels, _dt(x))
+    if ws is None:
+        ws = _ws(nb, dev)
+    check("moe_route_tree", lib.moe_route_tree(T, d, E, k, branch, levels, _dt(x), _p(x), _p(w_tree),
+                                               int(bool(renorm)), _p(ids), _p(tw), _p(ws), ws.numel(),
+                                               _stream(dev)))
+    return ids, tw
+
+
 def router_stats(logits: torch.Tensor, topk_ids: torch.Tensor, bias: Optional[torch.Tensor] = None):
     """Router by-products.  Returns (expert_counts int32 [E], prob_mean float32 [E],
     balance_loss float32 [1])."""

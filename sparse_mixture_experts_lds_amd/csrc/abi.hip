@@ -589,6 +589,43 @@ int moe_router_stats(int T, int E, int k, const float* logits, const float* expe
   return MOE_OK;
 }
 
+namespace {
+int check_tree(int T, int d, int E, int k, int branch, int levels, int act_dtype, TreeShape* sh) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E || branch <= 0 || levels <= 0) return MOE_EINVAL;
+  if (!act_dtype_ok(act_dtype) || d % 64 || k > kMaxK || k * branch > 1024) return MOE_EUNSUPPORTED;
+  if (!tree_shape(E, branch, levels, sh) || sh->n[levels - 1] > kMaxE) return MOE_EUNSUPPORTED;
+  if ((long long)T * k * branch * 16 >= (1LL << 40) || (long long)T * k >= (1LL << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+long long moe_tree_gate_rows(int E, int branch, int levels) {
+  TreeShape sh;
+  if (E <= 0 || branch <= 0 || levels <= 0) return MOE_EINVAL;
+  if (!tree_shape(E, branch, levels, &sh)) return MOE_EUNSUPPORTED;
+  return sh.rows;
+}
+
+size_t moe_route_tree_workspace_bytes(int T, int d, int E, int k, int branch, int levels, int act_dtype) {
+  TreeShape sh;
+  if (check_tree(T, d, E, k, branch, levels, act_dtype, &sh)) return 0;
+  return tree_ws_bytes(T, d, k, branch, levels, act_dtype == MOE_BF16, sh);
+}
+
+int moe_route_tree(int T, int d, int E, int k, int branch, int levels, int act_dtype, const void* x,
+                   const void* w_tree, int renorm, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                   void* stream) {
+  TreeShape sh;
+  const int rc = check_tree(T, d, E, k, branch, levels, act_dtype, &sh);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_tree || !topk_ids || !topk_w || !ws) return MOE_EINVAL;
+  if (ws_bytes < tree_ws_bytes(T, d, k, branch, levels, act_dtype == MOE_BF16, sh)) return MOE_EWORKSPACE;
+  MOE_HIP(launch_route_tree(T, d, E, k, branch, levels, act_dtype == MOE_BF16, x, w_tree, renorm, topk_ids, topk_w,
+                            ws, as_stream(stream)));
+  return MOE_OK;
+}
+
 size_t moe_permute_workspace_bytes(int T, int k, int E_loc) {
   if (T < 0 || k <= 0 || E_loc <= 0) return 0;
   return align_up(permute_ws_bytes(T * k, E_loc));

@@ -130,6 +130,28 @@ __device__ __forceinline__ float group_sum(float x) {
   }
   return x;
 }
+// Arg-max over a group of G lanes: the larger value, then the lower id among
+// equal values; every lane of the group ends with the winner.  Two reductions
+// (the maximum value, then the minimum id of the lanes that hold it) of one
+// DPP or lane-swap move and one min/max each per step.
+template <int G>
+__device__ __forceinline__ int group_min(int x) {
+  x = min(x, dpp<kRowRor8>(x));
+  x = min(x, dpp<kRowRor4>(x));
+  x = min(x, dpp<kQuadSwap2>(x));
+  x = min(x, dpp<kQuadSwap1>(x));
+  if constexpr (G == 64) {
+    x = min(x, xor16_lanes(x));
+    x = min(x, xor32_lanes(x));
+  }
+  return x;
+}
+template <int G>
+__device__ __forceinline__ void group_argmax(float& v, int& e) {
+  const float m = group_max<G>(v);
+  e = group_min<G>(v == m ? e : 0x7fffffff);
+  v = m;
+}
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 // ---------------------------------------------------------------- launchers
@@ -240,6 +262,20 @@ hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a
 // y and shared_y are fp32 when y_f32, else in the output dtype.
 hipError_t launch_combine(int T, int k, int d, bool out_bf16, bool y_f32, const void* y, const int32_t* pair_pos,
                           const float* tw, const void* shared_y, void* out, hipStream_t s);
+
+// Hierarchical routing down an expert tree (tree_route.hip).
+constexpr int kTreeMaxBranch = 64;
+constexpr int kTreeMaxLevels = 16;
+struct TreeShape {
+  int n[kTreeMaxLevels + 1];          // existing nodes per depth (n[0] = 1, n[L] = E)
+  long long first[kTreeMaxLevels + 1];// first gate row of each depth's children
+  long long rows;                     // gate rows of the table
+};
+// false unless 2 <= B <= kTreeMaxBranch, 1 <= L <= kTreeMaxLevels, 1 <= E <= B^L
+bool tree_shape(int E, int B, int L, TreeShape* sh);
+size_t tree_ws_bytes(int T, int d, int k, int B, int L, bool bf16, const TreeShape& sh);
+hipError_t launch_route_tree(int T, int d, int E, int k, int B, int L, bool bf16, const void* x, const void* w,
+                             int renorm, int32_t* ids, float* tw, void* ws, hipStream_t s);
 
 // INT4 quantiser.
 hipError_t launch_quantize_int4(int rows, int K, const float* w, uint8_t* packed, uint16_t* scales,

@@ -36,24 +36,6 @@ namespace {
 constexpr int kTokTile = 16;
 constexpr int kSelectGroupMinTok = 4096;  // 16-lane selection groups from here on
 
-__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
-  if (ov > v || (ov == v && oe < e)) {
-    v = ov;
-    e = oe;
-  }
-}
-template <int G>
-__device__ __forceinline__ void group_argmax(float& v, int& e) {  // larger value, then lower id
-  take_better(v, e, dppf<kRowRor8>(v), dpp<kRowRor8>(e));
-  take_better(v, e, dppf<kRowRor4>(v), dpp<kRowRor4>(e));
-  take_better(v, e, dppf<kQuadSwap2>(v), dpp<kQuadSwap2>(e));
-  take_better(v, e, dppf<kQuadSwap1>(v), dpp<kQuadSwap1>(e));
-  if constexpr (G == 64) {
-    take_better(v, e, xor16_lanes(v), xor16_lanes(e));
-    take_better(v, e, xor32_lanes(v), xor32_lanes(e));
-  }
-}
-
 // Softmax and top-k of one token held by one wave: lane l holds experts l+64i in
 // v[i] (-inf past E).  Writes k ids (descending logit, ties to the lower id) and
 // their gates (renormalised over the selection, or over all E).

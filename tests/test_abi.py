@@ -172,3 +172,33 @@ def test_layer_workspace_covers_router_slices():
     L2 = _cfg_desc("decode_bf16")
     L2.w_router = None
     assert lib.moe_layer_workspace_bytes(ctypes.byref(L2)) <= nb - 8 * 512 * 128 * 4
+
+
+def test_tree_router_shape_queries_and_argument_errors():
+    import oracle as orc
+    lib = moe.load()
+    # gate rows of the expert tree: one per non-root node (trimmed trees too)
+    for E, B, L in ((896, 32, 2), (32768, 32, 3), (20, 3, 3), (16, 2, 4), (8, 8, 1), (5, 8, 1), (1, 2, 3)):
+        assert moe.tree_gate_rows(E, B, L) == orc.tree_nodes(E, B, L)[1][L]
+    assert lib.moe_tree_gate_rows(9, 2, 3) == _lib.MOE_EUNSUPPORTED      # E > B^L
+    assert lib.moe_tree_gate_rows(8, 1, 3) == _lib.MOE_EUNSUPPORTED      # branch 1
+    assert lib.moe_tree_gate_rows(8, 65, 1) == _lib.MOE_EUNSUPPORTED     # branch past 64
+    assert lib.moe_tree_gate_rows(8, 2, 0) == _lib.MOE_EINVAL
+    P = ctypes.c_void_p(16)  # never dereferenced
+    need = lib.moe_route_tree_workspace_bytes(100, 64, 896, 16, 32, 2, 1)
+    assert need > 0
+
+    def call(T=100, d=64, E=896, k=16, B=32, L=2, dt=1, x=P, w=P, ids=P, tw=P, ws=P, nb=need):
+        return lib.moe_route_tree(T, d, E, k, B, L, dt, x, w, 1, ids, tw, ws, nb, None)
+
+    assert call(nb=need - 1) == _lib.MOE_EWORKSPACE
+    assert call(k=0) == _lib.MOE_EINVAL and call(E=8, k=9, B=8, L=1) == _lib.MOE_EINVAL
+    assert call(d=96) == _lib.MOE_EUNSUPPORTED                       # d not a multiple of 64
+    assert call(k=33) == _lib.MOE_EUNSUPPORTED                       # k past 32
+    assert call(k=32, B=64, E=4096) == _lib.MOE_EUNSUPPORTED         # k * branch past 1024
+    assert call(E=1025 * 2, B=2, L=12) == _lib.MOE_EUNSUPPORTED      # 1025 nodes above the leaves
+    assert call(E=2000, B=32, L=2) == _lib.MOE_EUNSUPPORTED          # E > B^L
+    assert call(dt=2) == _lib.MOE_EUNSUPPORTED                       # INT4 activations
+    assert call(x=None) == _lib.MOE_EINVAL and call(ws=None) == _lib.MOE_EINVAL
+    # T = 0 is a no-op that needs no buffers
+    assert lib.moe_route_tree(0, 64, 896, 16, 32, 2, 1, None, None, 1, None, None, None, 0, None) == _lib.MOE_OK
