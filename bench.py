@@ -15,7 +15,9 @@ microseconds, so the timed steps carry no others).
 The headline workload (default: the wide GeGLU layer, 16384 tokens, the
 largest of the five) is timed over exactly --steps steps after --warmup
 untimed ones; the other four workloads follow in the same run as sub-records
-under "configs", each over at least 50 steps after at least 10 warm-ups.
+under "configs", each over at least 50 steps after at least 10 warm-ups, and
+so do the two hierarchical-routing workloads (the routing step alone, down an
+expert tree of 896 and of 32,768 experts).
 Step times are medians of the per-step event times (means are reported too).
 
 Prints one JSON line.  ``value`` is routed tokens per second (T / median layer
@@ -60,6 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--warm-cache", action="store_true", help="do not flush the Infinity Cache between steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--tree", default=None, metavar="WORKLOAD",
+                   help="time only this hierarchical-routing workload and print its record (for profiling)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes (5 times), to scale hardware "
                         "byte counters against a kernel of known traffic")
@@ -475,6 +479,73 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
     return rec
 
 
+def measure_tree_route(moe, torch, name, steps, warmup, args, flush):
+    """Hierarchical routing down an expert tree (moe_route_tree) on one of its
+    workloads: the whole routing step (all its launches) timed per call after
+    a cache flush.  Algorithmic work: x read once, the gate table read once,
+    the ids and gates written; FLOPs 2 d per scored child, the beam's children
+    only (B per kept node per depth).  Context: the flat router on the same
+    pool where it applies (E <= 1024), else the flat logits GEMM alone
+    (x times all E leaf rows, a library GEMM)."""
+    from moe_synth import TREE_CONFIGS, make_tree_inputs
+
+    cfg = TREE_CONFIGS[name]
+    dev = "cuda:0"
+    rows = moe.tree_gate_rows(cfg.E, cfg.branch, cfg.levels)
+    x, w = make_tree_inputs(cfg, rows)
+    x, w = x.to(dev), w.to(dev)
+    ab = 4 if cfg.dtype == "f32" else 2
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.route_tree_workspace_bytes(cfg.T, cfg.d, cfg.E, cfg.k, cfg.branch, cfg.levels, x.dtype),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        moe.route_tree(x, w, cfg.E, cfg.k, cfg.branch, cfg.levels, cfg.renorm, ws=ws, out=(ids, tw))
+
+    for _ in range(warmup):
+        call()
+    ms = timed_calls(torch, call, flush, args, steps)
+    # nodes per depth and beam widths, from the tree's shape
+    n = [-(-cfg.E // cfg.branch ** (cfg.levels - l)) for l in range(cfg.levels + 1)]
+    widths = [1] + [min(cfg.k, n[l]) for l in range(1, cfg.levels)]
+    work = {"bytes": cfg.T * cfg.d * ab + rows * cfg.d * ab + cfg.T * cfg.k * 8,
+            "flops": 2.0 * cfg.T * cfg.d * cfg.branch * sum(widths)}
+    peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+    roof = roofline_entry(work, ms, peak)
+    roof.update({"kernel": "hierarchical routing step (all launches: per depth scores, grouping, selection)",
+                 "avg_ms": round(ms, 4), "traffic": None,
+                 "algorithmic": {"bytes": work["bytes"], "flops": work["flops"]}})
+    if cfg.E <= 1024:
+        leaf = w[rows - n[cfg.levels - 1] * cfg.branch:][:cfg.E].contiguous()  # the leaves' gate rows
+        flat_ms = timed_calls(torch, lambda: moe.route(x, leaf, cfg.k, cfg.renorm, want_logits=True), flush, args,
+                              steps)
+        flat = {"what": "flat router on the same pool (moe_route with a logits buffer: logits GEMM, softmax, "
+                        "top-k over all E)",
+                "ms": round(flat_ms, 4)}
+    else:
+        leaf = w[rows - n[cfg.levels - 1] * cfg.branch:][:cfg.E]
+        flat_ms = timed_calls(torch, lambda: torch.matmul(x, leaf.t()), flush, args, max(5, steps // 5))
+        flat = {"what": "flat logits GEMM alone (x times all E leaf rows, library GEMM, no selection)",
+                "ms": round(flat_ms, 4)}
+    rec = {
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "dtype": cfg.dtype,
+        "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
+                   "branch": cfg.branch, "levels": cfg.levels, "gate_rows": rows,
+                   "cache": "warm" if args.warm_cache else "cold (512 MiB flush before each call)"},
+        "roofline": roof,
+        "flat_router_context": flat,
+    }
+    del x, w, ws, ids, tw
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -486,7 +557,7 @@ def main(argv=None):
     import torch
 
     import sparse_mixture_experts_lds_amd as moe
-    from moe_synth import CONFIGS, WORKLOADS
+    from moe_synth import CONFIGS, TREE_CONFIGS, WORKLOADS
 
     moe.load()  # fails loudly when the HIP library is missing
     if not torch.cuda.is_available():
@@ -500,6 +571,14 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
+    if args.tree is not None:
+        if args.tree not in TREE_CONFIGS:
+            print("unknown tree workload %r (one of %s)" % (args.tree, ", ".join(TREE_CONFIGS)), file=sys.stderr)
+            return 2
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        print(json.dumps(measure_tree_route(moe, torch, args.tree, args.steps, args.warmup, args, flush)),
+              flush=True)
         return 0
     if args.workload not in CONFIGS:
         print("unknown workload %r (one of %s)" % (args.workload, ", ".join(WORKLOADS)), file=sys.stderr)
@@ -518,6 +597,10 @@ def main(argv=None):
             subs[name] = measure_workload(moe, torch, np, name, max(args.steps, SUB_MIN_STEPS),
                                           max(args.warmup, SUB_MIN_WARMUP), args, flush, extras=not args.no_extras)
             print("%s: %.4f ms per step" % (name, subs[name]["ms_per_step"]), file=sys.stderr, flush=True)
+        for name in TREE_CONFIGS:
+            subs[name] = measure_tree_route(moe, torch, name, max(args.steps, SUB_MIN_STEPS),
+                                            max(args.warmup, SUB_MIN_WARMUP), args, flush)
+            print("%s: %.4f ms per call" % (name, subs[name]["ms_per_step"]), file=sys.stderr, flush=True)
     rec = {
         "metric": METRIC,
         "value": head["value"],

@@ -616,6 +616,15 @@ hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, co
   if (T == 0) return hipSuccess;
   if (!logits_in && router_fused_ok(T, d, E, k, bf16))
     return launch_router_fused(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, s);
+  // Many experts and a logits buffer from the caller: the layer's two passes
+  // (logits GEMM on its own tiles into the buffer, then the selection) rather
+  // than 16-token tiles that each hold every expert's logits.  Measured on
+  // MI355X, 512 tokens x 896 experts x 7168 inputs: 0.79 ms in one pass.
+  if (!logits_in && logits_out && E > 256) {
+    hipError_t e = launch_router_logits(T, d, E, bf16, x, wr, logits_out, 1, s);
+    if (e != hipSuccess) return e;
+    return launch_select(T, E, k, logits_out, 1, bias, renorm, ids, tw, logits_out, s);
+  }
   const int nf = (E + 63) / 64;
 #define MOE_CALL(NFv) launch_nf<NFv>(T, d, E, k, bf16, x, wr, logits_in, bias, renorm, ids, tw, logits_out, s)
   if (nf <= 1) return MOE_CALL(1);

@@ -172,7 +172,8 @@ def test_layer_is_deterministic():
 @pytest.mark.parametrize("E,k,dt,T", [(8, 2, torch.float32, 131), (192, 4, torch.bfloat16, 131),
                                       (896, 16, torch.bfloat16, 131), (33, 5, torch.bfloat16, 131),
                                       (1024, 32, torch.bfloat16, 131), (192, 4, torch.bfloat16, 8200),
-                                      (64, 1, torch.bfloat16, 9001), (256, 8, torch.bfloat16, 8199)])
+                                      (64, 1, torch.bfloat16, 9001), (256, 8, torch.bfloat16, 8199),
+                                      (300, 4, torch.float32, 77)])
 def test_route_entry_point(E, k, dt, T):
     moe = _moe()
     rng = np.random.default_rng(E + k)
@@ -188,6 +189,27 @@ def test_route_entry_point(E, k, dt, T):
         ids_o = orc.select_topk(Lg, k)
         np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
         assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
+
+
+# Without a logits buffer the router keeps each 16-token tile's logits on chip
+# (with one, many experts take the two-pass logits GEMM and selection): the
+# picks must be a valid top-k of the exact logits up to fp32 reassociation,
+# and the gates the softmax at them.
+@pytest.mark.parametrize("E,k,T", [(896, 16, 131), (300, 4, 50)])
+def test_route_without_logits_buffer(E, k, T):
+    moe = _moe()
+    rng = np.random.default_rng(7 * E + k)
+    d = 256
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(torch.bfloat16)
+    ids, tw, _ = moe.route(x.to(DEV), w.to(DEV), k, True)
+    Lo = orc.router_logits(as_f64(x), as_f64(w))
+    ids = ids.cpu().numpy()
+    assert all(len(set(r)) == k for r in ids.tolist()) and ids.min() >= 0 and ids.max() < E
+    kth = -np.sort(-Lo, axis=1)[:, k - 1]
+    tol = 1e-4 * np.sqrt(np.mean(Lo ** 2))
+    assert np.all(np.take_along_axis(Lo, ids, axis=1) >= kth[:, None] - tol)
+    assert np.abs(tw.cpu().numpy() - orc.gates(Lo, ids, True)).max() <= 1e-5
 
 
 # bf16, T >= 4096, d a multiple of 128 up to 1024, E <= 64, k <= 16: logits
