@@ -421,6 +421,12 @@ int moe_layer_plan(const struct moe_layer_desc* L, struct moe_layer_plan_info* o
  *   out        out [T, d] act_dtype
  *   trace      NULL or a struct of optional outputs
  *   ws         at least moe_layer_workspace_bytes(desc)
+ * Precision: logits, gates and every sum are fp32.  The gated activations z
+ * are rounded to bf16 (bf16 weights) or kept in fp32 (INT4 weights); the
+ * expert and shared-expert outputs are kept in fp16 in bf16 layers (in fp32
+ * in fp32 layers) until the combine, which sums in fp32 and rounds once to
+ * act_dtype.  An expert output beyond fp16's range (65504 in magnitude)
+ * becomes infinite.
  */
 size_t moe_layer_workspace_bytes(const struct moe_layer_desc* L);
 int moe_layer_fwd(const struct moe_layer_desc* L, const void* x, const float* logits_in,

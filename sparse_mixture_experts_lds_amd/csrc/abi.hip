@@ -103,7 +103,8 @@ FfnGemmArgs gate_up_args(int E_loc, int rows_max, int d, int h, int act, const v
   return g;
 }
 
-FfnGemmArgs down_args(const FfnGemmArgs& gu, const void* wd, const void* sd, void* y, bool y_f32) {
+// ytype: storage of y (YType: the operand dtype, fp32, or fp16)
+FfnGemmArgs down_args(const FfnGemmArgs& gu, const void* wd, const void* sd, void* y, int ytype) {
   FfnGemmArgs dn = gu;
   dn.A = gu.out;
   dn.row_index = nullptr;
@@ -113,7 +114,8 @@ FfnGemmArgs down_args(const FfnGemmArgs& gu, const void* wd, const void* sd, voi
   dn.S0 = static_cast<const uint16_t*>(sd);
   dn.S1 = nullptr;
   dn.out = y;
-  dn.out_f32 = y_f32 ? 1 : 0;
+  dn.out_f32 = ytype == Y_F32 ? 1 : 0;
+  dn.out_f16 = ytype == Y_F16 ? 1 : 0;
   dn.a_rows = gu.rows_max;
   dn.K = gu.N;
   dn.N = gu.K;
@@ -127,7 +129,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
             const int32_t* row_index, int row_div, const int32_t* offsets, const int32_t* mtile,
             const int4* tile_tab, int BM,
             const FfnPlan& plan, const void* wg, const void* wu, const void* wd, const void* sg,
-            const void* su, const void* sd, void* z, void* y, bool y_f32, hipStream_t s,
+            const void* su, const void* sd, void* z, void* y, int ytype, hipStream_t s,
             void* mid_event = nullptr, void* const* kernel_events = nullptr,
             const int32_t* mtile_dn = nullptr, const int4* tiles_dn = nullptr) {
   const int wt = wtype_of(w_dtype);
@@ -139,7 +141,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
   }
   MOE_HIP(launch_ffn_gemm(g, true, wt, false, BM, plan.NF_up, s));
   if (mid_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(mid_event), s));
-  FfnGemmArgs dn = down_args(g, wd, sd, y, y_f32);
+  FfnGemmArgs dn = down_args(g, wd, sd, y, ytype);
   dn.ev_start = kernel_events ? kernel_events[2] : nullptr;
   dn.ev_stop = kernel_events ? kernel_events[3] : nullptr;
   int BMd = BM;
@@ -293,7 +295,9 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->pair_pos = c.take<int32_t>(P * 4);
   b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
   b->z = c.take<void>(rows * L->h * 4);  // fp32 when the down projection splits z
-  b->y = c.take<void>(rows * L->d * 4);  // expert outputs stay fp32 until the combine
+  // expert outputs: fp16 in bf16 layers (one rounding to an 11-bit significand
+  // before the combine's fp32 sum), fp32 in fp32 layers
+  b->y = c.take<void>(rows * L->d * 4);
   b->zs = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->h_shared * eb : 0);
   b->ys = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->d * 4 : 0);
   b->stats = c.take<void>(router_stats_ws_bytes(L->T, L->E));  // router by-product partials
@@ -744,7 +748,7 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   if (expert_offsets && own_dn) MOE_HIP(launch_mtile_prefix(E_loc, plan.BM_down, expert_offsets, mtile_dn, tab_dn, s));
   return run_ffn(E_loc, rows_max, d, h, act, w_dtype, x_perm, rows_max, nullptr, 1, expert_offsets,
                  expert_offsets ? mtile : nullptr, expert_offsets ? tab : nullptr, plan.BM, plan, w_gate, w_up,
-                 w_down, s_gate, s_up, s_down, z, y_perm, false, s, nullptr, nullptr, mtile_dn, tab_dn);
+                 w_down, s_gate, s_up, s_down, z, y_perm, Y_OUT, s, nullptr, nullptr, mtile_dn, tab_dn);
 }
 
 int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const int32_t* pair_pos,
@@ -754,7 +758,7 @@ int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const in
   int rc;
   if ((rc = check_width(d, act_dtype))) return rc;
   if (T > 0 && (!y_perm || !pair_pos || !topk_w || !out)) return MOE_EINVAL;
-  MOE_HIP(launch_combine(T, k, d, act_dtype == MOE_BF16, act_dtype == MOE_F32, y_perm, pair_pos, topk_w,
+  MOE_HIP(launch_combine(T, k, d, act_dtype == MOE_BF16, Y_OUT, y_perm, pair_pos, topk_w,
                          shared_y, out, as_stream(stream)));
   return MOE_OK;
 }
@@ -805,6 +809,7 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   int32_t* offsets = tr.expert_offsets ? tr.expert_offsets : b.offsets;
   int32_t* pair_pos = tr.pair_pos ? tr.pair_pos : b.pair_pos;
   const bool bf16 = L->act_dtype == MOE_BF16;
+  const int ytype = bf16 ? Y_F16 : Y_F32;  // storage of the expert outputs until the combine
   const int T = L->T, k = L->k;
   auto mark = [&](int i) -> hipError_t {
     return tr.events[i] ? hipEventRecord(static_cast<hipEvent_t>(tr.events[i]), s) : hipSuccess;
@@ -870,8 +875,8 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
       rg.ev_start = rg.ev_stop = nullptr;
     }
     MOE_HIP(mark(MOE_EV_GATE_UP));
-    FfnGemmArgs rd = down_args(rg, L->w_down, nullptr, b.y, true);
-    const FfnGemmArgs sd = down_args(sg, L->ws_down, nullptr, b.ys, true);
+    FfnGemmArgs rd = down_args(rg, L->w_down, nullptr, b.y, ytype);
+    const FfnGemmArgs sd = down_args(sg, L->ws_down, nullptr, b.ys, ytype);
     if (wide) {
       // the deeper problem's tiles are dispatched first
       if (L->h_shared > L->h) MOE_HIP(launch_ffn_gemm_wide_pair(sd, rd, false, plan.NF_down, kev[2], kev[3], s));
@@ -885,21 +890,21 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     MOE_HIP(mark(MOE_EV_DOWN));
   } else {
     rc = run_ffn(L->E_loc, rows, L->d, L->h, L->act, L->w_dtype, x, T, b.sorted_pair, k, offsets, b.mtile, b.tiles,
-                 plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, true, s,
+                 plan.BM, plan, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up, L->s_down, b.z, b.y, ytype, s,
                  tr.events[MOE_EV_GATE_UP], kev, b.mtile_dn, b.tiles_dn);
     if (rc) return rc;
     MOE_HIP(mark(MOE_EV_DOWN));
     // 5: the shared expert on every token, on the same stream
     if (smode == SharedMode::kSerial) {
       rc = run_ffn(1, T, L->d, L->h_shared, L->act, swt, x, T, nullptr, 1, nullptr, nullptr, nullptr, sp.BM, sp,
-                   L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, true, s);
+                   L->ws_gate, L->ws_up, L->ws_down, nullptr, nullptr, nullptr, b.zs, b.ys, ytype, s);
       if (rc) return rc;
       shared_y = b.ys;
     }
   }
   MOE_HIP(mark(MOE_EV_SHARED));
   // 6: the weighted combine
-  MOE_HIP(launch_combine(T, k, L->d, bf16, true, b.y, pair_pos, tw, shared_y, out, s));
+  MOE_HIP(launch_combine(T, k, L->d, bf16, ytype, b.y, pair_pos, tw, shared_y, out, s));
   MOE_HIP(mark(MOE_EV_END));
   return MOE_OK;
 }

@@ -11,18 +11,20 @@
 // output row and reads the k expert rows of that token, so no atomics are
 // needed and the result does not depend on scheduling.  Consecutive threads
 // cover consecutive pieces of a row: every load and store is coalesced.
-// Inside the layer the expert rows and the shared expert's output arrive in
-// fp32 (one rounding, at the end); the standalone entry point takes them in
-// the output dtype.
+// Inside a bf16 layer the expert rows and the shared expert's output arrive in
+// fp16 (a bf16 layer's y rounded once to fp16's 11-bit significand, then
+// summed in fp32 and rounded once to bf16), inside an fp32 layer in fp32; the
+// standalone entry point takes them in the output dtype.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-// 8 consecutive values of a row: bf16 (one 16-byte vector) or fp32 (two).
-template <bool F32>
+// 8 consecutive values of a row: fp32 (two 16-byte vectors), bf16 or fp16
+// (one).  TY: 0 bf16, 1 fp32, 2 fp16.
+template <int TY>
 __device__ __forceinline__ void load8(const void* base, size_t idx8, float* v) {
-  if constexpr (F32) {
+  if constexpr (TY == 1) {
     const u32x4* p = static_cast<const u32x4*>(base) + 2 * idx8;
     const u32x4 a = p[0], b = p[1];
 #pragma unroll
@@ -34,13 +36,19 @@ __device__ __forceinline__ void load8(const void* base, size_t idx8, float* v) {
     const u32x4 a = static_cast<const u32x4*>(base)[idx8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_bits_to_f32(a[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+      if constexpr (TY == 2) {
+        v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[i] & 0xFFFFu));
+        v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(a[i] >> 16));
+      } else {
+        v[2 * i] = bf16_bits_to_f32(a[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(a[i] >> 16);
+      }
     }
   }
 }
 
-template <bool OUT_BF16, bool Y_F32>
+// TY: storage of y and shared_y (0 bf16, 1 fp32, 2 fp16)
+template <bool OUT_BF16, int TY>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_row, const void* __restrict__ y,
                                                       const int32_t* __restrict__ pair_pos,
                                                       const float* __restrict__ tw,
@@ -49,7 +57,6 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_r
   const size_t t = i / v8_per_row;
   if (t >= (size_t)T) return;
   const int c = (int)(i - t * v8_per_row);
-  constexpr bool YF = Y_F32 || !OUT_BF16;
   float acc[8];
 #pragma unroll
   for (int v = 0; v < 8; ++v) acc[v] = 0.f;
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_r
   // indices and gates, then the rows of the kept ones, all in flight together,
   // then the sums in ascending slot order (the order of the definition)
   float sv[8];
-  if (shared_y) load8<YF>(shared_y, t * v8_per_row + c, sv);
+  if (shared_y) load8<TY>(shared_y, t * v8_per_row + c, sv);
   for (int j0 = 0; j0 < k; j0 += 4) {
     int pos[4];
     float w[4];
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_r
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (pos[u] >= 0) {
-        load8<YF>(y, (size_t)pos[u] * v8_per_row + c, yv[u]);
+        load8<TY>(y, (size_t)pos[u] * v8_per_row + c, yv[u]);
       } else {
 #pragma unroll
         for (int v = 0; v < 8; ++v) yv[u][v] = 0.f;
@@ -103,18 +110,20 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int v8_per_r
 
 }  // namespace
 
-hipError_t launch_combine(int T, int k, int d, bool out_bf16, bool y_f32, const void* y, const int32_t* pair_pos,
+hipError_t launch_combine(int T, int k, int d, bool out_bf16, int ytype, const void* y, const int32_t* pair_pos,
                           const float* tw, const void* shared_y, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int v8 = d / 8;
   const size_t n = (size_t)T * v8;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (out_bf16 && y_f32)
-    combine_kernel<true, true><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
-  else if (out_bf16)
-    combine_kernel<true, false><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  if (!out_bf16)  // fp32 layers keep y in fp32
+    combine_kernel<false, 1><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  else if (ytype == Y_F32)
+    combine_kernel<true, 1><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+  else if (ytype == Y_F16)
+    combine_kernel<true, 2><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
   else
-    combine_kernel<false, true><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
+    combine_kernel<true, 0><<<grid, 256, 0, s>>>(T, k, v8, y, pair_pos, tw, shared_y, out);
   return hipGetLastError();
 }
 

@@ -463,6 +463,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   const int NKB = K / KB;
   const int NIT = (NKB + NS - 1) / NS * NS;  // padded with all-zero activation blocks
   const bool f32out = F32 || args.out_f32;
+  const bool f16out = !f32out && !GATEUP && args.out_f16;
   const int osz = f32out ? 4 : 2;
   const int OS = BN * osz + 16;
   const int cpr = BN * osz / 16;  // 16-byte chunks per output row
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
             if constexpr (GATEUP) v = act_fn(v, args.act) * acc[mi][NF + f][r];
             unsigned char* dst = lds_raw + row * OS + col * osz;
             if (f32out) *reinterpret_cast<float*>(dst) = v;
+            else if (f16out) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_f16_bits(v);
             else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
           }
         }
@@ -577,7 +579,8 @@ hipError_t launch_one(const FfnGemmArgs* a, int np, hipStream_t s) {
   long long per_ub = 0;  // per-XCD tiles, upper bound
   for (int i = 0; i < np; ++i) {
     const FfnGemmArgs& p = a[i];
-    if (p.N % BN || (i > 0 && (p.K != a[0].K || p.N != a[0].N || p.act != a[0].act || p.out_f32 != a[0].out_f32)))
+    if (p.N % BN || (i > 0 && (p.K != a[0].K || p.N != a[0].N || p.act != a[0].act || p.out_f32 != a[0].out_f32 ||
+                               p.out_f16 != a[0].out_f16)))
       return hipErrorInvalidValue;
     const int mt = p.offsets ? ffn_max_mtiles(p.E_loc, p.rows_max, BM) : (p.rows_max + BM - 1) / BM;
     per_ub += ((long long)mt * (p.N / BN) + 7) / 8;

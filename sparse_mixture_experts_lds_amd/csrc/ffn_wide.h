@@ -157,7 +157,7 @@ struct Ops {
   uint32_t a_off[2];
 };
 
-template <bool GATEUP, bool OUT_F32, int ACT, int BW>
+template <bool GATEUP, int OUT, int ACT, int BW>
 __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
   using G = Geo<BW>;
   constexpr int OPB = G::OPB, STAGE = G::STAGE, NS = G::NS, LPS = G::LPS, LB = G::LB;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
     }
     // cst is now the stage of the next tile's k-block 0
 
-    unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT_F32 ? 4 : 2);
+    unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT == 1 ? 4 : 2);
     if constexpr (GATEUP) {
       // ---------------- gate/up epilogue.  Lane (lrow, q) holds, for tile row
       // 64 wr + 16 mi + lrow, g (fragment f) and u (fragment f + NF / 2) of the
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
       // LDS region, in two halves of HW/2 columns, and stores 16-byte row
       // chunks; a wave's LDS accesses complete in order, so no workgroup barrier
       // is needed between the writes and the reads
-      constexpr int osz = OUT_F32 ? 4 : 2;
+      constexpr int osz = OUT == 1 ? 4 : 2;
       constexpr int QC = HW / 2;          // output columns per half
       constexpr int OS = QC * osz + 16;   // LDS row stride of a wave's block (bytes)
       constexpr int cpr = QC * osz / 16;  // 16-byte chunks per row
@@ -460,7 +460,8 @@ __global__ __launch_bounds__(512) void wide_kernel(WideArgs wa) {
               for (int r = 0; r < 4; ++r) {
                 const float v = acc[mi][(NF / 2) * hh + ff][r];
                 unsigned char* dst = wl + (16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
-                if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = v;
+                if constexpr (OUT == 1) *reinterpret_cast<float*>(dst) = v;
+                else if constexpr (OUT == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_f16_bits(v);
                 else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
               }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -503,7 +504,8 @@ hipError_t launch_bw(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop
   for (int i = 0; i < np; ++i) {
     const FfnGemmArgs& p = a[i];
     if (p.N % BNO || p.K % (2 * KB) || (size_t)p.N * p.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    if (i > 0 && (p.out_f32 != a[0].out_f32 || p.act != a[0].act)) return hipErrorInvalidValue;
+    if (i > 0 && (p.out_f32 != a[0].out_f32 || p.out_f16 != a[0].out_f16 || p.act != a[0].act))
+      return hipErrorInvalidValue;
     const int mt = p.offsets ? ffn_max_mtiles(p.E_loc, p.rows_max, BM) : (p.rows_max + BM - 1) / BM;
     slots += ((long long)mt * (p.N / BNO) + 7) / 8;  // per-XCD slots of problem i
     w.p[i] = p;
@@ -526,9 +528,10 @@ hipError_t launch_bw(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop
     else
       kernel<<<dim3((unsigned)g), dim3(512), 0, s>>>(w);
   };
-  if (!GATEUP && a[0].out_f32) go(wide_kernel<false, true, 0, BW>);
-  else if (GATEUP && a[0].act == 1) go(wide_kernel<GATEUP, false, 1, BW>);
-  else go(wide_kernel<GATEUP, false, 0, BW>);
+  if (!GATEUP && a[0].out_f32) go(wide_kernel<false, 1, 0, BW>);
+  else if (!GATEUP && a[0].out_f16) go(wide_kernel<false, 2, 0, BW>);
+  else if (GATEUP && a[0].act == 1) go(wide_kernel<GATEUP, 0, 1, BW>);
+  else go(wide_kernel<GATEUP, 0, 0, BW>);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ struct Ops {
   uint32_t a_off[LA];
 };
 
-template <bool GATEUP, bool OUT_F32, int ACT>
+template <bool GATEUP, int OUT, int ACT>
 __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
   constexpr int BNO = GATEUP ? BW / 2 : BW;  // output columns per tile
   constexpr int MF = 4, NF = BW / 32;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
       if (j + 1 < NKB) step(fa0, fa1, st ^ 1, 1, 0, 0, no_loads{});
     }
 
-    unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT_F32 ? 4 : 2);
+    unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT == 1 ? 4 : 2);
     if constexpr (GATEUP) {
       // ---------------- gate/up epilogue (as ffn_wide.h): lane (lrow, q)
       // holds g (fragment f) and u (fragment f + NF/2) of four consecutive
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
       wait_vm<0>();
       lds_barrier();
       unsigned char* const lds = &stg[0][0];
-      constexpr int osz = OUT_F32 ? 4 : 2;
+      constexpr int osz = OUT == 1 ? 4 : 2;
       constexpr int NPART = HW * osz / 128;  // 4 (fp32) or 2 (bf16)
       constexpr int QC = HW / NPART;         // output columns per part
       constexpr int FPP = NF / NPART;        // fragments per part
@@ -347,7 +347,8 @@ __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
               for (int r = 0; r < 4; ++r) {
                 const float v = acc[mi][FPP * hh + ff][r];
                 unsigned char* dst = wl + (16 * mi + 4 * q + r) * OS + (16 * ff + lrow) * osz;
-                if constexpr (OUT_F32) *reinterpret_cast<float*>(dst) = v;
+                if constexpr (OUT == 1) *reinterpret_cast<float*>(dst) = v;
+                else if constexpr (OUT == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_f16_bits(v);
                 else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16_bits(v);
               }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -382,7 +383,8 @@ hipError_t launch(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, h
   for (int i = 0; i < np; ++i) {
     const FfnGemmArgs& p = a[i];
     if (p.N % BNO || p.K % (2 * KB) || (size_t)p.N * p.K * 2 > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    if (i > 0 && (p.out_f32 != a[0].out_f32 || p.act != a[0].act)) return hipErrorInvalidValue;
+    if (i > 0 && (p.out_f32 != a[0].out_f32 || p.out_f16 != a[0].out_f16 || p.act != a[0].act))
+      return hipErrorInvalidValue;
     const int mt = p.offsets ? ffn_max_mtiles(p.E_loc, p.rows_max, BM) : (p.rows_max + BM - 1) / BM;
     slots += ((long long)mt * (p.N / BNO) + 7) / 8;
     w.p[i] = p;
@@ -404,9 +406,10 @@ hipError_t launch(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, h
     else
       kernel<<<dim3((unsigned)g), dim3(512), 0, s>>>(w);
   };
-  if (!GATEUP && a[0].out_f32) go(wide64_kernel<false, true, 0>);
-  else if (GATEUP && a[0].act == 1) go(wide64_kernel<GATEUP, false, 1>);
-  else go(wide64_kernel<GATEUP, false, 0>);
+  if (!GATEUP && a[0].out_f32) go(wide64_kernel<false, 1, 0>);
+  else if (!GATEUP && a[0].out_f16) go(wide64_kernel<false, 2, 0>);
+  else if (GATEUP && a[0].act == 1) go(wide64_kernel<GATEUP, 0, 1>);
+  else go(wide64_kernel<GATEUP, 0, 0>);
   return hipGetLastError();
 }
 

@@ -36,6 +36,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// fp32 -> fp16 bit pattern, rounded to nearest even (v_cvt_f16_f32)
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
@@ -231,6 +233,7 @@ struct FfnGemmArgs {
   int a_rows;                // rows of A as addressed (a_rows * K elements must stay below 4 GiB)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
+  int out_f16;               // 1 (with out_f32 0, down projections only): store the output as fp16
   void* ev_start;            // hipEvent_t pair carried by the launch itself (NULL: none):
   void* ev_stop;             //   they time exactly this kernel and add no packet to the stream
 };
@@ -259,8 +262,10 @@ hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a
                                      void* ev_start, void* ev_stop, hipStream_t s);
 
 // Weighted combine.
-// y and shared_y are fp32 when y_f32, else in the output dtype.
-hipError_t launch_combine(int T, int k, int d, bool out_bf16, bool y_f32, const void* y, const int32_t* pair_pos,
+// Storage type of the expert outputs y and shared_y: the output dtype, fp32,
+// or fp16 (bf16 outputs only).
+enum YType { Y_OUT = 0, Y_F32 = 1, Y_F16 = 2 };
+hipError_t launch_combine(int T, int k, int d, bool out_bf16, int ytype, const void* y, const int32_t* pair_pos,
                           const float* tw, const void* shared_y, void* out, hipStream_t s);
 
 // Hierarchical routing down an expert tree (tree_route.hip).
