@@ -240,19 +240,30 @@ def timed_calls(torch, fn, flush, args, reps):
     return median([e0.elapsed_time(e1) for e0, e1 in ev])
 
 
-def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, reps=20):
+def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, x=None, W=None, ws=None, reps=20):
     """Per-expert counts, mean probabilities and balance loss of this batch's
-    routing (outside the timed step), and the HBM rate on its algorithmic
-    bytes (logits T*E*4 plus ids T*k*4)."""
+    routing: the standalone call on the logits and ids (outside the timed
+    step), with the HBM rate on its algorithmic bytes (logits T*E*4 plus ids
+    T*k*4); and their cost inside the layer, where the selection launch emits
+    them: the median layer time with the by-products minus without (both
+    with the routing trace)."""
     L = tr["logits"] if "logits" in tr else logits
     b = None if "logits" in tr else bias  # the trace logits already hold the bias
     ids = tr["topk_ids"]
     us = 1e3 * timed_calls(torch, lambda: moe.router_stats(L, ids, bias=b), flush, args, reps)
     nbytes = cfg.T * cfg.E * 4 + cfg.T * cfg.k * 4
     gbps = nbytes / (us * 1e-6) / 1e9
-    return {"kernel": "router by-products (counts, mean probability, balance loss)",
-            "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
-            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+    rec = {"kernel": "router by-products (counts, mean probability, balance loss)",
+           "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
+           "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+    if x is not None:
+        with_s = timed_calls(torch, lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True, stats=True),
+                             flush, args, reps)
+        without = timed_calls(torch, lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True), flush, args,
+                              reps)
+        rec["in_layer_us"] = round(1e3 * (with_s - without), 2)
+        rec["in_layer_note"] = "median layer time with the by-products minus without (both traced)"
+    return rec
 
 
 def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=20):
@@ -471,7 +482,7 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 4),
     }
     if extras:
-        rec["router_stats"] = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args)
+        rec["router_stats"] = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args, x=x, W=W, ws=ws)
         rec["owner_dispatch"] = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
         rec["backward"] = backward_timing(moe, torch, cfg, W, x, logits, work, flush, args)
     del W, ws, out, x, tr

@@ -74,6 +74,21 @@ int check_route_dims(int T, int E, int k) {
   return MOE_OK;
 }
 
+// The layer's router by-products come from its selection launch (one partial
+// row per selection workgroup) unless that makes more than this many
+// partial entries; then the standalone passes read the logits again.
+constexpr long long kSelStatsMaxEntries = 1LL << 21;
+
+long long sel_stats_rows(int T, int E, int k) {
+  return std::max(select_stats_rows(T, E, k, true), select_stats_rows(T, E, k, false));
+}
+
+size_t sel_stats_bytes(int T, int E, int k) {
+  const long long rows = sel_stats_rows(T, E, k), n = rows * E;
+  if (T <= 0 || rows > kStatsFinishMaxRows || n > kSelStatsMaxEntries) return 0;
+  return align_up((size_t)n * 8) + align_up((size_t)n * 4) + stats_finish_bytes(E);
+}
+
 // Argument blocks of the gate/up GEMM (z = act(A Wg^T) * (A Wu^T) over
 // grouped rows; `offsets` NULL means one group) and of the down GEMM that
 // follows it (y = z Wd^T).
@@ -300,7 +315,9 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->y = c.take<void>(rows * L->d * 4);
   b->zs = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->h_shared * eb : 0);
   b->ys = c.take<void>(L->h_shared > 0 ? (size_t)L->T * L->d * 4 : 0);
-  b->stats = c.take<void>(router_stats_ws_bytes(L->T, L->E));  // router by-product partials
+  // router by-product partials: from the selection's workgroups, or the
+  // standalone passes' blocks
+  b->stats = c.take<void>(std::max(router_stats_ws_bytes(L->T, L->E), sel_stats_bytes(L->T, L->E, L->k)));
   return c.used;
 }
 
@@ -827,10 +844,28 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   int nsplit = 1;
   const bool want_stats = tr.expert_counts || tr.prob_mean || tr.balance_loss;
   float* lout = nullptr;
-  if (!lsrc && router_fused_ok(T, L->d, L->E, k, bf16)) {
+  // by-products from the selection launch: one partial row per workgroup
+  const bool fused = !lsrc && router_fused_ok(T, L->d, L->E, k, bf16);
+  const int srows = select_stats_rows(T, L->E, k, fused);
+  // the same test that sized the workspace (for the larger of the two paths' rows)
+  const bool sel_stats = want_stats && sel_stats_bytes(T, L->E, k) > 0;
+  StatsPart stp{};
+  if (sel_stats) {
+    unsigned char* base = static_cast<unsigned char*>(b.stats);
+    const size_t n = (size_t)srows * L->E;
+    stp.part_p = reinterpret_cast<double*>(base);
+    stp.part_c = reinterpret_cast<int32_t*>(base + align_up(n * 8));
+    unsigned char* fin = base + align_up(n * 8) + align_up(n * 4);  // the finishing pass's memory
+    const size_t m = (size_t)kStatsMaxRowSplits * L->E;
+    stp.mid_p = reinterpret_cast<double*>(fin);
+    stp.mid_c = reinterpret_cast<int32_t*>(fin + align_up(m * 8));
+    stp.counter = reinterpret_cast<unsigned*>(fin + align_up(m * 8) + align_up(m * 4));
+  }
+  if (fused) {
     // one launch: the biased logits reach memory only when something reads them
-    lout = tr.logits ? tr.logits : (want_stats ? b.logits : nullptr);
-    MOE_HIP(launch_router_fused(T, L->d, L->E, k, x, L->w_router, L->expert_bias, L->renorm, ids, tw, lout, s));
+    lout = tr.logits ? tr.logits : (want_stats && !sel_stats ? b.logits : nullptr);
+    MOE_HIP(launch_router_fused(T, L->d, L->E, k, x, L->w_router, L->expert_bias, L->renorm, ids, tw, lout, s,
+                                sel_stats ? &stp : nullptr));
   } else {
     if (!lsrc) {
       nsplit = router_logits_splits(T, L->d, L->E, bf16);
@@ -840,11 +875,15 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
     }
     // the summed, biased logits go to the trace buffer, else (partial arrays)
     // over the first partial array when the by-products read them
-    lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats ? b.logits : nullptr);
-    MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s));
+    lout = tr.logits ? tr.logits : (nsplit > 1 && want_stats && !sel_stats ? b.logits : nullptr);
+    MOE_HIP(launch_select(T, L->E, k, lsrc, nsplit, L->expert_bias, L->renorm, ids, tw, lout, s,
+                          sel_stats ? &stp : nullptr));
   }
   // router by-products
-  if (want_stats)
+  if (sel_stats)
+    MOE_HIP(launch_stats_finish(T, L->E, srows, stp, tr.expert_counts, tr.prob_mean,
+                                tr.balance_loss, s));
+  else if (want_stats)
     MOE_HIP(launch_router_stats(T, L->E, k, lout ? lout : lsrc, lout ? nullptr : L->expert_bias, ids,
                                 tr.expert_counts, tr.prob_mean, tr.balance_loss, b.stats, s));
   MOE_HIP(mark(MOE_EV_ROUTED));

@@ -171,18 +171,41 @@ constexpr int kMaxRouterSplits = 8;
 int router_logits_splits(int T, int d, int E, bool bf16);
 hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, const void* wr, float* part,
                                 int nsplit, hipStream_t s);
+// Per-workgroup partial rows of the router by-products, written by a
+// selection launch that is handed one: softmax column sums (fp64) and pick
+// counts of the workgroup's tokens, one [E] row per workgroup.
+constexpr int kStatsMaxRowSplits = 8;      // row ranges of the by-products' finishing pass
+constexpr int kStatsFinishMaxRows = 1024;  // partial rows it adds at most (128 per range)
+struct StatsPart {
+  double* part_p;
+  int32_t* part_c;
+  double* mid_p;      // the finishing pass's per-row-range sums (stats_finish_bytes(E) with mid_c and counter)
+  int32_t* mid_c;
+  unsigned* counter;  // zeroed by the selection launch, counted by the finishing pass
+};
+
 // Router logits (+ bias), softmax and top-k in one launch for bf16 layers with
 // many tokens (router_fused_ok); logits_out (NULL allowed) receives the biased
 // logits.
 bool router_fused_ok(int T, int d, int E, int k, bool bf16);
 hipError_t launch_router_fused(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
-                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s);
+                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s,
+                               const StatsPart* stats = nullptr);
 // Softmax + top-k from logits given as nsplit partial arrays src[s][T][E]
 // (added in ascending s) plus bias; logits_out (NULL, or aliasing the first
 // partial array: every element is read and written by the same lane) receives
 // the sum + bias.
 hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
-                         int32_t* ids, float* tw, float* logits_out, hipStream_t s);
+                         int32_t* ids, float* tw, float* logits_out, hipStream_t s,
+                         const StatsPart* stats = nullptr);
+// Partial rows a selection launch writes with StatsPart (one per workgroup):
+// launch_select's, or the fused router's when fused.
+int select_stats_rows(int T, int E, int k, bool fused);
+// Counts, means and loss from nblk partial rows (workgroups over 64-expert
+// chunks and row ranges; the last to finish folds the loss).
+size_t stats_finish_bytes(int E);
+hipError_t launch_stats_finish(int T, int E, int nblk, const StatsPart& sp, int32_t* counts, float* prob_mean,
+                               float* loss, hipStream_t s);
 
 // Router by-products: per-expert token counts, mean softmax probabilities and
 // the balance loss from logits (+ bias) and top-k ids; ws holds

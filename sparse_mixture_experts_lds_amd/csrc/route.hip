@@ -218,9 +218,14 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
 // Softmax and top-k of one token held by a group of G lanes: lane gl holds
 // experts gl + G i in v[i] (-inf past E).  k rounds of a group arg-max pick
 // the experts; lane j keeps the j-th pick and writes its id and gate.
+// With `prob` non-null the lane also returns its experts' softmax
+// probabilities (p = exp(v - m) * (1 / sum), one division per token) and, in
+// `pick`, the id of its own pick (lanes >= k: -1), for the router
+// by-products.
 template <int G, int NV>
 __device__ __forceinline__ void select_group(const float (&v)[NV], int gl, int E, int k, int renorm,
-                                             int32_t* ids_row, float* tw_row) {
+                                             int32_t* ids_row, float* tw_row, float* prob = nullptr,
+                                             int* pick = nullptr) {
   float m = v[0];
 #pragma unroll
   for (int i = 1; i < NV; ++i) m = fmaxf(m, v[i]);
@@ -259,6 +264,39 @@ __device__ __forceinline__ void select_group(const float (&v)[NV], int gl, int E
     ids_row[gl] = my_e;
     tw_row[gl] = ex / denom;
   }
+  if (prob) {
+    const float inv = 1.f / sum_all;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) prob[i] = gl + G * i < E ? expf(v[i] - m) * inv : 0.f;
+    *pick = gl < k ? my_e : -1;
+  }
+}
+
+// Router by-products from a selection workgroup (StatsPart): each group hands
+// over its tokens' probabilities and picks; the workgroup adds them per expert
+// (fp64, groups in order) and writes one partial row of column sums and counts.
+template <int NG, int EW>
+struct StatsLds {
+  double red[NG][EW];
+  int cnt[EW];
+};
+
+// Every thread of the workgroup calls this once, after its group's tokens
+// have been added to acc (probabilities, lane's experts gl + G i) and cnt.
+template <int G, int NV, int NG, int EW>
+__device__ __forceinline__ void stats_flush(StatsLds<NG, EW>& L, const double (&acc)[NV], int gl, int grp, int E,
+                                            const StatsPart& sp) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *sp.counter = 0;  // for the finishing pass's election
+#pragma unroll
+  for (int i = 0; i < NV; ++i) L.red[grp][gl + G * i] = acc[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    double p = L.red[0][e];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) p += L.red[g][e];
+    sp.part_p[(size_t)blockIdx.x * E + e] = p;
+    sp.part_c[(size_t)blockIdx.x * E + e] = L.cnt[e];
+  }
 }
 
 // One group of G lanes per token: logits row (+ bias) from memory, optionally
@@ -268,14 +306,26 @@ __device__ __forceinline__ void select_group(const float (&v)[NV], int gl, int E
 // SPLIT: the logits come as nsplit (2 .. kMaxRouterSplits) partial arrays;
 // every partial is loaded before the first addition (the loads overlap), then
 // they are added in ascending slice order.
-template <int G, int NV, bool SPLIT>
+// STATS: the workgroup also writes one partial row of the router by-products
+// (a group past T adds nothing; no group leaves before the workgroup's
+// reduction).
+template <int G, int NV, bool SPLIT, bool STATS>
 __global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const float* src, int nsplit,
                                                      const float* __restrict__ bias, int renorm,
                                                      int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                     float* logits_out) {
-  const int gl = threadIdx.x & (G - 1);
-  const int t = blockIdx.x * (256 / G) + threadIdx.x / G;
-  if (t >= T) return;  // whole groups leave together
+                                                     float* logits_out, StatsPart sp) {
+  constexpr int NG = 256 / G;
+  __shared__ StatsLds<STATS ? NG : 1, STATS ? G * NV : 1> sl;
+  const int gl = threadIdx.x & (G - 1), grp = threadIdx.x / G;
+  const int t_raw = blockIdx.x * NG + grp;
+  if constexpr (STATS) {
+    for (int e = threadIdx.x; e < G * NV; e += 256) sl.cnt[e] = 0;
+    __syncthreads();
+  } else {
+    if (t_raw >= T) return;  // whole groups leave together
+  }
+  const bool live = t_raw < T;
+  const int t = live ? t_raw : T - 1;  // (STATS) a group past T works on the last token and writes nothing
   const float* row = src + (size_t)t * E;
   float v[NV];
   if constexpr (SPLIT) {
@@ -310,14 +360,27 @@ __global__ __launch_bounds__(256) void select_kernel(int T, int E, int k, const 
     const float x = v[i] + (bias ? bias[ec] : 0.f);
     v[i] = e < E ? x : -INFINITY;
   }
-  if (logits_out) {
+  if (logits_out && live) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = gl + G * i;
       if (e < E) logits_out[(size_t)t * E + e] = v[i];
     }
   }
-  select_group<G, NV>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
+  if constexpr (!STATS) {
+    select_group<G, NV>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
+  } else {
+    // the last token's ids and gates are written again by a group past T: the
+    // same values to the same places
+    float p[NV];
+    int pick;
+    select_group<G, NV>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k, p, &pick);
+    double acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = live ? (double)p[i] : 0.0;
+    if (live && pick >= 0) atomicAdd(&sl.cnt[pick], 1);
+    stats_flush<G, NV>(sl, acc, gl, grp, E, sp);
+  }
 }
 
 template <int NF>
@@ -349,13 +412,20 @@ hipError_t logits_nf(int T, int d, int E, bool bf16, const void* x, const void* 
 
 template <int G, int NV>
 hipError_t select_gn(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
-                     int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+                     int32_t* ids, float* tw, float* logits_out, const StatsPart& sp, hipStream_t s) {
   constexpr int TPB = 256 / G;  // tokens per workgroup
   const dim3 grid((T + TPB - 1) / TPB);
-  if (nsplit > 1)
-    select_kernel<G, NV, true><<<grid, 256, 0, s>>>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out);
-  else
-    select_kernel<G, NV, false><<<grid, 256, 0, s>>>(T, E, k, src, 1, bias, renorm, ids, tw, logits_out);
+  const bool st = sp.part_p != nullptr;
+#define MOE_GO(SPL, STA) select_kernel<G, NV, SPL, STA><<<grid, 256, 0, s>>>(T, E, k, src, nsplit, bias, renorm, \
+                                                                           ids, tw, logits_out, sp)
+  if (nsplit > 1) {
+    if (st) MOE_GO(true, true);
+    else MOE_GO(true, false);
+  } else {
+    if (st) MOE_GO(false, true);
+    else MOE_GO(false, false);
+  }
+#undef MOE_GO
   return hipGetLastError();
 }
 
@@ -483,16 +553,21 @@ constexpr int kRfMaxD = 1024;  // longest x row the LDS tile holds
 constexpr int kRfMinTok = 4096;
 constexpr int kRfMaxE = 64;
 
-template <int NFW>
+// STATS: the workgroup also writes one partial row of the router by-products.
+template <int NFW, bool STATS>
 __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, int k,
                                                            const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w,
                                                            const float* __restrict__ bias, int renorm,
                                                            int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                           float* __restrict__ logits_out) {
+                                                           float* __restrict__ logits_out, StatsPart sp) {
   constexpr int ES = 64 * NFW + 4;  // logits row stride in LDS (floats)
   __shared__ __attribute__((aligned(16))) unsigned char Xl[kRfTok * (2 * kRfMaxD + 16)];
   __shared__ float Ls[kRfTok * ES];
+  // (STATS) the by-product sums take the x tile's memory once the logits are in
+  using SL = StatsLds<16, 64 * NFW>;
+  static_assert(sizeof(SL) <= sizeof(Xl), "the by-product sums fit the x tile");
+  SL& sl = *reinterpret_cast<SL*>(Xl);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * kRfTok;
@@ -574,8 +649,15 @@ __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, 
   }
   __syncthreads();
 
+  if constexpr (STATS) {
+    for (int e = threadIdx.x; e < 64 * NFW; e += 256) sl.cnt[e] = 0;
+    __syncthreads();
+  }
   // selection: 16 groups of 16 lanes, two tokens each
   const int gl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  double acc[4 * NFW];
+#pragma unroll
+  for (int i = 0; i < 4 * NFW; ++i) acc[i] = 0.0;
 #pragma unroll
   for (int hh = 0; hh < kRfTok / 16; ++hh) {
     const int r = grp + 16 * hh, t = t0 + r;
@@ -586,9 +668,19 @@ __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, 
         const int e = gl + 16 * i;
         v[i] = e < E ? Ls[r * ES + e] : -INFINITY;
       }
-      select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
+      if constexpr (STATS) {
+        float p[4 * NFW];
+        int pick;
+        select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k, p, &pick);
+#pragma unroll
+        for (int i = 0; i < 4 * NFW; ++i) acc[i] += (double)p[i];
+        if (pick >= 0) atomicAdd(&sl.cnt[pick], 1);
+      } else {
+        select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
+      }
     }
   }
+  if constexpr (STATS) stats_flush<16, 4 * NFW>(sl, acc, gl, grp, E, sp);
   if (logits_out) {
     const int n = min(kRfTok, T - t0) * E;
     for (int c = threadIdx.x; c < n; c += 256) {
@@ -600,11 +692,17 @@ __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, 
 
 template <int NFW>
 hipError_t router_fused_nf(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
-                           int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+                           int renorm, int32_t* ids, float* tw, float* logits_out, const StatsPart& sp,
+                           hipStream_t s) {
   const dim3 grid((unsigned)((T + kRfTok - 1) / kRfTok));
-  router_fused_kernel<NFW><<<grid, 256, 0, s>>>(T, d, E, k, static_cast<const uint16_t*>(x),
-                                                static_cast<const uint16_t*>(wr), bias, renorm, ids, tw,
-                                                logits_out);
+  if (sp.part_p)
+    router_fused_kernel<NFW, true><<<grid, 256, 0, s>>>(T, d, E, k, static_cast<const uint16_t*>(x),
+                                                        static_cast<const uint16_t*>(wr), bias, renorm, ids, tw,
+                                                        logits_out, sp);
+  else
+    router_fused_kernel<NFW, false><<<grid, 256, 0, s>>>(T, d, E, k, static_cast<const uint16_t*>(x),
+                                                         static_cast<const uint16_t*>(wr), bias, renorm, ids, tw,
+                                                         logits_out, sp);
   return hipGetLastError();
 }
 
@@ -722,14 +820,23 @@ bool router_fused_ok(int T, int d, int E, int k, bool bf16) {
 }
 
 hipError_t launch_router_fused(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
-                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+                               int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s,
+                               const StatsPart* stats) {
   if (!router_fused_ok(T, d, E, k, true)) return hipErrorInvalidValue;
   static_assert(kRfMaxE <= 64, "one 16-expert fragment per wave");
-  return router_fused_nf<1>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, s);
+  const StatsPart sp = stats ? *stats : StatsPart{};
+  return router_fused_nf<1>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, sp, s);
+}
+
+int select_stats_rows(int T, int E, int k, bool fused) {
+  if (fused) return (T + kRfTok - 1) / kRfTok;
+  const int tpb = (E <= 256 && k <= 16 && T >= kSelectGroupMinTok) ? 16 : 4;  // tokens per select workgroup
+  return (T + tpb - 1) / tpb;
 }
 
 hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, const float* bias, int renorm,
-                         int32_t* ids, float* tw, float* logits_out, hipStream_t s) {
+                         int32_t* ids, float* tw, float* logits_out, hipStream_t s, const StatsPart* stats) {
+  const StatsPart sp = stats ? *stats : StatsPart{};
   if (T == 0) return hipSuccess;
   if (nsplit < 1 || nsplit > kMaxRouterSplits) return hipErrorInvalidValue;
   // 16 lanes per token while a lane holds at most 16 logits, the k picks fit in
@@ -739,7 +846,7 @@ hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, cons
   // arrays), 34.5 against 30.0.
   if (E <= 256 && k <= 16 && T >= kSelectGroupMinTok) {
     const int nv = (E + 15) / 16;
-#define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, s)
+#define MOE_CALL(NVv) select_gn<16, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, sp, s)
     if (nv <= 2) return MOE_CALL(2);
     if (nv <= 4) return MOE_CALL(4);
     if (nv <= 8) return MOE_CALL(8);
@@ -748,7 +855,7 @@ hipError_t launch_select(int T, int E, int k, const float* src, int nsplit, cons
 #undef MOE_CALL
   }
   const int nv = (E + 63) / 64;
-#define MOE_CALL(NVv) select_gn<64, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, s)
+#define MOE_CALL(NVv) select_gn<64, NVv>(T, E, k, src, nsplit, bias, renorm, ids, tw, logits_out, sp, s)
   if (nv <= 1) return MOE_CALL(1);
   if (nv <= 2) return MOE_CALL(2);
   if (nv <= 4) return MOE_CALL(4);

@@ -6,13 +6,13 @@
 //   loss     = E * sum_e (count[e] / T) * P[e]
 // with L = logits (+ bias).  Ids outside [0, E) match no expert.
 //
-// Three passes, each in a fixed order so the result does not depend on
+// Two passes, each in a fixed order so the result does not depend on
 // scheduling: each workgroup of the first pass owns a fixed strided set of
-// tokens (one wave per token row; lane l holds experts l + 64i), keeps fp64
-// column sums of the softmax in registers and integer counts in LDS, and
-// writes one [E] row of partials; the second pass adds the rows column by
-// column (one workgroup per 64 experts); the third folds the per-workgroup
-// loss terms.  The logits are read once: the first pass moves
+// tokens (a group of lanes per token row), keeps fp64 column sums of the
+// softmax in registers and integer counts in LDS, and writes one [E] row of
+// partials; the second pass adds the rows column by column (one workgroup per
+// 64 experts), and the last of its workgroups folds the loss terms in expert
+// order.  The logits are read once: the first pass moves
 // T*E*4 + T*k*4 bytes, the partial rows at most 12*E*256 more.
 #include <algorithm>
 
@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(int T, int E, int k,
                                                             const float* __restrict__ bias,
                                                             const int32_t* __restrict__ ids,
                                                             double* __restrict__ part_p,
-                                                            int32_t* __restrict__ part_c) {
+                                                            int32_t* __restrict__ part_c, unsigned* counter) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *counter = 0;  // for the second pass's election
   constexpr int NG = 256 / G;  // groups per workgroup
   constexpr int EW = NV * G;   // expert columns covered by a group (>= E)
   __shared__ double red[NG][EW];
@@ -120,37 +121,55 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(int T, int E, int k,
   }
 }
 
-// Second pass: workgroup c owns experts 64c..64c+63; wave w adds the partial
-// rows b = w, w + 16, ... (eight independent chains, folded in a fixed order),
-// then wave 0 adds the 16 wave sums in wave order.  Writes the counts and
-// means of its experts and its share of sum_e count[e] * colsum[e].
+// Second pass, a grid of (64-expert chunk c, row range r) workgroups: wave w
+// adds the partial rows b = b0 + w, b0 + w + 16, ... of range r (at most
+// kColRows, loaded together), then wave 0 adds the 16 wave sums in wave order
+// into mid[r][e].  The workgroup that counts last on `counter` (zeroed by the
+// first pass) finishes: thread e adds mid[0..RS-1][e] in order, writes the
+// count and mean of expert e, and the workgroup folds the loss terms
+// count[e] * colsum[e] in a fixed order.  Nothing waits:
+// the last arrival finds every range published (release/acquire on the
+// counter).
+constexpr int kMaxRowSplits = kStatsMaxRowSplits;
+constexpr int kColRows = 8;  // partial rows a thread of the second pass adds
+static_assert(kStatsFinishMaxRows == kMaxRowSplits * 16 * kColRows, "rows of the second pass");
+
 __global__ __launch_bounds__(64 * kColWaves) void stats_column_kernel(int T, int E, int nblk,
                                                                      const double* __restrict__ part_p,
                                                                      const int32_t* __restrict__ part_c,
                                                                      int32_t* __restrict__ counts,
                                                                      float* __restrict__ prob_mean,
-                                                                     double* __restrict__ chunk_loss) {
+                                                                     double* mid_p, int32_t* mid_c,
+                                                                     unsigned* counter, float* __restrict__ loss) {
   __shared__ double rs[kColWaves][64];
   __shared__ int rc[kColWaves][64];
+  __shared__ double lw[kColWaves];
+  __shared__ bool last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int RS = gridDim.y, r = blockIdx.y;
+  const int b0 = (int)((long long)nblk * r / RS), b1 = (int)((long long)nblk * (r + 1) / RS);
   const int e = blockIdx.x * 64 + lane;
-  double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int c = 0;
-  if (e < E) {
-    int b = wave;
-    for (; b + 7 * kColWaves < nblk; b += 8 * kColWaves) {
+  const int ec = e < E ? e : E - 1;
+  // rows b0 + wave + 16 q: at most kColRows per wave, all loads issued together
+  // (rows past the range re-read row b0 and are not added)
+  double s[kColRows];
+  int cv[kColRows];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        s[q] += part_p[(size_t)(b + q * kColWaves) * E + e];
-        c += part_c[(size_t)(b + q * kColWaves) * E + e];
-      }
-    }
-    for (; b < nblk; b += kColWaves) {
-      s[0] += part_p[(size_t)b * E + e];
-      c += part_c[(size_t)b * E + e];
-    }
+  for (int q = 0; q < kColRows; ++q) {
+    const int b = b0 + wave + kColWaves * q;
+    const int bb = b < b1 ? b : b0;
+    s[q] = part_p[(size_t)bb * E + ec];
+    cv[q] = part_c[(size_t)bb * E + ec];
   }
-  rs[wave][lane] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  double sum = 0.0;
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < kColRows; ++q)
+    if (b0 + wave + kColWaves * q < b1 && e < E) {
+      sum += s[q];
+      c += cv[q];
+    }
+  rs[wave][lane] = sum;
   rc[wave][lane] = c;
   __syncthreads();
   if (wave == 0) {
@@ -161,24 +180,60 @@ __global__ __launch_bounds__(64 * kColWaves) void stats_column_kernel(int T, int
       tot += rs[w][lane];
       ct += rc[w][lane];
     }
-    double term = 0.0;
     if (e < E) {
-      if (counts) counts[e] = ct;
-      if (prob_mean) prob_mean[e] = T > 0 ? (float)(tot / (double)T) : 0.f;
-      term = (double)ct * tot;
+      mid_p[(size_t)r * E + e] = tot;
+      mid_c[(size_t)r * E + e] = ct;
     }
-    // fixed-order fold of the 64 lane terms (lane 0's result is used)
-    for (int m = 32; m >= 1; m >>= 1) term += __shfl_down(term, m);
-    if (lane == 0) chunk_loss[blockIdx.x] = term;
+    // publish this workgroup's range, then count it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) {
+      const unsigned arrived = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = arrived == gridDim.x * gridDim.y - 1;
+    }
+  }
+  __syncthreads();
+  if (!last) return;  // the whole workgroup leaves together
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // thread t finishes expert t (E <= 1024): the ranges' sums in range order
+  const int t = threadIdx.x;
+  const int tc = t < E ? t : E - 1;
+  double mp[kStatsMaxRowSplits];
+  int mc[kStatsMaxRowSplits];
+#pragma unroll
+  for (int rr = 0; rr < kStatsMaxRowSplits; ++rr) {
+    const int ri = rr < RS ? rr : 0;
+    mp[rr] = mid_p[(size_t)ri * E + tc];
+    mc[rr] = mid_c[(size_t)ri * E + tc];
+  }
+  double tot = 0.0;
+  int ct = 0;
+#pragma unroll
+  for (int rr = 0; rr < kStatsMaxRowSplits; ++rr)
+    if (rr < RS) {
+      tot += mp[rr];
+      ct += mc[rr];
+    }
+  double term = 0.0;
+  if (t < E) {
+    if (counts) counts[t] = ct;
+    if (prob_mean) prob_mean[t] = T > 0 ? (float)(tot / (double)T) : 0.f;
+    term = (double)ct * tot;
+  }
+  if (!loss) return;
+  // fixed order: within each wave a shuffle tree, then the wave sums in order
+  for (int m = 32; m >= 1; m >>= 1) term += __shfl_down(term, m);
+  if (lane == 0) lw[wave] = term;
+  __syncthreads();
+  if (t == 0) {
+    double l = lw[0];
+#pragma unroll
+    for (int w = 1; w < kColWaves; ++w) l += lw[w];
+    loss[0] = T > 0 ? (float)((double)E * l / ((double)T * (double)T)) : 0.f;
   }
 }
 
-__global__ void stats_loss_kernel(int T, int E, int nchunk, const double* __restrict__ chunk_loss,
-                                  float* __restrict__ loss) {
-  if (threadIdx.x != 0) return;
-  double tot = 0.0;
-  for (int c = 0; c < nchunk; ++c) tot += chunk_loss[c];
-  loss[0] = T > 0 ? (float)((double)E * tot / ((double)T * (double)T)) : 0.f;
+inline int stats_row_splits(int nblk) {
+  return std::max(1, std::min(kMaxRowSplits, (nblk + kColWaves * kColRows - 1) / (kColWaves * kColRows)));
 }
 
 __global__ void stats_empty_kernel(int E, int32_t* __restrict__ counts, float* __restrict__ prob_mean,
@@ -192,8 +247,8 @@ __global__ void stats_empty_kernel(int E, int32_t* __restrict__ counts, float* _
 
 template <int G, int NV, int U>
 void launch_partial(int nblk, int T, int E, int k, const float* logits, const float* bias, const int32_t* ids,
-                    double* part_p, int32_t* part_c, hipStream_t s) {
-  stats_partial_kernel<G, NV, U><<<nblk, 256, 0, s>>>(T, E, k, logits, bias, ids, part_p, part_c);
+                    double* part_p, int32_t* part_c, unsigned* counter, hipStream_t s) {
+  stats_partial_kernel<G, NV, U><<<nblk, 256, 0, s>>>(T, E, k, logits, bias, ids, part_p, part_c, counter);
 }
 
 inline int stats_group(int E, int k) { return (E <= 256 && k <= 16) ? 16 : 64; }
@@ -201,7 +256,9 @@ inline int stats_group(int E, int k) { return (E <= 256 && k <= 16) ? 16 : 64; }
 struct StatsWs {
   double* part_p;
   int32_t* part_c;
-  double* chunk_loss;
+  double* mid_p;  // [kMaxRowSplits, E]
+  int32_t* mid_c;
+  unsigned* counter;
 };
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -212,7 +269,10 @@ StatsWs stats_ws(void* ws, int nblk, int E) {
   StatsWs w;
   w.part_p = reinterpret_cast<double*>(p);
   w.part_c = reinterpret_cast<int32_t*>(p + al256(n * 8));
-  w.chunk_loss = reinterpret_cast<double*>(p + al256(n * 8) + al256(n * 4));
+  const size_t m = (size_t)kMaxRowSplits * E;
+  w.mid_p = reinterpret_cast<double*>(p + al256(n * 8) + al256(n * 4));
+  w.mid_c = reinterpret_cast<int32_t*>(p + al256(n * 8) + al256(n * 4) + al256(m * 8));
+  w.counter = reinterpret_cast<unsigned*>(p + al256(n * 8) + al256(n * 4) + al256(m * 8) + al256(m * 4));
   return w;
 }
 
@@ -231,7 +291,22 @@ size_t router_stats_ws_bytes(int T, int E) {
   const int nblk = router_stats_blocks(T, E);
   if (nblk == 0) return 0;  // an empty batch needs no workspace
   const size_t n = (size_t)nblk * (size_t)E;
-  return al256(n * 8) + al256(n * 4) + al256(16 * 8);
+  const size_t m = (size_t)kMaxRowSplits * E;
+  return al256(n * 8) + al256(n * 4) + al256(m * 8) + al256(m * 4) + 256;
+}
+
+size_t stats_finish_bytes(int E) {
+  const size_t m = (size_t)kMaxRowSplits * E;
+  return al256(m * 8) + al256(m * 4) + 256;
+}
+
+hipError_t launch_stats_finish(int T, int E, int nblk, const StatsPart& sp, int32_t* counts, float* prob_mean,
+                               float* loss, hipStream_t s) {
+  if (nblk < 1 || nblk > kStatsFinishMaxRows) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((E + 63) / 64), (unsigned)stats_row_splits(nblk));
+  stats_column_kernel<<<grid, 64 * kColWaves, 0, s>>>(T, E, nblk, sp.part_p, sp.part_c, counts, prob_mean, sp.mid_p,
+                                                      sp.mid_c, sp.counter, loss);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_stats(int T, int E, int k, const float* logits, const float* bias, const int32_t* ids,
@@ -245,7 +320,8 @@ hipError_t launch_router_stats(int T, int E, int k, const float* logits, const f
   {
     const int G = stats_group(E, k);
     const int nv = (E + G - 1) / G;
-#define MOE_STATS(Gv, NVv, Uv) launch_partial<Gv, NVv, Uv>(nblk, T, E, k, logits, bias, ids, w.part_p, w.part_c, s)
+#define MOE_STATS(Gv, NVv, Uv) \
+  launch_partial<Gv, NVv, Uv>(nblk, T, E, k, logits, bias, ids, w.part_p, w.part_c, w.counter, s)
     if (G == 16) {
       if (nv <= 1) MOE_STATS(16, 1, 4);
       else if (nv <= 2) MOE_STATS(16, 2, 4);
@@ -263,16 +339,10 @@ hipError_t launch_router_stats(int T, int E, int k, const float* logits, const f
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nchunk = (E + 63) / 64;  // E <= 1024: at most 16
-  stats_column_kernel<<<nchunk, 64 * kColWaves, 0, s>>>(T, E, nblk, w.part_p, w.part_c, counts, prob_mean,
-                                                        w.chunk_loss);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (loss) {
-    stats_loss_kernel<<<1, 64, 0, s>>>(T, E, nchunk, w.chunk_loss, loss);
-    e = hipGetLastError();
-  }
-  return e;
+  const dim3 grid((unsigned)((E + 63) / 64), (unsigned)stats_row_splits(nblk));
+  stats_column_kernel<<<grid, 64 * kColWaves, 0, s>>>(T, E, nblk, w.part_p, w.part_c, counts, prob_mean, w.mid_p,
+                                                      w.mid_c, w.counter, loss);
+  return hipGetLastError();
 }
 
 }  // namespace moe

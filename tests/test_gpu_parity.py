@@ -43,6 +43,10 @@ SCALED = {
     # GeGLU and a ragged batch; every output compared
     "stream_swiglu": scaled("decode_bf16", T=512, d=256, E=64, k=4, h=1024, h_shared=256),
     "stream_geglu_ragged": scaled("decode_bf16", T=300, d=512, E=64, k=6, h=512, act="geglu", h_shared=0),
+    # more selection workgroups than the selection-emitted by-products take:
+    # the layer computes them in the standalone passes
+    "stats_standalone_passes": scaled("granular_bf16", T=17000, d=128, E=16, k=2, h=128, h_shared=0,
+                                      capacity_factor=None),
 }
 
 
