@@ -142,13 +142,18 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
   const int total_mt = a.offsets ? sload(a.mtile_start, a.E_loc) : (a.rows_max + BM - 1) / BM;
   const int total = total_mt * NBLK;
   const int per = (total + 7) / 8;
+  // groups of GM m-tiles, m-tile fastest inside a group: kGroupM shares a
+  // weight slice between neighbouring m-tiles of one expert; where experts
+  // average fewer than two m-tiles, GM = 1 puts an expert's n-tiles side by
+  // side instead, so its activation rows are fetched into one XCD's L2 once
+  const int GM = (a.offsets && total_mt < 2 * a.E_loc) ? 1 : kGroupM;
   auto decode = [&](int sl, Tile& t) -> bool {
     const int R = xcd * per + sl;
     if (sl >= per || R >= total) return false;
-    const int grp = R / (kGroupM * NBLK);
-    const int t0 = grp * kGroupM;
-    const int gm = min(kGroupM, total_mt - t0);
-    const int rr = R - grp * kGroupM * NBLK;
+    const int grp = R / (GM * NBLK);
+    const int t0 = grp * GM;
+    const int gm = min(GM, total_mt - t0);
+    const int rr = R - grp * GM * NBLK;
     const int nb = rr / gm;
     const int mt = t0 + (rr - nb * gm);
     if (a.tile_tab) {

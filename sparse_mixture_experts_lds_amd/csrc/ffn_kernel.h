@@ -214,11 +214,16 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
     const FfnGemmArgs& a = gp.p[pi];
     const int R = pi ? xcd * per1 + (sl - n0x) : xcd * per0 + sl;
     const int total_mt = (pi ? total1 : total0) / NBLK;
-    // groups of kGroupM m-tiles, m-tile fastest inside a group
-    const int grp = R / (kGroupM * NBLK);
-    const int t0 = grp * kGroupM;
-    const int gm = min(kGroupM, total_mt - t0);
-    const int rr = R - grp * kGroupM * NBLK;
+    // groups of GM m-tiles, m-tile fastest inside a group: GM = kGroupM
+    // shares each weight tile between neighbouring m-tiles of one expert;
+    // where experts average fewer than two m-tiles there is little of that to
+    // share, and GM = 1 puts an expert's n-tiles side by side instead, so its
+    // activation rows are fetched into one XCD's L2 once
+    const int GM = (a.offsets && total_mt < 2 * a.E_loc) ? 1 : kGroupM;
+    const int grp = R / (GM * NBLK);
+    const int t0 = grp * GM;
+    const int gm = min(GM, total_mt - t0);
+    const int rr = R - grp * GM * NBLK;
     const int nb = rr / gm;
     const int t = t0 + (rr - nb * gm);
     int4 ti;
