@@ -2,6 +2,7 @@
 // (the kernel template is in ffn_kernel.h; INT4 weights are in ffn_i4.hip).
 // Built with the MFMA "VGPR form": accumulators carried across the k-loop stay
 // in ordinary VGPRs instead of being shuffled between register files.
+#include "ffn_bs.h"
 #include "ffn_kernel.h"
 #include "ffn_wide.h"
 #include "ffn_wide64.h"
@@ -9,6 +10,12 @@
 namespace moe {
 
 using ffn_detail::launch_mf_nf;
+
+#ifndef MOE_BS_BNO
+#define MOE_BS_BNO 64
+#endif
+// outputs per tile of the weight-streaming gate/up kernel
+constexpr int kBsBno = MOE_BS_BNO;
 
 hipError_t launch_ffn_gemm_i4(const FfnGemmArgs& a, bool gateup, bool split, int BM, int NF, hipStream_t s);
 
@@ -89,6 +96,9 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   if (w_type == W_F32)
     return gateup ? launch_mf_nf<W_F32, true, false>(&a, 1, BM, NF, s) : launch_mf_nf<W_F32, false, false>(&a, 1, BM, NF, s);
   if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);
+  // few rows per expert: the weight-streaming kernel (its tiles are always 128
+  // outputs wide)
+  if (gateup && (BM == 32 || BM == 64) && ffn_bs::ok(&a, 1)) return ffn_bs::launch(&a, 1, BM / 16, kBsBno, s);
   if (gateup) return launch_mf_nf<W_BF16, true, false>(&a, 1, BM, NF, s);
   return split ? launch_mf_nf<W_BF16, false, true>(&a, 1, BM, NF, s) : launch_mf_nf<W_BF16, false, false>(&a, 1, BM, NF, s);
 }
@@ -102,6 +112,7 @@ hipError_t launch_ffn_gemm_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bo
   if (BM == ffn_wide::BM || (w_type != W_F32 && w_type != W_BF16)) return hipErrorInvalidValue;
   if (w_type == W_F32)
     return gateup ? launch_mf_nf<W_F32, true, false>(a, 2, BM, NF, s) : launch_mf_nf<W_F32, false, false>(a, 2, BM, NF, s);
+  if (gateup && (BM == 32 || BM == 64) && ffn_bs::ok(a, 2)) return ffn_bs::launch(a, 2, BM / 16, kBsBno, s);
   return gateup ? launch_mf_nf<W_BF16, true, false>(a, 2, BM, NF, s) : launch_mf_nf<W_BF16, false, false>(a, 2, BM, NF, s);
 }
 
