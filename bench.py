@@ -112,7 +112,7 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
             "kept_tokens": kept_tokens}
 
 
-GEMM_SOURCES = ("ffn_kernel.h", "ffn_wide.h", "ffn_wide64.h", "ffn_i4s.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
+GEMM_SOURCES = ("ffn_kernel.h", "ffn_wide.h", "ffn_wide64.h", "ffn_i4s.h", "ffn_bs.h", "ffn.hip", "ffn_i4.hip", "moe_internal.h")
 
 
 def gemm_source_hash():

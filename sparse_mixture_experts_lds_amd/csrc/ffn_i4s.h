@@ -363,9 +363,10 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
   wait_vm<0>();  // every load has landed before the workgroup ends
 }
 
-// Whether the streaming kernel takes this INT4 gate/up GEMM.
+// Whether the streaming kernel takes this INT4 gate/up GEMM.  The loads run
+// two k-blocks ahead within a tile, so a tile has at least two.
 inline bool ok(const FfnGemmArgs& a) {
-  return a.K % KB == 0 && a.N % BNO == 0 && a.out_f32 && (size_t)a.a_rows * a.K * 2 <= 0xFFFFFFFFull &&
+  return a.K % KB == 0 && a.K >= 2 * KB && a.N % BNO == 0 && a.out_f32 && (size_t)a.a_rows * a.K * 2 <= 0xFFFFFFFFull &&
          (size_t)a.N * (a.K / 2) <= 0x7FFFFFFFull;
 }
 

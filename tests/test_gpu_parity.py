@@ -377,6 +377,39 @@ def test_expert_ffn_entry_point(wdt, act, counts):
     assert out_err(yg, ref, "f32" if wdt == "f32" else "bf16") <= TOL[wdt]
 
 
+# INT4 experts of a few dozen rows: gate/up on 32-row tiles of 128 outputs
+# streaming the packed codes through LDS (d a multiple of 256 and at least
+# 512), down on the narrow 16-row tiles.  Ragged and empty experts; the second
+# shape has more gate/up tiles than workgroups, so a workgroup runs several
+# tiles and loads the next one's first k-blocks during the current one's last
+# (four k-blocks per tile there).
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+@pytest.mark.parametrize("shape", ["ragged", "many_tiles"])
+def test_expert_ffn_int4_streaming(act, shape):
+    moe = _moe()
+    rng = np.random.default_rng(31 if shape == "ragged" else 32)
+    if shape == "ragged":
+        counts, d, h = [0, 5, 33, 1, 0, 17, 16, 40, 2], 768, 512
+    else:
+        counts, d, h = list(rng.integers(0, 41, size=48)), 1024, 768
+    E_loc, rows = len(counts), int(sum(counts))
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = torch.from_numpy(rng.standard_normal((rows, d)).astype(np.float32)).to(torch.bfloat16)
+    ws = [(rng.standard_normal(s) / np.sqrt(s[-1])).astype(np.float32) for s in [(E_loc, h, d), (E_loc, h, d), (E_loc, d, h)]]
+    qs = [orc.quantize_int4(w) for w in ws]
+    y = moe.expert_ffn(a.to(DEV), torch.from_numpy(offs).to(DEV), *[torch.from_numpy(q[0]).to(DEV) for q in qs],
+                       act=act, sg=torch.from_numpy(qs[0][1]).to(DEV), su=torch.from_numpy(qs[1][1]).to(DEV),
+                       sd=torch.from_numpy(qs[2][1]).to(DEV))
+    W = [orc.dequantize_int4(*q) for q in qs]
+    a64 = as_f64(a)
+    ref = np.zeros((rows, d))
+    for e in range(E_loc):
+        sl = slice(offs[e], offs[e + 1])
+        if offs[e + 1] > offs[e]:
+            ref[sl] = orc.gated_ffn(a64[sl], W[0][e], W[1][e], W[2][e], act)
+    assert out_err(y.float().cpu().numpy(), ref, "bf16") <= TOL["i4g128"]
+
+
 # Enough 256-row wide tiles (10 m-tiles x 32 n-blocks) that the gate/up launch
 # runs several tiles back to back per workgroup, the next tile's operands
 # loaded during the current one's last k-blocks; ragged experts, so tiles end
