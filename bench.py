@@ -60,6 +60,9 @@ def parse_args(argv=None):
                    help="skip the backward, router by-products and owner dispatch timings")
     p.add_argument("--no-peaks", action="store_true", help="skip the on-box copy and GEMM rate measurements")
     p.add_argument("--warm-cache", action="store_true", help="do not flush the Infinity Cache between steps")
+    p.add_argument("--clean-flush", action="store_true",
+                   help="after the 512 MiB flush write, read another 512 MiB, so each step starts with clean "
+                        "cache lines only (no write-backs of the flush left for the timed work)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--tree", default=None, metavar="WORKLOAD",
@@ -226,13 +229,39 @@ def cpu_baseline(cfg, target_s):
                       "(%.1f s in all)" % (Ts, cfg.T, cfg.name, len(times), total)}
 
 
+class CacheFlush:
+    """The cold-cache step before each timed call: a 512 MiB scratch write,
+    which leaves the Infinity Cache full of dirty lines that the timed work
+    writes back as it evicts them.  With clean=True a 512 MiB read follows,
+    so the timed work starts with clean lines only.  Called with warm=True it
+    does nothing."""
+
+    def __init__(self, torch, warm=False, clean=False):
+        self.warm = warm
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        self.rd = None
+        if clean and not warm:
+            self.rd = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda:0")
+
+    def __call__(self, i):
+        if self.warm:
+            return
+        self.buf.fill_(i & 0xFF)
+        if self.rd is not None:
+            self.rd.sum()
+
+    def label(self, what="step"):
+        if self.warm:
+            return "warm"
+        return "cold (512 MiB flush %sbefore each %s)" % ("write + 512 MiB read " if self.rd is not None else "", what)
+
+
 def timed_calls(torch, fn, flush, args, reps):
     """Median time in ms of `fn()` over `reps` calls, each after a cache flush."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     fn()
     for i, (e0, e1) in enumerate(ev):
-        if not args.warm_cache:
-            flush.fill_(i & 0xFF)
+        flush(i)
         e0.record()
         fn()
         e1.record()
@@ -405,8 +434,7 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
         return ev
 
     def step(i, **kw):
-        if not args.warm_cache:
-            flush.fill_(i & 0xFF)
+        flush(i)
         moe.layer_fwd(x, W, logits=logits, out=out, ws=ws, **kw)
 
     for i in range(warmup):
@@ -471,7 +499,7 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E,
                    "experts_local": cfg.E_loc, "top_k": cfg.k, "hidden": cfg.h, "shared_hidden": cfg.h_shared,
                    "act": cfg.act, "weights": cfg.w_dtype, "capacity": inp.capacity,
-                   "cache": "warm" if args.warm_cache else "cold (512 MiB flush before each step)"},
+                   "cache": flush.label()},
         "roofline": roof,
         "layer_roofline": roofline_entry(work["layer"], ms, peak),
         "layer_algorithmic": {"bytes": work["layer"]["bytes"], "flops": work["layer"]["flops"]},
@@ -481,6 +509,14 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
         "step_ms_note": "per-segment medians from an untimed pass with an event at every boundary",
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 4),
     }
+    if extras and not flush.warm and flush.rd is None:
+        # secondary: the same forward after a flush that leaves clean lines
+        # only; the difference from ms_per_step is the write-back of the
+        # flush's dirty lines, which the primary number includes
+        clean = CacheFlush(torch, clean=True)
+        rec["clean_cold_ms_per_step"] = round(
+            timed_calls(torch, lambda: moe.layer_fwd(x, W, logits=logits, out=out, ws=ws), clean, args, steps), 4)
+        del clean
     if extras:
         rec["router_stats"] = router_stats_timing(moe, torch, cfg, tr, logits, W.bias, flush, args, x=x, W=W, ws=ws)
         rec["owner_dispatch"] = dispatch_timing(moe, torch, cfg, tr, x, flush, args)
@@ -548,7 +584,7 @@ def measure_tree_route(moe, torch, name, steps, warmup, args, flush):
         "dtype": cfg.dtype,
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "branch": cfg.branch, "levels": cfg.levels, "gate_rows": rows,
-                   "cache": "warm" if args.warm_cache else "cold (512 MiB flush before each call)"},
+                   "cache": flush.label("call")},
         "roofline": roof,
         "flat_router_context": flat,
     }
@@ -587,7 +623,7 @@ def main(argv=None):
         if args.tree not in TREE_CONFIGS:
             print("unknown tree workload %r (one of %s)" % (args.tree, ", ".join(TREE_CONFIGS)), file=sys.stderr)
             return 2
-        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+        flush = CacheFlush(torch, args.warm_cache, args.clean_flush)
         print(json.dumps(measure_tree_route(moe, torch, args.tree, args.steps, args.warmup, args, flush)),
               flush=True)
         return 0
@@ -595,7 +631,7 @@ def main(argv=None):
         print("unknown workload %r (one of %s)" % (args.workload, ", ".join(WORKLOADS)), file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    flush = CacheFlush(torch, args.warm_cache, args.clean_flush)
 
     head = measure_workload(moe, torch, np, args.workload, args.steps, args.warmup, args, flush,
                             extras=not args.no_extras)
