@@ -10,7 +10,10 @@ events on the layer's stream bracket the layer itself, and a start/stop pair
 attached to the launch of the dominant routed GEMM (hipExtLaunchKernel) times
 that kernel.  A separate untimed pass with an event at every step boundary
 splits the time by step (each event record idles the GPU for a few
-microseconds, so the timed steps carry no others).
+microseconds, so the timed steps carry no others).  The flush leaves the
+Infinity Cache full of dirty lines, whose write-back the timed work pays as it
+evicts them; the headline record also gives the forward's median after a
+flush followed by a 512 MiB read (clean lines only) as clean_cold_ms_per_step.
 
 The headline workload (default: the wide GeGLU layer, 16384 tokens, the
 largest of the five) is timed over exactly --steps steps after --warmup
@@ -60,6 +63,8 @@ def parse_args(argv=None):
                    help="skip the backward, router by-products and owner dispatch timings")
     p.add_argument("--no-peaks", action="store_true", help="skip the on-box copy and GEMM rate measurements")
     p.add_argument("--warm-cache", action="store_true", help="do not flush the Infinity Cache between steps")
+    p.add_argument("--no-clean-cold", action="store_true",
+                   help="skip the secondary forward timing after a clean flush")
     p.add_argument("--clean-flush", action="store_true",
                    help="after the 512 MiB flush write, read another 512 MiB, so each step starts with clean "
                         "cache lines only (no write-backs of the flush left for the timed work)")
@@ -509,7 +514,7 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
         "step_ms_note": "per-segment medians from an untimed pass with an event at every boundary",
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 4),
     }
-    if extras and not flush.warm and flush.rd is None:
+    if extras and not flush.warm and flush.rd is None and not args.no_clean_cold:
         # secondary: the same forward after a flush that leaves clean lines
         # only; the difference from ms_per_step is the write-back of the
         # flush's dirty lines, which the primary number includes
