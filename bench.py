@@ -291,13 +291,29 @@ def router_stats_timing(moe, torch, cfg, tr, logits, bias, flush, args, x=None, 
            "us_per_call": round(us, 2), "bytes": nbytes, "achieved_GBps": round(gbps, 1),
            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
     if x is not None:
-        with_s = timed_calls(torch, lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True, stats=True),
-                             flush, args, reps)
-        without = timed_calls(torch, lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True), flush, args,
-                              reps)
-        rec["in_layer_us"] = round(1e3 * (with_s - without), 2)
-        rec["in_layer_note"] = "median layer time with the by-products minus without (both traced)"
+        d = paired_diff_ms(torch, lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True, stats=True),
+                           lambda: moe.layer_fwd(x, W, logits=logits, ws=ws, trace=True), flush, 2 * reps)
+        rec["in_layer_us"] = round(1e3 * d, 2)
+        rec["in_layer_note"] = ("median over %d pairs of the layer time with the by-products minus without "
+                                "(both traced, each after its own flush, the pair's order alternating)" % (2 * reps))
     return rec
+
+
+def paired_diff_ms(torch, fa, fb, flush, pairs):
+    """Median over `pairs` of the time of fa() minus that of fb(), the two run
+    back to back, each after a cache flush, in alternating order."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(pairs)]
+    fa()
+    fb()
+    for i, e in enumerate(ev):
+        order = ((fa, e[0], e[1]), (fb, e[2], e[3]))
+        for j, (fn, e0, e1) in enumerate(order if i % 2 == 0 else order[::-1]):
+            flush(2 * i + j)
+            e0.record()
+            fn()
+            e1.record()
+    torch.cuda.synchronize()
+    return median([e[0].elapsed_time(e[1]) - e[2].elapsed_time(e[3]) for e in ev])
 
 
 def dispatch_timing(moe, torch, cfg, tr, x, flush, args, reps=20):
