@@ -1021,8 +1021,17 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     return (bf && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
   };
 
-  // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients
-  if ((rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, own_rc ? b.mtile_rc : b.mtile,
+  // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients.
+  // Where the forward's gate/up takes the wide tiles, the recompute is that
+  // launch again with the gate backward in its epilogue (after dz'): g and u
+  // never leave registers, and the gate gradients come out as partial sums
+  // per 64 hidden units (in G's memory), added up in a fixed order.
+  const FfnPlan wide_plan{256, 4, 4, false, 0};
+  const FfnGemmArgs gu_bwd = gate_up_args(E_loc, rows, d, h, L->act, x, T, b.sorted_pair, k, b.offsets, b.mtile_rc,
+                                          b.tiles_rc, wide_plan, L->w_gate, L->w_up, nullptr, nullptr, b.ZW);
+  const bool fused_gb = wide_rc && gateup_bwd_wide_ok(gu_bwd);
+  if (!fused_gb &&
+      (rc = recompute_gu(wt, true, x, T, k, b.sorted_pair, b.offsets, own_rc ? b.mtile_rc : b.mtile,
                          own_rc ? b.tiles_rc : b.tiles, E_loc, rows, d, h, BMrc, L->w_gate, L->w_up, b.G, b.U, s)))
     return rc;
   bwdg::NnArgs n{};
@@ -1044,8 +1053,16 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   n.N = h;
   n.K = d;
   MOE_HIP(run_nn(n));
-  MOE_HIP(launch_gate_bwd(bf, L->act, rows, h, b.offsets + E_loc, b.G, b.U, b.dZ, b.sorted_pair, b.tw, b.dGU, b.ZW,
-                          b.dgate, s));
+  if (fused_gb) {
+    // the rows' gates in U's memory, the gate-gradient partials in G's
+    MOE_HIP(launch_row_gates(rows, b.offsets + E_loc, b.sorted_pair, b.tw, b.U, s));
+    const GateBwdOut gbo{b.dZ, b.U, static_cast<uint16_t*>(b.dGU), static_cast<uint16_t*>(b.ZW), b.G};
+    MOE_HIP(launch_gateup_bwd_wide(&gu_bwd, &gbo, 1, s));
+    MOE_HIP(launch_gate_part_sum(rows, h, b.offsets + E_loc, b.G, b.sorted_pair, b.dgate, s));
+  } else {
+    MOE_HIP(launch_gate_bwd(bf, L->act, rows, h, b.offsets + E_loc, b.G, b.U, b.dZ, b.sorted_pair, b.tw, b.dGU,
+                            b.ZW, b.dgate, s));
+  }
   if (gr->dw_down) {
     bwdg::TnArgs t{};
     t.A = dout;
@@ -1110,8 +1127,12 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     const int swt = wtype_of(L->act_dtype);
     // the forward's shared plan: wide tiles take it to the wide kernel here too
     const int BMsr = (shared_plan(T, d, hs, swt).BM == 256 && wide_rc_nf(bf, d, hs)) ? 256 : (bf ? BMb : 32);
-    if ((rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMsr, L->ws_gate,
-                           L->ws_up, b.Gs, b.Us, s)))
+    // as for the routed experts: the wide gate/up launch with the gate backward in its epilogue
+    const FfnGemmArgs sgu_bwd = gate_up_args(1, T, d, hs, L->act, x, T, nullptr, 1, nullptr, nullptr, nullptr,
+                                             wide_plan, L->ws_gate, L->ws_up, nullptr, nullptr, b.ZWs);
+    const bool fused_sgb = BMsr == 256 && gateup_bwd_wide_ok(sgu_bwd);
+    if (!fused_sgb && (rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMsr,
+                                         L->ws_gate, L->ws_up, b.Gs, b.Us, s)))
       return rc;
     const int BMs = (bf && T >= 4096) ? 128 : 64;
     const int gm = (T + BMs - 1) / BMs;
@@ -1135,8 +1156,14 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     n.N = hs;
     n.K = d;
     MOE_HIP(run_nn_shared(n));
-    MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs, nullptr,
-                            s));
+    if (fused_sgb) {
+      // the shared expert's gate gradient is not needed: its partials go to Gs and stay there
+      const GateBwdOut gbo{b.dZs, nullptr, static_cast<uint16_t*>(b.dGUs), static_cast<uint16_t*>(b.ZWs), b.Gs};
+      MOE_HIP(launch_gateup_bwd_wide(&sgu_bwd, &gbo, 1, s));
+    } else {
+      MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs,
+                              nullptr, s));
+    }
     if (gr->dws_down && (rc = tn_single(bf, dout, d, b.ZWs, hs, T, d, hs, d, gr->dws_down, gr->dws_down, hs, b.part,
                                         s)))
       return rc;

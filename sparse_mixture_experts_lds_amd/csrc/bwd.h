@@ -69,6 +69,13 @@ hipError_t launch_bwd_tn_wide(const bwdg::TnArgs& a, int grid_z, hipStream_t s);
 hipError_t launch_gate_bwd(bool bf16, int act, int rows, int h, const int32_t* n_rows, const float* G,
                            const float* U, const float* dZ, const int32_t* sorted_pair, const float* tw,
                            void* dGU, void* ZW, float* dgate, hipStream_t s);
+// w_row[r] = tw[sorted_pair[r]] for grouped rows r < *n_rows.
+hipError_t launch_row_gates(int rows, const int32_t* n_rows, const int32_t* sorted_pair, const float* tw,
+                            float* w_row, hipStream_t s);
+// dgate[pair of r] = the sum, in a fixed order, of part[r][0 .. h/64) (the
+// partials of a gate/up launch with the gate backward in its epilogue).
+hipError_t launch_gate_part_sum(int rows, int h, const int32_t* n_rows, const float* part,
+                                const int32_t* sorted_pair, float* dgate, hipStream_t s);
 // Softmax / gate / balance backward per token: dL (fp32 [T, E], may be NULL),
 // dLc (compute dtype, [T, Epad], zero past E) and the pair gradients of the
 // gates (fp32 [T, k], 0 for pairs not kept; may be NULL).

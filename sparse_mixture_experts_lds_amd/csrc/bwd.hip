@@ -43,27 +43,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int rows, int h, const in
     float dg[4], du[4], zw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a, ad;
-      // a as the forward's epilogue forms it (silu_hw, gelu_hw)
-      if constexpr (ACT == 0) {
-        const float sg = sigmoid_hw(g[i]);
-        a = g[i] * sg;
-        ad = sg * (1.f + g[i] * (1.f - sg));
-      } else {
-        float e;
-        const float c = gelu_tail(g[i], e);
-        const float h = 0.5f * g[i] * c;
-        a = g[i] >= 0.f ? g[i] - h : h;
-        const float phi = g[i] >= 0.f ? 1.f - 0.5f * c : 0.5f * c;
-        ad = phi + g[i] * e * 0.39894228040143268f;
-      }
-      float z = a * u[i];
-      if constexpr (sizeof(T) == 2) z = bf16_bits_to_f32(f32_to_bf16_bits(z));
+      const float z = gate_bwd_point<ACT, sizeof(T) == 2>(g[i], u[i], dz1[i], w, dg[i], du[i], zw[i]);
       part += dz1[i] * z;
-      const float dzw = w * dz1[i];
-      dg[i] = dzw * u[i] * ad;
-      du[i] = dzw * a;
-      zw[i] = w * z;
     }
     T* dgu = dGU + (size_t)r * 2 * h;
     if constexpr (sizeof(T) == 2) {
@@ -85,6 +66,32 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(int rows, int h, const in
   }
   part = wave_sum(part);
   if (lane == 0 && dgate) dgate[p] = part;
+}
+
+// The gate gradient of each grouped row from the partial sums a fused gate/up
+// launch wrote (one per 64-wide block of hidden units): a 16-lane group per
+// row adds its nb partials lane-strided, then across the group in a fixed
+// shuffle order.
+__global__ __launch_bounds__(256) void gate_part_sum_kernel(int rows, int nb, const int32_t* __restrict__ n_rows,
+                                                            const float* __restrict__ part,
+                                                            const int32_t* __restrict__ sorted_pair,
+                                                            float* __restrict__ dgate) {
+  const int gl = threadIdx.x & 15;
+  const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int n = n_rows ? *n_rows : rows;
+  if (r >= n || r >= rows) return;  // whole groups leave together
+  float v = 0.f;
+  for (int j = gl; j < nb; j += 16) v += part[(size_t)r * nb + j];
+  v = group_sum<16>(v);
+  if (gl == 0) dgate[sorted_pair ? sorted_pair[r] : r] = v;
+}
+
+// The gate of each grouped row's pair, w_row[r] = tw[sorted_pair[r]].
+__global__ __launch_bounds__(256) void row_gates_kernel(int rows, const int32_t* __restrict__ n_rows,
+                                                        const int32_t* __restrict__ sorted_pair,
+                                                        const float* __restrict__ tw, float* __restrict__ w_row) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < rows && r < *n_rows) w_row[r] = tw[sorted_pair[r]];
 }
 
 // ---------------------------------------------------------------- router
@@ -333,6 +340,22 @@ hipError_t launch_bwd_tn(bool bf16, const bwdg::TnArgs& a, int grid_z, hipStream
     bwdg::tn_kernel<uint16_t><<<grid, bwdg::NTH, 0, s>>>(a);
   else
     bwdg::tn_kernel<float><<<grid, bwdg::NTH, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_gates(int rows, const int32_t* n_rows, const int32_t* sorted_pair, const float* tw,
+                            float* w_row, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  row_gates_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(rows, n_rows, sorted_pair, tw, w_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_part_sum(int rows, int h, const int32_t* n_rows, const float* part,
+                                const int32_t* sorted_pair, float* dgate, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (h % 64) return hipErrorInvalidValue;
+  gate_part_sum_kernel<<<dim3((unsigned)((rows + 15) / 16)), 256, 0, s>>>(rows, h / 64, n_rows, part, sorted_pair,
+                                                                         dgate);
   return hipGetLastError();
 }
 

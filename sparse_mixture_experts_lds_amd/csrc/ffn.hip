@@ -116,6 +116,18 @@ hipError_t launch_ffn_gemm_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bo
   return gateup ? launch_mf_nf<W_BF16, true, false>(a, 2, BM, NF, s) : launch_mf_nf<W_BF16, false, false>(a, 2, BM, NF, s);
 }
 
+bool gateup_bwd_wide_ok(const FfnGemmArgs& a) {
+  return a.K % (2 * ffn_wide64::KB) == 0 && a.N % (ffn_wide64::BW / 2) == 0 && !a.out_f32 && a.W1 &&
+         a.a_rows >= 0 && (size_t)a.a_rows * (size_t)a.K * 2 <= 0xFFFFFFFFull;
+}
+
+hipError_t launch_gateup_bwd_wide(const FfnGemmArgs* a, const GateBwdOut* gb, int np, hipStream_t s) {
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  for (int i = 0; i < np; ++i)
+    if (!gateup_bwd_wide_ok(a[i])) return hipErrorInvalidValue;
+  return ffn_wide64::launch<true, true>(a, np, nullptr, nullptr, s, gb);
+}
+
 hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int NF,
                                      void* ev_start, void* ev_stop, hipStream_t s) {
   const FfnGemmArgs a[2] = {a0, a1};

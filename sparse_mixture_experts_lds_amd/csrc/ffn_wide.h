@@ -137,6 +137,7 @@ __device__ __forceinline__ int4 sload4(const int4* p, int i) {
 struct WideArgs {
   FfnGemmArgs p[2];
   int np;  // 1 or 2
+  GateBwdOut gb[2];  // gate/up launches with the gate backward in their epilogue only
 };
 
 // tiles of one problem: m-tiles x weight-row blocks

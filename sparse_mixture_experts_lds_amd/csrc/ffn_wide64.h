@@ -70,7 +70,9 @@ struct Ops {
   uint32_t a_off[LA];
 };
 
-template <bool GATEUP, int OUT, int ACT>
+// GBWD (gate/up only): the epilogue does the gate backward (GateBwdOut)
+// instead of storing z.
+template <bool GATEUP, int OUT, int ACT, bool GBWD = false>
 __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
   constexpr int BNO = GATEUP ? BW / 2 : BW;  // output columns per tile
   constexpr int MF = 4, NF = BW / 32;
@@ -291,7 +293,58 @@ __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
     }
 
     unsigned char* obase = static_cast<unsigned char*>(args.out) + ((size_t)tc.row0 * N + tc.n0) * (OUT == 1 ? 4 : 2);
-    if constexpr (GATEUP) {
+    if constexpr (GATEUP && GBWD) {
+      // ---------------- gate backward epilogue: lane (lrow, q) holds g and u
+      // of hidden units c0 + 16 f + 0..3 of tile row 64 wr + 16 mi + lrow
+      // (c0 = n0 + 64 wc + 4 q); with that row's dz' it writes [dg | du] and
+      // w z, and the four lanes q of the row add their 16 products dz' z in a
+      // fixed order into the row's partial of the 64-wide block n0 / 64 + wc
+      if (active) {
+        const GateBwdOut& gb = wa.gb[tc.pi];
+        const int nbk = N / 64;
+#pragma unroll
+        for (int mi = 0; mi < MF; ++mi) {
+          const int row = 64 * wr + 16 * mi + lrow;
+          float part = 0.f;
+          if (row < nrows) {
+            const int rg = tc.row0 + row;
+            const int c0 = tc.n0 + HW / 2 * wc + 4 * q;
+            // the row's gate and its dz' loaded together (one row at a time:
+            // the next tile's first fragments hold registers too)
+            const float w = gb.w_row ? gb.w_row[rg] : 1.f;
+            const float* dzr = gb.dZ + (size_t)rg * N + c0;
+            f32x4 dz[NF / 2];
+#pragma unroll
+            for (int f = 0; f < NF / 2; ++f) dz[f] = *reinterpret_cast<const f32x4*>(dzr + 16 * f);
+            uint16_t* dgr = gb.dGU + (size_t)rg * 2 * N + c0;
+            uint16_t* zwr = gb.ZW + (size_t)rg * N + c0;
+#pragma unroll
+            for (int f = 0; f < NF / 2; ++f) {
+              float dg[4], du[4], zw[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float z = gate_bwd_point<ACT, true>(acc[mi][f][r], acc[mi][f + NF / 2][r], dz[f][r], w, dg[r],
+                                                          du[r], zw[r]);
+                part += dz[f][r] * z;
+              }
+              *reinterpret_cast<uint2*>(dgr + 16 * f) = uint2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+              *reinterpret_cast<uint2*>(dgr + N + 16 * f) =
+                  uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+              *reinterpret_cast<uint2*>(zwr + 16 * f) = uint2{pack_bf16x2(zw[0], zw[1]), pack_bf16x2(zw[2], zw[3])};
+            }
+          }
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+          if (q == 0 && row < nrows) gb.part[(size_t)(tc.row0 + row) * nbk + tc.n0 / 64 + wc] = part;
+        }
+      }
+      if (!has_next) break;
+      tc = tn;
+      cur = nxt;
+      sln = next_slot(sln + S, tn);
+      has_next = sln < nslots;
+      if (has_next) make_ops(tn, nxt);
+    } else if constexpr (GATEUP) {
       // ---------------- gate/up epilogue (as ffn_wide.h): lane (lrow, q)
       // holds g (fragment f) and u (fragment f + NF/2) of four consecutive
       // outputs of tile row 64 wr + 16 mi + lrow; z goes out from registers
@@ -372,13 +425,21 @@ __global__ __launch_bounds__(512) void wide64_kernel(WideArgs wa) {
 // np problems (1 or 2) of the same kind in one launch, problem 0's tiles first;
 // the events, if any, are attached to the launch.  Every K must be a multiple
 // of 128 (an even number of 64-deep k-blocks).
-template <bool GATEUP>
-hipError_t launch(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, hipStream_t s) {
+template <bool GATEUP, bool GBWD = false>
+hipError_t launch(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, hipStream_t s,
+                  const GateBwdOut* gb = nullptr) {
   constexpr int BNO = GATEUP ? BW / 2 : BW;
   if (np < 1 || np > 2) return hipErrorInvalidValue;
   if (GATEUP && a[0].out_f32) return hipErrorInvalidValue;  // gate/up writes z in bf16
   WideArgs w{};
   w.np = np;
+  if (GBWD) {
+    if (!GATEUP || !gb) return hipErrorInvalidValue;
+    for (int i = 0; i < np; ++i) {
+      if (!gb[i].dZ || !gb[i].dGU || !gb[i].ZW || !gb[i].part) return hipErrorInvalidValue;
+      w.gb[i] = gb[i];
+    }
+  }
   long long slots = 0;
   for (int i = 0; i < np; ++i) {
     const FfnGemmArgs& p = a[i];
@@ -406,10 +467,15 @@ hipError_t launch(const FfnGemmArgs* a, int np, void* ev_start, void* ev_stop, h
     else
       kernel<<<dim3((unsigned)g), dim3(512), 0, s>>>(w);
   };
-  if (!GATEUP && a[0].out_f32) go(wide64_kernel<false, 1, 0>);
-  else if (!GATEUP && a[0].out_f16) go(wide64_kernel<false, 2, 0>);
-  else if (GATEUP && a[0].act == 1) go(wide64_kernel<GATEUP, 0, 1>);
-  else go(wide64_kernel<GATEUP, 0, 0>);
+  if constexpr (GBWD) {
+    if (a[0].act == 1) go(wide64_kernel<true, 0, 1, true>);
+    else go(wide64_kernel<true, 0, 0, true>);
+  } else {
+    if (!GATEUP && a[0].out_f32) go(wide64_kernel<false, 1, 0>);
+    else if (!GATEUP && a[0].out_f16) go(wide64_kernel<false, 2, 0>);
+    else if (GATEUP && a[0].act == 1) go(wide64_kernel<GATEUP, 0, 1>);
+    else go(wide64_kernel<GATEUP, 0, 0>);
+  }
   return hipGetLastError();
 }
 

@@ -96,6 +96,36 @@ __device__ __forceinline__ float gelu_hw(float g) {
   return g >= 0.f ? g - h : h;
 }
 
+// Gate backward at one hidden unit of a pair row with gate w (ACT 0 SiLU, 1
+// GELU, each as the forward's epilogue forms it): a = act(g), a' = act'(g),
+// z = a u (rounded to bf16 when BF16, as the forward stores it); dg =
+// w dz' u a', du = w dz' a, zw = w z.  Returns z, whose products with dz'
+// sum to the pair's gate gradient.
+template <int ACT, bool BF16>
+__device__ __forceinline__ float gate_bwd_point(float g, float u, float dz1, float w, float& dg, float& du,
+                                                float& zw) {
+  float a, ad;
+  if constexpr (ACT == 0) {
+    const float sg = sigmoid_hw(g);
+    a = g * sg;
+    ad = sg * (1.f + g * (1.f - sg));
+  } else {
+    float e;
+    const float c = gelu_tail(g, e);
+    const float h = 0.5f * g * c;
+    a = g >= 0.f ? g - h : h;
+    const float phi = g >= 0.f ? 1.f - 0.5f * c : 0.5f * c;
+    ad = phi + g * e * 0.39894228040143268f;
+  }
+  float z = a * u;
+  if constexpr (BF16) z = bf16_bits_to_f32(f32_to_bf16_bits(z));
+  const float dzw = w * dz1;
+  dg = dzw * u * ad;
+  du = dzw * a;
+  zw = w * z;
+  return z;
+}
+
 // Reductions over a group of G lanes (G = 16: one DPP row; G = 64: the wave).
 // Every lane of the group ends with the result.
 template <int CTRL>
@@ -240,6 +270,19 @@ hipError_t launch_mtile_prefix(int E_loc, int BM, const int32_t* offsets, int32_
                                int4* tile_tab, hipStream_t s);
 
 // Grouped GEMMs.
+// Where a gate/up launch that recomputes g and u for the backward sends its
+// results instead of z (per problem): for grouped row r with gate w =
+// w_row[r] (or 1) it writes dGU[r] = [dg | du] and ZW[r] = w z (bf16), and
+// part[r][j] = the sum of dz'[r, c] z[r, c] over hidden units c of 64-wide
+// block j.
+struct GateBwdOut {
+  const float* dZ;     // [rows, h] dz' = dout Wd per grouped row
+  const float* w_row;  // [rows] gate of each grouped row's pair, NULL: 1
+  uint16_t* dGU;       // [rows, 2h]
+  uint16_t* ZW;        // [rows, h]
+  float* part;         // [rows, h / 64]
+};
+
 struct FfnGemmArgs {
   const void* A;             // activations [rows, K] (bf16 or f32)
   const int32_t* row_index;  // NULL: A row = grouped row; else A row = row_index[r] / row_div
@@ -281,6 +324,11 @@ hipError_t launch_ffn_gemm_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bo
 // Two problems of the same kind (bf16 weights, wide 256-row tiles, 64 * NF
 // weight rows per tile, same activation and output type) in one launch, the
 // tiles of a0 dispatched first; the events, if any, time the launch.
+// The wide gate/up GEMM (bf16, 256-row tiles of 128 outputs; K and N
+// multiples of 128) of np problems with the gate backward in its epilogue
+// (GateBwdOut) instead of the z store; a's out is not written.
+bool gateup_bwd_wide_ok(const FfnGemmArgs& a);
+hipError_t launch_gateup_bwd_wide(const FfnGemmArgs* a, const GateBwdOut* gb, int np, hipStream_t s);
 hipError_t launch_ffn_gemm_wide_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int NF,
                                      void* ev_start, void* ev_stop, hipStream_t s);
 
