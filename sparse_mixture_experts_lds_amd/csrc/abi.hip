@@ -1021,12 +1021,46 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     return (bf && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
   };
 
+  // The shared expert's set-up, here because its fused gate/up launch (below)
+  // can ride in the routed one.
+  const int swt = wtype_of(L->act_dtype);
+  const int BMsr = (hs > 0 && shared_plan(T, d, hs, swt).BM == 256 && wide_rc_nf(bf, d, hs)) ? 256 : (bf ? BMb : 32);
+  const FfnPlan wide_plan{256, 4, 4, false, 0};
+  const FfnGemmArgs sgu_bwd = gate_up_args(1, T, d, hs, L->act, x, T, nullptr, 1, nullptr, nullptr, nullptr,
+                                           wide_plan, L->ws_gate, L->ws_up, nullptr, nullptr, b.ZWs);
+  const bool fused_sgb = hs > 0 && BMsr == 256 && gateup_bwd_wide_ok(sgu_bwd);
+  const int BMs = (bf && T >= 4096) ? 128 : 64;
+  const int gms = (T + BMs - 1) / BMs;
+  // the shared expert's rows are one dense group: wide tiles from as many
+  // tokens as the forward gives it wide tiles
+  auto run_nn_shared = [&](const bwdg::NnArgs& a) -> hipError_t {
+    return (bf && T >= kSharedWideMinRows && bwd_nn_wide_ok(a)) ? launch_bwd_nn_wide(a, s)
+                                                                : launch_bwd_nn(bf, a, BMs, gms, s);
+  };
+  // dz's = dout Wsd
+  auto shared_dz = [&]() -> hipError_t {
+    bwdg::NnArgs m{};
+    m.A = dout;
+    m.lda = d;
+    m.a_div = 1;
+    m.B1 = L->ws_down;
+    m.K1 = d;
+    m.ldb = hs;
+    m.K_valid = d;
+    m.C = b.dZs;
+    m.ldc = hs;
+    m.rows = T;
+    m.N = hs;
+    m.K = d;
+    return run_nn_shared(m);
+  };
+  const GateBwdOut sgbo{b.dZs, nullptr, static_cast<uint16_t*>(b.dGUs), static_cast<uint16_t*>(b.ZWs), b.Gs};
+
   // 2. routed experts: g, u again; dz' = dout Wd; gate backward; weight and data gradients.
   // Where the forward's gate/up takes the wide tiles, the recompute is that
   // launch again with the gate backward in its epilogue (after dz'): g and u
   // never leave registers, and the gate gradients come out as partial sums
   // per 64 hidden units (in G's memory), added up in a fixed order.
-  const FfnPlan wide_plan{256, 4, 4, false, 0};
   const FfnGemmArgs gu_bwd = gate_up_args(E_loc, rows, d, h, L->act, x, T, b.sorted_pair, k, b.offsets, b.mtile_rc,
                                           b.tiles_rc, wide_plan, L->w_gate, L->w_up, nullptr, nullptr, b.ZW);
   const bool fused_gb = wide_rc && gateup_bwd_wide_ok(gu_bwd);
@@ -1057,7 +1091,16 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     // the rows' gates in U's memory, the gate-gradient partials in G's
     MOE_HIP(launch_row_gates(rows, b.offsets + E_loc, b.sorted_pair, b.tw, b.U, s));
     const GateBwdOut gbo{b.dZ, b.U, static_cast<uint16_t*>(b.dGU), static_cast<uint16_t*>(b.ZW), b.G};
-    MOE_HIP(launch_gateup_bwd_wide(&gu_bwd, &gbo, 1, s));
+    if (fused_sgb) {
+      // the shared expert's gate/up rides in the same launch as in the forward
+      // (its dz' first); its gate-gradient partials go to Gs and stay there
+      MOE_HIP(shared_dz());
+      const FfnGemmArgs two[2] = {gu_bwd, sgu_bwd};
+      const GateBwdOut outs[2] = {gbo, sgbo};
+      MOE_HIP(launch_gateup_bwd_wide(two, outs, 2, s));
+    } else {
+      MOE_HIP(launch_gateup_bwd_wide(&gu_bwd, &gbo, 1, s));
+    }
     MOE_HIP(launch_gate_part_sum(rows, h, b.offsets + E_loc, b.G, b.sorted_pair, b.dgate, s));
   } else {
     MOE_HIP(launch_gate_bwd(bf, L->act, rows, h, b.offsets + E_loc, b.G, b.U, b.dZ, b.sorted_pair, b.tw, b.dGU,
@@ -1124,45 +1167,17 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
 
   // 3. shared expert on every token (gate 1)
   if (hs > 0) {
-    const int swt = wtype_of(L->act_dtype);
-    // the forward's shared plan: wide tiles take it to the wide kernel here too
-    const int BMsr = (shared_plan(T, d, hs, swt).BM == 256 && wide_rc_nf(bf, d, hs)) ? 256 : (bf ? BMb : 32);
-    // as for the routed experts: the wide gate/up launch with the gate backward in its epilogue
-    const FfnGemmArgs sgu_bwd = gate_up_args(1, T, d, hs, L->act, x, T, nullptr, 1, nullptr, nullptr, nullptr,
-                                             wide_plan, L->ws_gate, L->ws_up, nullptr, nullptr, b.ZWs);
-    const bool fused_sgb = BMsr == 256 && gateup_bwd_wide_ok(sgu_bwd);
-    if (!fused_sgb && (rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs, BMsr,
-                                         L->ws_gate, L->ws_up, b.Gs, b.Us, s)))
-      return rc;
-    const int BMs = (bf && T >= 4096) ? 128 : 64;
-    const int gm = (T + BMs - 1) / BMs;
-    // the shared expert's rows are one dense group: wide tiles from as many
-    // tokens as the forward gives it wide tiles
-    auto run_nn_shared = [&](const bwdg::NnArgs& a) -> hipError_t {
-      return (bf && T >= kSharedWideMinRows && bwd_nn_wide_ok(a)) ? launch_bwd_nn_wide(a, s)
-                                                                  : launch_bwd_nn(bf, a, BMs, gm, s);
-    };
-    n = bwdg::NnArgs{};
-    n.A = dout;
-    n.lda = d;
-    n.a_div = 1;
-    n.B1 = L->ws_down;
-    n.K1 = d;
-    n.ldb = hs;
-    n.K_valid = d;
-    n.C = b.dZs;
-    n.ldc = hs;
-    n.rows = T;
-    n.N = hs;
-    n.K = d;
-    MOE_HIP(run_nn_shared(n));
-    if (fused_sgb) {
-      // the shared expert's gate gradient is not needed: its partials go to Gs and stay there
-      const GateBwdOut gbo{b.dZs, nullptr, static_cast<uint16_t*>(b.dGUs), static_cast<uint16_t*>(b.ZWs), b.Gs};
-      MOE_HIP(launch_gateup_bwd_wide(&sgu_bwd, &gbo, 1, s));
-    } else {
-      MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs,
-                              nullptr, s));
+    // (done in the routed launch when both gate/up launches took the gate backward)
+    if (!(fused_gb && fused_sgb)) {
+      if (!fused_sgb && (rc = recompute_gu(swt, false, x, T, 1, nullptr, nullptr, nullptr, nullptr, 1, T, d, hs,
+                                           BMsr, L->ws_gate, L->ws_up, b.Gs, b.Us, s)))
+        return rc;
+      MOE_HIP(shared_dz());
+      if (fused_sgb)
+        MOE_HIP(launch_gateup_bwd_wide(&sgu_bwd, &sgbo, 1, s));
+      else
+        MOE_HIP(launch_gate_bwd(bf, L->act, T, hs, nullptr, b.Gs, b.Us, b.dZs, nullptr, nullptr, b.dGUs, b.ZWs,
+                                nullptr, s));
     }
     if (gr->dws_down && (rc = tn_single(bf, dout, d, b.ZWs, hs, T, d, hs, d, gr->dws_down, gr->dws_down, hs, b.part,
                                         s)))
