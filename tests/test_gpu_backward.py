@@ -44,6 +44,10 @@ BWD = {
     # none (their weight gradients are zero)
     "wide_skewed": scaled("granular_bf16", T=4096, d=256, E=64, h=512, h_shared=0, capacity_factor=None,
                           zipf_bias=1.5),
+    # GeGLU on the wide tiles: the routed and shared gate/up recomputes with
+    # the gate backward in their epilogue, in one launch (Zipf-skewed experts
+    # of one to several 256-row tiles)
+    "wide_geglu_recompute": scaled("wide_geglu_bf16", T=4096, d=256, E=8, h=1024, h_shared=512),
 }
 
 
@@ -108,10 +112,21 @@ def check_backward(inp, balance=0.0, report=None):
     return g
 
 
+# the cases meant for the wide tiles (and their shared expert in the routed launches)
+WIDE_BWD = {"wide_recompute", "wide_skewed", "wide_geglu_recompute"}
+
+
 @pytest.mark.parametrize("name", list(BWD))
 def test_backward_scaled(name):
     rep = {}
-    check_backward(make_inputs(BWD[name]), report=rep)
+    inp = make_inputs(BWD[name])
+    if name in WIDE_BWD:
+        moe = _moe()
+        plan = moe.layer_plan(device_weights(inp), inp.cfg.T, inp.cfg.d, 1)
+        assert plan["tile_m"] == 256, plan
+        if inp.cfg.h_shared:
+            assert plan["shared_in_routed_launches"] == 1, plan
+    check_backward(inp, report=rep)
     print(name, {k: "%.2e" % v for k, v in rep.items()})
 
 
