@@ -102,12 +102,13 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
     P = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
     zb = 4 if (split_z or cfg.dtype == "f32") else 2
+    yb = 4 if cfg.dtype == "f32" else 2  # expert outputs: fp16 in bf16 layers
     gu = {"flops": 4.0 * d * h * P, "bytes": touched * wb_gu + kept_tokens * d * ab,
           "overhead_bytes": P * h * zb}
-    dn = {"flops": 2.0 * d * h * P, "bytes": touched * wb_dn, "overhead_bytes": P * h * zb + P * d * 4}
-    # the shared expert's GEMMs over all T tokens
-    sgu = {"flops": 4.0 * d * hs * T, "bytes": 2 * hs * d * ab, "overhead_bytes": T * hs * zb}
-    sdn = {"flops": 2.0 * d * hs * T, "bytes": d * hs * ab, "overhead_bytes": T * hs * zb + T * d * 4}
+    dn = {"flops": 2.0 * d * h * P, "bytes": touched * wb_dn, "overhead_bytes": P * h * zb + P * d * yb}
+    # the shared expert's GEMMs over all T tokens (its z in the activation dtype)
+    sgu = {"flops": 4.0 * d * hs * T, "bytes": 2 * hs * d * ab, "overhead_bytes": T * hs * ab}
+    sdn = {"flops": 2.0 * d * hs * T, "bytes": d * hs * ab, "overhead_bytes": T * hs * ab + T * d * yb}
     router_f = 2.0 * T * d * cfg.E if cfg.has_router else 0.0
     router_b = cfg.E * d * ab if cfg.has_router else T * cfg.E * 4
     layer_f = router_f + 6.0 * d * h * P + (6.0 * d * hs * T if hs else 0.0)
