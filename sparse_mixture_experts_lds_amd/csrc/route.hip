@@ -145,7 +145,14 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
         }
       }
     } else {
+      // fp32: products and sums in fp64 (each fp32 product is exact there),
+      // so the logits carry only their final rounding to fp32; fp32 sums over
+      // d inputs moved the gates, and through them the layer's fp32 output,
+      // by up to 1e-5 of its RMS on layers whose capacity drops most rows
       constexpr int KC = 16;
+      f64x4 accd[NF];
+#pragma unroll
+      for (int i = 0; i < NF; ++i) accd[i] = f64x4{0.0, 0.0, 0.0, 0.0};
       const float* x = static_cast<const float*>(xv);
       const float* w = static_cast<const float*>(wv);
       const float* xrow = x + (size_t)(tok_ok ? t : 0) * d + q;
@@ -173,19 +180,25 @@ __global__ __launch_bounds__(256) void route_kernel(int T, int d, int E, int k, 
             const float a = tok_ok ? av[c] : 0.f;
 #pragma unroll
             for (int i = 0; i < NF; ++i)
-              acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, e_ok[i] ? bv[c][i] : 0.f, acc[i], 0, 0, 0);
+              accd[i] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a, (double)(e_ok[i] ? bv[c][i] : 0.f),
+                                                              accd[i], 0, 0, 0);
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] = (float)accd[i][r];
     }
-    // D[i][j]: lane holds column j = lane & 15 and rows 4q + r.
+    // D[i][j]: lane holds column j = lane & 15 and rows 4q + r (bf16 and fp32
+    // MFMAs) or q + 4r (the fp64 MFMA, checked with an in-bounds probe on the GPU)
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const int e = 16 * (wave + 4 * i) + row;
       if (e < E) {
         const float bv = (SELECT && bias) ? bias[e] : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ls[(4 * q + r) * ES + e] = acc[i][r] + bv;
+        for (int r = 0; r < 4; ++r) Ls[(BF16 ? 4 * q + r : q + 4 * r) * ES + e] = acc[i][r] + bv;
       }
     }
   }
