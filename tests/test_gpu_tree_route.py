@@ -165,3 +165,31 @@ def test_route_tree_full_size(name):
     rep = {}
     _check(as_f64(x), as_f64(w), cfg.branch, cfg.levels, cfg.E, cfg.k, cfg.renorm, ids, tw, report=rep)
     print(name, rep)
+
+
+def _random_tree(seed):
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(2, 65))
+    Lmax = 1
+    while Lmax < 4 and B ** (Lmax + 1) <= 32768:
+        Lmax += 1
+    L = int(rng.integers(1, Lmax + 1))
+    E = int(rng.integers(2, min(B ** L, 4096) + 1))
+    k = int(rng.integers(1, min(E, 32, 1024 // B) + 1))
+    T = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(64, 700))]))
+    d = int(64 * rng.integers(1, 9))
+    dt = str(rng.choice(["bf16", "f32"]))
+    return _cfg("random_tree_%d" % seed, T, d, E, k, B, L, dt, renorm=bool(rng.random() < 0.5), seed=seed)
+
+
+# seeded random trees: branching 2..64, one to four levels, trimmed last
+# nodes, beams from 1 to the widest candidate set, both dtypes
+@pytest.mark.parametrize("seed", range(32))
+def test_route_tree_random(seed):
+    moe = _moe()
+    cfg = _random_tree(seed)
+    print(cfg, flush=True)
+    x, w, _, _, ids, tw = _run(cfg, moe)
+    rep = {}
+    _check(as_f64(x), as_f64(w), cfg.branch, cfg.levels, cfg.E, cfg.k, cfg.renorm, ids, tw, report=rep)
+    print(seed, rep)
