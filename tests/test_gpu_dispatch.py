@@ -164,3 +164,35 @@ def test_owner_shares_sum_to_full_layer_full_scale():
     assert np.all(ds <= halfulp + _half_ulp_bf16(full) + 1e-3 * rms)
     # every pair of the batch was dispatched once
     assert int(oo[-1]) == T * k
+
+
+# seeded random groupings: token counts from 1 up, 1..32 slots, 2..1024
+# experts on 1..64 owners (both rules), with and without capacity, ids with
+# repeats within a token, some ids foreign (outside [0, E))
+@pytest.mark.parametrize("seed", range(24))
+def test_dispatch_owners_random(seed):
+    moe = _moe()
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(2, 1025))
+    n = int(rng.choice([d for d in range(1, min(E, 64) + 1) if E % d == 0]))
+    k = int(rng.integers(1, 33))
+    T = int(rng.choice([1, int(rng.integers(2, 100)), int(rng.integers(100, 5000))]))
+    rule = str(rng.choice(["round_robin", "contiguous"]))
+    cap = int(rng.integers(1, 64)) if rng.random() < 0.3 else 0
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if rng.random() < 0.3:
+        ids[rng.random((T, k)) < 0.05] = int(rng.choice([-1, E]))
+    d = 64 * int(rng.integers(1, 5))
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    print(dict(T=T, k=k, E=E, n=n, rule=rule, cap=cap, d=d), flush=True)
+    r = moe.dispatch_owners(torch.from_numpy(ids).to(DEV), E, n, rule, cap, x=x.to(DEV))
+    torch.cuda.synchronize()
+    o = orc.owner_dispatch(ids, E, n, rule, capacity=cap)
+    rows = int(o["expert_offsets"][-1])
+    np.testing.assert_array_equal(r["owner_offsets"].cpu().numpy(), o["owner_offsets"])
+    np.testing.assert_array_equal(r["recv_offsets"].cpu().numpy(), o["recv_offsets"])
+    np.testing.assert_array_equal(r["expert_offsets"].cpu().numpy(), o["expert_offsets"])
+    np.testing.assert_array_equal(r["sorted_pair"].cpu().numpy()[:rows], o["sorted_pair"])
+    np.testing.assert_array_equal(r["pair_pos"].cpu().numpy()[:T * k], o["pair_pos"])
+    xs = r["x_send"][:rows].cpu().view(torch.int16).numpy()
+    np.testing.assert_array_equal(xs, x.view(torch.int16).numpy()[o["sorted_pair"] // k])

@@ -195,6 +195,35 @@ def test_route_entry_point(E, k, dt, T):
         assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
 
 
+# Seeded random routing problems across the router's paths (LDS-resident
+# weights, the grouped logits GEMM, input slices, the one-launch router and
+# the 16-token tiles), with and without bias and renormalisation: logits
+# within the dtype's accuracy, picks bit-exact on the GPU's own logits
+@pytest.mark.parametrize("seed", range(24))
+def test_route_random(seed):
+    moe = _moe()
+    rng = np.random.default_rng(3000 + seed)
+    dt = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    E = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 1025))]))
+    k = int(rng.integers(1, min(E, 32) + 1))
+    d = 64 * int(rng.integers(1, 17))
+    T = int(rng.choice([1, int(rng.integers(2, 200)), int(rng.integers(200, 9000))]))
+    T = max(1, min(T, int(3e8 // (d * E))))
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dt)
+    w = torch.from_numpy((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)).to(dt)
+    b = torch.from_numpy(rng.standard_normal(E).astype(np.float32)) if rng.random() < 0.5 else None
+    renorm = bool(rng.random() < 0.5)
+    print(dict(T=T, d=d, E=E, k=k, dt=str(dt), bias=b is not None, renorm=renorm), flush=True)
+    ids, tw, L = moe.route(x.to(DEV), w.to(DEV), k, renorm, bias=None if b is None else b.to(DEV),
+                           want_logits=True)
+    Lg = L.cpu().numpy().astype(np.float64)
+    Lo = orc.router_logits(as_f64(x), as_f64(w), None if b is None else as_f64(b))
+    assert relerr(Lg, Lo) <= (1e-5 if dt == torch.float32 else 1e-4)
+    ids_o = orc.select_topk(Lg, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    assert np.abs(tw.cpu().numpy() - orc.gates(Lg, ids_o, renorm)).max() <= 1e-6
+
+
 # Without a logits buffer the router keeps each 16-token tile's logits on chip
 # (with one, many experts take the two-pass logits GEMM and selection): the
 # picks must be a valid top-k of the exact logits up to fp32 reassociation,

@@ -1,8 +1,8 @@
 """GPU parity of the whole layer on seeded random shapes, against the float64
 oracle (the same protocol as test_gpu_parity.check_layer: selection and
 grouping bit-exact on the GPU's own logits and ids, outputs within the dtype
-tolerance of the oracle), and of its backward on random bf16 and fp32 shapes
-(the protocol of test_gpu_backward.check_backward).
+tolerance of the oracle), and of its backward on random bf16 shapes (the
+protocol of test_gpu_backward.check_backward).
 
 Each case draws, from its seed: a base workload (its dtype, weights and
 activation), token count, widths, expert count, top-k, shared expert,
