@@ -84,7 +84,7 @@ def median(v):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
-def algorithmic_work(cfg, counts, kept_tokens, split_z):
+def algorithmic_work(cfg, counts, kept_tokens):
     """FLOPs and bytes that the layer and each GEMM launch must move, from the
     actual routing.  Algorithmic bytes: the weight matrices of every touched
     expert read once, the activation rows read once, the layer output written
@@ -101,7 +101,7 @@ def algorithmic_work(cfg, counts, kept_tokens, split_z):
         wb_dn = d * h * wb
     P = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
-    zb = 4 if (split_z or cfg.dtype == "f32") else 2
+    zb = 4 if cfg.dtype == "f32" else 2  # z: fp16 in INT4 layers, else the activation dtype
     yb = 4 if cfg.dtype == "f32" else 2  # expert outputs: fp16 in bf16 layers
     gu = {"flops": 4.0 * d * h * P, "bytes": touched * wb_gu + kept_tokens * d * ab,
           "overhead_bytes": P * h * zb}
@@ -442,7 +442,7 @@ def measure_workload(moe, torch, np, name, steps, warmup, args, flush, extras=Tr
     torch.cuda.synchronize()
     counts = np.diff(tr["expert_offsets"].cpu().numpy())
     kept_tokens = int(((tr["pair_pos"].cpu().numpy().reshape(cfg.T, cfg.k) >= 0).any(1)).sum())
-    work = algorithmic_work(cfg, counts, kept_tokens, cfg.w_dtype == "i4g128")
+    work = algorithmic_work(cfg, counts, kept_tokens)
 
     n_ev = len(EVENT_NAMES)
     stream = torch.cuda.current_stream()

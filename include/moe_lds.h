@@ -288,7 +288,8 @@ int moe_dispatch_owners(int T, int k, int E, int n_owners, int placement, int ca
  * expert e and each row r in [expert_offsets[e], expert_offsets[e+1]):
  *
  *   g = W_gate[e] a,  u = W_up[e] a,  z = act(g) * u,  y_perm[r] = W_down[e] z
- *   with a = x_perm[r].  Accumulation in fp32; z is rounded to act_dtype.
+ *   with a = x_perm[r].  Accumulation in fp32; z is rounded to act_dtype, or
+ *   to fp16 with INT4 weights (beyond fp16's range, 65504, it becomes infinite).
  *
  *   E_loc, d, h     local experts, model width, expert hidden width
  *   rows_max        rows of x_perm / y_perm (>= expert_offsets[E_loc]); the
@@ -422,11 +423,11 @@ int moe_layer_plan(const struct moe_layer_desc* L, struct moe_layer_plan_info* o
  *   trace      NULL or a struct of optional outputs
  *   ws         at least moe_layer_workspace_bytes(desc)
  * Precision: logits, gates and every sum are fp32.  The gated activations z
- * are rounded to bf16 (bf16 weights) or kept in fp32 (INT4 weights); the
- * expert and shared-expert outputs are kept in fp16 in bf16 layers (in fp32
- * in fp32 layers) until the combine, which sums in fp32 and rounds once to
- * act_dtype.  An expert output beyond fp16's range (65504 in magnitude)
- * becomes infinite.
+ * are rounded to bf16 (bf16 weights) or to fp16 (INT4 weights); the expert
+ * and shared-expert outputs are kept in fp16 in bf16 layers (in fp32 in fp32
+ * layers) until the combine, which sums in fp32 and rounds once to
+ * act_dtype.  An INT4 layer's z or an expert output beyond fp16's range
+ * (65504 in magnitude) becomes infinite.
  */
 size_t moe_layer_workspace_bytes(const struct moe_layer_desc* L);
 int moe_layer_fwd(const struct moe_layer_desc* L, const void* x, const float* logits_in,

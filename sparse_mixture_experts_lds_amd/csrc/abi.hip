@@ -114,7 +114,7 @@ FfnGemmArgs gate_up_args(int E_loc, int rows_max, int d, int h, int act, const v
   g.K = d;
   g.N = h;
   g.act = act == MOE_GEGLU ? 1 : 0;
-  g.out_f32 = plan.split_z ? 1 : 0;
+  g.out_f16 = plan.z_f16 ? 1 : 0;
   return g;
 }
 
@@ -168,7 +168,7 @@ int run_ffn(int E_loc, int rows_max, int d, int h, int act, int w_dtype, const v
       dn.tile_tab = tiles_dn;
     }
   }
-  MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.split_z, BMd, plan.NF_down, s));
+  MOE_HIP(launch_ffn_gemm(dn, false, wt, plan.z_f16, BMd, plan.NF_down, s));
   return MOE_OK;
 }
 
@@ -196,11 +196,11 @@ FfnPlan shared_plan(int T, int d, int hs, int wt) {
 enum class SharedMode { kNone, kWidePair, kNarrowPair, kSerial };
 SharedMode shared_mode(const moe_layer_desc* L, const FfnPlan& plan, const FfnPlan& sp) {
   if (L->h_shared <= 0) return SharedMode::kNone;
-  if (L->w_dtype == MOE_BF16 && L->act_dtype == MOE_BF16 && plan.BM == 256 && sp.BM == 256 && !plan.split_z &&
+  if (L->w_dtype == MOE_BF16 && L->act_dtype == MOE_BF16 && plan.BM == 256 && sp.BM == 256 && !plan.z_f16 &&
       plan.NF_up == sp.NF_up && plan.NF_down == sp.NF_down)
     return SharedMode::kWidePair;
   if (plan.BM != 256 && L->w_dtype == L->act_dtype && L->w_dtype != MOE_I4G128 && L->h_shared == L->h &&
-      !plan.split_z && (!plan.BM_down || plan.BM_down == plan.BM))
+      !plan.z_f16 && (!plan.BM_down || plan.BM_down == plan.BM))
     return SharedMode::kNarrowPair;
   return SharedMode::kSerial;
 }
@@ -276,7 +276,7 @@ FfnPlan layer_plan(const moe_layer_desc* L, int rows) {
   if (L->tile_m) p.BM = L->tile_m;
   if (L->tile_n_up) p.NF_up = L->tile_n_up / 64;
   if (L->tile_n_down) p.NF_down = L->tile_n_down / 64;
-  p.split_z = wt == W_I4;
+  p.z_f16 = wt == W_I4;
   return p;
 }
 
@@ -309,7 +309,7 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
   b->sorted_pair = c.take<int32_t>(P * 4);
   b->pair_pos = c.take<int32_t>(P * 4);
   b->counts = c.take<int32_t>(permute_ws_bytes((int)P, L->E_loc));
-  b->z = c.take<void>(rows * L->h * 4);  // fp32 when the down projection splits z
+  b->z = c.take<void>(rows * L->h * 4);  // room for the fp32 z of fp32 layers
   // expert outputs: fp16 in bf16 layers (one rounding to an 11-bit significand
   // before the combine's fp32 sum), fp32 in fp32 layers
   b->y = c.take<void>(rows * L->d * 4);

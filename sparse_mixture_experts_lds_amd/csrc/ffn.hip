@@ -16,8 +16,17 @@ using ffn_detail::launch_mf_nf;
 #endif
 // outputs per tile of the weight-streaming gate/up kernel
 constexpr int kBsBno = MOE_BS_BNO;
+#ifndef MOE_I4_BM_DOWN
+#define MOE_I4_BM_DOWN 32
+#endif
+#ifndef MOE_I4_NF_DOWN
+#define MOE_I4_NF_DOWN 2
+#endif
+// rows and 64-column fragments per tile of the INT4 down projection
+constexpr int kI4BmDown = MOE_I4_BM_DOWN;
+constexpr int kI4NfDown = MOE_I4_NF_DOWN;
 
-hipError_t launch_ffn_gemm_i4(const FfnGemmArgs& a, bool gateup, bool split, int BM, int NF, hipStream_t s);
+hipError_t launch_ffn_gemm_i4(const FfnGemmArgs& a, bool gateup, bool z16, int BM, int NF, hipStream_t s);
 
 int ffn_max_mtiles(int E_loc, int rows_max, int BM) {
   // sum_e ceil(n_e / BM) <= ceil(rows / BM) + (number of non-empty groups - 1)
@@ -43,7 +52,7 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
       // costs do not shrink with the tile)
       p.BM = 256;
       p.NF_up = p.NF_down = 4;
-      p.split_z = false;
+      p.z_f16 = false;
       return p;
     }
   }
@@ -55,15 +64,16 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   if (w_type == W_I4 && BM > 64) BM = 64;
   // INT4 with up to ~32 rows per expert: gate/up on 32-row tiles of 64
   // columns (each weight slice read once per expert, two workgroups per CU),
-  // down on 16-row tiles of 128 columns, whose 32-row version holds one
-  // workgroup per CU.  Measured on MI355X (28-of-896-expert share, ~26 rows
-  // per expert): 0.40 against 0.50 ms per layer.
+  // down on the same 32-row tiles, 128 columns wide (with its fp16 z the
+  // kernel keeps two workgroups per CU).  Measured on MI355X (INT4 share, 25
+  // touched experts of 1 to 472 rows): down 0.114-0.119 ms against
+  // 0.124-0.127 on 16-row tiles and 0.138-0.141 on 16 x 64 tiles.
   if (w_type == W_I4 && avg_rows <= 32) {
     p.BM = 32;
     p.NF_up = 1;
-    p.BM_down = 16;
-    p.NF_down = d % 128 == 0 ? 2 : 1;
-    p.split_z = true;
+    p.BM_down = kI4BmDown == p.BM ? 0 : kI4BmDown;
+    p.NF_down = d % (64 * kI4NfDown) == 0 ? kI4NfDown : 1;
+    p.z_f16 = true;
     return p;
   }
   if (w_type == W_F32 && BM > 32) BM = 32;
@@ -71,20 +81,21 @@ FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type) {
   p.NF_up = (BM <= 64 && h % 128 == 0) ? 2 : 1;
   p.NF_down = (d % 128 == 0) ? 2 : 1;
   if (w_type == W_F32) p.NF_up = p.NF_down = 1;
-  // INT4 shares carry the gated activations in fp32 into the down projection
-  // (hi/lo bf16 split): their weight stream leaves the matrix cores idle
-  // enough to afford the second MFMA.
-  p.split_z = w_type == W_I4;
+  // INT4 shares carry the gated activations into the down projection in fp16
+  // (three more significand bits than bf16, half the bytes of fp32)
+  p.z_f16 = w_type == W_I4;
   return p;
 }
 
-hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM, int NF,
+hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool z16, int BM, int NF,
                            hipStream_t s) {
+  // z16: fp16 activations (the z of INT4 layers), INT4 down projections only
+  if (z16 && (gateup || w_type != W_I4)) return hipErrorInvalidValue;
   // activation rows are addressed with 32-bit byte offsets
-  const size_t gelt = (w_type == W_F32 || split) ? 4 : 2;
+  const size_t gelt = w_type == W_F32 ? 4 : 2;
   if (a.a_rows < 0 || (size_t)a.a_rows * (size_t)a.K * gelt > 0xFFFFFFFFull) return hipErrorInvalidValue;
   if (BM == ffn_wide::BM) {
-    if (w_type != W_BF16 || split) return hipErrorInvalidValue;
+    if (w_type != W_BF16) return hipErrorInvalidValue;
     // NF: weight rows per tile / 64 (4 -> 256, 2 -> 128); 256 weight rows and
     // K a multiple of 128 take the 64-deep k-blocks
     if (NF == 4 && a.K % 128 == 0)
@@ -95,12 +106,12 @@ hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool s
   }
   if (w_type == W_F32)
     return gateup ? launch_mf_nf<W_F32, true, false>(&a, 1, BM, NF, s) : launch_mf_nf<W_F32, false, false>(&a, 1, BM, NF, s);
-  if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, split, BM, NF, s);
+  if (w_type == W_I4) return launch_ffn_gemm_i4(a, gateup, z16, BM, NF, s);
   // few rows per expert: the weight-streaming kernel (its tiles are always 128
   // outputs wide)
   if (gateup && (BM == 32 || BM == 64) && ffn_bs::ok(&a, 1)) return ffn_bs::launch(&a, 1, BM / 16, kBsBno, s);
   if (gateup) return launch_mf_nf<W_BF16, true, false>(&a, 1, BM, NF, s);
-  return split ? launch_mf_nf<W_BF16, false, true>(&a, 1, BM, NF, s) : launch_mf_nf<W_BF16, false, false>(&a, 1, BM, NF, s);
+  return launch_mf_nf<W_BF16, false, false>(&a, 1, BM, NF, s);
 }
 
 hipError_t launch_ffn_gemm_pair(const FfnGemmArgs& a0, const FfnGemmArgs& a1, bool gateup, int w_type, int BM,

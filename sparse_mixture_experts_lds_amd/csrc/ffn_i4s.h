@@ -318,7 +318,7 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
     // k-block (free until the next k-block's barrier; the first barrier below
     // waits until every wave has finished reading it).  Lane (lrow, q) then
     // holds g (f = 0) and u (f = 1) of output n0 + 16 og + lrow for tile rows
-    // 16 mi + 4 q + r; z goes out in fp32.
+    // 16 mi + 4 q + r; z goes out in fp16 (out_f16) or fp32.
     {
       const int st_free = st >= 1 ? st - 1 : NS - 1;
       float* const xch = reinterpret_cast<float*>(&stg[0][0] + st_free * STAGE) + (og * 64 + lane) * 16;
@@ -339,7 +339,6 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[mi][f][r] += o[r];
           }
-        float* const out = static_cast<float*>(a.out);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -348,7 +347,9 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
             if (row < nrows) {
               const float gv = acc[mi][0][r];
               const float z = (ACT == 0 ? silu_hw(gv) : gelu_hw(gv)) * acc[mi][1][r];
-              out[(size_t)(tc.row0 + row) * N + tc.n0 + 16 * og + lrow] = z;
+              const size_t o = (size_t)(tc.row0 + row) * N + tc.n0 + 16 * og + lrow;
+              if (a.out_f16) static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_f16_bits(z);
+              else static_cast<float*>(a.out)[o] = z;
             }
           }
       }
@@ -366,7 +367,8 @@ __global__ __launch_bounds__(1024) void i4s_gateup_kernel(FfnGemmArgs a) {
 // Whether the streaming kernel takes this INT4 gate/up GEMM.  The loads run
 // two k-blocks ahead within a tile, so a tile has at least two.
 inline bool ok(const FfnGemmArgs& a) {
-  return a.K % KB == 0 && a.K >= 2 * KB && a.N % BNO == 0 && a.out_f32 && (size_t)a.a_rows * a.K * 2 <= 0xFFFFFFFFull &&
+  return a.K % KB == 0 && a.K >= 2 * KB && a.N % BNO == 0 && (a.out_f32 || a.out_f16) &&
+         (size_t)a.a_rows * a.K * 2 <= 0xFFFFFFFFull &&
          (size_t)a.N * (a.K / 2) <= 0x7FFFFFFFull;
 }
 

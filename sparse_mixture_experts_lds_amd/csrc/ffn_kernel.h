@@ -60,6 +60,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 #define MOE_FFN_STAGES 4
 #endif
 constexpr int kStages = MOE_FFN_STAGES;
+#ifndef MOE_I4_DOWN_STAGES
+#define MOE_I4_DOWN_STAGES 4
+#endif
+constexpr int kI4DownStages = MOE_I4_DOWN_STAGES;
 constexpr int kGroupM = 8;
 
 template <int WT>
@@ -109,7 +113,19 @@ __device__ __forceinline__ u32x4 i4_word_to_bf16x8(uint32_t w) {
   return o;
 }
 
-// Reorder 8 bf16 (a0..a7) to a0,a4,a1,a5,a2,a6,a3,a7.
+// The same four pairs as fp16, 1032 + code: 0x6400 is 1024, where the unit in
+// the last place of fp16 is 1.
+__device__ __forceinline__ u32x4 i4_word_to_f16x8(uint32_t w) {
+  const uint32_t v = w ^ 0x88888888u;
+  u32x4 o;
+  o[0] = (v & 0x000F000Fu) | 0x64006400u;
+  o[1] = ((v >> 4) & 0x000F000Fu) | 0x64006400u;
+  o[2] = ((v >> 8) & 0x000F000Fu) | 0x64006400u;
+  o[3] = ((v >> 12) & 0x000F000Fu) | 0x64006400u;
+  return o;
+}
+
+// Reorder 8 16-bit values (a0..a7) to a0,a4,a1,a5,a2,a6,a3,a7.
 __device__ __forceinline__ u32x4 perm_04152637(u32x4 d) {
   u32x4 o;
   o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
@@ -126,6 +142,13 @@ __device__ __forceinline__ float sum_bf16x8(u32x4 d) {
   return s;
 }
 
+__device__ __forceinline__ float sum_f16x8(u32x4 d) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += half_bits_to_f32(d[i] & 0xFFFFu) + half_bits_to_f32(d[i] >> 16);
+  return s;
+}
+
 // Tiles one workgroup can hold decoded in LDS (row sources of NT_MAX tiles: 8 KB).
 template <int BM>
 struct TileCap {
@@ -138,7 +161,7 @@ struct GemmPair {
   int np;  // 1 or 2
 };
 
-template <int WT, int MF, int NF, bool GATEUP, bool SPLIT>
+template <int WT, int MF, int NF, bool GATEUP, bool A16>
 __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   const FfnGemmArgs& args = gp.p[0];  // K, N, act, out_f32: common to both problems
   using Tr = Traits<WT>;
@@ -148,12 +171,11 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   constexpr int KB = Tr::KB;
   constexpr bool F32 = WT == W_F32;
   constexpr bool I4 = WT == W_I4;
-  static_assert(!(SPLIT && F32), "fp32 operands need no split");
-  // SPLIT: the activations arrive in fp32 and are staged as two bf16 planes,
-  // hi = bf16(v) and lo = bf16(v - hi), each multiplied by the weights.
+  static_assert(!A16 || (I4 && !GATEUP), "fp16 activations: INT4 down projections only");
+  // A16: the activations (the z of an INT4 layer) are fp16; the codes are
+  // then decoded to fp16 and multiplied on the fp16 MFMA (else bf16).
   constexpr int LELT = F32 ? 4 : 2;                    // LDS element bytes
-  constexpr int GELT = (F32 || SPLIT) ? 4 : 2;         // global activation element bytes
-  constexpr int NPL = SPLIT ? 2 : 1;                   // LDS planes
+  constexpr int GELT = F32 ? 4 : 2;                    // global activation element bytes
   constexpr int AS = KB + 16 / LELT;                   // LDS row stride in elements (+16 B)
   constexpr int CHE = 16 / LELT;                       // elements per staged chunk (16 B of LDS)
   constexpr int CPR = KB / CHE;                        // chunks per staged row
@@ -162,12 +184,12 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   constexpr int STEPS = Tr::QS / Tr::EPS;
   // register stages (prefetch distance NS-1); the largest tiles keep one stage
   // less so that two workgroups still fit on a CU
-  constexpr int NS = MF * NB_FR >= 16 ? 3 : kStages;
+  constexpr int NS = A16 ? kI4DownStages : (MF * NB_FR >= 16 ? 3 : kStages);
   constexpr int NT_MAX = TileCap<BM>::NT_MAX;
 
   // LDS: the activation double buffer, reused after each tile's k-loop as the
   // output staging tile; the decoded tiles of this workgroup.
-  constexpr int ABUF = NPL * BM * AS * LELT;
+  constexpr int ABUF = BM * AS * LELT;
   constexpr int RING = 2 * ABUF;
   constexpr int OS_MAX = BN * 4 + 16;  // output row stride in bytes for fp32 outputs (+16 B pad)
   constexpr int LDS_BYTES = RING > BM * OS_MAX ? RING : BM * OS_MAX;
@@ -344,44 +366,30 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
       }
     }
   };
-  auto lds_a_at = [&](int lb, int pl) -> unsigned char* { return lds_raw + lb * ABUF + pl * (BM * AS * LELT); };
+  auto lds_a_at = [&](int lb) -> unsigned char* { return lds_raw + lb * ABUF; };
   auto store_a = [&](int st, int lb) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       if (a_dst[j] < 0) continue;
-      u32x4 hi = a_reg[st][j][0], lo = u32x4{0, 0, 0, 0};
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v0 = __uint_as_float(a_reg[st][j][i >> 1][2 * (i & 1)]);
-          const float v1 = __uint_as_float(a_reg[st][j][i >> 1][2 * (i & 1) + 1]);
-          const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
-          hi[i] = h0 | (h1 << 16);
-          lo[i] = pack_bf16x2(v0 - bf16_bits_to_f32(h0), v1 - bf16_bits_to_f32(h1));
-        }
-      }
+      u32x4 v = a_reg[st][j][0];
       if constexpr (I4) {
         // per-row sum of the group (16 lanes hold one row's 16 chunks)
-        float sm = sum_bf16x8(hi);
-        if constexpr (SPLIT) sm += sum_bf16x8(lo);
+        float sm = A16 ? sum_f16x8(v) : sum_bf16x8(v);
         sm += wave_shfl_xor(sm, 1);
         sm += wave_shfl_xor(sm, 2);
         sm += wave_shfl_xor(sm, 4);
         sm += wave_shfl_xor(sm, 8);
         if ((lane & 15) == 0) lds_s[lb][(tid + 256 * j) / CPR] = sm;
-        hi = perm_04152637(hi);
-        if constexpr (SPLIT) lo = perm_04152637(lo);
+        v = perm_04152637(v);
       }
-      *reinterpret_cast<u32x4*>(lds_a_at(lb, 0) + a_dst[j]) = hi;
-      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(lds_a_at(lb, NPL - 1) + a_dst[j]) = lo;
+      *reinterpret_cast<u32x4*>(lds_a_at(lb) + a_dst[j]) = v;
     }
   };
 
   f32x4 acc[MF][NB_FR];
 
   auto compute = [&](int st, int lb) {
-    const unsigned char* As = lds_a_at(lb, 0);
-    const unsigned char* Al = lds_a_at(lb, NPL - 1);
+    const unsigned char* As = lds_a_at(lb);
     if constexpr (WT == W_F32) {
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
@@ -400,21 +408,18 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
     } else if constexpr (WT == W_BF16) {
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
-        bf16x8 a[MF], al[MF];
+        bf16x8 a[MF];
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi) {
           const int off = ((16 * mi + lrow) * AS + Tr::QS * q + 8 * s) * 2;
           a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + off));
-          if constexpr (SPLIT) al[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Al + off));
         }
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
           const bf16x8 b = __builtin_bit_cast(bf16x8, bbuf[st][f][s]);
 #pragma unroll
-          for (int mi = 0; mi < MF; ++mi) {
+          for (int mi = 0; mi < MF; ++mi)
             acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, acc[mi][f], 0, 0, 0);
-            if constexpr (SPLIT) acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mi], b, acc[mi][f], 0, 0, 0);
-          }
         }
       }
     } else {  // INT4
@@ -425,23 +430,30 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
         for (int f = 0; f < NB_FR; ++f) gacc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
-        bf16x8 a[MF], al[MF];
+        u32x4 a[MF];
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi) {
           const int off = ((16 * mi + lrow) * AS + Tr::QS * q + 8 * s) * 2;
-          a[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + off));
-          if constexpr (SPLIT) al[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Al + off));
+          a[mi] = *reinterpret_cast<const u32x4*>(As + off);
         }
 #pragma unroll
         for (int f = 0; f < NB_FR; ++f) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, i4_word_to_bf16x8(bbuf[st][f][0][s]));
+          const uint32_t w = bbuf[st][f][0][s];
 #pragma unroll
           for (int mi = 0; mi < MF; ++mi) {
-            gacc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b, gacc[mi][f], 0, 0, 0);
-            if constexpr (SPLIT) gacc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mi], b, gacc[mi][f], 0, 0, 0);
+            if constexpr (A16)
+              gacc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[mi]),
+                                                                   __builtin_bit_cast(f16x8, i4_word_to_f16x8(w)),
+                                                                   gacc[mi][f], 0, 0, 0);
+            else
+              gacc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mi]),
+                                                                    __builtin_bit_cast(bf16x8, i4_word_to_bf16x8(w)),
+                                                                    gacc[mi][f], 0, 0, 0);
           }
         }
       }
+      // gacc = sum a (offset + code), the offset 1032 (fp16) or 136 (bf16)
+      constexpr float kOff = A16 ? -1032.0f : -136.0f;
 #pragma unroll
       for (int mi = 0; mi < MF; ++mi) {
         const f32x4 rs = *reinterpret_cast<const f32x4*>(&lds_s[lb][16 * mi + 4 * q]);
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
         for (int f = 0; f < NB_FR; ++f) {
           const float sc = sbuf[st][f];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mi][f][r] = fmaf(sc, fmaf(-136.0f, rs[r], gacc[mi][f][r]), acc[mi][f][r]);
+          for (int r = 0; r < 4; ++r) acc[mi][f][r] = fmaf(sc, fmaf(kOff, rs[r], gacc[mi][f][r]), acc[mi][f][r]);
         }
       }
     }
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   const int NKB = K / KB;
   const int NIT = (NKB + NS - 1) / NS * NS;  // padded with all-zero activation blocks
   const bool f32out = F32 || args.out_f32;
-  const bool f16out = !f32out && !GATEUP && args.out_f16;
+  const bool f16out = !f32out && args.out_f16;
   const int osz = f32out ? 4 : 2;
   const int OS = BN * osz + 16;
   const int cpr = BN * osz / 16;  // 16-byte chunks per output row
@@ -557,14 +569,14 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmPair gp) {
   }
 }
 
-template <int WT, int MF, int NF, bool GU, bool SPLIT>
+template <int WT, int MF, int NF, bool GU, bool A16>
 int resident_groups(int& cus) {
   static int cached_occ = -1, cached_cus = -1;
   if (cached_occ < 0) {
     int dev = 0, occ = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>, 256, 0) !=
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_gemm_kernel<WT, MF, NF, GU, A16>, 256, 0) !=
             hipSuccess) {
       occ = 1;
       n = 256;
@@ -576,7 +588,7 @@ int resident_groups(int& cus) {
   return cached_occ;
 }
 
-template <int WT, int MF, int NF, bool GU, bool SPLIT>
+template <int WT, int MF, int NF, bool GU, bool A16>
 hipError_t launch_one(const FfnGemmArgs* a, int np, hipStream_t s) {
   const int BM = 16 * MF, BN = 64 * NF;
   GemmPair gp{};
@@ -595,14 +607,14 @@ hipError_t launch_one(const FfnGemmArgs* a, int np, hipStream_t s) {
   // Persistent grid: every resident slot once, but no more than the tiles there
   // can be, and enough workgroups that none holds more than NT_MAX tiles.
   int cus = 256;
-  const int occ = resident_groups<WT, MF, NF, GU, SPLIT>(cus);
+  const int occ = resident_groups<WT, MF, NF, GU, A16>(cus);
   constexpr int NT_MAX = TileCap<16 * MF>::NT_MAX;
   const long long slots = (long long)occ * cus / 8;
   long long S = std::max<long long>(slots, (per_ub + NT_MAX - 1) / NT_MAX);
   S = std::min<long long>(S, per_ub);
   const long long g = 8 * S;
   const dim3 grid((unsigned)g), block(256);
-  auto kernel = ffn_gemm_kernel<WT, MF, NF, GU, SPLIT>;
+  auto kernel = ffn_gemm_kernel<WT, MF, NF, GU, A16>;
   if (a[0].ev_start || a[0].ev_stop)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<hipEvent_t>(a[0].ev_start),
                           static_cast<hipEvent_t>(a[0].ev_stop), 0, gp);
@@ -613,11 +625,11 @@ hipError_t launch_one(const FfnGemmArgs* a, int np, hipStream_t s) {
 
 // np problems (1 or 2) of the same K and N in one launch, problem 0's tiles
 // dispatched first
-template <int WT, bool GU, bool SPLIT>
+template <int WT, bool GU, bool A16>
 hipError_t launch_mf_nf(const FfnGemmArgs* a, int np, int BM, int NF, hipStream_t s) {
   if (np < 1 || np > 2) return hipErrorInvalidValue;
 #define MOE_CASE(MFv, NFv) \
-  if (BM == 16 * MFv && NF == NFv) return launch_one<WT, MFv, NFv, GU, SPLIT>(a, np, s);
+  if (BM == 16 * MFv && NF == NFv) return launch_one<WT, MFv, NFv, GU, A16>(a, np, s);
   if constexpr (WT == W_F32) {
     MOE_CASE(1, 1) MOE_CASE(1, 2) MOE_CASE(2, 1) MOE_CASE(2, 2)
   } else if constexpr (WT == W_I4) {

@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 enum WType { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
 
@@ -300,7 +301,7 @@ struct FfnGemmArgs {
   int a_rows;                // rows of A as addressed (a_rows * K elements must stay below 4 GiB)
   int act;                   // 0 SiLU, 1 GELU (gate/up only)
   int out_f32;               // 1: store the output as fp32 whatever the operand type
-  int out_f16;               // 1 (with out_f32 0, down projections only): store the output as fp16
+  int out_f16;               // 1 (with out_f32 0): store the output as fp16
   void* ev_start;            // hipEvent_t pair carried by the launch itself (NULL: none):
   void* ev_stop;             //   they time exactly this kernel and add no packet to the stream
 };
@@ -308,14 +309,14 @@ struct FfnGemmArgs {
 struct FfnPlan {
   int BM;                    // rows per tile (16 * MF)
   int NF_up, NF_down;        // 16-col fragments per wave
-  bool split_z;              // z kept in fp32, down projection on its hi/lo bf16 parts
+  bool z_f16;                // INT4: z stored in fp16, the down projection on the fp16 MFMA
   int BM_down;               // rows per tile of the down GEMM when it differs (its own m-tile table), else 0
 };
 // avg_rows: expected rows per group (local expert); groups: number of groups.
 FfnPlan plan_ffn(double avg_rows, int groups, int d, int h, int w_type);
 int ffn_max_mtiles(int E_loc, int rows_max, int BM);
-// split: (down projection only) A is fp32 and is multiplied as hi + lo bf16 parts.
-hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool split, int BM,
+// z16: (INT4 down projections only) A is fp16 and is multiplied on the fp16 MFMA.
+hipError_t launch_ffn_gemm(const FfnGemmArgs& a, bool gateup, int w_type, bool z16, int BM,
                            int NF, hipStream_t s);
 // Two problems of the same kind, K and N on the narrow kernel (fp32 or bf16
 // weights, BM rows per tile), problem 0's tiles dispatched first; a0's events,
