@@ -7,8 +7,8 @@
 // MoEEvolve "Architecture" / kieve-moe "Features": SwiGLU / GeGLU experts):
 //   z[r, n] = act(sum_k a[r,k] Wg[e,n,k]) * (sum_k a[r,k] Wu[e,n,k]),
 //   W[n, k] = scale[n, k / 128] * code[n, k]
-// for every grouped row r of local expert e; z is written in fp32 (the down
-// projection takes it as two bf16 planes).
+// for every grouped row r of local expert e; z is written in fp16 (as INT4
+// layers keep it for their down projection) or in fp32.
 //
 // Why a second INT4 kernel.  A share with a few dozen rows per expert is a
 // weight stream: its time is the time to move the packed codes.  Loaded into
