@@ -324,7 +324,7 @@ size_t carve_layer(const moe_layer_desc* L, void* ws, LayerBufs* b) {
 // ---------------------------------------------------------------- backward
 struct BwdBufs {
   int32_t *ids, *offsets, *mtile, *sorted_pair, *pair_pos, *counts, *mtile_rc, *cnt;
-  int4 *tiles, *tiles_rc;
+  int4 *tiles, *tiles_rc, *chunks, *chunk_ext;
   float *tw, *Lraw, *Lw, *G, *U, *dZ, *dgate, *dXp, *Gs, *Us, *dZs, *dXs, *dL, *dXr, *part, *colpart;
   void *dGU, *ZW, *dGUs, *ZWs, *dLc, *stats;
 };
@@ -361,6 +361,12 @@ int tn_slices(int rows, int M, int N) {
   int S = (512 + tiles - 1) / tiles;
   S = std::min(S, std::max(1, rows / 256));
   return std::max(1, std::min(S, 64));
+}
+
+// Most grouped rows one local expert can hold: a token selects an expert at
+// most once, and the capacity (when > 0) caps it.
+inline int bwd_group_max(const moe_layer_desc* L) {
+  return L->capacity > 0 ? std::min(L->capacity, L->T) : L->T;
 }
 
 size_t carve_bwd(const moe_layer_desc* L, void* ws, BwdBufs* b) {
@@ -411,6 +417,19 @@ size_t carve_bwd(const moe_layer_desc* L, void* ws, BwdBufs* b) {
     part = std::max(part, (size_t)tn_slices(L->T, L->d, (int)hs) * d * hs);
     part = std::max(part, (size_t)tn_slices(L->T, 2 * (int)hs, L->d) * 2 * hs * d);
   }
+  // the routed weight gradients' row chunks (dWd: d x h, dWg and dWu: 2h x d
+  // per expert): their virtual groups and partial slots
+  size_t vmax = 0, xmax = 0;
+  const size_t Ms[2] = {d, 2 * h}, Ns[2] = {h, d};
+  for (int i = 0; i < 2; ++i) {
+    const int CH = tn_chunk_rows((int)rows, bwd_group_max(L), (int)Ms[i], (int)Ns[i]);
+    if (!CH) continue;
+    vmax = std::max(vmax, (size_t)L->E_loc + rows / CH);
+    xmax = std::max(xmax, rows / CH);
+    part = std::max(part, rows / CH * Ms[i] * Ns[i]);
+  }
+  b->chunks = c.take<int4>(vmax * sizeof(int4));
+  b->chunk_ext = c.take<int4>(xmax * sizeof(int4));
   b->part = c.take<float>(part * 4);
   b->colpart = c.take<float>(colsum_ws_floats(L->T, L->E) * 4);
   return c.used;
@@ -1020,6 +1039,21 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   auto run_tn = [&](const bwdg::TnArgs& a) -> hipError_t {
     return (bf && bwd_tn_wide_ok(a)) ? launch_bwd_tn_wide(a, E_loc, s) : launch_bwd_tn(bf, a, E_loc, s);
   };
+  // A routed weight gradient on the wide kernel whose groups may hold more
+  // rows than an even share of the launch: the groups are cut into row
+  // chunks (a device-built table), chunks past a group's first write partial
+  // slots, and those are added to the group's gradient in chunk order.
+  auto run_tn_routed = [&](bwdg::TnArgs a) -> hipError_t {
+    const int CH = (bf && bwd_tn_wide_ok(a)) ? tn_chunk_rows(rows, bwd_group_max(L), a.M, a.N) : 0;
+    if (!CH) return run_tn(a);
+    const int Vmax = E_loc + rows / CH, Xmax = rows / CH;
+    hipError_t e = launch_tn_chunk_table(E_loc, b.offsets, CH, Vmax, Xmax, b.chunks, b.chunk_ext, s);
+    if (e != hipSuccess) return e;
+    a.chunks = b.chunks;
+    a.part = b.part;
+    if ((e = launch_bwd_tn_wide(a, Vmax, s)) != hipSuccess) return e;
+    return launch_tn_chunk_add(Xmax, a.M, a.N, a.M1, a.C1, a.C2, a.ldc, a.c_stride, b.part, b.chunk_ext, s);
+  };
 
   // The shared expert's set-up, here because its fused gate/up launch (below)
   // can ride in the routed one.
@@ -1123,7 +1157,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     t.M = d;
     t.N = h;
     t.mtiles = (d + bwdg::kTnTile - 1) / bwdg::kTnTile;
-    MOE_HIP(run_tn(t));
+    MOE_HIP(run_tn_routed(t));
   }
   if (gr->dw_gate) {
     bwdg::TnArgs t{};
@@ -1143,7 +1177,7 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
     t.M = 2 * h;
     t.N = d;
     t.mtiles = (2 * h + bwdg::kTnTile - 1) / bwdg::kTnTile;
-    MOE_HIP(run_tn(t));
+    MOE_HIP(run_tn_routed(t));
   }
   n = bwdg::NnArgs{};
   n.A = b.dGU;

@@ -46,6 +46,11 @@ struct TnArgs {
   long long c_stride;
   int M, N;  // M % 8 == 0, N % 8 == 0
   int mtiles;
+  // (wide kernel only) virtual groups: blockIdx z takes chunks[z] = {group g
+  // (< 0: none), first row, end row, slot}; slot < 0 writes C_g as above,
+  // else the [M][N] block part + slot * M * N
+  const int4* chunks;
+  float* part;
 };
 
 
@@ -83,6 +88,24 @@ hipError_t launch_router_bwd(bool bf16, int T, int E, int Epad, int k, int renor
                              const int32_t* ids, const int32_t* pair_pos, const float* dgate,
                              const int32_t* count, float bal_scale, float* dL, void* dLc, float* dgates_out,
                              hipStream_t s);
+// Rows per chunk of a grouped weight gradient on the wide kernel (M x N per
+// group, at most rows_max rows in all, at most group_max in one group): a
+// group with more rows is cut into chunks of at most that many, so that no
+// tile runs much longer than an even share of the launch; 0 when no group
+// can need it.
+int tn_chunk_rows(int rows_max, int group_max, int M, int N);
+// Virtual groups for chunk size CH (tn_chunk_rows): chunks[v] = {e, first
+// row, end row, slot} for every chunk of every group e < E (slot -1 for a
+// group's first chunk, else its partial slot), {-1, 0, 0, -1} up to Vmax;
+// ext[i] = {first slot, number of slots, e, 0} for the i-th group with more
+// than one chunk, {0, 0, -1, 0} up to Xmax.  Vmax >= E + rows / CH and
+// Xmax >= rows / CH.
+hipError_t launch_tn_chunk_table(int E, const int32_t* offsets, int CH, int Vmax, int Xmax, int4* chunks,
+                                 int4* ext, hipStream_t s);
+// C_e += the partial slots of each listed group e, in slot order (layout as
+// TnArgs C1, C2, M1).
+hipError_t launch_tn_chunk_add(int Xmax, int M, int N, int M1, float* C1, float* C2, int ldc, long long c_stride,
+                               const float* part, const int4* ext, hipStream_t s);
 // C = sum over S slices of part[z][M][N] in slice order (rows m >= M1 to C2).
 hipError_t launch_sum_slices(int S, int M, int N, int M1, const float* part, float* C1, float* C2, int ldc,
                              hipStream_t s);

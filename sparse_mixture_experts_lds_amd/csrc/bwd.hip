@@ -195,6 +195,68 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(int S, int M, int N, in
     C2[(size_t)(m - M1) * ldc + n] = acc;
 }
 
+// Virtual groups of a chunked weight gradient (one workgroup; E <= 1024):
+// c_e = max(1, ceil(n_e / CH)) chunks per group, numbered in group order by
+// an inclusive scan; the j-th chunk of group e (j >= 1) takes partial slot
+// v0_e - e + j - 1 (the chunks past the first of the groups before it).  The
+// groups with more than one chunk are listed in group order (a second scan).
+__global__ __launch_bounds__(1024) void tn_chunk_table_kernel(int E, const int32_t* __restrict__ offsets, int CH,
+                                                              int Vmax, int Xmax, int4* __restrict__ chunks,
+                                                              int4* __restrict__ ext) {
+  __shared__ int scan[2][1024];
+  const int e = threadIdx.x;
+  int n = 0, c = 0;
+  if (e < E) {
+    n = offsets[e + 1] - offsets[e];
+    c = n > CH ? (n + CH - 1) / CH : 1;
+  }
+  scan[0][e] = c;
+  scan[1][e] = c > 1 ? 1 : 0;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? scan[0][e - off] : 0;
+    const int w = e >= off ? scan[1][e - off] : 0;
+    __syncthreads();
+    scan[0][e] += v;
+    scan[1][e] += w;
+    __syncthreads();
+  }
+  const int v0 = scan[0][e] - c;
+  const int V = scan[0][1023], X = scan[1][1023];
+  if (e < E) {
+    const int r0 = offsets[e];
+    for (int j = 0; j < c && v0 + j < Vmax; ++j)
+      chunks[v0 + j] = int4{e, r0 + j * CH, min(r0 + (j + 1) * CH, r0 + n), j == 0 ? -1 : v0 - e + j - 1};
+    const int xi = scan[1][e] - 1;
+    if (c > 1 && xi < Xmax) ext[xi] = int4{v0 - e, c - 1, e, 0};
+  }
+  for (int v = V + e; v < Vmax; v += 1024) chunks[v] = int4{-1, 0, 0, -1};
+  for (int i = X + e; i < Xmax; i += 1024) ext[i] = int4{0, 0, -1, 0};
+}
+
+// Workgroup (x, i) adds listed group i's partial slots, in slot order.
+__global__ __launch_bounds__(256) void tn_chunk_add_kernel(int M, int N, int M1, float* __restrict__ C1,
+                                                           float* __restrict__ C2, int ldc, long long c_stride,
+                                                           const float* __restrict__ part,
+                                                           const int4* __restrict__ ext) {
+  const int4 x = ext[blockIdx.y];
+  const int e = x.z;
+  if (e < 0 || x.y <= 0) return;
+  const size_t MN = (size_t)M * N;
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < MN; i += (size_t)gridDim.x * 1024) {
+    const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+    float* const dst = m < M1 ? C1 + (size_t)e * c_stride + (size_t)m * ldc + n
+                              : C2 + (size_t)e * c_stride + (size_t)(m - M1) * ldc + n;
+    f32x4 v = *reinterpret_cast<const f32x4*>(dst);
+    for (int j = 0; j < x.y; ++j) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(part + (size_t)(x.x + j) * MN + i);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] += p[t];
+    }
+    *reinterpret_cast<f32x4*>(dst) = v;
+  }
+}
+
 constexpr int kColRows = 64;  // rows per partial of the column sum
 
 __global__ __launch_bounds__(256) void colsum_part_kernel(int Tn, int E, const float* __restrict__ X,
@@ -393,6 +455,32 @@ hipError_t launch_sum_slices(int S, int M, int N, int M1, const float* part, flo
   const size_t n = (size_t)M * N;
   if (n == 0) return hipSuccess;
   sum_slices_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(S, M, N, M1, part, C1, C2, ldc);
+  return hipGetLastError();
+}
+
+int tn_chunk_rows(int rows_max, int group_max, int M, int N) {
+  // an even share of a launch's rows x tiles over the 256 CUs of an MI355X
+  const long long tiles = (long long)(M / bwdw::BT) * (N / bwdw::BT);
+  long long ch = ((long long)rows_max * tiles / 256 + 255) / 256 * 256;
+  if (ch < 2048) ch = 2048;
+  if (rows_max <= ch || group_max <= ch) return 0;
+  return (int)ch;
+}
+
+hipError_t launch_tn_chunk_table(int E, const int32_t* offsets, int CH, int Vmax, int Xmax, int4* chunks,
+                                 int4* ext, hipStream_t s) {
+  if (E <= 0 || E > 1024 || CH <= 0 || Vmax < E || Xmax < 1) return hipErrorInvalidValue;
+  tn_chunk_table_kernel<<<1, 1024, 0, s>>>(E, offsets, CH, Vmax, Xmax, chunks, ext);
+  return hipGetLastError();
+}
+
+hipError_t launch_tn_chunk_add(int Xmax, int M, int N, int M1, float* C1, float* C2, int ldc, long long c_stride,
+                               const float* part, const int4* ext, hipStream_t s) {
+  if (Xmax <= 0 || (size_t)M * N == 0) return hipSuccess;
+  if (N % 4 || ldc % 4) return hipErrorInvalidValue;
+  const size_t blocks = std::min<size_t>(((size_t)M * N + 1023) / 1024, 256);
+  tn_chunk_add_kernel<<<dim3((unsigned)blocks, (unsigned)Xmax), 256, 0, s>>>(M, N, M1, C1, C2, ldc, c_stride,
+                                                                            part, ext);
   return hipGetLastError();
 }
 

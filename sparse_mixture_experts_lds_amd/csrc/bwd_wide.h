@@ -272,8 +272,15 @@ __global__ __launch_bounds__(512) void wide_tn_kernel(bwdg::TnArgs a, int groups
   const int rem = R - z * (MT * NT);
   const int mt = rem / NT, nt = rem - (rem / NT) * NT;
   const int m0 = mt * BT, n0 = nt * BT;
-  int r0, r1;
-  if (a.offsets) {
+  int r0, r1, g = z, slot = -1;
+  if (a.chunks) {
+    const int4 ck = a.chunks[z];
+    g = __builtin_amdgcn_readfirstlane(ck.x);
+    if (g < 0) return;  // past the virtual groups
+    r0 = ck.y;
+    r1 = ck.z;
+    slot = __builtin_amdgcn_readfirstlane(ck.w);
+  } else if (a.offsets) {
     r0 = a.offsets[z];
     r1 = a.offsets[z + 1];
   } else {
@@ -352,8 +359,9 @@ __global__ __launch_bounds__(512) void wide_tn_kernel(bwdg::TnArgs a, int groups
   // an empty group still writes its (zero) gradient
   store_tile(&stg[0][0], acc, true, [&](int r) -> float* {
     const int m = m0 + r;
-    return m < a.M1 ? a.C1 + (size_t)z * a.c_stride + (size_t)m * a.ldc + n0
-                    : a.C2 + (size_t)z * a.c_stride + (size_t)(m - a.M1) * a.ldc + n0;
+    if (slot >= 0) return a.part + (size_t)slot * a.M * a.N + (size_t)m * a.N + n0;
+    return m < a.M1 ? a.C1 + (size_t)g * a.c_stride + (size_t)m * a.ldc + n0
+                    : a.C2 + (size_t)g * a.c_stride + (size_t)(m - a.M1) * a.ldc + n0;
   });
 }
 
