@@ -46,6 +46,12 @@
  *     and calls on different streams may run concurrently (except
  *     moe_permute_noalloc calls on one GPU, which share its scratch).
  *   - Arrays are dense and row-major; weight matrices are [out, in].
+ *     Activations, weights (packed INT4 codes included), expert and layer
+ *     outputs, their gradients and every workspace start at a multiple of 16
+ *     bytes; the other arrays (indices, offsets, gates, logits, biases, scales,
+ *     counts) at a multiple of 4.  hipMalloc and torch allocations satisfy
+ *     both; a call given an array that does not returns MOE_EINVAL (the
+ *     arrays a descriptor, trace or gradient struct points to included).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; no call synchronises the device or reads device memory
  *     on the host.

@@ -215,8 +215,26 @@ int layer_rows_max(const moe_layer_desc* L) {
   return (int)r;
 }
 
+// The kernels read and write activations, weights, expert and layer outputs,
+// their gradients and the workspaces with 16-byte accesses (row chunks, MFMA
+// fragments, loads straight into LDS), so those arrays must start at a
+// multiple of 16 bytes; the others (indices, offsets, gates, logits, biases,
+// scales, counts) at a multiple of 4.  hipMalloc and torch allocations are
+// 256-byte aligned; NULL passes.
+template <typename... P>
+inline bool all_a16(const P*... p) {
+  return ((reinterpret_cast<uintptr_t>(p) % 16 == 0) && ...);
+}
+template <typename... P>
+inline bool all_a4(const P*... p) {
+  return ((reinterpret_cast<uintptr_t>(p) % 4 == 0) && ...);
+}
+
 int check_layer(const moe_layer_desc* L) {
   if (!L) return MOE_EINVAL;
+  if (!all_a16(L->w_router, L->w_gate, L->w_up, L->w_down, L->ws_gate, L->ws_up, L->ws_down) ||
+      !all_a4(L->expert_map, L->expert_bias, L->s_gate, L->s_up, L->s_down))
+    return MOE_EINVAL;
   int rc = check_route_dims(L->T, L->E, L->k);
   if (rc) return rc;
   if (!act_ok(L->act) || !act_dtype_ok(L->act_dtype)) return MOE_EUNSUPPORTED;
@@ -567,6 +585,7 @@ int check_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* e
   if (!expert_map && E_loc != E) return MOE_EINVAL;
   if (!expert_offsets) return MOE_EINVAL;
   if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos)) return MOE_EINVAL;
+  if (!all_a4(topk_ids, expert_map, expert_offsets, sorted_pair, pair_pos) || !all_a16(x, x_perm)) return MOE_EINVAL;
   if (x_perm) {
     if (!act_dtype_ok(act_dtype)) return MOE_EUNSUPPORTED;
     if ((rc = check_width(d, act_dtype))) return rc;
@@ -604,6 +623,7 @@ int moe_route(int T, int d, int E, int k, int act_dtype, const void* x, const vo
     if (!x || !w_router) return MOE_EINVAL;
   }
   if (T > 0 && (!topk_ids || !topk_w)) return MOE_EINVAL;
+  if (!all_a16(x, w_router) || !all_a4(logits_in, expert_bias, topk_ids, topk_w, logits_out)) return MOE_EINVAL;
   MOE_HIP(launch_route(T, d, E, k, act_dtype == MOE_BF16, x, w_router, logits_in, expert_bias, renorm,
                        topk_ids, topk_w, logits_out, as_stream(stream)));
   return MOE_OK;
@@ -620,6 +640,8 @@ int moe_router_stats(int T, int E, int k, const float* logits, const float* expe
   int rc = check_route_dims(T, E, k);
   if (rc) return rc;
   if (T > 0 && (!logits || !topk_ids)) return MOE_EINVAL;
+  if (!all_a4(logits, expert_bias, topk_ids, expert_counts, prob_mean, balance_loss) || !all_a16(ws))
+    return MOE_EINVAL;
   const size_t need = router_stats_ws_bytes(T, E);
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (need > 0 && !ws) return MOE_EINVAL;
@@ -660,6 +682,7 @@ int moe_route_tree(int T, int d, int E, int k, int branch, int levels, int act_d
   if (rc) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !w_tree || !topk_ids || !topk_w || !ws) return MOE_EINVAL;
+  if (!all_a16(x, w_tree, ws) || !all_a4(topk_ids, topk_w)) return MOE_EINVAL;
   if (ws_bytes < tree_ws_bytes(T, d, k, branch, levels, act_dtype == MOE_BF16, sh)) return MOE_EWORKSPACE;
   MOE_HIP(launch_route_tree(T, d, E, k, branch, levels, act_dtype == MOE_BF16, x, w_tree, renorm, topk_ids, topk_w,
                             ws, as_stream(stream)));
@@ -679,7 +702,7 @@ int moe_permute(int T, int k, int E, const int32_t* topk_ids, const int32_t* exp
                                x, d, act_dtype, x_perm);
   if (rc) return rc;
   if (ws_bytes < moe_permute_workspace_bytes(T, k, E_loc)) return MOE_EWORKSPACE;
-  if (T > 0 && !ws) return MOE_EINVAL;
+  if ((T > 0 && !ws) || !all_a16(ws)) return MOE_EINVAL;
   hipStream_t s = as_stream(stream);
   MOE_HIP(launch_permute(T, k, E, topk_ids, expert_map, E_loc, capacity, 16, expert_offsets, nullptr, nullptr,
                          sorted_pair, pair_pos, static_cast<int32_t*>(ws), s));
@@ -731,6 +754,9 @@ int moe_dispatch_owners(int T, int k, int E, int n_owners, int placement, int ca
   }
   if (ws_bytes < moe_dispatch_owners_workspace_bytes(T, k, E)) return MOE_EWORKSPACE;
   if (!ws) return MOE_EINVAL;
+  if (!all_a4(topk_ids, owner_offsets, recv_offsets, expert_offsets, sorted_pair, pair_pos) ||
+      !all_a16(x, x_send, ws))
+    return MOE_EINVAL;
   Carver c(ws);
   int32_t* map = c.take<int32_t>((size_t)E * 4);
   int32_t* eo_ws = c.take<int32_t>((size_t)(E + 1) * 4);
@@ -765,6 +791,8 @@ int moe_expert_ffn(int E_loc, int rows_max, int d, int h, int act, int act_dtype
   if (!w_gate || !w_up || !w_down) return MOE_EINVAL;
   if (w_dtype == MOE_I4G128 && (!s_gate || !s_up || !s_down)) return MOE_EINVAL;
   if (rows_max > 0 && (!x_perm || !y_perm)) return MOE_EINVAL;
+  if (!all_a16(x_perm, w_gate, w_up, w_down, y_perm, ws) || !all_a4(expert_offsets, s_gate, s_up, s_down))
+    return MOE_EINVAL;
   // the grouped GEMMs address activation rows with 32-bit byte offsets
   if ((size_t)rows_max * d * 4 > 0xFFFFFFFFull || (size_t)rows_max * h * 4 > 0xFFFFFFFFull) return MOE_EUNSUPPORTED;
   if (ws_bytes < moe_expert_ffn_workspace_bytes(E_loc, rows_max, d, h, act_dtype)) return MOE_EWORKSPACE;
@@ -794,6 +822,7 @@ int moe_combine(int T, int k, int d, int act_dtype, const void* y_perm, const in
   int rc;
   if ((rc = check_width(d, act_dtype))) return rc;
   if (T > 0 && (!y_perm || !pair_pos || !topk_w || !out)) return MOE_EINVAL;
+  if (!all_a16(y_perm, shared_y, out) || !all_a4(pair_pos, topk_w)) return MOE_EINVAL;
   MOE_HIP(launch_combine(T, k, d, act_dtype == MOE_BF16, Y_OUT, y_perm, pair_pos, topk_w,
                          shared_y, out, as_stream(stream)));
   return MOE_OK;
@@ -831,6 +860,10 @@ int moe_layer_fwd(const moe_layer_desc* L, const void* x, const float* logits_in
   if (rc) return rc;
   if (!logits_in && !L->w_router) return MOE_EINVAL;
   if (L->T > 0 && (!x || !out)) return MOE_EINVAL;
+  if (!all_a16(x, out, ws) || !all_a4(logits_in)) return MOE_EINVAL;
+  if (trace && !all_a4(trace->logits, trace->topk_ids, trace->topk_w, trace->expert_offsets, trace->pair_pos,
+                       trace->expert_counts, trace->prob_mean, trace->balance_loss))
+    return MOE_EINVAL;
   const size_t need = moe_layer_workspace_bytes(L);
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (L->T == 0) return MOE_OK;
@@ -985,6 +1018,10 @@ int moe_layer_bwd(const moe_layer_desc* L, const void* x, const float* logits_in
   if (gr->dw_router && !L->w_router) return MOE_EINVAL;
   if (gr->dbias && !L->expert_bias) return MOE_EINVAL;
   if (!(balance == balance)) return MOE_EINVAL;  // NaN
+  if (!all_a16(x, dout, ws, gr->dx, gr->dw_router, gr->dw_gate, gr->dw_up, gr->dw_down, gr->dws_gate, gr->dws_up,
+               gr->dws_down) ||
+      !all_a4(logits_in, gr->dlogits, gr->dbias, gr->dgates))
+    return MOE_EINVAL;
   const size_t need = moe_layer_bwd_workspace_bytes(L);
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (L->T == 0) return MOE_OK;
@@ -1275,6 +1312,7 @@ int moe_quantize_int4(int rows, int K, const float* w, uint8_t* packed, uint16_t
   if (rows < 0 || K <= 0) return MOE_EINVAL;
   if (K % kI4Group) return MOE_EUNSUPPORTED;
   if (rows > 0 && (!w || !packed || !scales)) return MOE_EINVAL;
+  if (!all_a4(w, packed, scales)) return MOE_EINVAL;
   MOE_HIP(launch_quantize_int4(rows, K, w, packed, scales, as_stream(stream)));
   return MOE_OK;
 }

@@ -68,6 +68,24 @@ def test_argument_errors_before_launch():
     assert lib.moe_quantize_int4(4, 200, P, P, P, None) == _lib.MOE_EUNSUPPORTED
 
 
+def test_misaligned_arrays_rejected_before_launch():
+    lib = moe.load()
+    # Q is a multiple of 4 bytes, not of 16; R of neither
+    P, Q, R = ctypes.c_void_p(16), ctypes.c_void_p(20), ctypes.c_void_p(18)
+    assert lib.moe_route(4, 64, 8, 2, 1, Q, P, None, None, 1, P, P, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_route(4, 64, 8, 2, 1, P, P, None, None, 1, R, P, None, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine(4, 2, 128, 1, Q, P, P, None, P, None) == _lib.MOE_EINVAL
+    assert lib.moe_combine(4, 2, 128, 1, P, R, P, None, P, None) == _lib.MOE_EINVAL
+    nb = lib.moe_expert_ffn_workspace_bytes(4, 64, 256, 128, 1)
+    assert lib.moe_expert_ffn(4, 64, 256, 128, 0, 1, 1, P, P, P, P, Q, None, None, None, P, P, nb, None) == _lib.MOE_EINVAL
+    assert lib.moe_quantize_int4(4, 256, P, R, P, None) == _lib.MOE_EINVAL
+    nl = lib.moe_layer_workspace_bytes(ctypes.byref(_desc()))
+    assert lib.moe_layer_fwd(ctypes.byref(_desc()), Q, None, P, None, P, nl, None) == _lib.MOE_EINVAL
+    bad = _desc()
+    bad.w_gate = 24
+    assert lib.moe_layer_fwd(ctypes.byref(bad), P, None, P, None, P, nl, None) == _lib.MOE_EINVAL
+
+
 def _desc(**over):
     L = _lib.LayerDesc()
     base = dict(T=64, d=128, E=8, k=2, h=128, act=0, act_dtype=1, w_dtype=1, renorm=1, capacity=0,
