@@ -28,6 +28,7 @@
 // logits and selects its tokens' experts in the same launch.
 #include <algorithm>
 
+#include "ffn_wide.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -546,25 +547,50 @@ hipError_t router_lds_nf(int T, int d, int E, int nsplit, const void* x, const v
   return hipGetLastError();
 }
 
-// Router logits and selection in one pass (bf16 x and router weight, E <= 64
-// NFW experts): a workgroup takes kRfTok tokens and every expert.  Its x rows
-// go to LDS once.  Wave w owns the 16-expert fragments w, w + 4, w + 8, ... and
-// streams their router rows from memory straight into MFMA B fragments, kRfPf
-// 32-input steps ahead of the MFMAs.  The tile's logits (+ bias) land in LDS;
-// 16-lane groups then pick each token's top k from there, and the logits are
-// copied out in row order when asked for.  Against a logits GEMM followed by a
-// selection pass, the logits make no round trip through memory and one launch
-// goes; in exchange every workgroup takes in the whole router weight, so the
-// path is taken for few experts only.  Measured on MI355X (cold cache, bench
-// timing of the routing step): 16384 tokens x 768 inputs x 32 experts, 19.8
-// against 22.9 us for the LDS-resident logits kernel plus selection; 8192 x
-// 768 x 192, 25.7 against 25.0 us for the grouped GEMM with 64-token tiles
-// plus selection, where each CU takes in 344 KB against 295 KB.
-constexpr int kRfTok = 32;     // tokens per workgroup: two 16-row A fragments
-constexpr int kRfPf = 4;       // 32-input steps of router rows in flight per wave
-constexpr int kRfMaxD = 1024;  // longest x row the LDS tile holds
+// Router logits and selection in one pass (bf16 x and router weight, E <= 256
+// in 64-expert slices, NFW = ceil(E / 64)): a workgroup takes kRfTok tokens
+// and every expert.  The tile's x rows and the router rows go through LDS in
+// 64-input k-blocks, on a ring of NS stages filled by loads that write LDS
+// directly (128-byte row pieces, 16-byte chunks XOR-swizzled by (row / 2) % 8
+// so that the sixteen rows one LDS read serves fall on distinct banks), NS - 1
+// k-blocks ahead of the MFMAs, one barrier per k-block.  Wave w owns the
+// 16-expert fragments w, w + 4, w + 8, ... of every k-block.  The tile's
+// logits (+ bias) then land in LDS (in the ring's memory); 16-lane groups
+// pick each token's top k from there, and the logits are copied out in row
+// order when asked for.  Against a logits GEMM followed by a selection pass
+// the logits make no round trip through memory and one launch goes; every
+// workgroup takes in the whole router weight, which the L2 serves.  Measured
+// on MI355X (cold cache, bench timing of the routing step): 8192 tokens x 768
+// inputs x 192 experts, 19.9 against 24.5 us for the grouped logits GEMM plus
+// selection (each CU takes in 343 KB, at about 25 GB/s); 16384 x 768 x 32,
+// 16.2 against 18.9 us for the previous one-launch kernel, which streamed the
+// router rows from memory straight into MFMA registers.  Starting each
+// workgroup's k-loop at a different k-block (so that the CUs of an XCD ask
+// for different slices of the weight first) changed nothing measurable.
+constexpr int kRfTok = 32;      // tokens per workgroup: two 16-row A fragments
+constexpr int kRfKB = 64;       // inputs per k-block (two 32-deep MFMA steps)
 constexpr int kRfMinTok = 4096;
-constexpr int kRfMaxE = 64;
+constexpr int kRfMaxE = 256;
+constexpr int kRfMaxD = 16384;
+constexpr int kRfRing = 144 * 1024;  // LDS bytes the ring may take
+
+template <int NFW>
+struct RfGeo {
+  static constexpr int XB = kRfTok * kRfKB * 2;     // token rows of one k-block (4 KB)
+  static constexpr int WB = 64 * NFW * kRfKB * 2;   // router rows of one k-block
+  static constexpr int STAGE = XB + WB;
+  static constexpr int NS = kRfRing / STAGE < 6 ? kRfRing / STAGE : 6;
+  static constexpr int LOADS = STAGE / 1024;        // 1 KB loads per stage
+  static constexpr int LPW = LOADS / 4;             // per wave
+  static_assert(LOADS % 4 == 0 && NS >= 3 && (NS - 2) * LPW < 64, "ring geometry");
+};
+
+// s_waitcnt vmcnt(n) for n < 64 (expcnt and lgkmcnt left alone)
+template <int n>
+__device__ __forceinline__ void rf_wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
 
 // STATS: the workgroup also writes one partial row of the router by-products.
 template <int NFW, bool STATS>
@@ -574,103 +600,104 @@ __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, 
                                                            const float* __restrict__ bias, int renorm,
                                                            int32_t* __restrict__ ids, float* __restrict__ tw,
                                                            float* __restrict__ logits_out, StatsPart sp) {
+  using G = RfGeo<NFW>;
+  constexpr int NS = G::NS, LPW = G::LPW, ROWB = kRfKB * 2;
   constexpr int ES = 64 * NFW + 4;  // logits row stride in LDS (floats)
-  __shared__ __attribute__((aligned(16))) unsigned char Xl[kRfTok * (2 * kRfMaxD + 16)];
-  __shared__ float Ls[kRfTok * ES];
-  // (STATS) the by-product sums take the x tile's memory once the logits are in
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS * G::STAGE];
+  // after the k-loop the ring holds the logits tile, then (STATS) the by-product sums
   using SL = StatsLds<16, 64 * NFW>;
-  static_assert(sizeof(SL) <= sizeof(Xl), "the by-product sums fit the x tile");
-  SL& sl = *reinterpret_cast<SL*>(Xl);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int LS_BYTES = (kRfTok * ES * 4 + 15) / 16 * 16;
+  static_assert(LS_BYTES + sizeof(SL) <= sizeof(ring), "logits and by-product sums fit the ring");
+  float* const Ls = reinterpret_cast<float*>(ring);
+  SL& sl = *reinterpret_cast<SL*>(ring + LS_BYTES);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * kRfTok;
-  const int XRS = 2 * d + 16;  // x row stride in LDS (bytes); the pad spreads rows over the banks
-  const int cpr = d / 8;       // 16-byte chunks per x row
-  const int nk = d / 32;       // MFMA input steps (a multiple of kRfPf)
+  const int nkb = d / kRfKB;
 
-  // x rows of the tile (rows past T re-read row T-1; their logits are not
-  // used).  Straight-line code: a chunk index past the tile repeats the last
-  // chunk, which writes the same bytes to the same place again.
-  constexpr int XCH = kRfTok * kRfMaxD / 8 / 256;
-  const int nch = kRfTok * cpr;
-  u32x4 xv[XCH];
+  // The wave's LPW loads of a stage: load l = wave * LPW + j fills 8 rows
+  // (1 KB): token rows 8 l .. for l < 4, else router rows 8 (l - 4) ..;
+  // lane takes row + lane / 8 and stores chunk lane % 8 of it, which holds
+  // logical chunk (lane % 8) ^ ((row / 2) % 8).  Token rows past T re-read row
+  // T - 1 and router rows past E row E - 1 (their logits are not used).
+  const unsigned char* const xb = reinterpret_cast<const unsigned char*>(x) + (size_t)t0 * d * 2;
+  const unsigned char* const wbp = reinterpret_cast<const unsigned char*>(w);
+  uint32_t off[LPW];
 #pragma unroll
-  for (int u = 0; u < XCH; ++u) {
-    const int c = min((int)threadIdx.x + 256 * u, nch - 1);
-    const int r = c / cpr;
-    xv[u] = *reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + r, T - 1) * d + 8 * (c - r * cpr));
+  for (int j = 0; j < LPW; ++j) {
+    const int l = wave * LPW + j;
+    const int r = (l < 4 ? 8 * l : 8 * (l - 4)) + (lane >> 3);
+    const int src = l < 4 ? min(r, T - 1 - t0) : min(r, E - 1);
+    off[j] = (uint32_t)src * (uint32_t)(d * 2) + (uint32_t)((((lane & 7) ^ ((r >> 1) & 7))) * 16);
   }
-  // the first kRfPf steps of this wave's router rows (rows past E re-read row E-1)
-  const uint16_t* wp[NFW];
-  u32x4 wb[kRfPf][NFW];
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)&ring[0]);
+  auto issue = [&](int st, int kb) {
 #pragma unroll
-  for (int i = 0; i < NFW; ++i) wp[i] = w + (size_t)min(16 * (wave + 4 * i) + row, E - 1) * d + 8 * q;
-#pragma unroll
-  for (int s = 0; s < kRfPf; ++s)
-#pragma unroll
-    for (int i = 0; i < NFW; ++i) wb[s][i] = *reinterpret_cast<const u32x4*>(wp[i] + 32 * s);
-#pragma unroll
-  for (int u = 0; u < XCH; ++u) {
-    const int c = min((int)threadIdx.x + 256 * u, nch - 1);
-    const int r = c / cpr;
-    *reinterpret_cast<u32x4*>(Xl + r * XRS + 16 * (c - r * cpr)) = xv[u];
-  }
-  __syncthreads();
-
-  // Waves whose fragments lie past E run on row E-1 as well (their columns are
-  // not read); keeping every wave on one straight path keeps the loads where
-  // they are written.
-  {
-    f32x4 acc[2][NFW];
-#pragma unroll
-    for (int i = 0; i < NFW; ++i) acc[0][i] = acc[1][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A fragment: token row (+16 for the second), inputs 8 q .. 8 q + 7 of the step
-    const unsigned char* xa = Xl + row * XRS + 16 * q;
-    int kb = 0;
-    do {  // nk >= kRfPf; no guard branch for the first router loads to sink behind
-#pragma unroll
-      for (int s = 0; s < kRfPf; ++s) {
-        const int kk = kb + s;
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + 64 * kk));
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xa + 16 * XRS + 64 * kk));
-#pragma unroll
-        for (int i = 0; i < NFW; ++i) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, wb[s][i]);
-          acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][i], 0, 0, 0);
-          acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][i], 0, 0, 0);
-        }
-        // refill the slot kRfPf steps ahead (the last steps re-read a valid one)
-        const int kn = min(kk + kRfPf, nk - 1);
-#pragma unroll
-        for (int i = 0; i < NFW; ++i) wb[s][i] = *reinterpret_cast<const u32x4*>(wp[i] + 32 * kn);
-        // keep each step's refill behind its MFMAs, so kRfPf - 1 steps of
-        // loads stay in flight throughout the loop
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      kb += kRfPf;
-    } while (kb < nk);
-    // D: lane holds expert 16 f + row for tokens 16 m + 4 q + r
-#pragma unroll
-    for (int i = 0; i < NFW; ++i) {
-      const int e = 16 * (wave + 4 * i) + row;
-      const float be = (bias && e < E) ? bias[e] : 0.f;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ls[(16 * m + 4 * q + r) * ES + e] = acc[m][i][r] + be;
+    for (int j = 0; j < LPW; ++j) {
+      const int l = wave * LPW + j;
+      // x rows take the stage's first 4 KB, router rows follow: load l lands at l KB
+      const uint32_t dst = lds0 + (uint32_t)(st * G::STAGE + l * 1024);
+      ffn_wide::dma16(l < 4 ? xb : wbp, off[j] + (uint32_t)(kb * ROWB), dst);
     }
+  };
+
+  // fragment reads: lane (row, q) of step s needs logical chunk 4 s + q of its
+  // row; fragment rows start at multiples of 16, so the swizzle is (row / 2) % 8
+  f32x4 acc[2][NFW];
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) acc[0][i] = acc[1][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nkb) issue(p, p);
+  int st = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    // k-block kb landed for this wave (later ones may stay in flight), then
+    // for every wave; the stage k-block kb - 1 used is free again
+    if (kb + NS - 2 < nkb) rf_wait_vm<(NS - 2) * LPW>();
+    else rf_wait_vm<0>();
+    ffn_wide::lds_barrier();
+    if (kb + NS - 1 < nkb) issue(st == 0 ? NS - 1 : st - 1, kb + NS - 1);
+    const unsigned char* const S = ring + st * G::STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int co = (((4 * s + q) ^ ((row >> 1) & 7))) * 16;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + row * ROWB + co));
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + (16 + row) * ROWB + co));
+#pragma unroll
+      for (int i = 0; i < NFW; ++i) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(S + G::XB + (16 * (wave + 4 * i) + row) * ROWB + co));
+        acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][i], 0, 0, 0);
+        acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][i], 0, 0, 0);
+      }
+    }
+    st = st == NS - 1 ? 0 : st + 1;
   }
+  // every wave is past its reads of the ring (and every load has landed: the
+  // last k-block waited for all of them) before the logits overwrite it
+  __syncthreads();
+  // D: lane holds expert 16 f + row for tokens 16 m + 4 q + r
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) {
+    const int e = 16 * (wave + 4 * i) + row;
+    const float be = (bias && e < E) ? bias[e] : 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ls[(16 * m + 4 * q + r) * ES + e] = acc[m][i][r] + be;
+  }
+  if constexpr (STATS)
+    for (int e = threadIdx.x; e < 64 * NFW; e += 256) sl.cnt[e] = 0;
   __syncthreads();
 
-  if constexpr (STATS) {
-    for (int e = threadIdx.x; e < 64 * NFW; e += 256) sl.cnt[e] = 0;
-    __syncthreads();
-  }
   // selection: 16 groups of 16 lanes, two tokens each
   const int gl = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  double acc[4 * NFW];
+  double pacc[4 * NFW];
 #pragma unroll
-  for (int i = 0; i < 4 * NFW; ++i) acc[i] = 0.0;
+  for (int i = 0; i < 4 * NFW; ++i) pacc[i] = 0.0;
 #pragma unroll
   for (int hh = 0; hh < kRfTok / 16; ++hh) {
     const int r = grp + 16 * hh, t = t0 + r;
@@ -686,14 +713,14 @@ __global__ __launch_bounds__(256) void router_fused_kernel(int T, int d, int E, 
         int pick;
         select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k, p, &pick);
 #pragma unroll
-        for (int i = 0; i < 4 * NFW; ++i) acc[i] += (double)p[i];
+        for (int i = 0; i < 4 * NFW; ++i) pacc[i] += (double)p[i];
         if (pick >= 0) atomicAdd(&sl.cnt[pick], 1);
       } else {
         select_group<16, 4 * NFW>(v, gl, E, k, renorm, ids + (size_t)t * k, tw + (size_t)t * k);
       }
     }
   }
-  if constexpr (STATS) stats_flush<16, 4 * NFW>(sl, acc, gl, grp, E, sp);
+  if constexpr (STATS) stats_flush<16, 4 * NFW>(sl, pacc, gl, grp, E, sp);
   if (logits_out) {
     const int n = min(kRfTok, T - t0) * E;
     for (int c = threadIdx.x; c < n; c += 256) {
@@ -718,7 +745,6 @@ hipError_t router_fused_nf(int T, int d, int E, int k, const void* x, const void
                                                          logits_out, sp);
   return hipGetLastError();
 }
-
 }  // namespace
 
 hipError_t launch_route(int T, int d, int E, int k, bool bf16, const void* x, const void* wr,
@@ -828,17 +854,22 @@ hipError_t launch_router_logits(int T, int d, int E, bool bf16, const void* x, c
 }
 
 bool router_fused_ok(int T, int d, int E, int k, bool bf16) {
-  return bf16 && T >= kRfMinTok && E >= 1 && E <= kRfMaxE && k >= 1 && k <= 16 && d >= 32 * kRfPf &&
-         d % (32 * kRfPf) == 0 && d <= kRfMaxD;
+  return bf16 && T >= kRfMinTok && E >= 1 && E <= kRfMaxE && k >= 1 && k <= 16 && d >= kRfKB &&
+         d % kRfKB == 0 && d <= kRfMaxD;
 }
 
 hipError_t launch_router_fused(int T, int d, int E, int k, const void* x, const void* wr, const float* bias,
                                int renorm, int32_t* ids, float* tw, float* logits_out, hipStream_t s,
                                const StatsPart* stats) {
   if (!router_fused_ok(T, d, E, k, true)) return hipErrorInvalidValue;
-  static_assert(kRfMaxE <= 64, "one 16-expert fragment per wave");
   const StatsPart sp = stats ? *stats : StatsPart{};
-  return router_fused_nf<1>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, sp, s);
+  const int nf = (E + 63) / 64;
+#define MOE_CALL(NFv) router_fused_nf<NFv>(T, d, E, k, x, wr, bias, renorm, ids, tw, logits_out, sp, s)
+  if (nf <= 1) return MOE_CALL(1);
+  if (nf <= 2) return MOE_CALL(2);
+  if (nf <= 3) return MOE_CALL(3);
+  return MOE_CALL(4);
+#undef MOE_CALL
 }
 
 int select_stats_rows(int T, int E, int k, bool fused) {

@@ -245,15 +245,16 @@ def test_route_without_logits_buffer(E, k, T):
     assert np.abs(tw.cpu().numpy() - orc.gates(Lo, ids, True)).max() <= 1e-5
 
 
-# bf16, T >= 4096, d a multiple of 128 up to 1024, E <= 64, k <= 16: logits
-# and selection come from one launch (32 tokens and every expert per
-# workgroup).  Cases: ragged last workgroup, waves holding no expert (E = 32,
-# E = 7), the longest row (1024) with k = 16, the shortest (128).  The
-# E = 160 .. 256 cases at the same sizes take the grouped logits GEMM and the
-# selection kernel.
+# bf16, T >= 4096, d a multiple of 64, E <= 256, k <= 16: logits and
+# selection come from one launch (32 tokens and every expert per workgroup,
+# one to four 64-expert slices).  Cases: ragged last workgroup, waves holding
+# no expert (E = 32, E = 7), each slice count with a ragged last slice (E =
+# 65, 100, 129, 160, 200, 256), one k-block (d = 64), fewer k-blocks than the
+# ring has stages (d = 128, 192), long rows (1024, 2048), k = 16, T = 4096.
 @pytest.mark.parametrize("E,k,d,T", [(32, 2, 768, 16385), (7, 3, 512, 4100), (64, 1, 128, 5000),
                                      (48, 16, 1024, 4097), (192, 4, 768, 8192), (160, 16, 768, 4133),
-                                     (256, 8, 1024, 4097)])
+                                     (256, 8, 1024, 4097), (65, 2, 64, 4096), (100, 6, 192, 4111),
+                                     (129, 16, 320, 4129), (200, 4, 2048, 4103), (256, 1, 768, 8191)])
 def test_route_one_launch_path(E, k, d, T):
     moe = _moe()
     rng = np.random.default_rng(1000 + E + k + d)
